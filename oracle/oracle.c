@@ -1,0 +1,601 @@
+/*
+ * oracle.c -- a plain, slow CPU implementation of batched paged attention over a
+ * block-pooled KV cache.
+ *
+ * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg may load this library.  The GPU library never links, calls or
+ * reads it, and the two share no source, header, table or helper.
+ *
+ * What each function follows (page title, then the section on that page):
+ *   - "ManagedPagedAttention.cs" (TensorSharp), class summary: tensor layouts
+ *     q/out [tokens, heads, dim], pools [blocks, blockSize, kvHeads, dim], and the
+ *     per-sequence metadata queryStartLoc / seqLens / blockTables / positions /
+ *     slotMapping with slot = blockId * blockSize + offset.
+ *   - same page, Forward: the q-head -> kv-head map h / (H / Hkv) and the visible
+ *     range (end = causal ? pos + 1 : seqLen, start = max(0, end - window) when the
+ *     window is positive).
+ *   - same page, WriteKvToPagedPool: the slot scatter, applied in token order.
+ *   - "Paged attention for decode in C", sections 2.1-2.2: position j lives in slot
+ *     j mod b of block table[j / b]; a decode query sits at position n - 1.
+ *     Section 2.6: validation before anything is written.  Section 3: the worked
+ *     example the tests pin against.
+ *   - "paged_attention_v2_pytorch.py", phase 1 and phase 2: per-partition
+ *     max logit, exp-sum and output, reduced by log-sum-exp weights.
+ *   - "cpu_mla_prefill.cpp", MlaPrefillAttention: the two-pass softmax (max, then
+ *     exp-sum and weighted sum), zero output and lse = -inf for an empty row, lse
+ *     in natural log.  MergeAttnStates: the merge and its two edge cases.
+ *
+ * Arithmetic: every stored element is decoded exactly to binary32 and then widened
+ * to binary64; every sum, exp and log is binary64.  Work is split over (sequence,
+ * kv-head) tasks with a fixed assignment, so results do not depend on the number of
+ * threads.  Outputs are written only after all checks pass.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_OK 0
+#define ORC_EINVAL 1
+#define ORC_ESHAPE 2
+#define ORC_EUNSUPPORTED 3
+
+#define ORC_F32 0
+#define ORC_F16 1
+#define ORC_BF16 2
+
+/* ------------------------------------------------------------------------- */
+/* Element decoding                                                           */
+/* ------------------------------------------------------------------------- */
+
+static int elem_bytes(int dtype) {
+  if (dtype == ORC_F32) return 4;
+  if (dtype == ORC_F16 || dtype == ORC_BF16) return 2;
+  return 0;
+}
+
+/* IEEE 754 binary16: sign bit, 5 exponent bits with bias 15, 10 fraction bits. */
+static double half_to_double(uint16_t h) {
+  int sign = h >> 15;
+  int e = (h >> 10) & 0x1f;
+  int f = h & 0x3ff;
+  double mag;
+  if (e == 0)
+    mag = ldexp((double)f, -24); /* zero or subnormal: f * 2^-24 */
+  else if (e == 31)
+    mag = f ? NAN : INFINITY;
+  else
+    mag = ldexp((double)(1024 + f), e - 25); /* (1 + f / 2^10) * 2^(e - 15) */
+  return sign ? -mag : mag;
+}
+
+/* bfloat16 is the high half of a binary32 word. */
+static double bf16_to_double(uint16_t h) {
+  uint32_t bits = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+static double load_elem(const void* base, int dtype, int64_t i) {
+  if (dtype == ORC_F32) return (double)((const float*)base)[i];
+  if (dtype == ORC_F16) return half_to_double(((const uint16_t*)base)[i]);
+  return bf16_to_double(((const uint16_t*)base)[i]);
+}
+
+/* Decode n stored elements to binary64 (exposed so the decoders can be pinned). */
+int orc_decode_elems(const void* src, int dtype, int64_t n, double* out) {
+  if (elem_bytes(dtype) == 0) return ORC_EUNSUPPORTED;
+  for (int64_t i = 0; i < n; ++i) out[i] = load_elem(src, dtype, i);
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* A fixed-assignment parallel loop: task i runs on thread i mod nthreads.    */
+/* ------------------------------------------------------------------------- */
+
+typedef void (*task_fn)(void* ctx, int64_t task);
+
+struct worker_arg {
+  task_fn fn;
+  void* ctx;
+  int64_t ntasks;
+  int nthreads;
+  int tid;
+};
+
+static void* worker_main(void* p) {
+  struct worker_arg* a = (struct worker_arg*)p;
+  for (int64_t i = a->tid; i < a->ntasks; i += a->nthreads) a->fn(a->ctx, i);
+  return NULL;
+}
+
+static void parallel_for(int64_t ntasks, int nthreads, task_fn fn, void* ctx) {
+  if (nthreads < 1) nthreads = 1;
+  if ((int64_t)nthreads > ntasks) nthreads = (int)(ntasks > 0 ? ntasks : 1);
+  if (nthreads == 1) {
+    for (int64_t i = 0; i < ntasks; ++i) fn(ctx, i);
+    return;
+  }
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  struct worker_arg* args = (struct worker_arg*)malloc(sizeof(struct worker_arg) * (size_t)nthreads);
+  for (int i = 0; i < nthreads; ++i) {
+    args[i].fn = fn;
+    args[i].ctx = ctx;
+    args[i].ntasks = ntasks;
+    args[i].nthreads = nthreads;
+    args[i].tid = i;
+    pthread_create(&th[i], NULL, worker_main, &args[i]);
+  }
+  for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+  free(args);
+  free(th);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Explicit gather through a block table                                      */
+/* ------------------------------------------------------------------------- */
+
+/* Copy positions 0..n-1 of one sequence, kv head g, out of a pool laid out as
+ * [num_blocks, block_size, num_kv_heads, head_dim] into dst[j * head_dim + d].
+ * Position j is in block table[j / block_size] at offset j % block_size.        */
+static void gather_head(const void* pool, int dtype, int block_size, int num_kv_heads,
+                        int head_dim, const int32_t* table, int64_t n, int g, double* dst) {
+  for (int64_t j = 0; j < n; ++j) {
+    int64_t block_id = table[j / block_size];
+    int64_t slot = block_id * block_size + j % block_size;
+    int64_t base = (slot * num_kv_heads + g) * head_dim;
+    for (int d = 0; d < head_dim; ++d) dst[j * head_dim + d] = load_elem(pool, dtype, base + d);
+  }
+}
+
+/* Gather every kv head: out[(j * num_kv_heads + g) * head_dim + d].
+ * The table must hold at least ceil(seq_len / block_size) ids below num_blocks. */
+int orc_gather(const void* pool, int dtype, int64_t num_blocks, int block_size, int num_kv_heads,
+               int head_dim, const int32_t* table, int32_t table_len, int32_t seq_len, double* out) {
+  if (elem_bytes(dtype) == 0) return ORC_EUNSUPPORTED;
+  if (block_size < 1 || num_kv_heads < 1 || head_dim < 1 || seq_len < 0) return ORC_EINVAL;
+  int64_t need = ((int64_t)seq_len + block_size - 1) / block_size;
+  if (need > table_len) return ORC_EINVAL;
+  for (int64_t i = 0; i < need; ++i)
+    if (table[i] < 0 || table[i] >= num_blocks) return ORC_EINVAL;
+  for (int64_t j = 0; j < seq_len; ++j) {
+    int64_t block_id = table[j / block_size];
+    int64_t slot = block_id * block_size + j % block_size;
+    for (int g = 0; g < num_kv_heads; ++g) {
+      int64_t base = (slot * num_kv_heads + g) * head_dim;
+      for (int d = 0; d < head_dim; ++d)
+        out[(j * num_kv_heads + g) * head_dim + d] = load_elem(pool, dtype, base + d);
+    }
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* The two-pass softmax over an explicitly gathered cache                    */
+/* ------------------------------------------------------------------------- */
+
+/* One query q[dk] against keys K[j * dk + d] and values V[j * dv + d] for the
+ * visible positions lo <= j < hi.  Pass 1 forms each score scale * <q, k_j> and the
+ * maximum m; pass 2 forms e_j = exp(s_j - m), l = sum e_j and a = sum e_j v_j.  The
+ * output is a * (1 / l).  An empty range gives a zero output, m = -inf, l = 0.
+ * s is scratch of at least hi - lo doubles.                                      */
+static void attend(const double* q, const double* K, const double* V, int dk, int dv, int64_t lo,
+                   int64_t hi, double scale, double* s, double* out, double* m_out, double* l_out) {
+  for (int d = 0; d < dv; ++d) out[d] = 0.0;
+  if (hi <= lo) {
+    *m_out = -INFINITY;
+    *l_out = 0.0;
+    return;
+  }
+  double m = -INFINITY;
+  for (int64_t j = lo; j < hi; ++j) {
+    double dot = 0.0;
+    for (int d = 0; d < dk; ++d) dot += q[d] * K[j * dk + d];
+    s[j - lo] = scale * dot;
+    if (s[j - lo] > m) m = s[j - lo];
+  }
+  double l = 0.0;
+  for (int64_t j = lo; j < hi; ++j) {
+    s[j - lo] = exp(s[j - lo] - m);
+    l += s[j - lo];
+  }
+  for (int64_t j = lo; j < hi; ++j)
+    for (int d = 0; d < dv; ++d) out[d] += s[j - lo] * V[j * dv + d];
+  double inv = 1.0 / l;
+  for (int d = 0; d < dv; ++d) out[d] *= inv;
+  *m_out = m;
+  *l_out = l;
+}
+
+static double lse_of(double m, double l) { return l > 0.0 ? m + log(l) : -INFINITY; }
+
+/* The core on caller-gathered arrays: row r has query q[r * dk ..], visible range
+ * [lo[r], hi[r]) of K / V (n_keys rows).  Writes out[r * dv ..] and lse[r].      */
+int orc_attend_gathered(const double* q, const double* K, const double* V, int64_t n_keys, int dk,
+                        int dv, const int64_t* lo, const int64_t* hi, int64_t num_rows, double scale,
+                        double* out, double* lse) {
+  for (int64_t r = 0; r < num_rows; ++r)
+    if (lo[r] < 0 || hi[r] > n_keys) return ORC_EINVAL;
+  int64_t widest = 1;
+  for (int64_t r = 0; r < num_rows; ++r)
+    if (hi[r] - lo[r] > widest) widest = hi[r] - lo[r];
+  double* s = (double*)malloc(sizeof(double) * (size_t)widest);
+  for (int64_t r = 0; r < num_rows; ++r) {
+    double m, l;
+    attend(q + r * dk, K, V, dk, dv, lo[r], hi[r], scale, s, out + r * dv, &m, &l);
+    lse[r] = lse_of(m, l);
+  }
+  free(s);
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Paged attention over many sequences                                         */
+/* ------------------------------------------------------------------------- */
+
+struct pool_desc {
+  const void* k;
+  const void* v;
+  int dtype;
+  int64_t num_blocks;
+  int block_size;
+  int num_kv_heads;
+  int dk;
+  int dv;
+};
+
+struct attn_job {
+  struct pool_desc pool;
+  const void* q;
+  int q_dtype;
+  int num_heads;
+  int64_t num_tokens;
+  const int32_t* query_start_loc;
+  int num_seqs;
+  const int32_t* seq_lens;
+  const int32_t* positions;
+  const int32_t* block_tables;
+  int max_blocks;
+  double scale;
+  int causal;
+  int sliding_window;
+  const uint8_t* row_mask; /* [T * H], nullable: compute every row */
+  double* out;             /* [T, H, dv] */
+  double* lse;             /* [H, T], nullable */
+  /* split-KV outputs (partition_size > 0) */
+  int partition_size;
+  int max_partitions;
+  double* max_logits; /* [S, H, max_partitions] */
+  double* exp_sums;   /* [S, H, max_partitions] */
+  double* tmp_out;    /* [S, H, max_partitions, dv] */
+};
+
+/* Visible positions of a query: [start, end) with end = pos + 1 when causal and
+ * n otherwise, and start = max(0, end - window) when the window is positive.  */
+static void visible_range(const struct attn_job* job, int64_t t, int64_t n, int64_t* start,
+                          int64_t* end) {
+  int64_t e = job->causal ? (int64_t)job->positions[t] + 1 : n;
+  int64_t s = 0;
+  if (job->sliding_window > 0) {
+    s = e - job->sliding_window;
+    if (s < 0) s = 0;
+  }
+  *start = s;
+  *end = e;
+}
+
+static int row_wanted(const struct attn_job* job, int64_t t, int h) {
+  return job->row_mask == NULL || job->row_mask[t * job->num_heads + h];
+}
+
+/* Task = (sequence s, kv head g): gather that head's K and V once, then answer every
+ * requested (token, q-head) row of the group. */
+static void attn_task(void* ctx, int64_t task) {
+  const struct attn_job* job = (const struct attn_job*)ctx;
+  const struct pool_desc* P = &job->pool;
+  int s = (int)(task / P->num_kv_heads);
+  int g = (int)(task % P->num_kv_heads);
+  int group = job->num_heads / P->num_kv_heads;
+  int64_t t0 = job->query_start_loc[s], t1 = job->query_start_loc[s + 1];
+  int64_t n = job->seq_lens[s];
+
+  int any = 0;
+  for (int64_t t = t0; t < t1 && !any; ++t)
+    for (int h = g * group; h < (g + 1) * group; ++h)
+      if (row_wanted(job, t, h)) any = 1;
+  if (!any) return;
+
+  const int32_t* table = job->block_tables + (int64_t)s * job->max_blocks;
+  double* K = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * (size_t)P->dk);
+  double* V = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * (size_t)P->dv);
+  double* sc = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+  double* qrow = (double*)malloc(sizeof(double) * (size_t)P->dk);
+  double* orow = (double*)malloc(sizeof(double) * (size_t)P->dv);
+  gather_head(P->k, P->dtype, P->block_size, P->num_kv_heads, P->dk, table, n, g, K);
+  gather_head(P->v, P->dtype, P->block_size, P->num_kv_heads, P->dv, table, n, g, V);
+
+  for (int64_t t = t0; t < t1; ++t) {
+    int64_t start, end;
+    visible_range(job, t, n, &start, &end);
+    for (int h = g * group; h < (g + 1) * group; ++h) {
+      if (!row_wanted(job, t, h)) continue;
+      for (int d = 0; d < P->dk; ++d)
+        qrow[d] = load_elem(job->q, job->q_dtype, (t * job->num_heads + h) * P->dk + d);
+      if (job->partition_size <= 0) {
+        double m, l;
+        attend(qrow, K, V, P->dk, P->dv, start, end, job->scale, sc, orow, &m, &l);
+        memcpy(job->out + (t * job->num_heads + h) * P->dv, orow, sizeof(double) * (size_t)P->dv);
+        if (job->lse) job->lse[(int64_t)h * job->num_tokens + t] = lse_of(m, l);
+      } else {
+        /* Split-KV: partition p covers [p * P, (p + 1) * P) of the sequence. */
+        int64_t np = (n + job->partition_size - 1) / job->partition_size;
+        for (int64_t p = 0; p < np; ++p) {
+          int64_t lo = p * job->partition_size, hi = lo + job->partition_size;
+          if (hi > n) hi = n;
+          if (lo < start) lo = start;
+          if (hi > end) hi = end;
+          double m, l;
+          attend(qrow, K, V, P->dk, P->dv, lo, hi, job->scale, sc, orow, &m, &l);
+          int64_t idx = ((int64_t)s * job->num_heads + h) * job->max_partitions + p;
+          job->max_logits[idx] = m;
+          job->exp_sums[idx] = l;
+          memcpy(job->tmp_out + idx * P->dv, orow, sizeof(double) * (size_t)P->dv);
+        }
+      }
+    }
+  }
+  free(orow);
+  free(qrow);
+  free(sc);
+  free(V);
+  free(K);
+}
+
+/* Synchronous checks shared by every attention entry point.  Shape errors first,
+ * then the content of the tables. */
+static int check_job(const struct attn_job* job) {
+  const struct pool_desc* P = &job->pool;
+  if (elem_bytes(P->dtype) == 0 || elem_bytes(job->q_dtype) == 0) return ORC_EUNSUPPORTED;
+  if (P->num_kv_heads < 1 || job->num_heads < 1 || P->dk < 1 || P->dv < 1) return ORC_ESHAPE;
+  if (job->num_heads % P->num_kv_heads != 0) return ORC_ESHAPE;
+  if (P->block_size < 1 || P->num_blocks < 1 || job->num_seqs < 0 || job->max_blocks < 0)
+    return ORC_EINVAL;
+  if (job->query_start_loc[0] != 0) return ORC_EINVAL;
+  for (int s = 0; s < job->num_seqs; ++s)
+    if (job->query_start_loc[s + 1] < job->query_start_loc[s]) return ORC_EINVAL;
+  if (job->query_start_loc[job->num_seqs] != job->num_tokens) return ORC_EINVAL;
+  if (job->causal && job->num_tokens > 0 && job->positions == NULL) return ORC_EINVAL;
+  for (int s = 0; s < job->num_seqs; ++s) {
+    int64_t n = job->seq_lens[s];
+    if (n < 0) return ORC_EINVAL;
+    int64_t need = (n + P->block_size - 1) / P->block_size;
+    if (need > job->max_blocks) return ORC_EINVAL;
+    const int32_t* table = job->block_tables + (int64_t)s * job->max_blocks;
+    for (int64_t i = 0; i < need; ++i)
+      if (table[i] < 0 || table[i] >= P->num_blocks) return ORC_EINVAL;
+    if (job->causal)
+      for (int64_t t = job->query_start_loc[s]; t < job->query_start_loc[s + 1]; ++t)
+        if (job->positions[t] < 0 || job->positions[t] >= n) return ORC_EINVAL;
+  }
+  return ORC_OK;
+}
+
+/* Varlen: any mix of prefill chunks and single decode tokens, packed by
+ * query_start_loc.  out is [T, H, dv]; lse is [H, T] (nullable).  row_mask [T * H]
+ * selects rows to compute (nullable = all); rows not selected are left untouched. */
+int orc_varlen(const void* k_pool, const void* v_pool, int kv_dtype, int64_t num_blocks,
+               int block_size, int num_kv_heads, int dk, int dv, const void* q, int q_dtype,
+               int num_heads, int64_t num_tokens, const int32_t* query_start_loc, int num_seqs,
+               const int32_t* seq_lens, const int32_t* positions, const int32_t* block_tables,
+               int max_blocks, double scale, int causal, int sliding_window,
+               const uint8_t* row_mask, double* out, double* lse, int num_threads) {
+  struct attn_job job;
+  memset(&job, 0, sizeof job);
+  job.pool.k = k_pool;
+  job.pool.v = v_pool;
+  job.pool.dtype = kv_dtype;
+  job.pool.num_blocks = num_blocks;
+  job.pool.block_size = block_size;
+  job.pool.num_kv_heads = num_kv_heads;
+  job.pool.dk = dk;
+  job.pool.dv = dv;
+  job.q = q;
+  job.q_dtype = q_dtype;
+  job.num_heads = num_heads;
+  job.num_tokens = num_tokens;
+  job.query_start_loc = query_start_loc;
+  job.num_seqs = num_seqs;
+  job.seq_lens = seq_lens;
+  job.positions = positions;
+  job.block_tables = block_tables;
+  job.max_blocks = max_blocks;
+  job.scale = scale;
+  job.causal = causal;
+  job.sliding_window = sliding_window;
+  job.row_mask = row_mask;
+  job.out = out;
+  job.lse = lse;
+  int st = check_job(&job);
+  if (st != ORC_OK) return st;
+  parallel_for((int64_t)num_seqs * num_kv_heads, num_threads, attn_task, &job);
+  return ORC_OK;
+}
+
+/* Decode: one query per sequence at position n - 1, causal, optional window.
+ * A context length below 1 is invalid.  q and out are [S, H, dim]; lse [H, S].
+ * With partition_size > 0 the per-partition states are written instead of out:
+ * max_logits / exp_sums [S, H, max_partitions] and tmp_out [S, H, max_partitions,
+ * dv] hold, for each partition p < ceil(n / partition_size), the maximum score, the
+ * sum of exp(score - max) and the normalised partial output over the partition's
+ * visible positions; an empty partition holds (-inf, 0, 0).  Entries at
+ * p >= ceil(n / partition_size) are left untouched.                                */
+int orc_decode(const void* k_pool, const void* v_pool, int kv_dtype, int64_t num_blocks,
+               int block_size, int num_kv_heads, int dk, int dv, const void* q, int q_dtype,
+               int num_heads, const int32_t* block_tables, int max_blocks, const int32_t* seq_lens,
+               int num_seqs, double scale, int sliding_window, int partition_size,
+               int max_partitions, double* out, double* lse, double* max_logits,
+               double* exp_sums, double* tmp_out, int num_threads) {
+  if (num_seqs < 0) return ORC_EINVAL;
+  for (int s = 0; s < num_seqs; ++s)
+    if (seq_lens[s] < 1) return ORC_EINVAL;
+  if (partition_size > 0) {
+    if (partition_size % block_size != 0) return ORC_EINVAL;
+    for (int s = 0; s < num_seqs; ++s)
+      if ((seq_lens[s] + (int64_t)partition_size - 1) / partition_size > max_partitions)
+        return ORC_EINVAL;
+  } else if (partition_size < 0) {
+    return ORC_EINVAL;
+  }
+  int32_t* qsl = (int32_t*)malloc(sizeof(int32_t) * (size_t)(num_seqs + 1));
+  int32_t* pos = (int32_t*)malloc(sizeof(int32_t) * (size_t)(num_seqs > 0 ? num_seqs : 1));
+  for (int s = 0; s <= num_seqs; ++s) qsl[s] = s;
+  for (int s = 0; s < num_seqs; ++s) pos[s] = seq_lens[s] - 1;
+
+  struct attn_job job;
+  memset(&job, 0, sizeof job);
+  job.pool.k = k_pool;
+  job.pool.v = v_pool;
+  job.pool.dtype = kv_dtype;
+  job.pool.num_blocks = num_blocks;
+  job.pool.block_size = block_size;
+  job.pool.num_kv_heads = num_kv_heads;
+  job.pool.dk = dk;
+  job.pool.dv = dv;
+  job.q = q;
+  job.q_dtype = q_dtype;
+  job.num_heads = num_heads;
+  job.num_tokens = num_seqs;
+  job.query_start_loc = qsl;
+  job.num_seqs = num_seqs;
+  job.seq_lens = seq_lens;
+  job.positions = pos;
+  job.block_tables = block_tables;
+  job.max_blocks = max_blocks;
+  job.scale = scale;
+  job.causal = 1;
+  job.sliding_window = sliding_window;
+  job.out = out;
+  job.lse = lse;
+  job.partition_size = partition_size;
+  job.max_partitions = max_partitions;
+  job.max_logits = max_logits;
+  job.exp_sums = exp_sums;
+  job.tmp_out = tmp_out;
+  int st = check_job(&job);
+  if (st == ORC_OK) parallel_for((int64_t)num_seqs * num_kv_heads, num_threads, attn_task, &job);
+  free(pos);
+  free(qsl);
+  return st;
+}
+
+/* Phase-2 reduction of decode partitions, for each (s, h) over p < ceil(n_s / P):
+ * M = max_p m_p, w_p = l_p * exp(m_p - M), out = sum_p w_p o_p / sum_p w_p.
+ * The o_p are the normalised partition outputs written by orc_decode.           */
+int orc_reduce_partitions(const double* max_logits, const double* exp_sums, const double* tmp_out,
+                          const int32_t* seq_lens, int num_seqs, int num_heads, int partition_size,
+                          int max_partitions, int dv, double* out) {
+  if (partition_size < 1) return ORC_EINVAL;
+  for (int s = 0; s < num_seqs; ++s) {
+    int64_t np = ((int64_t)seq_lens[s] + partition_size - 1) / partition_size;
+    if (np > max_partitions) return ORC_EINVAL;
+    for (int h = 0; h < num_heads; ++h) {
+      int64_t base = ((int64_t)s * num_heads + h) * max_partitions;
+      double* o = out + ((int64_t)s * num_heads + h) * dv;
+      double M = -INFINITY;
+      for (int64_t p = 0; p < np; ++p)
+        if (max_logits[base + p] > M) M = max_logits[base + p];
+      for (int d = 0; d < dv; ++d) o[d] = 0.0;
+      if (M == -INFINITY) continue;
+      double total = 0.0;
+      for (int64_t p = 0; p < np; ++p) {
+        if (exp_sums[base + p] == 0.0) continue;
+        double w = exp_sums[base + p] * exp(max_logits[base + p] - M);
+        total += w;
+        for (int d = 0; d < dv; ++d) o[d] += w * tmp_out[(base + p) * dv + d];
+      }
+      for (int d = 0; d < dv; ++d) o[d] /= total;
+    }
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Merge of two attention states                                               */
+/* ------------------------------------------------------------------------- */
+
+/* For each token t and head h: tokens at or past prefill_tokens_with_context (when it
+ * is >= 0) take the suffix state as it is.  Otherwise a +-inf lse counts as -inf; if
+ * both are then -inf the prefix output is copied and the merged lse is -inf; if not,
+ * with M the larger lse, weights exp(p - M) and exp(s - M) are normalised and the
+ * outputs blended, and the merged lse is M + ln(sum of weights).
+ * prefix/suffix outputs are [T, H, D] in `dtype`; every lse is binary32 [H, T].    */
+int orc_merge_states(const void* prefix_out, const float* prefix_lse, const void* suffix_out,
+                     const float* suffix_lse, int dtype, int64_t num_tokens, int num_heads,
+                     int head_dim, int64_t prefill_tokens_with_context, double* out,
+                     double* out_lse) {
+  if (elem_bytes(dtype) == 0) return ORC_EUNSUPPORTED;
+  if (num_tokens < 0 || num_heads < 1 || head_dim < 1) return ORC_EINVAL;
+  int64_t with_prefix = prefill_tokens_with_context < 0 ? num_tokens : prefill_tokens_with_context;
+  for (int64_t t = 0; t < num_tokens; ++t) {
+    for (int h = 0; h < num_heads; ++h) {
+      int64_t row = (t * num_heads + h) * head_dim;
+      int64_t li = (int64_t)h * num_tokens + t;
+      double* o = out + row;
+      if (t >= with_prefix) {
+        for (int d = 0; d < head_dim; ++d) o[d] = load_elem(suffix_out, dtype, row + d);
+        if (out_lse) out_lse[li] = (double)suffix_lse[li];
+        continue;
+      }
+      double p = (double)prefix_lse[li];
+      double s = (double)suffix_lse[li];
+      if (isinf(p)) p = -INFINITY;
+      if (isinf(s)) s = -INFINITY;
+      double M = fmax(p, s);
+      if (isinf(M)) {
+        for (int d = 0; d < head_dim; ++d) o[d] = load_elem(prefix_out, dtype, row + d);
+        if (out_lse) out_lse[li] = M;
+        continue;
+      }
+      double pw = exp(p - M), sw = exp(s - M);
+      double sum = pw + sw;
+      for (int d = 0; d < head_dim; ++d)
+        o[d] = load_elem(prefix_out, dtype, row + d) * (pw / sum) +
+               load_elem(suffix_out, dtype, row + d) * (sw / sum);
+      if (out_lse) out_lse[li] = log(sum) + M;
+    }
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* KV write through the slot mapping                                           */
+/* ------------------------------------------------------------------------- */
+
+/* Token t's K row [num_kv_heads * dk] and V row [num_kv_heads * dv] go to slot
+ * slot_mapping[t], i.e. block slot / block_size at offset slot % block_size, which in
+ * the [blocks, block_size, heads, dim] layout is row `slot` of the pool.  Every slot
+ * is checked against [0, num_blocks * block_size) before anything is written; rows
+ * are then copied byte for byte in token order, so a repeated slot keeps the last. */
+int orc_write_kv(void* k_pool, void* v_pool, int dtype, int64_t num_blocks, int block_size,
+                 int num_kv_heads, int dk, int dv, const void* k_new, const void* v_new,
+                 const int32_t* slot_mapping, int64_t num_tokens) {
+  int eb = elem_bytes(dtype);
+  if (eb == 0) return ORC_EUNSUPPORTED;
+  if (block_size < 1 || num_blocks < 1 || num_kv_heads < 1 || dk < 1 || dv < 1 || num_tokens < 0)
+    return ORC_EINVAL;
+  int64_t num_slots = num_blocks * block_size;
+  for (int64_t t = 0; t < num_tokens; ++t)
+    if (slot_mapping[t] < 0 || slot_mapping[t] >= num_slots) return ORC_EINVAL;
+  size_t krow = (size_t)num_kv_heads * (size_t)dk * (size_t)eb;
+  size_t vrow = (size_t)num_kv_heads * (size_t)dv * (size_t)eb;
+  for (int64_t t = 0; t < num_tokens; ++t) {
+    int64_t block_id = slot_mapping[t] / block_size;
+    int64_t offset = slot_mapping[t] % block_size;
+    int64_t row = block_id * block_size + offset;
+    memcpy((char*)k_pool + (size_t)row * krow, (const char*)k_new + (size_t)t * krow, krow);
+    memcpy((char*)v_pool + (size_t)row * vrow, (const char*)v_new + (size_t)t * vrow, vrow);
+  }
+  return ORC_OK;
+}

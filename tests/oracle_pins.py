@@ -1,0 +1,554 @@
+"""Pins of the CPU oracle against facts fixed outside it.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and raises AssertionError when the
+oracle disagrees with what the pages or the mathematics fix:
+
+* the worked example of "Paged attention for decode in C", section 3 (golden file);
+* torch's scaled_dot_product_attention and logsumexp in float64 on the logical,
+  unpaged cache with the GQA heads repeated -- the dense path of the
+  "ar_modules_attention.py" page -- for decode, prefill chunks, windows, GQA and
+  unequal QK / V head dims;
+* numpy's float16 and torch's bfloat16 conversions for every 16-bit pattern;
+* closed forms and invariants: one visible key returns its value exactly, q = 0
+  averages the visible values, partitions reduce to the unsplit result, merging the
+  two halves of a context gives the whole, block permutations and batching change
+  no bit;
+* the rejection rules of the decode page's section 2.6 and the merge edge rules of
+  the "cpu_mla_prefill.cpp" page (MergeAttnStates).
+
+The same functions run against deliberately broken builds of the oracle in
+test_oracle_mutants.py, which checks that each planted mistake fails at least one.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+EINVAL, ESHAPE = 1, 2
+
+
+# --------------------------------------------------------------------------------
+# Test-side helpers: logical caches, a test-side pool writer, dense references.
+# --------------------------------------------------------------------------------
+
+def stored(values_f64, dtype):
+    """Round float values to storage (f32 / f16 / bf16 bits) with library routines."""
+    a = np.asarray(values_f64, dtype=np.float32)
+    if dtype == "f32":
+        return a.copy()
+    if dtype == "f16":
+        return a.astype(np.float16)
+    return torch.from_numpy(a.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def widen(a, dtype):
+    """Storage -> float64 with numpy / torch (independent of the oracle's decoders)."""
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).double().numpy()
+    return np.asarray(a).astype(np.float64)
+
+
+def nan_storage(dtype):
+    return {"f32": np.float32(np.nan), "f16": np.float16(np.nan), "bf16": np.uint16(0x7FC0)}[dtype]
+
+
+class Case:
+    """A batch of sequences with logical caches, scattered into a pool by the test."""
+
+    def __init__(self, rng, lengths, H, Hkv, dk, dv, dtype, b, spare_blocks=3, shared=None):
+        self.lengths = list(lengths)
+        self.H, self.Hkv, self.dk, self.dv, self.dtype, self.b = H, Hkv, dk, dv, dtype, b
+        need = [(n + b - 1) // b for n in lengths]
+        self.max_blocks = max(1, max(need))
+        fresh = sum(need) - (shared[1] * (len(shared[0]) - 1) if shared else 0)
+        self.num_blocks = fresh + spare_blocks
+        ids = rng.permutation(self.num_blocks)
+        self.tables = np.full((len(lengths), self.max_blocks), ids[-1], dtype=np.int32)
+        cur = 0
+        prefix = None
+        for s, k in enumerate(need):
+            start = 0
+            if shared and s in shared[0] and prefix is not None:
+                self.tables[s, :shared[1]] = prefix
+                start = shared[1]
+            self.tables[s, start:k] = ids[cur:cur + k - start]
+            cur += k - start
+            if shared and s in shared[0] and prefix is None:
+                prefix = self.tables[s, :shared[1]].copy()
+        self.K = [stored(rng.standard_normal((n, Hkv, dk)), dtype) for n in lengths]
+        self.V = [stored(rng.standard_normal((n, Hkv, dv)), dtype) for n in lengths]
+        if shared:
+            first = shared[0][0]
+            P = shared[1] * b
+            for s in shared[0]:
+                self.K[s][:P] = self.K[first][:P]
+                self.V[s][:P] = self.V[first][:P]
+        nan = nan_storage(dtype)
+        self.k_pool = np.full((self.num_blocks, b, Hkv, dk), nan, dtype=self.K[0].dtype if lengths else np.float32)
+        self.v_pool = np.full((self.num_blocks, b, Hkv, dv), nan, dtype=self.k_pool.dtype)
+        for s, n in enumerate(lengths):
+            for j in range(n):
+                self.k_pool[self.tables[s, j // b], j % b] = self.K[s][j]
+                self.v_pool[self.tables[s, j // b], j % b] = self.V[s][j]
+
+
+def dense_reference(q_rows, K, V, lo, hi, scale, group):
+    """torch SDPA (float64, CPU) on the logical cache with GQA heads repeated and a
+    boolean visibility mask; lse from torch.logsumexp of the masked scores.
+    q_rows [R, H, dk]; K [n, Hkv, dk]; V [n, Hkv, dv]; lo/hi [R] visible ranges.
+    Rows with nothing visible are returned as NaN (SDPA leaves them undefined)."""
+    R, H, dk = q_rows.shape
+    n = K.shape[0]
+    q = torch.from_numpy(np.ascontiguousarray(q_rows, dtype=np.float64)).permute(1, 0, 2).unsqueeze(0)
+    k = torch.from_numpy(np.ascontiguousarray(K, dtype=np.float64)).repeat_interleave(group, dim=1)
+    v = torch.from_numpy(np.ascontiguousarray(V, dtype=np.float64)).repeat_interleave(group, dim=1)
+    k = k.permute(1, 0, 2).unsqueeze(0).contiguous()
+    v = v.permute(1, 0, 2).unsqueeze(0).contiguous()
+    j = torch.arange(n)
+    mask = (j[None, :] >= torch.as_tensor(lo)[:, None]) & (j[None, :] < torch.as_tensor(hi)[:, None])
+    out = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask[None, None], scale=scale)
+    scores = (q @ k.transpose(-1, -2)) * scale
+    scores = scores.masked_fill(~mask[None, None], float("-inf"))
+    lse = torch.logsumexp(scores, dim=-1)
+    out = out[0].permute(1, 0, 2).numpy().copy()  # [R, H, dv]
+    lse = lse[0].numpy().copy()  # [H, R]
+    empty = (torch.as_tensor(hi) <= torch.as_tensor(lo)).numpy()
+    out[empty] = np.nan
+    return out, lse
+
+
+def _varlen_segments(rng, case, segments, causal, window):
+    """q and positions for (context, new) segments over case.lengths."""
+    qsl = np.zeros(len(segments) + 1, dtype=np.int32)
+    qsl[1:] = np.cumsum([nq for _, nq in segments])
+    T = int(qsl[-1])
+    positions = np.concatenate([np.arange(c, c + nq) for c, nq in segments]).astype(np.int32) if T else \
+        np.zeros(0, np.int32)
+    q = stored(rng.standard_normal((T, case.H, case.dk)), case.dtype)
+    return q, qsl, positions
+
+
+def _ranges(positions, n, causal, window):
+    end = positions + 1 if causal else np.full_like(positions, n)
+    start = np.maximum(0, end - window) if window > 0 else np.zeros_like(end)
+    return start, end
+
+
+# --------------------------------------------------------------------------------
+# Pins
+# --------------------------------------------------------------------------------
+
+def _hand_pool():
+    g = json.load(open(os.path.join(GOLDEN, "decode_hand_example.json")))
+    b, D = g["block_size"], g["head_dim"]
+    kp = np.full((g["num_blocks"], b, 1, D), np.nan, dtype=np.float32)
+    vp = np.full_like(kp, np.nan)
+    for j in range(g["seq_len"]):
+        kp[g["table"][j // b], j % b, 0] = g["k"][j]
+        vp[g["table"][j // b], j % b, 0] = g["v"][j]
+    return g, kp, vp
+
+
+def pin_hand_example(orc):
+    """Section 3 of the decode page: o = [3, 4]; l and a as printed (7 decimals)."""
+    g, kp, vp = _hand_pool()
+    q = np.array([[g["q"]]], dtype=np.float32)
+    bt = np.array([g["table"]], dtype=np.int32)
+    st, out, lse = orc.decode(kp, vp, "f32", q, "f32", bt, [g["seq_len"]], g["scale"])
+    assert st == 0, st
+    np.testing.assert_allclose(out[0, 0], g["expect"]["out"], rtol=0, atol=1e-12)
+    l_total = math.exp(lse[0, 0] - g["expect"]["running_after_block"][-1]["m"])
+    tol = 0.5 * 10 ** -g["printed_decimals"] + 1e-12
+    assert abs(l_total - g["expect"]["l"]) <= tol, l_total
+    np.testing.assert_allclose(out[0, 0] * l_total, g["expect"]["a"], rtol=0, atol=tol * 10)
+    # the same through varlen: one token at position 2, causal
+    st, out2, lse2 = orc.varlen(kp, vp, "f32", q, "f32", [0, 1], [g["seq_len"]], [2], bt, g["scale"], True, 0)
+    assert st == 0 and np.array_equal(out2, out) and np.array_equal(lse2, lse)
+
+
+def pin_hand_example_per_block(orc):
+    """Partitions of one block each reproduce the page's per-block running update:
+    block 1 alone is the difference between the printed running values."""
+    g, kp, vp = _hand_pool()
+    q = np.array([[g["q"]]], dtype=np.float32)
+    bt = np.array([g["table"]], dtype=np.int32)
+    st, ml, es, to = orc.decode(kp, vp, "f32", q, "f32", bt, [g["seq_len"]], g["scale"],
+                                partition_size=g["block_size"], max_partitions=2)
+    assert st == 0, st
+    run = g["expect"]["running_after_block"]
+    tol = 0.5 * 10 ** -g["printed_decimals"] + 1e-12
+    l0, a0 = run[0]["l"], np.array(run[0]["a"])
+    l1, a1 = run[1]["l"] - run[0]["l"], np.array(run[1]["a"]) - np.array(run[0]["a"])
+    assert ml[0, 0, 0] == run[0]["m"] and ml[0, 0, 1] == run[1]["m"], ml
+    assert abs(es[0, 0, 0] - l0) <= tol and abs(es[0, 0, 1] - l1) <= 2 * tol, es
+    np.testing.assert_allclose(to[0, 0, 0] * es[0, 0, 0], a0, atol=10 * tol, rtol=0)
+    np.testing.assert_allclose(to[0, 0, 1] * es[0, 0, 1], a1, atol=10 * tol, rtol=0)
+    red = orc.reduce_partitions(ml, es, to, [g["seq_len"]], g["block_size"])
+    np.testing.assert_allclose(red[0, 0], g["expect"]["out"], atol=1e-12, rtol=0)
+
+
+def pin_hand_example_written_through_slots(orc):
+    """The worked example's cache written through the slot mapping gives the same."""
+    g, kp_ref, vp_ref = _hand_pool()
+    b = g["block_size"]
+    kp = np.full_like(kp_ref, np.nan)
+    vp = np.full_like(vp_ref, np.nan)
+    slots = np.array([g["table"][j // b] * b + j % b for j in range(g["seq_len"])], dtype=np.int32)
+    k_new = np.array(g["k"], dtype=np.float32)[:, None, :]
+    v_new = np.array(g["v"], dtype=np.float32)[:, None, :]
+    assert orc.write_kv(kp, vp, "f32", k_new, v_new, slots) == 0
+    assert np.array_equal(kp, kp_ref, equal_nan=True) and np.array_equal(vp, vp_ref, equal_nan=True)
+    q = np.array([[g["q"]]], dtype=np.float32)
+    st, out, _ = orc.decode(kp, vp, "f32", q, "f32", np.array([g["table"]], np.int32), [g["seq_len"]], 1.0)
+    assert st == 0
+    np.testing.assert_allclose(out[0, 0], g["expect"]["out"], atol=1e-12, rtol=0)
+
+
+def pin_decode_matches_dense(orc):
+    """Decode page's differential test: GQA 6:2, D = 32, lengths 1 / 37 / 70 in
+    shuffled blocks, window 0 and 20, against SDPA on the gathered logical cache."""
+    rng = np.random.default_rng(7)
+    for dtype in ("f32", "f16", "bf16"):
+        case = Case(rng, [1, 37, 70], H=6, Hkv=2, dk=32, dv=32, dtype=dtype, b=16)
+        q = stored(rng.standard_normal((3, 6, 32)), dtype)
+        for window in (0, 20):
+            st, out, lse = orc.decode(case.k_pool, case.v_pool, dtype, q, dtype, case.tables, case.lengths,
+                                      0.17, sliding_window=window)
+            assert st == 0, st
+            for s, n in enumerate(case.lengths):
+                pos = np.array([n - 1])
+                lo, hi = _ranges(pos, n, True, window)
+                ref, rlse = dense_reference(widen(q[s:s + 1], dtype), widen(case.K[s], dtype),
+                                            widen(case.V[s], dtype), lo, hi, 0.17, 3)
+                np.testing.assert_allclose(out[s], ref[0], atol=1e-12, rtol=1e-12)
+                np.testing.assert_allclose(lse[:, s], rlse[:, 0], atol=1e-12, rtol=1e-12)
+
+
+def pin_varlen_matches_dense(orc):
+    """Prefill chunks mixed with decode tokens, causal and not, windows, GQA 4:1, 2:1
+    and 1:1, QK dim 48 with V dim 32, against SDPA + logsumexp per sequence."""
+    rng = np.random.default_rng(11)
+    for (H, Hkv, dk, dv, dtype) in ((8, 2, 48, 32, "bf16"), (4, 2, 32, 32, "f16"), (3, 3, 16, 24, "f32")):
+        segments = [(0, 9), (5, 1), (30, 12), (50, 1), (0, 1), (17, 0)]
+        lengths = [c + nq for c, nq in segments]
+        case = Case(rng, lengths, H=H, Hkv=Hkv, dk=dk, dv=dv, dtype=dtype, b=4)
+        for causal, window in ((True, 0), (True, 7), (False, 0), (False, 10)):
+            q, qsl, positions = _varlen_segments(rng, case, segments, causal, window)
+            st, out, lse = orc.varlen(case.k_pool, case.v_pool, dtype, q, dtype, qsl, lengths,
+                                      positions if causal else None, case.tables, 0.3, causal, window)
+            assert st == 0, st
+            for s, n in enumerate(lengths):
+                t0, t1 = qsl[s], qsl[s + 1]
+                if t1 == t0:
+                    continue
+                lo, hi = _ranges(positions[t0:t1], n, causal, window)
+                ref, rlse = dense_reference(widen(q[t0:t1], dtype), widen(case.K[s], dtype),
+                                            widen(case.V[s], dtype), lo, hi, 0.3, H // Hkv)
+                np.testing.assert_allclose(out[t0:t1], ref, atol=1e-12, rtol=1e-12)
+                np.testing.assert_allclose(lse[:, t0:t1], rlse, atol=1e-12, rtol=1e-12)
+
+
+def pin_empty_rows(orc):
+    """A sequence of length 0 read non-causally gives zero outputs and lse = -inf."""
+    rng = np.random.default_rng(3)
+    case = Case(rng, [0, 5], H=2, Hkv=1, dk=8, dv=8, dtype="f32", b=4)
+    q = stored(rng.standard_normal((3, 2, 8)), "f32")
+    st, out, lse = orc.varlen(case.k_pool, case.v_pool, "f32", q, "f32", [0, 2, 3], [0, 5], None, case.tables,
+                              1.0, False, 0)
+    assert st == 0
+    assert np.all(out[:2] == 0.0) and np.all(np.isneginf(lse[:, :2])), (out[:2], lse)
+    assert np.all(np.isfinite(out[2])) and np.all(np.isfinite(lse[:, 2]))
+
+
+def pin_decoders(orc):
+    """Every f16 and bf16 bit pattern decodes as numpy / torch decode it."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = orc.decode_elems(bits.view(np.float16), "f16")
+    ref = bits.view(np.float16).astype(np.float64)
+    assert np.array_equal(got, ref, equal_nan=True)
+    got = orc.decode_elems(bits, "bf16")
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    assert np.array_equal(got, ref, equal_nan=True)
+
+
+def pin_permutation_invariance(orc):
+    """Brute force over every physical block order of tiny caches: the result is
+    bitwise the same for all orders and equals the dense reference."""
+    rng = np.random.default_rng(5)
+    for b, n in ((1, 5), (2, 7), (4, 13)):
+        nblk = (n + b - 1) // b
+        K = rng.standard_normal((n, 1, 4)).astype(np.float32)
+        V = rng.standard_normal((n, 1, 4)).astype(np.float32)
+        q = rng.standard_normal((1, 1, 4)).astype(np.float32)
+        for window in range(0, n + 1):
+            first = None
+            for perm in itertools.permutations(range(nblk)):
+                kp = np.full((nblk, b, 1, 4), np.nan, np.float32)
+                vp = np.full_like(kp, np.nan)
+                for j in range(n):
+                    kp[perm[j // b], j % b] = K[j]
+                    vp[perm[j // b], j % b] = V[j]
+                st, out, lse = orc.decode(kp, vp, "f32", q, "f32", np.array([perm], np.int32), [n], 0.5,
+                                          sliding_window=window)
+                assert st == 0
+                if first is None:
+                    first = (out.copy(), lse.copy())
+                    lo, hi = _ranges(np.array([n - 1]), n, True, window)
+                    ref, rlse = dense_reference(q.astype(np.float64), K.astype(np.float64), V.astype(np.float64),
+                                                lo, hi, 0.5, 1)
+                    np.testing.assert_allclose(out[0], ref[0], atol=1e-13, rtol=0)
+                    np.testing.assert_allclose(lse[:, 0], rlse[:, 0], atol=1e-13, rtol=0)
+                else:
+                    assert np.array_equal(out, first[0]) and np.array_equal(lse, first[1])
+
+
+def pin_closed_forms(orc):
+    """One visible key returns its value exactly and lse = its score; q = 0 returns
+    the mean of the visible values."""
+    rng = np.random.default_rng(9)
+    case = Case(rng, [23, 40], H=4, Hkv=2, dk=16, dv=16, dtype="f32", b=4)
+    q = stored(rng.standard_normal((2, 4, 16)), "f32")
+    st, out, lse = orc.decode(case.k_pool, case.v_pool, "f32", q, "f32", case.tables, case.lengths, 0.25,
+                              sliding_window=1)
+    assert st == 0
+    for s, n in enumerate(case.lengths):
+        for h in range(4):
+            g = h // 2
+            assert np.array_equal(out[s, h], case.V[s][n - 1, g].astype(np.float64))
+            score = 0.25 * float(np.dot(q[s, h].astype(np.float64), case.K[s][n - 1, g].astype(np.float64)))
+            assert abs(lse[h, s] - score) <= 1e-14 * max(1.0, abs(score))
+    qz = np.zeros_like(q)
+    st, out, lse = orc.decode(case.k_pool, case.v_pool, "f32", qz, "f32", case.tables, case.lengths, 0.25,
+                              sliding_window=9)
+    for s, n in enumerate(case.lengths):
+        for h in range(4):
+            mean = case.V[s][n - 9:n, h // 2].astype(np.float64).mean(axis=0)
+            np.testing.assert_allclose(out[s, h], mean, atol=1e-14, rtol=0)
+            assert abs(lse[h, s] - math.log(9)) < 1e-14
+
+
+def pin_partitions_reduce_to_unsplit(orc):
+    """Split-KV states (normalised partial outputs) reduce to the unsplit result, for
+    several partition sizes and windows; a partition covering the whole context equals
+    the unsplit output bit for bit; partitions outside the window are (-inf, 0, 0)."""
+    rng = np.random.default_rng(13)
+    case = Case(rng, [1, 15, 16, 17, 90, 133], H=4, Hkv=1, dk=16, dv=8, dtype="bf16", b=4)
+    q = stored(rng.standard_normal((6, 4, 16)), "bf16")
+    for window in (0, 5, 37):
+        st, out, lse = orc.decode(case.k_pool, case.v_pool, "bf16", q, "bf16", case.tables, case.lengths, 0.4,
+                                  sliding_window=window)
+        assert st == 0
+        for P in (4, 8, 32, 136):
+            pmax = -(-max(case.lengths) // P)
+            st, ml, es, to = orc.decode(case.k_pool, case.v_pool, "bf16", q, "bf16", case.tables, case.lengths,
+                                        0.4, sliding_window=window, partition_size=P, max_partitions=pmax)
+            assert st == 0
+            red = orc.reduce_partitions(ml, es, to, case.lengths, P)
+            np.testing.assert_allclose(red, out, atol=1e-13, rtol=0)
+            for s, n in enumerate(case.lengths):
+                start = max(0, n - window) if window > 0 else 0
+                for p in range(-(-n // P)):
+                    if (p + 1) * P <= start:
+                        assert np.all(np.isneginf(ml[s, :, p])) and np.all(es[s, :, p] == 0)
+                        assert np.all(to[s, :, p] == 0)
+                if P >= n:
+                    assert np.array_equal(to[s, :, 0], out[s])
+
+
+def pin_merge_halves_equal_whole(orc):
+    """Attention over a context equals the merge of attention over its two halves
+    (both read non-causally), in out and lse."""
+    rng = np.random.default_rng(17)
+    n = 57
+    case = Case(rng, [n, 30, n - 30], H=2, Hkv=2, dk=8, dv=8, dtype="f32", b=4)
+    # sequences 1 and 2 hold positions [0, 30) and [30, 57) of sequence 0
+    for j in range(n):
+        src = case.k_pool[case.tables[0, j // 4], j % 4]
+        vsrc = case.v_pool[case.tables[0, j // 4], j % 4]
+        s, jj = (1, j) if j < 30 else (2, j - 30)
+        case.k_pool[case.tables[s, jj // 4], jj % 4] = src
+        case.v_pool[case.tables[s, jj // 4], jj % 4] = vsrc
+    q = stored(rng.standard_normal((5, 2, 8)), "f32")
+    whole = orc.varlen(case.k_pool, case.v_pool, "f32", q, "f32", [0, 5], [n], None, case.tables[:1], 0.5, False, 0)
+    a = orc.varlen(case.k_pool, case.v_pool, "f32", q, "f32", [0, 5], [30], None, case.tables[1:2], 0.5, False, 0)
+    bb = orc.varlen(case.k_pool, case.v_pool, "f32", q, "f32", [0, 5], [n - 30], None, case.tables[2:3], 0.5, False,
+                    0)
+    merged, mlse = orc.merge_states(a[1].astype(np.float32), a[2].astype(np.float32), bb[1].astype(np.float32),
+                                    bb[2].astype(np.float32))
+    np.testing.assert_allclose(merged, whole[1], atol=1e-6, rtol=0)  # inputs rounded to fp32
+    np.testing.assert_allclose(mlse, whole[2], atol=1e-6, rtol=0)
+    # merging with an empty (-inf) state returns the other state exactly
+    empty_lse = np.full((2, 5), -np.inf, np.float32)
+    x_out, x_lse = a[1].astype(np.float32), a[2].astype(np.float32)
+    m2, l2 = orc.merge_states(x_out, x_lse, np.zeros_like(x_out), empty_lse)
+    assert np.array_equal(m2, x_out.astype(np.float64)) and np.array_equal(l2, x_lse.astype(np.float64))
+    m3, l3 = orc.merge_states(np.zeros_like(x_out), empty_lse, x_out, x_lse)
+    assert np.array_equal(m3, x_out.astype(np.float64)) and np.array_equal(l3, x_lse.astype(np.float64))
+
+
+def pin_merge_edge_rules(orc):
+    """MergeAttnStates edge rules: +-inf lse counts as -inf; both -inf copies the
+    prefix with lse -inf; one side -inf returns the other side unchanged; tokens at or
+    past prefill_tokens_with_context copy the suffix."""
+    rng = np.random.default_rng(19)
+    T, H, D = 6, 5, 8
+    po = rng.standard_normal((T, H, D)).astype(np.float32)
+    so = rng.standard_normal((T, H, D)).astype(np.float32)
+    pl = rng.standard_normal((H, T)).astype(np.float32)
+    sl = rng.standard_normal((H, T)).astype(np.float32)
+    inf = np.float32(np.inf)
+    pl[0, 0], sl[0, 0] = inf, 1.5        # prefix +inf -> suffix wins
+    pl[1, 0], sl[1, 0] = 0.25, inf       # suffix +inf -> prefix wins
+    pl[2, 0], sl[2, 0] = -inf, -inf      # both -inf -> prefix copy, lse -inf
+    pl[3, 0], sl[3, 0] = inf, -inf       # +inf and -inf -> both -inf
+    pl[4, 0], sl[4, 0] = inf, inf        # both +inf -> both -inf
+    out, olse = orc.merge_states(po, pl, so, sl, "f32", prefill_tokens_with_context=4)
+    f = lambda a: a.astype(np.float64)
+    assert np.array_equal(out[0, 0], f(so[0, 0])) and olse[0, 0] == np.float64(np.float32(1.5))
+    assert np.array_equal(out[0, 1], f(po[0, 1])) and olse[1, 0] == np.float64(np.float32(0.25))
+    for h in (2, 3, 4):
+        assert np.array_equal(out[0, h], f(po[0, h])) and np.isneginf(olse[h, 0])
+    # pass-through rows
+    assert np.array_equal(out[4:], f(so[4:])) and np.array_equal(olse[:, 4:], f(sl[:, 4:]))
+    # regular rows are convex blends: between the two inputs elementwise
+    lo = np.minimum(po[1:4], so[1:4]) - 1e-6
+    hi = np.maximum(po[1:4], so[1:4]) + 1e-6
+    assert np.all(out[1:4] >= lo) and np.all(out[1:4] <= hi)
+    assert np.all(olse[:, 1:4] >= np.maximum(pl[:, 1:4], sl[:, 1:4]) - 1e-12)
+    assert np.all(olse[:, 1:4] <= np.maximum(pl[:, 1:4], sl[:, 1:4]) + math.log(2) + 1e-12)
+
+
+def pin_invariance(orc):
+    """Forks and batching (decode page, section 2.5 and its shared-blocks test): 16
+    sequences, the first two blocks shared by all; each sequence alone gives the same
+    bits as in the batch; one thread gives the same bits as eight; two sequences with
+    the same table and query give the same row."""
+    rng = np.random.default_rng(21)
+    lengths = list(rng.integers(33, 90, size=16))
+    case = Case(rng, lengths, H=4, Hkv=2, dk=16, dv=16, dtype="f16", b=16, shared=(list(range(16)), 2))
+    q = stored(rng.standard_normal((16, 4, 16)), "f16")
+    q[5] = q[3]
+    tables = case.tables.copy()
+    tables[5] = tables[3]
+    lens = np.array(lengths, np.int32)
+    lens[5] = lens[3]
+    st, out, lse = orc.decode(case.k_pool, case.v_pool, "f16", q, "f16", tables, lens, 0.25, threads=8)
+    assert st == 0
+    st1, out1, lse1 = orc.decode(case.k_pool, case.v_pool, "f16", q, "f16", tables, lens, 0.25, threads=1)
+    assert np.array_equal(out, out1) and np.array_equal(lse, lse1)
+    assert np.array_equal(out[5], out[3])
+    for s in range(16):
+        st, o1, l1 = orc.decode(case.k_pool, case.v_pool, "f16", q[s:s + 1], "f16", tables[s:s + 1], lens[s:s + 1],
+                                0.25, threads=1)
+        assert np.array_equal(o1[0], out[s]) and np.array_equal(l1[:, 0], lse[:, s])
+    # the shared prefix gathers to the same bits for every fork
+    g0 = orc.gather(case.k_pool, "f16", 16, tables[0], 32)
+    for s in range(1, 16):
+        assert np.array_equal(orc.gather(case.k_pool, "f16", 16, tables[s], 32), g0)
+
+
+def pin_write_kv_round_trip(orc):
+    """Scatter through the slot mapping, then gather through the table: identity, bit
+    for bit; a repeated slot keeps the last token written."""
+    rng = np.random.default_rng(23)
+    for dtype in ("f32", "f16", "bf16"):
+        b, Hkv, dk, dv, n = 4, 3, 8, 12, 29
+        nb = 10
+        table = rng.permutation(nb)[:8].astype(np.int32)
+        k_new = stored(rng.standard_normal((n, Hkv, dk)), dtype)
+        v_new = stored(rng.standard_normal((n, Hkv, dv)), dtype)
+        slots = np.array([table[j // b] * b + j % b for j in range(n)], dtype=np.int32)
+        kp = np.zeros((nb, b, Hkv, dk), dtype=k_new.dtype)
+        vp = np.zeros((nb, b, Hkv, dv), dtype=k_new.dtype)
+        assert orc.write_kv(kp, vp, dtype, k_new, v_new, slots) == 0
+        assert np.array_equal(orc.gather(kp, dtype, b, table, n), widen(k_new, dtype))
+        assert np.array_equal(orc.gather(vp, dtype, b, table, n), widen(v_new, dtype))
+        dup = slots.copy()
+        dup[7] = dup[3]
+        assert orc.write_kv(kp, vp, dtype, k_new, v_new, dup) == 0
+        assert np.array_equal(kp.reshape(-1, Hkv, dk)[dup[3]], k_new[7])
+
+
+def pin_rejections(orc):
+    """Decode page, section 2.6 and its bad-tables test, plus the varlen and write
+    readings: each bad input is rejected and the outputs keep their sentinel."""
+    rng = np.random.default_rng(29)
+    case = Case(rng, [5, 9], H=4, Hkv=2, dk=8, dv=8, dtype="f32", b=4, spare_blocks=0)
+    q = stored(rng.standard_normal((2, 4, 8)), "f32")
+    good_t, good_l = case.tables.copy(), np.array(case.lengths, np.int32)
+
+    def dec(tables=good_t, lens=good_l, H=4, **kw):
+        qq = q if H == 4 else stored(rng.standard_normal((2, H, 8)), "f32")
+        sentinel = np.full((2, H, 8), 7.0)
+        r = orc.decode(case.k_pool, case.v_pool, "f32", qq, "f32", tables, lens, 1.0, out=sentinel, **kw)
+        return r[0], sentinel
+
+    st, _ = dec()
+    assert st == 0
+    bad = good_l.copy(); bad[0] = 0                      # empty context
+    st, o = dec(lens=bad); assert st == EINVAL and np.all(o == 7.0), st
+    for s in (0, 1):                                     # needs 4 blocks, a row holds 3
+        bad = good_l.copy(); bad[s] = 13                 # (row 0 is followed by valid ids)
+        st, o = dec(lens=bad); assert st == EINVAL and np.all(o == 7.0), st
+    t = good_t.copy(); t[1, 1] = case.num_blocks + 5     # id past the pool
+    st, o = dec(tables=t); assert st == EINVAL and np.all(o == 7.0), st
+    t = good_t.copy(); t[0, 0] = -1                      # negative id
+    st, o = dec(tables=t); assert st == EINVAL and np.all(o == 7.0), st
+    st, o = dec(H=3); assert st == ESHAPE and np.all(o == 7.0), st      # H % Hkv != 0
+    st, _ = dec(partition_size=6, max_partitions=4); assert st == EINVAL, st   # not a multiple of b
+    st, _ = dec(partition_size=4, max_partitions=2); assert st == EINVAL, st   # 9 tokens need 3
+    # varlen: positions and query_start_loc
+    qv = stored(rng.standard_normal((4, 4, 8)), "f32")
+
+    def var(qsl, pos, lens=good_l, causal=True):
+        sentinel = np.full((4, 4, 8), 7.0)
+        r = orc.varlen(case.k_pool, case.v_pool, "f32", qv, "f32", qsl, lens, pos, good_t, 1.0, causal, 0,
+                       out=sentinel)
+        return r[0], sentinel
+
+    st, _ = var([0, 2, 4], [3, 4, 7, 8]); assert st == 0
+    st, o = var([0, 2, 4], [3, 5, 7, 8]); assert st == EINVAL and np.all(o == 7.0)   # pos >= n
+    st, o = var([0, 2, 4], [3, -1, 7, 8]); assert st == EINVAL and np.all(o == 7.0)  # pos < 0
+    st, o = var([0, 3, 2], [3, 4, 7, 8]); assert st == EINVAL and np.all(o == 7.0)   # decreasing
+    st, o = var([0, 2, 3], [3, 4, 7, 8]); assert st == EINVAL and np.all(o == 7.0)   # last != T
+    st, o = var([1, 2, 4], [3, 4, 7, 8]); assert st == EINVAL and np.all(o == 7.0)   # first != 0
+    # write_kv: a slot outside the pool leaves the pool untouched
+    kp, vp = case.k_pool.copy(), case.v_pool.copy()
+    kn = np.ones((2, 2, 8), np.float32)
+    n_slots = case.num_blocks * 4
+    for bad_slot in (n_slots, -1):
+        assert orc.write_kv(kp, vp, "f32", kn, kn, np.array([0, bad_slot], np.int32)) == EINVAL
+        assert np.array_equal(kp, case.k_pool, equal_nan=True) and np.array_equal(vp, case.v_pool, equal_nan=True)
+
+
+PINS = [pin_hand_example, pin_hand_example_per_block, pin_hand_example_written_through_slots,
+        pin_decode_matches_dense, pin_varlen_matches_dense, pin_empty_rows, pin_decoders,
+        pin_permutation_invariance, pin_closed_forms, pin_partitions_reduce_to_unsplit,
+        pin_merge_halves_equal_whole, pin_merge_edge_rules, pin_invariance, pin_write_kv_round_trip,
+        pin_rejections]
+
+
+def run_all(path):
+    """Run every pin against the oracle built at `path`; print one JSON line naming
+    the pins that failed (used on mutant builds, in a child process)."""
+    import sys
+
+    here = os.path.dirname(os.path.abspath(__file__))
+    sys.path.insert(0, os.path.dirname(here))
+    from oracle.oracle import Oracle
+
+    orc = Oracle(path)
+    failed = []
+    for pin in PINS:
+        try:
+            pin(orc)
+        except Exception as e:  # noqa: BLE001 - any failure kills the mutant
+            failed.append([pin.__name__, type(e).__name__])
+    print(json.dumps({"failed": failed}))

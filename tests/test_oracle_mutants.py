@@ -1,0 +1,78 @@
+"""Planted mistakes in the oracle must fail at least one pin.
+
+Each mutant edits one passage of oracle.c (on the CPU, in a temporary copy), builds
+it, and runs every pin of oracle_pins.py against that build in a child process (a
+mutant that reads out of bounds may crash; that also counts as caught).  The list
+covers the pitfall table of "Paged attention for decode in C" (section 5) where it
+applies to a two-pass oracle, the printed phase-2 form of the PagedAttention V2 page,
+and the merge edge cases of MergeAttnStates.
+"""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+from oracle import oracle as oracle_mod
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# name -> (text in oracle.c, replacement).  Pitfall s13 (accepting an empty context) is
+# not listed: a decode query at position n - 1 = -1 is also refused by the position
+# rule, so dropping the length check alone changes nothing (an equivalent mutant).
+MUTANTS = {
+    # decode page, section 5
+    "s03_logical_index_as_block_id": ("int64_t block_id = table[j / block_size];",
+                                      "int64_t block_id = j / block_size;"),
+    "s04_no_kv_head_offset": ("int64_t base = (slot * num_kv_heads + g) * head_dim;",
+                              "int64_t base = (slot * num_kv_heads) * head_dim;"),
+    "s05_round_robin_heads": ("for (int h = g * group; h < (g + 1) * group; ++h)",
+                              "for (int h = g; h < job->num_heads; h += P->num_kv_heads)"),
+    "s06_window_of_w_plus_1": ("s = e - job->sliding_window;", "s = e - job->sliding_window - 1;"),
+    "s07_query_at_n": ("pos[s] = seq_lens[s] - 1;", "pos[s] = seq_lens[s];"),
+    "s08_v_from_k_slab": ("gather_head(P->v, P->dtype", "gather_head(P->k, P->dtype"),
+    "s14_trust_max_blocks": ("if (need > job->max_blocks) return ORC_EINVAL;", ""),
+    "s15_trust_block_ids": ("if (table[i] < 0 || table[i] >= P->num_blocks) return ORC_EINVAL;", ""),
+    # phase 2 of the PagedAttention V2 page as printed: un-normalised partition outputs
+    "unnormalised_partition_outputs": (
+        "memcpy(job->tmp_out + idx * P->dv, orow, sizeof(double) * (size_t)P->dv);",
+        "for (int d = 0; d < P->dv; ++d) job->tmp_out[idx * P->dv + d] = orow[d] * l;"),
+    "reduce_without_rescale": ("double w = exp_sums[base + p] * exp(max_logits[base + p] - M);",
+                               "double w = exp_sums[base + p];"),
+    # arithmetic slips
+    "scale_dropped": ("s[j - lo] = scale * dot;", "s[j - lo] = dot;"),
+    "causal_excludes_self": ("int64_t e = job->causal ? (int64_t)job->positions[t] + 1 : n;",
+                             "int64_t e = job->causal ? (int64_t)job->positions[t] : n;"),
+    "lse_without_max": ("return l > 0.0 ? m + log(l) : -INFINITY;", "return l > 0.0 ? log(l) : -INFINITY;"),
+    "no_final_normalisation": ("double inv = 1.0 / l;", "double inv = 1.0;"),
+    "f16_exponent_bias": ("mag = ldexp((double)(1024 + f), e - 25);", "mag = ldexp((double)(1024 + f), e - 24);"),
+    "bf16_wrong_shift": ("uint32_t bits = (uint32_t)h << 16;", "uint32_t bits = (uint32_t)h << 15;"),
+    "write_kv_row_is_token": ("int64_t row = block_id * block_size + offset;", "int64_t row = t;"),
+    # MergeAttnStates edge rules
+    "merge_keeps_plus_inf": ("if (isinf(p)) p = -INFINITY;", ""),
+    "merge_both_ninf_emits_suffix": (
+        "for (int d = 0; d < head_dim; ++d) o[d] = load_elem(prefix_out, dtype, row + d);\n        if (out_lse) out_lse[li] = M;",
+        "for (int d = 0; d < head_dim; ++d) o[d] = load_elem(suffix_out, dtype, row + d);\n        if (out_lse) out_lse[li] = M;"),
+    "merge_pass_through_off_by_one": ("if (t >= with_prefix) {", "if (t > with_prefix) {"),
+    "merge_swapped_weights": ("load_elem(prefix_out, dtype, row + d) * (pw / sum)", "load_elem(prefix_out, dtype, row + d) * (sw / sum)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    src = open(oracle_mod.SOURCE).read()
+    old, new = MUTANTS[name]
+    assert src.count(old) >= 1, f"mutant {name}: passage not found in oracle.c"
+    mutated = tmp_path / "oracle_mutant.c"
+    mutated.write_text(src.replace(old, new))
+    lib = str(tmp_path / "liboracle_mutant.so")
+    oracle_mod.build(str(mutated), lib)
+    code = f"import sys; sys.path.insert(0, {ROOT!r}); from tests import oracle_pins; oracle_pins.run_all({lib!r})"
+    proc = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300, cwd=ROOT)
+    if proc.returncode != 0:
+        return  # crashed: caught
+    lines = [ln for ln in proc.stdout.splitlines() if ln.startswith("{")]
+    assert lines, proc.stdout + proc.stderr
+    failed = json.loads(lines[-1])["failed"]
+    assert failed, f"mutant {name} passed every pin"
