@@ -1,0 +1,155 @@
+/*
+ * pa.h -- batched paged attention over a block-pooled KV cache, for AMD Instinct
+ * MI355X (gfx950).  C ABI: plain pointers and sizes, no framework types.
+ *
+ * Data model (TensorSharp "ManagedPagedAttention.cs", class summary; "Paged attention
+ * for decode in C", section 2.1):
+ *   - A pool holds K and V in blocks of `block_size` token slots:
+ *       K [num_blocks, block_size, num_kv_heads, head_dim_k]
+ *       V [num_blocks, block_size, num_kv_heads, head_dim_v]
+ *     row-major, all in the pool's element type.  Slot = block_id * block_size +
+ *     offset is the flat index of a [num_kv_heads, head_dim] row.
+ *   - Sequence s owns row s of `block_tables` ([num_seqs, max_blocks], int32): its
+ *     position j lives at offset j % block_size of block block_tables[s][j / block_size].
+ *     Ids are arbitrary; several tables may name one block (shared prefixes).
+ *   - q and out are [tokens, num_heads, head_dim].  q head h reads kv head
+ *     h / (num_heads / num_kv_heads) (grouped-query attention).
+ *   - A query at position pos of a sequence of seq_len tokens sees positions
+ *     [start, end): end = pos + 1 when causal, else seq_len; start = max(0, end -
+ *     sliding_window) when sliding_window > 0, else 0.  Scores are
+ *     scale * <q, k_j>, normalised by softmax over the visible positions.
+ *   - lse arrays are float32 [num_heads, tokens] in natural log; a row that sees no
+ *     position has output 0 and lse -inf ("cpu_mla_prefill.cpp", MlaPrefillAttention).
+ *
+ * Ownership and streams: the caller owns every buffer.  The library allocates no
+ * memory, keeps no state between calls, and enqueues all work on `stream` (a
+ * hipStream_t; NULL is the default stream) without synchronising.  Device pointers
+ * must stay valid until the work completes.  The pool descriptor is host memory and
+ * is read during the call only.
+ *
+ * Errors: every entry point returns a pa_status synchronously.  Argument errors
+ * (null pointers, sizes, unsupported combinations) are found on the host, and then
+ * nothing is enqueued, so outputs are untouched.  Errors in device-resident content
+ * (block ids, lengths, positions, slots, query_start_loc) can only be found on the
+ * device: when `status` (a device int32) is non-NULL, a validation kernel runs first
+ * on the same stream and stores PA_OK or PA_EINVAL there, and every later kernel of
+ * the call exits before writing anything if it holds an error.  Read it after the
+ * stream synchronises.  With status == NULL no validation runs; kernels still never
+ * read or write outside the pool, the tables or the outputs (bad ids are clamped),
+ * but results for invalid content are unspecified.
+ *
+ * Element offsets are computed in 64 bits, so pools may exceed 2^31 elements.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_EINVAL = 1,       /* bad argument or bad device content */
+  PA_ESHAPE = 2,       /* num_heads % num_kv_heads != 0, or dims that disagree */
+  PA_EUNSUPPORTED = 3, /* an element type / head-dim / group combination not built */
+  PA_EDEVICE = 4       /* a HIP launch failed */
+} pa_status;
+
+typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+typedef struct pa_kv_pool {
+  void* k;              /* device, [num_blocks, block_size, num_kv_heads, head_dim_k] */
+  void* v;              /* device, [num_blocks, block_size, num_kv_heads, head_dim_v] */
+  int64_t num_blocks;   /* >= 1 */
+  int32_t block_size;   /* tokens per block, >= 1 */
+  int32_t num_kv_heads; /* >= 1 */
+  int32_t head_dim_k;   /* QK head dim */
+  int32_t head_dim_v;   /* V head dim */
+  int32_t dtype;        /* pa_dtype of both pools */
+} pa_kv_pool;
+
+/* Static text for a status code. */
+const char* pa_strerror(int status);
+
+/* Write new tokens' K and V into their pool slots (TensorSharp page,
+ * WriteKvToPagedPool).  k_new [num_tokens, num_kv_heads, head_dim_k] and v_new
+ * [num_tokens, num_kv_heads, head_dim_v] are device arrays in the pool dtype;
+ * token t goes to slot slot_mapping[t] (device int32).  Bytes are copied unchanged.
+ * Device check (with status): every slot in [0, num_blocks * block_size).  A slot
+ * repeated within one call is written by one of its tokens, unspecified which.
+ * num_tokens == 0 enqueues nothing. */
+int pa_write_kv(const pa_kv_pool* pool, const void* k_new, const void* v_new,
+                const int32_t* slot_mapping, int64_t num_tokens, int32_t* status, void* stream);
+
+/* One decode step ("Paged attention for decode in C", sections 2.2-2.6): for each
+ * sequence s and head h, the query q[s, h, :] sits at position seq_lens[s] - 1
+ * (causal) and attends over its visible positions.
+ *   q [num_seqs, num_heads, head_dim_k] in q_dtype (must equal the pool dtype);
+ *   out [num_seqs, num_heads, head_dim_v] in out_dtype (PA_F32 or q_dtype);
+ *   block_tables [num_seqs, max_blocks]; seq_lens [num_seqs] (device int32).
+ * partition_size == 0: one pass per (sequence, kv head).
+ * partition_size > 0 (a multiple of block_size): split-KV, after
+ * "paged_attention_v2_pytorch.py".  Partition p covers positions
+ * [p * partition_size, (p + 1) * partition_size); for p < ceil(seq_len /
+ * partition_size) the call stores, in caller-owned float32 workspaces,
+ *   max_logits [num_seqs, num_heads, max_partitions]  max score over the partition,
+ *   exp_sums   [num_seqs, num_heads, max_partitions]  sum of exp(score - max),
+ *   tmp_out    [num_seqs, num_heads, max_partitions, head_dim_v]  the partition's
+ *              softmax-normalised output,
+ * with (-inf, 0, 0) for a partition outside the window; entries at larger p are
+ * not touched.  A second kernel then combines the partitions into out with
+ * log-sum-exp weights exp_sums * exp(max_logits - max).  The workspaces may be NULL
+ * when partition_size == 0.
+ * Device checks (with status): seq_len >= 1, ceil(seq_len / block_size) <=
+ * max_blocks, the first ceil(seq_len / block_size) ids in [0, num_blocks), and
+ * ceil(seq_len / partition_size) <= max_partitions.
+ * Supported: head_dim_k == head_dim_v in {32, 64, 128, 256}; num_heads /
+ * num_kv_heads <= 16; any block_size. */
+int pa_decode(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out, int32_t out_dtype,
+              const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
+              int32_t num_seqs, int32_t num_heads, float scale, int32_t sliding_window,
+              int32_t partition_size, int32_t max_partitions, float* max_logits, float* exp_sums,
+              float* tmp_out, int32_t* status, void* stream);
+
+/* Variable-length attention over many sequences in one call (TensorSharp page,
+ * Forward; "cpu_mla_prefill.cpp", MlaPrefillAttention): prefill chunks and single
+ * decode tokens mixed.  Sequence s owns query tokens [query_start_loc[s],
+ * query_start_loc[s + 1]) of q [num_tokens, num_heads, head_dim_k] and holds
+ * seq_lens[s] >= 0 cached positions.  positions [num_tokens] give each token's
+ * absolute position (used for the causal bound only; may be NULL when causal == 0).
+ * out [num_tokens, num_heads, head_dim_v] in out_dtype (PA_F32 or q_dtype);
+ * lse [num_heads, num_tokens] float32, nullable.  max_query_len is an upper bound on
+ * any sequence's token count (sizes the grid).  A row that sees nothing gets
+ * out = 0 and lse = -inf; sequences with no tokens are skipped.
+ * Device checks (with status): query_start_loc[0] == 0, non-decreasing, last entry
+ * == num_tokens; every token count <= max_query_len; seq_len >= 0;
+ * ceil(seq_len / block_size) <= max_blocks with those ids in [0, num_blocks); when
+ * causal, every position in [0, seq_len).
+ * Supported: (head_dim_k, head_dim_v) in {(32,32), (64,64), (128,128), (256,256),
+ * (192,128)}; num_heads / num_kv_heads <= 16; any block_size. */
+int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out, int32_t out_dtype,
+              float* lse, const int32_t* query_start_loc, const int32_t* seq_lens,
+              const int32_t* positions, const int32_t* block_tables, int32_t max_blocks,
+              int32_t num_seqs, int64_t num_tokens, int32_t max_query_len, int32_t num_heads,
+              float scale, int32_t causal, int32_t sliding_window, int32_t* status, void* stream);
+
+/* Merge two attention states over disjoint key sets ("cpu_mla_prefill.cpp",
+ * MergeAttnStates).  prefix_out, suffix_out, out: [num_tokens, num_heads, head_dim] in
+ * dtype; prefix_lse, suffix_lse, out_lse (nullable): float32 [num_heads, num_tokens].
+ * Tokens t >= prefill_tokens_with_context (when that is >= 0) copy the suffix state.
+ * Otherwise an lse of +inf is treated as -inf; if both are then -inf the prefix
+ * output is copied and out_lse = -inf; else with M = max of the two, weights
+ * exp(lse - M) are normalised, the outputs blended and out_lse = M + ln(sum of
+ * weights).  out may alias prefix_out or suffix_out. */
+int pa_merge_states(void* out, float* out_lse, const void* prefix_out, const float* prefix_lse,
+                    const void* suffix_out, const float* suffix_lse, int64_t num_tokens,
+                    int32_t num_heads, int32_t head_dim, int64_t prefill_tokens_with_context,
+                    int32_t dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

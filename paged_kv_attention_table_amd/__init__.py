@@ -1,0 +1,7 @@
+"""Batched paged attention over a block-pooled KV cache for AMD MI355X (gfx950).
+
+The compute lives in libpa.so (hand-written HIP kernels behind the C ABI of
+include/pa.h); ``binding`` exposes its entry points to torch tensors on the GPU.
+"""
+from .binding import (PaError, PaKvPool, load, make_pool, pa_decode, pa_merge_states,  # noqa: F401
+                      pa_varlen, pa_write_kv, strerror)

@@ -1,0 +1,75 @@
+"""Chunked-context prefill: each request's new tokens attend non-causally to its
+cached context, read in fixed-size chunks, and causally to themselves; the partial
+states are merged by their log-sum-exp ("cpu_mla_prefill.cpp": MlaPrefillAttention
+for each piece, MergeAttnStates to combine them).
+
+The page cites this composition (a chunked-context driver over the gather, prefill
+and merge kernels) without printing it; the order used here is
+    state <- chunk 0;  state <- merge(state, chunk c) for c = 1 .. C-1;
+    out   <- merge(state, new tokens causal).
+A request whose context ends before chunk c contributes an empty (-inf) state for
+it, which the merge rules absorb.
+
+The plan holds only device metadata and workspaces; ``run`` issues pa_varlen and
+pa_merge_states calls on the current stream.  No arithmetic happens here.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from .binding import pa_merge_states, pa_varlen
+
+
+class ChunkedPrefillPlan:
+    def __init__(self, *, ctx_lens, new_lens, ctx_tables, new_tables, chunk, block_size, num_heads, head_dim_v,
+                 scale, device="cuda"):
+        ctx_lens = np.asarray(ctx_lens, dtype=np.int64)
+        new_lens = np.asarray(new_lens, dtype=np.int64)
+        if chunk % block_size:
+            raise ValueError("chunk must be a multiple of block_size")
+        R = ctx_lens.size
+        per = chunk // block_size
+        self.scale = float(scale)
+        self.num_chunks = int((ctx_lens.max() + chunk - 1) // chunk) if R and ctx_lens.max() > 0 else 0
+        pad = int(ctx_tables.max()) if ctx_tables.size else 0
+        self.chunks = []
+        for c in range(self.num_chunks):
+            lens = np.clip(ctx_lens - c * chunk, 0, chunk).astype(np.int32)
+            tab = np.full((R, per), pad, dtype=np.int32)
+            src = np.asarray(ctx_tables)[:, c * per:(c + 1) * per]
+            tab[:, :src.shape[1]] = src
+            self.chunks.append((torch.from_numpy(lens).to(device), torch.from_numpy(tab).to(device)))
+        qsl = np.zeros(R + 1, dtype=np.int32)
+        qsl[1:] = np.cumsum(new_lens)
+        self.T = int(qsl[-1])
+        self.max_q = int(new_lens.max()) if R else 0
+        self.qsl = torch.from_numpy(qsl).to(device)
+        self.new_lens = torch.from_numpy(new_lens.astype(np.int32)).to(device)
+        self.new_tables = torch.from_numpy(np.ascontiguousarray(new_tables, dtype=np.int32)).to(device)
+        self.positions = torch.from_numpy(
+            np.concatenate([np.arange(n, dtype=np.int32) for n in new_lens]) if self.T else np.zeros(0, np.int32)
+        ).to(device)
+        H, Dv = num_heads, head_dim_v
+        f32 = dict(dtype=torch.float32, device=device)
+        self.state_out = torch.empty((self.T, H, Dv), **f32)
+        self.state_lse = torch.empty((H, self.T), **f32)
+        self.piece_out = torch.empty((self.T, H, Dv), **f32)
+        self.piece_lse = torch.empty((H, self.T), **f32)
+
+    def run(self, k_pool, v_pool, q, out, out_lse=None, stream=None):
+        """out [T, H, Dv] (float32) <- attention of q over context chunks + new tokens."""
+        for c, (lens, tab) in enumerate(self.chunks):
+            dst_out, dst_lse = (self.state_out, self.state_lse) if c == 0 else (self.piece_out, self.piece_lse)
+            pa_varlen(k_pool, v_pool, q, dst_out, self.qsl, lens, None, tab, self.max_q, self.scale, causal=False,
+                      lse=dst_lse, stream=stream)
+            if c > 0:
+                pa_merge_states(self.state_out, self.state_lse, self.state_out, self.state_lse, self.piece_out,
+                                self.piece_lse, stream=stream)
+        if not self.chunks:
+            pa_varlen(k_pool, v_pool, q, out, self.qsl, self.new_lens, self.positions, self.new_tables, self.max_q,
+                      self.scale, causal=True, lse=out_lse, stream=stream)
+            return
+        pa_varlen(k_pool, v_pool, q, self.piece_out, self.qsl, self.new_lens, self.positions, self.new_tables,
+                  self.max_q, self.scale, causal=True, lse=self.piece_lse, stream=stream)
+        pa_merge_states(out, out_lse, self.state_out, self.state_lse, self.piece_out, self.piece_lse, stream=stream)

@@ -1,0 +1,288 @@
+// The C entry points declared in include/pa.h: synchronous argument checks, then
+// kernel launches on the caller's stream.  The library allocates nothing.
+#include <math.h>
+
+#include "pa_common.h"
+#include "pa_internal.h"
+
+namespace pa {
+hipError_t launch_rows_f32(const RowsArgs& a, int dk, int dv, dim3 grid, hipStream_t stream);
+hipError_t launch_rows_f16(const RowsArgs& a, int dk, int dv, dim3 grid, hipStream_t stream);
+hipError_t launch_rows_bf16(const RowsArgs& a, int dk, int dv, dim3 grid, hipStream_t stream);
+
+hipError_t launch_rows(const RowsArgs& a, int dtype, int dk, int dv, dim3 grid, hipStream_t stream) {
+  if (dtype == PA_F32) return launch_rows_f32(a, dk, dv, grid, stream);
+  if (dtype == PA_F16) return launch_rows_f16(a, dk, dv, grid, stream);
+  if (dtype == PA_BF16) return launch_rows_bf16(a, dk, dv, grid, stream);
+  return hipErrorInvalidValue;
+}
+
+bool rows_supported(int dtype, int dk, int dv, int group) {
+  if (dtype != PA_F32 && dtype != PA_F16 && dtype != PA_BF16) return false;
+  const bool dims = (dk == dv && (dk == 32 || dk == 64 || dk == 128 || dk == 256)) || (dk == 192 && dv == 128);
+  if (!dims || group < 1 || group > 16) return false;
+  if (group > 8 && dv > 128) return false;
+  return true;
+}
+}  // namespace pa
+
+using namespace pa;
+
+namespace {
+
+int element_bytes(int dtype) {
+  switch (dtype) {
+    case PA_F32: return 4;
+    case PA_F16:
+    case PA_BF16: return 2;
+    default: return 0;
+  }
+}
+
+int check_pool(const pa_kv_pool* pool) {
+  if (pool == nullptr || pool->k == nullptr || pool->v == nullptr) return PA_EINVAL;
+  if (pool->num_blocks < 1 || pool->block_size < 1 || pool->num_kv_heads < 1 || pool->head_dim_k < 1 ||
+      pool->head_dim_v < 1)
+    return PA_EINVAL;
+  if (element_bytes(pool->dtype) == 0) return PA_EUNSUPPORTED;
+  return PA_OK;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_EDEVICE; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_strerror(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_EINVAL: return "invalid argument or device content (block table, length, position or slot)";
+    case PA_ESHAPE: return "shape mismatch (num_heads not a multiple of num_kv_heads, or dims disagree)";
+    case PA_EUNSUPPORTED: return "unsupported element type, head dim or head-group size";
+    case PA_EDEVICE: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+int pa_write_kv(const pa_kv_pool* pool, const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                int64_t num_tokens, int32_t* status, void* stream) {
+  int st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return PA_EINVAL;
+  if (num_tokens > 0 && (k_new == nullptr || v_new == nullptr || slot_mapping == nullptr)) return PA_EINVAL;
+  const int eb = element_bytes(pool->dtype);
+  WriteArgs a;
+  a.k_pool = pool->k;
+  a.v_pool = pool->v;
+  a.num_slots = pool->num_blocks * pool->block_size;
+  a.k_row_bytes = (int64_t)pool->num_kv_heads * pool->head_dim_k * eb;
+  a.v_row_bytes = (int64_t)pool->num_kv_heads * pool->head_dim_v * eb;
+  if (a.k_row_bytes % 4 != 0 || a.v_row_bytes % 4 != 0) return PA_EUNSUPPORTED;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.status = status;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (status != nullptr) {
+    ValidateArgs v = {};
+    v.mode = kValidateWrite;
+    v.num_blocks = pool->num_blocks;
+    v.block_size = pool->block_size;
+    v.slot_mapping = slot_mapping;
+    v.num_new_tokens = num_tokens;
+    v.status = status;
+    st = from_hip(launch_validate(v, s));
+    if (st != PA_OK) return st;
+  }
+  if (num_tokens == 0) return PA_OK;
+  return from_hip(launch_write(a, s));
+}
+
+int pa_decode(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out, int32_t out_dtype,
+              const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens, int32_t num_seqs,
+              int32_t num_heads, float scale, int32_t sliding_window, int32_t partition_size,
+              int32_t max_partitions, float* max_logits, float* exp_sums, float* tmp_out, int32_t* status,
+              void* stream) {
+  int st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_heads < 1 || max_blocks < 1 || partition_size < 0) return PA_EINVAL;
+  if (num_seqs > 0 && (q == nullptr || out == nullptr || block_tables == nullptr || seq_lens == nullptr))
+    return PA_EINVAL;
+  if (num_heads % pool->num_kv_heads != 0) return PA_ESHAPE;
+  if (pool->head_dim_k != pool->head_dim_v) return PA_EUNSUPPORTED;
+  if (q_dtype != pool->dtype) return PA_EUNSUPPORTED;
+  if (out_dtype != PA_F32 && out_dtype != q_dtype) return PA_EUNSUPPORTED;
+  const int group = num_heads / pool->num_kv_heads;
+  if (!rows_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group)) return PA_EUNSUPPORTED;
+  if (!isfinite(scale)) return PA_EINVAL;
+  if (partition_size > 0) {
+    if (partition_size % pool->block_size != 0) return PA_EINVAL;
+    if (max_partitions < 1 || max_logits == nullptr || exp_sums == nullptr || tmp_out == nullptr)
+      return PA_EINVAL;
+    if (max_partitions > 8192) return PA_EUNSUPPORTED;
+  }
+  if (num_seqs > 65535 * 1024) return PA_EUNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (status != nullptr) {
+    ValidateArgs v = {};
+    v.mode = kValidateDecode;
+    v.num_blocks = pool->num_blocks;
+    v.block_size = pool->block_size;
+    v.block_tables = block_tables;
+    v.max_blocks = max_blocks;
+    v.seq_lens = seq_lens;
+    v.num_seqs = num_seqs;
+    v.partition_size = partition_size;
+    v.max_partitions = max_partitions;
+    v.status = status;
+    st = from_hip(launch_validate(v, s));
+    if (st != PA_OK) return st;
+  }
+  if (num_seqs == 0) return PA_OK;
+
+  RowsArgs a = {};
+  a.k_pool = pool->k;
+  a.v_pool = pool->v;
+  a.num_blocks = pool->num_blocks;
+  a.block_size = pool->block_size;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.q = q;
+  a.out = out;
+  a.out_dtype = out_dtype;
+  a.lse = nullptr;
+  a.block_tables = block_tables;
+  a.max_blocks = max_blocks;
+  a.seq_lens = seq_lens;
+  a.query_start_loc = nullptr;
+  a.positions = nullptr;
+  a.num_seqs = num_seqs;
+  a.num_rows = num_seqs;
+  a.num_heads = num_heads;
+  a.group = group;
+  a.scale_log2 = scale * kLog2e;
+  a.causal = 1;
+  a.window = sliding_window;
+  a.partition_size = partition_size;
+  a.max_partitions = partition_size > 0 ? max_partitions : 1;
+  a.max_logits = max_logits;
+  a.exp_sums = exp_sums;
+  a.tmp_out = tmp_out;
+  a.status = status;
+  const dim3 grid((unsigned)num_seqs, (unsigned)pool->num_kv_heads, (unsigned)(partition_size > 0 ? max_partitions : 1));
+  st = from_hip(launch_rows(a, pool->dtype, pool->head_dim_k, pool->head_dim_v, grid, s));
+  if (st != PA_OK || partition_size == 0) return st;
+
+  ReduceArgs r = {};
+  r.max_logits = max_logits;
+  r.exp_sums = exp_sums;
+  r.tmp_out = tmp_out;
+  r.seq_lens = seq_lens;
+  r.max_blocks = max_blocks;
+  r.block_size = pool->block_size;
+  r.num_seqs = num_seqs;
+  r.num_heads = num_heads;
+  r.head_dim = pool->head_dim_v;
+  r.partition_size = partition_size;
+  r.max_partitions = max_partitions;
+  r.out = out;
+  r.out_dtype = out_dtype;
+  r.status = status;
+  return from_hip(launch_reduce(r, s));
+}
+
+int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out, int32_t out_dtype, float* lse,
+              const int32_t* query_start_loc, const int32_t* seq_lens, const int32_t* positions,
+              const int32_t* block_tables, int32_t max_blocks, int32_t num_seqs, int64_t num_tokens,
+              int32_t max_query_len, int32_t num_heads, float scale, int32_t causal, int32_t sliding_window,
+              int32_t* status, void* stream) {
+  int st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_tokens < 0 || num_heads < 1 || max_blocks < 1 || max_query_len < 0) return PA_EINVAL;
+  if (query_start_loc == nullptr) return PA_EINVAL;
+  if (num_seqs > 0 && (seq_lens == nullptr || block_tables == nullptr)) return PA_EINVAL;
+  if (num_tokens > 0 && (q == nullptr || out == nullptr || num_seqs == 0)) return PA_EINVAL;
+  if (causal && num_tokens > 0 && positions == nullptr) return PA_EINVAL;
+  if (num_heads % pool->num_kv_heads != 0) return PA_ESHAPE;
+  if (q_dtype != pool->dtype) return PA_EUNSUPPORTED;
+  if (out_dtype != PA_F32 && out_dtype != q_dtype) return PA_EUNSUPPORTED;
+  const int group = num_heads / pool->num_kv_heads;
+  if (!rows_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group)) return PA_EUNSUPPORTED;
+  if (!isfinite(scale)) return PA_EINVAL;
+  if (num_tokens > 0x7fffffffLL) return PA_EUNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (status != nullptr) {
+    ValidateArgs v = {};
+    v.mode = kValidateVarlen;
+    v.num_blocks = pool->num_blocks;
+    v.block_size = pool->block_size;
+    v.block_tables = block_tables;
+    v.max_blocks = max_blocks;
+    v.seq_lens = seq_lens;
+    v.num_seqs = num_seqs;
+    v.query_start_loc = query_start_loc;
+    v.num_tokens = num_tokens;
+    v.max_query_len = max_query_len;
+    v.positions = positions;
+    v.causal = causal;
+    v.status = status;
+    st = from_hip(launch_validate(v, s));
+    if (st != PA_OK) return st;
+  }
+  if (num_tokens == 0) return PA_OK;
+
+  RowsArgs a = {};
+  a.k_pool = pool->k;
+  a.v_pool = pool->v;
+  a.num_blocks = pool->num_blocks;
+  a.block_size = pool->block_size;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.q = q;
+  a.out = out;
+  a.out_dtype = out_dtype;
+  a.lse = lse;
+  a.block_tables = block_tables;
+  a.max_blocks = max_blocks;
+  a.seq_lens = seq_lens;
+  a.query_start_loc = query_start_loc;
+  a.positions = causal ? positions : nullptr;
+  a.num_seqs = num_seqs;
+  a.num_rows = num_tokens;
+  a.num_heads = num_heads;
+  a.group = group;
+  a.scale_log2 = scale * kLog2e;
+  a.causal = causal ? 1 : 0;
+  a.window = sliding_window;
+  a.partition_size = 0;
+  a.max_partitions = 1;
+  a.status = status;
+  const dim3 grid((unsigned)num_tokens, (unsigned)pool->num_kv_heads, 1);
+  return from_hip(launch_rows(a, pool->dtype, pool->head_dim_k, pool->head_dim_v, grid, s));
+}
+
+int pa_merge_states(void* out, float* out_lse, const void* prefix_out, const float* prefix_lse,
+                    const void* suffix_out, const float* suffix_lse, int64_t num_tokens, int32_t num_heads,
+                    int32_t head_dim, int64_t prefill_tokens_with_context, int32_t dtype, void* stream) {
+  if (num_tokens < 0 || num_heads < 1 || head_dim < 1) return PA_EINVAL;
+  if (element_bytes(dtype) == 0) return PA_EUNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (out == nullptr || prefix_out == nullptr || prefix_lse == nullptr || suffix_out == nullptr ||
+      suffix_lse == nullptr)
+    return PA_EINVAL;
+  MergeArgs a;
+  a.out = out;
+  a.out_lse = out_lse;
+  a.prefix_out = prefix_out;
+  a.prefix_lse = prefix_lse;
+  a.suffix_out = suffix_out;
+  a.suffix_lse = suffix_lse;
+  a.num_tokens = num_tokens;
+  a.num_heads = num_heads;
+  a.head_dim = head_dim;
+  a.with_prefix = prefill_tokens_with_context < 0 ? num_tokens : prefill_tokens_with_context;
+  a.dtype = dtype;
+  return from_hip(launch_merge(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,117 @@
+// Kernel argument blocks and launcher declarations shared by the host entry points
+// (pa_api.hip) and the kernel translation units.  Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// One workgroup answers one query row for one kv head (all q heads of its group),
+// optionally restricted to one context partition.
+struct RowsArgs {
+  const void* k_pool;
+  const void* v_pool;
+  int64_t num_blocks;
+  int block_size;
+  int num_kv_heads;
+  const void* q;
+  void* out;
+  int out_dtype;
+  float* lse;  // [H, rows], nullable
+  const int32_t* block_tables;
+  int max_blocks;
+  const int32_t* seq_lens;
+  const int32_t* query_start_loc;  // nullptr: decode (row = sequence, query at n - 1)
+  const int32_t* positions;        // varlen causal positions, nullable
+  int num_seqs;
+  int64_t num_rows;  // decode: sequences; varlen: tokens
+  int num_heads;
+  int group;  // q heads per kv head
+  float scale_log2;
+  int causal;
+  int window;
+  int partition_size;  // 0: whole visible range
+  int max_partitions;
+  float* max_logits;
+  float* exp_sums;
+  float* tmp_out;
+  const int32_t* status;
+};
+
+struct ValidateArgs {
+  int mode;  // kValidateWrite / kValidateDecode / kValidateVarlen
+  int64_t num_blocks;
+  int block_size;
+  const int32_t* slot_mapping;
+  int64_t num_new_tokens;
+  const int32_t* block_tables;
+  int max_blocks;
+  const int32_t* seq_lens;
+  int num_seqs;
+  int partition_size;
+  int max_partitions;
+  const int32_t* query_start_loc;
+  int64_t num_tokens;
+  int max_query_len;
+  const int32_t* positions;
+  int causal;
+  int32_t* status;
+};
+constexpr int kValidateWrite = 0;
+constexpr int kValidateDecode = 1;
+constexpr int kValidateVarlen = 2;
+
+struct WriteArgs {
+  void* k_pool;
+  void* v_pool;
+  int64_t num_slots;
+  int64_t k_row_bytes;  // num_kv_heads * head_dim_k * element bytes
+  int64_t v_row_bytes;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* slot_mapping;
+  int64_t num_tokens;
+  const int32_t* status;
+};
+
+struct ReduceArgs {
+  const float* max_logits;
+  const float* exp_sums;
+  const float* tmp_out;
+  const int32_t* seq_lens;
+  int max_blocks;
+  int block_size;
+  int num_seqs;
+  int num_heads;
+  int head_dim;
+  int partition_size;
+  int max_partitions;
+  void* out;
+  int out_dtype;
+  const int32_t* status;
+};
+
+struct MergeArgs {
+  void* out;
+  float* out_lse;
+  const void* prefix_out;
+  const float* prefix_lse;
+  const void* suffix_out;
+  const float* suffix_lse;
+  int64_t num_tokens;
+  int num_heads;
+  int head_dim;
+  int64_t with_prefix;  // tokens at or past this index copy the suffix
+  int dtype;
+};
+
+// Returns hipErrorInvalidValue (without launching) for a combination not built.
+hipError_t launch_rows(const RowsArgs& a, int dtype, int dk, int dv, dim3 grid, hipStream_t stream);
+hipError_t launch_validate(const ValidateArgs& a, hipStream_t stream);
+hipError_t launch_write(const WriteArgs& a, hipStream_t stream);
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+bool rows_supported(int dtype, int dk, int dv, int group);
+
+}  // namespace pa

@@ -1,0 +1,10 @@
+// F16 instantiations of the per-row paged attention kernel.
+#include "pa_rows.h"
+
+namespace pa {
+
+hipError_t launch_rows_f16(const RowsArgs& a, int dk, int dv, dim3 grid, hipStream_t stream) {
+  return launch_rows_typed<F16>(a, dk, dv, grid, stream);
+}
+
+}  // namespace pa

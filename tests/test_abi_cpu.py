@@ -1,0 +1,117 @@
+"""The C-ABI library without a GPU: it loads, exports every function include/pa.h
+declares, and refuses bad arguments synchronously (these checks run on the host
+before any HIP call, so they need no device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_kv_attention_table_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "pa.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(pa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("pa_write_kv", "pa_decode", "pa_varlen", "pa_merge_states", "pa_strerror"):
+        assert n in names, names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = binding.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(binding.EXPORTS)
+
+
+def test_strerror_texts():
+    for code in range(5):
+        assert binding.strerror(code)
+    assert binding.strerror(99) == "unknown status"
+
+
+def _pool(**kw):
+    d = dict(k=0x1000, v=0x2000, num_blocks=4, block_size=16, num_kv_heads=2, head_dim_k=64, head_dim_v=64,
+             dtype=binding.PA_F16)
+    d.update(kw)
+    return binding.PaKvPool(d["k"], d["v"], d["num_blocks"], d["block_size"], d["num_kv_heads"], d["head_dim_k"],
+                            d["head_dim_v"], d["dtype"])
+
+
+FAKE = ctypes.c_void_p(0x3000)  # never dereferenced: every case below fails before any launch
+
+
+@pytest.mark.parametrize("pool,H,expect", [
+    (None, 4, binding.PA_EINVAL),
+    (dict(k=0), 4, binding.PA_EINVAL),
+    (dict(num_blocks=0), 4, binding.PA_EINVAL),
+    (dict(dtype=7), 4, binding.PA_EUNSUPPORTED),
+    ({}, 3, binding.PA_ESHAPE),
+    (dict(head_dim_k=64, head_dim_v=32), 4, binding.PA_EUNSUPPORTED),
+    (dict(head_dim_k=48, head_dim_v=48), 4, binding.PA_EUNSUPPORTED),
+    ({}, 2 * 17, binding.PA_EUNSUPPORTED),
+])
+def test_decode_host_checks(pool, H, expect):
+    lib = binding.load()
+    p = None if pool is None else ctypes.byref(_pool(**pool))
+    st = lib.pa_decode(p, FAKE, binding.PA_F16, FAKE, binding.PA_F32, FAKE, 4, FAKE, 2, H, 0.1, 0, 0, 0, None,
+                       None, None, None, None)
+    assert st == expect
+
+
+def test_decode_partition_checks():
+    lib = binding.load()
+    p = ctypes.byref(_pool())
+    args = lambda P, pmax, ws: (p, FAKE, binding.PA_F16, FAKE, binding.PA_F32, FAKE, 4, FAKE, 2, 4, 0.1, 0, P, pmax,
+                                ws, ws, ws, None, None)
+    assert lib.pa_decode(*args(24, 4, FAKE)) == binding.PA_EINVAL      # not a multiple of the block size
+    assert lib.pa_decode(*args(32, 0, FAKE)) == binding.PA_EINVAL      # no partitions
+    assert lib.pa_decode(*args(32, 4, None)) == binding.PA_EINVAL      # missing workspace
+    assert lib.pa_decode(*args(-16, 4, FAKE)) == binding.PA_EINVAL
+    # q dtype must match the pool, out must be f32 or q's dtype
+    assert lib.pa_decode(p, FAKE, binding.PA_BF16, FAKE, binding.PA_F32, FAKE, 4, FAKE, 2, 4, 0.1, 0, 0, 0, None,
+                         None, None, None, None) == binding.PA_EUNSUPPORTED
+    assert lib.pa_decode(p, FAKE, binding.PA_F16, FAKE, binding.PA_BF16, FAKE, 4, FAKE, 2, 4, 0.1, 0, 0, 0, None,
+                         None, None, None, None) == binding.PA_EUNSUPPORTED
+
+
+def test_varlen_host_checks():
+    lib = binding.load()
+    p = ctypes.byref(_pool())
+    # causal without positions
+    assert lib.pa_varlen(p, FAKE, binding.PA_F16, FAKE, binding.PA_F32, None, FAKE, FAKE, None, FAKE, 4, 2, 10, 8,
+                         4, 0.1, 1, 0, None, None) == binding.PA_EINVAL
+    # no query_start_loc
+    assert lib.pa_varlen(p, FAKE, binding.PA_F16, FAKE, binding.PA_F32, None, None, FAKE, FAKE, FAKE, 4, 2, 10, 8,
+                         4, 0.1, 1, 0, None, None) == binding.PA_EINVAL
+    # tokens but no sequences
+    assert lib.pa_varlen(p, FAKE, binding.PA_F16, FAKE, binding.PA_F32, None, FAKE, FAKE, FAKE, FAKE, 4, 0, 10, 8,
+                         4, 0.1, 1, 0, None, None) == binding.PA_EINVAL
+    assert lib.pa_varlen(p, FAKE, binding.PA_F16, FAKE, binding.PA_F32, None, FAKE, FAKE, FAKE, FAKE, 4, 2, 10, 8,
+                         5, 0.1, 1, 0, None, None) == binding.PA_ESHAPE
+
+
+def test_write_and_merge_host_checks():
+    lib = binding.load()
+    p = ctypes.byref(_pool())
+    assert lib.pa_write_kv(p, FAKE, FAKE, FAKE, -1, None, None) == binding.PA_EINVAL
+    assert lib.pa_write_kv(p, None, FAKE, FAKE, 3, None, None) == binding.PA_EINVAL
+    assert lib.pa_write_kv(ctypes.byref(_pool(head_dim_k=1, head_dim_v=1, num_kv_heads=1)), FAKE, FAKE, FAKE, 3,
+                           None, None) == binding.PA_EUNSUPPORTED
+    assert lib.pa_merge_states(FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 0, 8, -1, 0, None) == binding.PA_EINVAL
+    assert lib.pa_merge_states(FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 2, 8, -1, 9, None) == binding.PA_EUNSUPPORTED
+    assert lib.pa_merge_states(FAKE, None, None, FAKE, FAKE, FAKE, 4, 2, 8, -1, 0, None) == binding.PA_EINVAL
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+
+    t = torch.zeros(2, 2, 2, 2)
+    with pytest.raises(TypeError):
+        binding.make_pool(t, t)

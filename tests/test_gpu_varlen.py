@@ -1,0 +1,229 @@
+"""pa_varlen, pa_merge_states and the chunked-context composition on the GPU against
+the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_attention_table_amd import pa_merge_states, pa_varlen, pa_write_kv
+from paged_kv_attention_table_amd import workloads as W
+from paged_kv_attention_table_amd.chunked import ChunkedPrefillPlan
+from tests.gpu_util import TOL, OnDevice, assert_close, bits_equal, dev, host, threads, workload
+
+pytestmark = pytest.mark.gpu
+
+
+def run_varlen(d, out_dtype=torch.float32, causal=None, window=None):
+    w = d.w
+    causal = w.causal if causal is None else causal
+    window = w.sliding_window if window is None else window
+    T, H = w.num_tokens, w.num_heads
+    out = torch.full((T, H, w.dv), float("nan"), dtype=out_dtype, device="cuda")
+    lse = torch.full((H, T), float("nan"), device="cuda")
+    status = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    max_q = int(np.diff(w.query_start_loc).max()) if w.num_seqs else 0
+    pa_varlen(d.k_pool, d.v_pool, d.q, out, d.qsl, d.seq_lens, d.positions if causal else None, d.tables, max_q,
+              w.scale, causal=causal, sliding_window=window, lse=lse, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    return out, lse
+
+
+def oracle_varlen(orc, d, causal=None, window=None, row_mask=None):
+    w = d.w
+    causal = w.causal if causal is None else causal
+    window = w.sliding_window if window is None else window
+    kp, vp = d.host_pools_after_write(orc)
+    st, out, lse = orc.varlen(kp, vp, w.dtype, w.q, w.dtype, w.query_start_loc, w.seq_lens,
+                              w.positions if causal else None, w.block_tables, w.scale, causal, window,
+                              row_mask=row_mask, threads=threads())
+    assert st == 0
+    return out, lse
+
+
+@pytest.mark.parametrize("name", ["config4-small", "config4", "config4-shuffled"])
+def test_varlen_parity(orc, name):
+    w = workload(name)
+    d = OnDevice(w)
+    out, lse = run_varlen(d)
+    ref, rlse = oracle_varlen(orc, d)
+    assert_close(host(out), ref, TOL[w.dtype], f"{name} out")
+    assert_close(host(lse), rlse, TOL[w.dtype], f"{name} lse")
+
+
+SMALL = [
+    # (dtype, H, Hkv, dk, dv, segments, causal, window, block_size)
+    ("f32", 4, 2, 64, 64, [(0, 37), (20, 1), (5, 16), (90, 3)], True, 0, 16),
+    ("f32", 4, 2, 64, 64, [(0, 37), (20, 1), (5, 16), (90, 3)], False, 25, 16),
+    ("f16", 16, 2, 128, 128, [(3, 50), (140, 1), (0, 1), (33, 17)], True, 40, 8),
+    ("bf16", 6, 6, 192, 128, [(0, 70), (300, 21), (17, 0), (64, 64)], True, 0, 16),
+    ("bf16", 6, 6, 192, 128, [(0, 70), (300, 21), (17, 0), (64, 64)], False, 0, 16),
+    ("bf16", 8, 1, 256, 256, [(10, 33), (1, 1)], True, 0, 32),
+    ("f16", 2, 2, 32, 32, [(0, 9), (19, 5)], True, 3, 4),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_varlen_small_shapes(orc, case):
+    dtype, H, Hkv, dk, dv, segs, causal, window, b = SMALL[case]
+    w = W.make_paged(f"small{case}", 500 + case, dtype=dtype, block_size=b, num_heads=H, num_kv_heads=Hkv, dk=dk,
+                     dv=dv, segments=segs, causal=causal, sliding_window=window)
+    d = OnDevice(w)
+    out, lse = run_varlen(d)
+    ref, rlse = oracle_varlen(orc, d)
+    assert_close(host(out), ref, TOL[dtype], "out")
+    assert_close(host(lse), rlse, TOL[dtype], "lse")
+
+
+def test_varlen_empty_context_rows(orc):
+    """Non-causal rows of a sequence with no cached positions: out 0, lse -inf."""
+    w = W.make_paged("empty", 611, dtype="bf16", block_size=16, num_heads=4, num_kv_heads=2, dk=64, dv=64,
+                     segments=[(40, 3), (0, 0), (25, 2)], causal=False)
+    d = OnDevice(w)
+    lens = d.seq_lens.clone()
+    lens[2] = 0
+    out = torch.full((w.num_tokens, 4, 64), float("nan"), device="cuda")
+    lse = torch.full((4, w.num_tokens), float("nan"), device="cuda")
+    pa_varlen(d.k_pool, d.v_pool, d.q, out, d.qsl, lens, None, d.tables, 3, w.scale, causal=False, lse=lse)
+    torch.cuda.synchronize()
+    o, l = host(out), host(lse)
+    assert np.all(o[3:] == 0) and np.all(np.isneginf(l[:, 3:]))
+    assert np.all(np.isfinite(o[:3])) and np.all(np.isfinite(l[:, :3]))
+
+
+def test_varlen_batch_invariance():
+    """A sequence alone, at a different query offset, gives the same bits."""
+    w = workload("config4-small")
+    d = OnDevice(w)
+    out, lse = run_varlen(d)
+    full, full_lse = host(out), host(lse)
+    qsl = w.query_start_loc
+    for s in range(w.num_seqs):
+        t0, t1 = int(qsl[s]), int(qsl[s + 1])
+        if t1 == t0:
+            continue
+        o = torch.empty((t1 - t0, w.num_heads, w.dv), device="cuda")
+        l = torch.empty((w.num_heads, t1 - t0), device="cuda")
+        pa_varlen(d.k_pool, d.v_pool, d.q[t0:t1].contiguous(), o, dev(np.array([0, t1 - t0], np.int32)),
+                  d.seq_lens[s:s + 1].contiguous(), d.positions[t0:t1].contiguous(), d.tables[s:s + 1].contiguous(),
+                  t1 - t0, w.scale, causal=True, sliding_window=w.sliding_window, lse=l)
+        torch.cuda.synchronize()
+        assert bits_equal(host(o), full[t0:t1]) and bits_equal(host(l), full_lse[:, t0:t1]), f"sequence {s}"
+
+
+# ------------------------------------------------------------------------------------
+# merge
+# ------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("ptwc", [-1, 250])
+def test_merge_parity_and_edge_rows(orc, ptwc):
+    T, H, D = 300, 16, 128
+    po, pl, so, sl, special = W.merge_case(1234, T, H, D)
+    out = torch.full((T, H, D), float("nan"), device="cuda")
+    out_lse = torch.full((H, T), float("nan"), device="cuda")
+    pa_merge_states(out, out_lse, dev(po), dev(pl), dev(so), dev(sl), prefill_tokens_with_context=ptwc)
+    torch.cuda.synchronize()
+    ref, rlse = orc.merge_states(po, pl, so, sl, "f32", ptwc)
+    got, glse = host(out).astype(np.float64), host(out_lse).astype(np.float64)
+    limit = T if ptwc < 0 else ptwc
+    exact = special.T.copy()  # [T, H]
+    exact[limit:] = True
+    regular = ~exact
+    assert np.array_equal(got[exact], ref[exact]), "edge / pass-through rows must be exact copies"
+    assert np.array_equal(glse.T[exact], rlse.T[exact])
+    assert_close(got[regular], ref[regular], 1e-5, "merged out")
+    assert_close(glse.T[regular], rlse.T[regular], 1e-5, "merged lse")
+
+
+def test_merge_bf16_and_aliasing(orc):
+    T, H, D = 64, 8, 64
+    po, pl, so, sl, special = W.merge_case(99, T, H, D, special_fraction=0.2)
+    po16 = W._round_to(po, "bf16")
+    so16 = W._round_to(so, "bf16")
+    out = dev(po16.copy(), "bf16")  # out aliases prefix_out
+    lse = dev(pl.copy())            # out_lse aliases prefix_lse
+    pa_merge_states(out, lse, out, lse, dev(so16, "bf16"), dev(sl))
+    torch.cuda.synchronize()
+    ref, rlse = orc.merge_states(po16, pl, so16, sl, "bf16")
+    got = torch.from_numpy(host(out).view(np.int16)).view(torch.bfloat16).double().numpy()
+    assert np.all(np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref)), "more than one bf16 ulp from the oracle"
+    ex = special.T
+    assert np.array_equal(host(out).view(np.uint16)[ex], W._round_to(ref.astype(np.float32), "bf16")[ex])
+    assert_close(host(lse).T[~ex], rlse.T[~ex], 1e-5, "lse")
+
+
+# ------------------------------------------------------------------------------------
+# chunked-context prefill (MLA-style)
+# ------------------------------------------------------------------------------------
+
+def chunked_on_device(cp):
+    k_pool, v_pool = dev(cp.k_pool, cp.dtype), dev(cp.v_pool, cp.dtype)
+    st = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    pa_write_kv(k_pool, v_pool, dev(cp.k_new, cp.dtype), dev(cp.v_new, cp.dtype), dev(cp.slot_mapping), status=st)
+    plan = ChunkedPrefillPlan(ctx_lens=cp.ctx_lens, new_lens=cp.new_lens, ctx_tables=cp.ctx_tables,
+                              new_tables=cp.new_tables, chunk=cp.chunk, block_size=cp.block_size,
+                              num_heads=cp.num_heads, head_dim_v=cp.dv, scale=cp.scale)
+    q = dev(cp.q, cp.dtype)
+    out = torch.full((cp.num_tokens, cp.num_heads, cp.dv), float("nan"), device="cuda")
+    lse = torch.full((cp.num_heads, cp.num_tokens), float("nan"), device="cuda")
+    plan.run(k_pool, v_pool, q, out, lse)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    return host(out), host(lse)
+
+
+def oracle_chunked(orc, cp, rows):
+    """The whole result by definition: token i of request r sees every context
+    position and new positions 0..i, gathered explicitly through both tables."""
+    kp, vp = cp.k_pool.copy(), cp.v_pool.copy()
+    assert orc.write_kv(kp, vp, cp.dtype, cp.k_new, cp.v_new, cp.slot_mapping) == 0
+    qsl = cp.query_start_loc
+    q64 = orc.decode_elems(cp.q, cp.dtype)
+    want = {}
+    for r in range(cp.ctx_lens.size):
+        ctx, n = int(cp.ctx_lens[r]), int(cp.new_lens[r])
+        sel = [(t, h) for (t, h) in rows if qsl[r] <= t < qsl[r + 1]]
+        if not sel:
+            continue
+        K = np.concatenate([orc.gather(kp, cp.dtype, cp.block_size, cp.ctx_tables[r], ctx),
+                            orc.gather(kp, cp.dtype, cp.block_size, cp.new_tables[r], n)])
+        V = np.concatenate([orc.gather(vp, cp.dtype, cp.block_size, cp.ctx_tables[r], ctx),
+                            orc.gather(vp, cp.dtype, cp.block_size, cp.new_tables[r], n)])
+        for h in sorted({h for _, h in sel}):
+            ts = [t for (t, hh) in sel if hh == h]
+            i = np.array(ts) - qsl[r]
+            o, l = orc.attend_gathered(q64[ts, h], K[:, h], V[:, h], np.zeros_like(i), ctx + i + 1, cp.scale)
+            for k, t in enumerate(ts):
+                want[(t, h)] = (o[k], l[k])
+    return want
+
+
+@pytest.mark.parametrize("name", ["config5-small", "config5-small-permuted"])
+def test_chunked_prefill_small(orc, name):
+    cp = workload(name)
+    out, lse = chunked_on_device(cp)
+    rows = [(t, h) for t in range(cp.num_tokens) for h in range(cp.num_heads)]
+    want = oracle_chunked(orc, cp, rows)
+    ref = np.stack([want[r][0] for r in rows]).reshape(out.shape)
+    rlse = np.array([want[r][1] for r in rows]).reshape(cp.num_tokens, cp.num_heads).T
+    assert_close(out, ref, TOL[cp.dtype], "out")
+    assert_close(lse, rlse, TOL[cp.dtype], "lse")
+
+
+def test_chunked_prefill_full_sampled(orc):
+    """Full-size MLA-style workload; the oracle answers 4 seeded heads x 24 seeded
+    tokens per request (always including each request's first and last token)."""
+    cp = workload("config5")
+    out, lse = chunked_on_device(cp)
+    rng = np.random.default_rng(5005)
+    qsl = cp.query_start_loc
+    rows = []
+    for r in range(cp.ctx_lens.size):
+        toks = {int(qsl[r]), int(qsl[r + 1]) - 1} | set(rng.integers(qsl[r], qsl[r + 1], size=22).tolist())
+        heads = rng.choice(cp.num_heads, size=4, replace=False)
+        rows += [(t, int(h)) for t in sorted(toks) for h in heads]
+    want = oracle_chunked(orc, cp, rows)
+    got = np.stack([out[t, h] for t, h in rows])
+    ref = np.stack([want[r][0] for r in rows])
+    assert_close(got, ref, TOL[cp.dtype], "sampled out")
+    assert_close(np.array([lse[h, t] for t, h in rows]), np.array([want[r][1] for r in rows]), TOL[cp.dtype],
+                 "sampled lse")
