@@ -108,6 +108,99 @@ def cpu_baseline_decode(w, budget_s):
             "sample": f"first {take} of {S} sequences, whole decode call (gather + two-pass fp64), {dt:.2f} s"}
 
 
+def varlen_flops(w):
+    """Algorithmic flops of one varlen call: visible (query, key) pairs times
+    2 * (head_dim_k + head_dim_v), summed over q heads."""
+    total = 0
+    for s in range(w.num_seqs):
+        t0, t1 = int(w.query_start_loc[s]), int(w.query_start_loc[s + 1])
+        pos = w.positions[t0:t1].astype(np.int64)
+        end = pos + 1 if w.causal else np.full(t1 - t0, int(w.seq_lens[s]))
+        start = np.maximum(0, end - w.sliding_window) if w.sliding_window > 0 else np.zeros_like(end)
+        total += int((end - start).sum())
+    return total * w.num_heads * 2 * (w.dk + w.dv)
+
+
+def chunked_flops(cp):
+    total = 0
+    for ctx, n in zip(cp.ctx_lens.astype(np.int64), cp.new_lens.astype(np.int64)):
+        total += n * ctx + n * (n + 1) // 2
+    return int(total) * cp.num_heads * 2 * (cp.dk + cp.dv)
+
+
+def run_prefill(args):
+    """Secondary workloads: mixed varlen (config of 4 prefill chunks + 12 decode
+    tokens) or the MLA-style chunked prefill.  Prints one JSON line in TFLOP/s."""
+    import torch
+
+    from paged_kv_attention_table_amd import pa_varlen, pa_write_kv
+    from paged_kv_attention_table_amd import workloads as W
+    from paged_kv_attention_table_amd.chunked import ChunkedPrefillPlan
+
+    if args.workload == "varlen":
+        w = W.config4()
+        kp, vp = dev(w.k_pool, w.dtype), dev(w.v_pool, w.dtype)
+        q = dev(w.q, w.dtype)
+        qsl, lens, pos, tables = dev(w.query_start_loc), dev(w.seq_lens), dev(w.positions), dev(w.block_tables)
+        k_new, v_new, slots = dev(w.k_new, w.dtype), dev(w.v_new, w.dtype), dev(w.slot_mapping)
+        out = torch.empty((w.num_tokens, w.num_heads, w.dv), device="cuda")
+        lse = torch.empty((w.num_heads, w.num_tokens), device="cuda")
+        max_q = int(np.diff(w.query_start_loc).max())
+        flops = varlen_flops(w)
+
+        def attn():
+            pa_varlen(kp, vp, q, out, qsl, lens, pos, tables, max_q, w.scale, causal=True,
+                      sliding_window=w.sliding_window, lse=lse)
+
+        def step():
+            pa_write_kv(kp, vp, k_new, v_new, slots)
+            attn()
+        name, dtype = w.name, w.dtype
+        cfg = {"workload": name, "prefill_seqs": 4, "decode_seqs": 12, "num_tokens": w.num_tokens,
+               "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.dk,
+               "sliding_window": w.sliding_window, "step": "pa_write_kv + pa_varlen"}
+    else:
+        cp = W.config5()
+        kp, vp = dev(cp.k_pool, cp.dtype), dev(cp.v_pool, cp.dtype)
+        q = dev(cp.q, cp.dtype)
+        k_new, v_new, slots = dev(cp.k_new, cp.dtype), dev(cp.v_new, cp.dtype), dev(cp.slot_mapping)
+        plan = ChunkedPrefillPlan(ctx_lens=cp.ctx_lens, new_lens=cp.new_lens, ctx_tables=cp.ctx_tables,
+                                  new_tables=cp.new_tables, chunk=cp.chunk, block_size=cp.block_size,
+                                  num_heads=cp.num_heads, head_dim_v=cp.dv, scale=cp.scale)
+        out = torch.empty((cp.num_tokens, cp.num_heads, cp.dv), device="cuda")
+        lse = torch.empty((cp.num_heads, cp.num_tokens), device="cuda")
+        flops = chunked_flops(cp)
+
+        def attn():
+            plan.run(kp, vp, q, out, lse)
+
+        def step():
+            pa_write_kv(kp, vp, k_new, v_new, slots)
+            attn()
+        name, dtype = cp.name, cp.dtype
+        cfg = {"workload": name, "requests": int(cp.ctx_lens.size), "num_tokens": cp.num_tokens,
+               "num_heads": cp.num_heads, "head_dim_k": cp.dk, "head_dim_v": cp.dv, "chunk": cp.chunk,
+               "step": "pa_write_kv + chunked pa_varlen + pa_merge_states"}
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    avg_ms, med_ms = time_calls(attn, max(10, args.steps // 2))
+    value = flops / (ms * 1e-3) / 1e12
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+    line = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": dtype, "data": "synthetic", "config": dict(cfg, flops_per_step=flops),
+            "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "avg_ms": round(avg_ms, 5), "median_ms": round(med_ms, 5)}}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -118,8 +211,8 @@ def main():
     from paged_kv_attention_table_amd import pa_decode, pa_write_kv
     from paged_kv_attention_table_amd import workloads as W
 
-    if args.workload not in ("decode", "long"):
-        raise SystemExit("only the decode workloads are wired into this bench so far")
+    if args.workload in ("varlen", "mla"):
+        return run_prefill(args)
     w = W.config2() if args.workload == "decode" else W.config3()
     P = args.partition_size if args.partition_size is not None else 512
     kp, vp = dev(w.k_pool, w.dtype), dev(w.v_pool, w.dtype)

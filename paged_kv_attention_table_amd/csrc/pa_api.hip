@@ -4,6 +4,7 @@
 
 #include "pa_common.h"
 #include "pa_internal.h"
+#include "pa_prefill.h"
 
 namespace pa {
 hipError_t launch_rows_f32(const RowsArgs& a, int dk, int dv, dim3 grid, hipStream_t stream);
@@ -15,6 +16,21 @@ hipError_t launch_rows(const RowsArgs& a, int dtype, int dk, int dv, dim3 grid, 
   if (dtype == PA_F16) return launch_rows_f16(a, dk, dv, grid, stream);
   if (dtype == PA_BF16) return launch_rows_bf16(a, dk, dv, grid, stream);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, int dk, int dv, dim3 grid, hipStream_t stream);
+hipError_t launch_prefill_f16(const PrefillArgs& a, int dk, int dv, dim3 grid, hipStream_t stream);
+
+hipError_t launch_prefill(const PrefillArgs& a, int dtype, int dk, int dv, dim3 grid, hipStream_t stream) {
+  if (dtype == PA_BF16) return launch_prefill_bf16(a, dk, dv, grid, stream);
+  if (dtype == PA_F16) return launch_prefill_f16(a, dk, dv, grid, stream);
+  return hipErrorInvalidValue;
+}
+
+bool prefill_supported(int dtype, int dk, int dv, int group) {
+  if (dtype != PA_BF16 && dtype != PA_F16) return false;
+  const bool dims = (dk == 128 && dv == 128) || (dk == 192 && dv == 128) || (dk == 64 && dv == 64);
+  return dims && group >= 1 && group <= kPrefillRows;
 }
 
 bool rows_supported(int dtype, int dk, int dv, int group) {
@@ -208,9 +224,11 @@ int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
   if (q_dtype != pool->dtype) return PA_EUNSUPPORTED;
   if (out_dtype != PA_F32 && out_dtype != q_dtype) return PA_EUNSUPPORTED;
   const int group = num_heads / pool->num_kv_heads;
-  if (!rows_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group)) return PA_EUNSUPPORTED;
+  if (!rows_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group) &&
+      !prefill_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group))
+    return PA_EUNSUPPORTED;
   if (!isfinite(scale)) return PA_EINVAL;
-  if (num_tokens > 0x7fffffffLL) return PA_EUNSUPPORTED;
+  if (num_tokens > 0x7fffffffLL || num_seqs > 65535) return PA_EUNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (status != nullptr) {
     ValidateArgs v = {};
@@ -257,7 +275,46 @@ int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
   a.partition_size = 0;
   a.max_partitions = 1;
   a.status = status;
-  const dim3 grid((unsigned)num_tokens, (unsigned)pool->num_kv_heads, 1);
+
+  if (!prefill_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group) || max_query_len <= 1) {
+    // every token through the per-row kernel
+    a.single_token_seqs = 0;
+    const dim3 grid((unsigned)num_tokens, (unsigned)pool->num_kv_heads, 1);
+    return from_hip(launch_rows(a, pool->dtype, pool->head_dim_k, pool->head_dim_v, grid, s));
+  }
+  // sequences with several tokens: tiled MFMA kernel; single tokens: per-row kernel
+  PrefillArgs p = {};
+  p.k_pool = pool->k;
+  p.v_pool = pool->v;
+  p.num_blocks = pool->num_blocks;
+  p.block_size = pool->block_size;
+  p.num_kv_heads = pool->num_kv_heads;
+  p.q = q;
+  p.out = out;
+  p.out_dtype = out_dtype;
+  p.lse = lse;
+  p.block_tables = block_tables;
+  p.max_blocks = max_blocks;
+  p.seq_lens = seq_lens;
+  p.query_start_loc = query_start_loc;
+  p.positions = causal ? positions : nullptr;
+  p.num_seqs = num_seqs;
+  p.num_tokens = num_tokens;
+  p.num_heads = num_heads;
+  p.group = group;
+  p.tokens_per_tile = kPrefillRows / group;
+  const bool rows_take_singles = rows_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group);
+  p.min_q_len = rows_take_singles ? 2 : 1;
+  p.scale_log2 = scale * kLog2e;
+  p.causal = causal ? 1 : 0;
+  p.window = sliding_window;
+  p.status = status;
+  const unsigned tiles = (unsigned)((max_query_len + p.tokens_per_tile - 1) / p.tokens_per_tile);
+  st = from_hip(launch_prefill(p, pool->dtype, pool->head_dim_k, pool->head_dim_v,
+                               dim3(tiles, (unsigned)num_seqs, (unsigned)pool->num_kv_heads), s));
+  if (st != PA_OK || !rows_take_singles) return st;
+  a.single_token_seqs = 1;
+  const dim3 grid((unsigned)num_seqs, (unsigned)pool->num_kv_heads, 1);
   return from_hip(launch_rows(a, pool->dtype, pool->head_dim_k, pool->head_dim_v, grid, s));
 }
 

@@ -24,6 +24,7 @@ struct RowsArgs {
   const int32_t* seq_lens;
   const int32_t* query_start_loc;  // nullptr: decode (row = sequence, query at n - 1)
   const int32_t* positions;        // varlen causal positions, nullable
+  int single_token_seqs;           // varlen: row = sequence, only sequences of one token
   int num_seqs;
   int64_t num_rows;  // decode: sequences; varlen: tokens
   int num_heads;
@@ -108,6 +109,9 @@ struct MergeArgs {
 
 // Returns hipErrorInvalidValue (without launching) for a combination not built.
 hipError_t launch_rows(const RowsArgs& a, int dtype, int dk, int dv, dim3 grid, hipStream_t stream);
+struct PrefillArgs;
+hipError_t launch_prefill(const PrefillArgs& a, int dtype, int dk, int dv, dim3 grid, hipStream_t stream);
+bool prefill_supported(int dtype, int dk, int dv, int group);
 hipError_t launch_validate(const ValidateArgs& a, hipStream_t stream);
 hipError_t launch_write(const WriteArgs& a, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);

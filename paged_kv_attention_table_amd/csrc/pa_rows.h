@@ -35,14 +35,6 @@ namespace pa {
 
 constexpr int kRowsWaves = 4;
 
-// Physical row (slot) of position j of a sequence, with the block id clamped into
-// the pool so that unvalidated calls never address outside it.
-__device__ __forceinline__ int64_t slot_of(const int32_t* table, int j, int block_size, int64_t num_blocks) {
-  int64_t blk = table[j / block_size];
-  blk = blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
-  return blk * block_size + j % block_size;
-}
-
 template <typename T, int DK, int DV, int GMAX>
 __global__ __launch_bounds__(256) void attn_rows_kernel(const RowsArgs a) {
   constexpr int EB = T::bytes;
@@ -77,6 +69,11 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const RowsArgs a) {
   const int b = a.block_size;
   if (a.query_start_loc == nullptr) {
     s = row;
+  } else if (a.single_token_seqs) {
+    s = row;  // one workgroup per sequence; only sequences with exactly one token
+    const int t0 = a.query_start_loc[s];
+    if (a.query_start_loc[s + 1] - t0 != 1) return;
+    q_row = t0;
   } else {
     int lo_s = 0, hi_s = a.num_seqs - 1;  // last s with query_start_loc[s] <= row
     while (lo_s < hi_s) {
@@ -93,7 +90,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const RowsArgs a) {
     pos = n - 1;
     end = n;
   } else if (a.causal) {
-    pos = a.positions[row];
+    pos = a.positions[q_row];
     pos = pos < 0 ? 0 : (pos >= n ? n - 1 : pos);
     end = pos + 1;
   } else {

@@ -59,6 +59,12 @@ SMALL = [
     ("bf16", 6, 6, 192, 128, [(0, 70), (300, 21), (17, 0), (64, 64)], False, 0, 16),
     ("bf16", 8, 1, 256, 256, [(10, 33), (1, 1)], True, 0, 32),
     ("f16", 2, 2, 32, 32, [(0, 9), (19, 5)], True, 3, 4),
+    # tiled kernel: uneven head groups, 16 heads per kv head, head dim 64
+    ("bf16", 6, 2, 128, 128, [(7, 100), (0, 1), (250, 45)], True, 0, 16),
+    ("f16", 32, 2, 128, 128, [(40, 9), (3, 1), (0, 20)], True, 17, 16),
+    ("bf16", 4, 1, 64, 64, [(300, 130), (0, 2), (77, 1)], False, 0, 16),
+    # 32 q heads per kv head: single tokens also go through the tiled kernel
+    ("bf16", 32, 1, 128, 128, [(50, 1), (20, 9), (0, 1)], True, 0, 16),
 ]
 
 
