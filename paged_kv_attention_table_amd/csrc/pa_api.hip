@@ -66,6 +66,14 @@ int check_pool(const pa_kv_pool* pool) {
 
 int from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_EDEVICE; }
 
+// log2(x) when x is a power of two, else -1.
+int pow2_shift(int x) {
+  if (x <= 0 || (x & (x - 1)) != 0) return -1;
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
 }  // namespace
 
 extern "C" {
@@ -302,6 +310,7 @@ int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
   p.num_tokens = num_tokens;
   p.num_heads = num_heads;
   p.group = group;
+  p.block_shift = pow2_shift(pool->block_size);
   p.tokens_per_tile = kPrefillRows / group;
   const bool rows_take_singles = rows_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group);
   p.min_q_len = rows_take_singles ? 2 : 1;

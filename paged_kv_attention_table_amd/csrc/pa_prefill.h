@@ -3,10 +3,12 @@
 // semantics; the online softmax of "Paged attention for decode in C", section 2.2,
 // applied per key tile).
 //
-// Workgroup = (query tile, sequence, kv head g): 128 rows, each a (token, q head)
-// pair of the group, 4 waves of 32 rows (two 16-row blocks).  Key tiles of 32
-// positions aligned to absolute positions are gathered through the block table into
-// LDS (double-buffered, loads for tile t+1 in flight while tile t is computed).
+// Workgroup = (query tile, sequence, kv head g): 256 rows, each a (token, q head)
+// pair of the group, 8 waves of 32 rows (two 16-row blocks).  Key tiles of 32
+// positions aligned to absolute positions are gathered through the block table:
+// global loads for tile t+2 are issued into one of two register sets while tile t
+// is computed from one of two LDS buffers, so each load has two tiles of compute to
+// arrive; the 256 rows share every K/V byte brought in.
 //   S^T[key][row] = K_tile . Q^T  -- 16x16x32 MFMA; A = K rows read from LDS with
 //                                    16-byte reads, B = the rows' q, kept in VGPRs.
 //   O^T[d][row]  += V^T . P^T     -- 16x16x32 MFMA; A = V^T obtained from the
@@ -49,7 +51,8 @@ struct PrefillArgs {
   int64_t num_tokens;
   int num_heads;
   int group;
-  int tokens_per_tile;  // 128 / group (rounded down)
+  int block_shift;      // log2(block_size) when it is a power of two, else -1
+  int tokens_per_tile;  // 256 / group (rounded down)
   int min_q_len;        // sequences with fewer tokens are left to the per-row kernel
   float scale_log2;
   int causal;
@@ -57,7 +60,8 @@ struct PrefillArgs {
   const int32_t* status;
 };
 
-constexpr int kPrefillRows = 128;
+constexpr int kPrefillRows = 256;
+constexpr int kPrefillThreads = 512;
 constexpr int kPrefillKeys = 32;
 
 template <typename T>
@@ -73,25 +77,50 @@ __device__ __forceinline__ f32x4 mfma_16x16x32<F16>(u32x4 a, u32x4 b, f32x4 c) {
                                                 0, 0);
 }
 
-__device__ __forceinline__ uint32_t pack2(uint32_t lo, uint32_t hi) { return lo | (hi << 16); }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to packed 16-bit (round to nearest even), one v_cvt_pk each.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+}
+
+constexpr float kRescaleLog2 = 8.0f;  // move the reference max only past 2^8
+constexpr float kHugeScore = 1.0e30f;
+
+// Per-thread share of one K/V tile, in 16-byte chunks.
+template <int DK, int DV>
+struct TileRegs {
+  static constexpr int KCH = DK / 8, VCH = DV / 8;  // chunks per position
+  static constexpr int KN = (kPrefillKeys * KCH + kPrefillThreads - 1) / kPrefillThreads;
+  static constexpr int VN = (kPrefillKeys * VCH + kPrefillThreads - 1) / kPrefillThreads;
+  u32x4 k[KN];
+  u32x4 v[VN];
+};
 
 template <typename T, int DK, int DV>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(kPrefillThreads, 1) void prefill_kernel(const PrefillArgs a) {
   constexpr int KT = kPrefillKeys;
+  constexpr int NTH = kPrefillThreads;
   constexpr int KPAD = 16;  // elements of padding per LDS row (32 bytes)
   constexpr int KROW = DK + KPAD, VROW = DV + KPAD;
-  constexpr int KCH = DK / 8, VCH = DV / 8;         // 16-byte chunks per row
-  constexpr int KLD = KT * KCH / 256, VLD = KT * VCH / 256;  // chunks per thread
+  using Regs = TileRegs<DK, DV>;
+  constexpr int KCH = Regs::KCH, VCH = Regs::VCH;
   constexpr int KSTEPS = DK / 32;
   constexpr int ND = DV / 16;
-  static_assert(KT * KCH % 256 == 0 && KT * VCH % 256 == 0, "tile split");
 
   __shared__ __align__(16) uint16_t k_lds[2][KT][KROW];
   __shared__ __align__(16) uint16_t v_lds[2][KT][VROW];
   __shared__ int range_lo, range_hi;
 
   if (status_failed(a.status)) return;
-  const int tile = blockIdx.x, s = blockIdx.y, g = blockIdx.z;
+  // Tiles run last-first: under a causal mask the later tiles see more keys, so
+  // the longest workgroups start first.
+  const int tile = gridDim.x - 1 - blockIdx.x, s = blockIdx.y, g = blockIdx.z;
   const int q0 = a.query_start_loc[s];
   const int q_len = a.query_start_loc[s + 1] - q0;
   const int TPT = a.tokens_per_tile;
@@ -160,7 +189,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   for (int nd = 0; nd < ND; ++nd)
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) o[nd][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-INFINITY, -INFINITY};
+  // Finite start for the reference max: rows that see nothing keep l = 0, and no
+  // -inf - -inf ever occurs.
+  float m_run[2] = {-kHugeScore, -kHugeScore};
   float l_run[2] = {0.f, 0.f};
 
   if (klo < khi) {
@@ -169,146 +200,215 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     const char* vbase = static_cast<const char*>(a.v_pool);
     const int hkv = a.num_kv_heads, b = a.block_size;
     const int t_first = klo & ~(KT - 1);
+    const int num_tiles = (khi - t_first + KT - 1) / KT;
 
-    u32x4 kreg[KLD], vreg[VLD];
-    auto fetch = [&](int t0) {
+    // Addresses.  When the block size is a power of two of at least 16, a 32-key
+    // tile aligned to 32 positions spans at most two blocks: their ids are read
+    // with wave-uniform scalar loads (counted apart from the vector loads, so the
+    // K/V prefetches of earlier tiles are not waited for) and turned into two row
+    // base pointers; each thread then adds a fixed in-block offset.  Keys past the
+    // visible range are loaded from valid (clamped) blocks and zeroed when stashed.
+    // Other block sizes look ids up per key.
+    const bool tile_ids = a.block_shift >= 4;
+    const int max_idx = a.max_blocks - 1;
+    const int64_t krow_bytes = (int64_t)hkv * DK * 2, vrow_bytes = (int64_t)hkv * DV * 2;
+    auto tile_bases = [&](int t0, const char*& k0, const char*& k1, const char*& v0, const char*& v1) {
+      const int i0 = __builtin_amdgcn_readfirstlane(t0 >> a.block_shift);
+      const int i1 = i0 + 1 < max_idx ? i0 + 1 : max_idx;
+      int64_t b0 = table[i0], b1 = table[__builtin_amdgcn_readfirstlane(i1)];
+      b0 = b0 < 0 ? 0 : (b0 >= a.num_blocks ? a.num_blocks - 1 : b0);
+      b1 = b1 < 0 ? 0 : (b1 >= a.num_blocks ? a.num_blocks - 1 : b1);
+      k0 = kbase + b0 * b * krow_bytes + (int64_t)g * DK * 2;
+      k1 = kbase + b1 * b * krow_bytes + (int64_t)g * DK * 2;
+      v0 = vbase + b0 * b * vrow_bytes + (int64_t)g * DV * 2;
+      v1 = vbase + b1 * b * vrow_bytes + (int64_t)g * DV * 2;
+    };
+    // global -> registers for tile i
+    auto fetch = [&](int i, Regs& R) {
+      const int t0 = t_first + i * KT;
+      if (tile_ids) {
+        const char *k0, *k1, *v0, *v1;
+        tile_bases(t0, k0, k1, v0, v1);
+        const int i0 = t0 >> a.block_shift;
 #pragma unroll
-      for (int u = 0; u < KLD; ++u) {
-        const int id = tid + 256 * u, key = id / KCH, ch = id % KCH;
-        const int j = t0 + key;
-        if (j >= klo && j < khi) {
-          const int64_t slot = slot_of(table, j, b, a.num_blocks);
-          kreg[u] = *reinterpret_cast<const u32x4*>(kbase + ((slot * hkv + g) * DK + ch * 8) * 2);
-        } else {
-          kreg[u] = u32x4{0u, 0u, 0u, 0u};
+        for (int u = 0; u < Regs::KN; ++u) {
+          const int id = tid + NTH * u, key = (id < KT * KCH ? id : 0) / KCH, ch = id % KCH;
+          const int j = t0 + key;
+          const char* base = (j >> a.block_shift) == i0 ? k0 : k1;
+          R.k[u] = *reinterpret_cast<const u32x4*>(base + (j & (b - 1)) * krow_bytes + ch * 16);
         }
-      }
 #pragma unroll
-      for (int u = 0; u < VLD; ++u) {
-        const int id = tid + 256 * u, key = id / VCH, ch = id % VCH;
-        const int j = t0 + key;
-        if (j >= klo && j < khi) {
-          const int64_t slot = slot_of(table, j, b, a.num_blocks);
-          vreg[u] = *reinterpret_cast<const u32x4*>(vbase + ((slot * hkv + g) * DV + ch * 8) * 2);
-        } else {
-          vreg[u] = u32x4{0u, 0u, 0u, 0u};
+        for (int u = 0; u < Regs::VN; ++u) {
+          const int id = tid + NTH * u, key = (id < KT * VCH ? id : 0) / VCH, ch = id % VCH;
+          const int j = t0 + key;
+          const char* base = (j >> a.block_shift) == i0 ? v0 : v1;
+          R.v[u] = *reinterpret_cast<const u32x4*>(base + (j & (b - 1)) * vrow_bytes + ch * 16);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < Regs::KN; ++u) {
+          const int id = tid + NTH * u, key = (id < KT * KCH ? id : 0) / KCH, ch = id % KCH;
+          int j = t0 + key;
+          j = j < klo ? klo : (j >= khi ? khi - 1 : j);
+          const int64_t slot = slot_fast(table, j, b, a.block_shift, a.num_blocks);
+          R.k[u] = *reinterpret_cast<const u32x4*>(kbase + slot * krow_bytes + (int64_t)g * DK * 2 + ch * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < Regs::VN; ++u) {
+          const int id = tid + NTH * u, key = (id < KT * VCH ? id : 0) / VCH, ch = id % VCH;
+          int j = t0 + key;
+          j = j < klo ? klo : (j >= khi ? khi - 1 : j);
+          const int64_t slot = slot_fast(table, j, b, a.block_shift, a.num_blocks);
+          R.v[u] = *reinterpret_cast<const u32x4*>(vbase + slot * vrow_bytes + (int64_t)g * DV * 2 + ch * 16);
         }
       }
     };
-    auto stash = [&](int buf) {
+    // registers -> LDS buffer, zeros for keys outside [klo, khi) on edge tiles
+    auto stash = [&](const Regs& R, int i, int buf) {
+      const int t0 = t_first + i * KT;
+      const bool edge = t0 < klo || t0 + KT > khi;
+      const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int u = 0; u < KLD; ++u) {
-        const int id = tid + 256 * u, key = id / KCH, ch = id % KCH;
-        *reinterpret_cast<u32x4*>(&k_lds[buf][key][ch * 8]) = kreg[u];
+      for (int u = 0; u < Regs::KN; ++u) {
+        const int id = tid + NTH * u, key = id / KCH, ch = id % KCH;
+        const int j = t0 + key;
+        u32x4 x = R.k[u];
+        if (edge && (j < klo || j >= khi)) x = zero;
+        if (id < KT * KCH) *reinterpret_cast<u32x4*>(&k_lds[buf][key][ch * 8]) = x;
       }
 #pragma unroll
-      for (int u = 0; u < VLD; ++u) {
-        const int id = tid + 256 * u, key = id / VCH, ch = id % VCH;
-        *reinterpret_cast<u32x4*>(&v_lds[buf][key][ch * 8]) = vreg[u];
+      for (int u = 0; u < Regs::VN; ++u) {
+        const int id = tid + NTH * u, key = id / VCH, ch = id % VCH;
+        const int j = t0 + key;
+        u32x4 x = R.v[u];
+        if (edge && (j < klo || j >= khi)) x = zero;
+        if (id < KT * VCH) *reinterpret_cast<u32x4*>(&v_lds[buf][key][ch * 8]) = x;
       }
     };
-
-    fetch(t_first);
-    stash(0);
-    __syncthreads();
-    int buf = 0;
-    for (int t0 = t_first; t0 < khi; t0 += KT) {
-      const bool more = t0 + KT < khi;
-      if (more) fetch(t0 + KT);
-
-      // does any row of this wave see a key of the tile?
+    // one key tile from LDS buffer `buf`
+    auto compute = [&](int i, int buf) {
+      const int t0 = t_first + i * KT;
       bool mine = false;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) mine |= (vis_lo[rb] < t0 + KT) && (vis_hi[rb] > t0) && (vis_lo[rb] < vis_hi[rb]);
-      if (__any(mine)) {
-        // S^T for two 16-key blocks and both row blocks
-        f32x4 sc[2][2];
+      if (!__any(mine)) return;
+      // S^T for two 16-key blocks and both row blocks
+      f32x4 sc[2][2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb) sc[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int rb = 0; rb < 2; ++rb) sc[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int kk = 0; kk < KSTEPS; ++kk) {
-            const u32x4 ka = *reinterpret_cast<const u32x4*>(&k_lds[buf][kb * 16 + r16][32 * kk + 8 * c]);
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+          const u32x4 ka = *reinterpret_cast<const u32x4*>(&k_lds[buf][kb * 16 + r16][32 * kk + 8 * c]);
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) sc[kb][rb] = mfma_16x16x32<T>(ka, qb[rb][kk], sc[kb][rb]);
-          }
+          for (int rb = 0; rb < 2; ++rb) sc[kb][rb] = mfma_16x16x32<T>(ka, qb[rb][kk], sc[kb][rb]);
         }
-        // online softmax per row; P^T packed as the B operand of the PV product
-        u32x4 pb[2], pl[2];
+      }
+      // Online softmax per row, in raw score units: p = 2^((s - m) * c) with
+      // c = scale * log2(e), one fma and one v_exp per score.  The reference max m
+      // is only moved (and O, l rescaled) when the tile max exceeds it by more than
+      // 2^8 in p; otherwise p may exceed 1 by up to 256, which f16 / bf16 and the
+      // fp32 accumulators hold exactly as well, and O / l is unchanged.  Tiles that
+      // lie inside every row's visible range skip the masking.
+      bool inside = true;
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          float sv[8];
-          float mx = -INFINITY;
+      for (int rb = 0; rb < 2; ++rb) inside &= !row_ok[rb] || (vis_lo[rb] <= t0 && vis_hi[rb] >= t0 + KT);
+      const bool masked = !__all(inside);
+      u32x4 pb[2], pl[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        float sv[8];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) sv[kb * 4 + ii] = sc[kb][rb][ii];
+        if (masked) {
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int j = t0 + kb * 16 + 4 * c + i;
-              const bool vis = j >= vis_lo[rb] && j < vis_hi[rb];
-              sv[kb * 4 + i] = vis ? sc[kb][rb][i] * a.scale_log2 : -INFINITY;
-              mx = fmaxf(mx, sv[kb * 4 + i]);
+            for (int ii = 0; ii < 4; ++ii) {
+              const int j = t0 + kb * 16 + 4 * c + ii;
+              if (j < vis_lo[rb] || j >= vis_hi[rb]) sv[kb * 4 + ii] = -INFINITY;
             }
-          mx = fmaxf(mx, shfl_xor(mx, 16));
-          mx = fmaxf(mx, shfl_xor(mx, 32));
+        }
+        float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+        mx = fmaxf(mx, shfl_xor(mx, 16));
+        mx = fmaxf(mx, shfl_xor(mx, 32));
+        if (__any((mx - m_run[rb]) * a.scale_log2 > kRescaleLog2)) {
           const float m_new = fmaxf(m_run[rb], mx);
-          const bool live = m_new != -INFINITY;
-          const float alpha = live ? exp2f(m_run[rb] - m_new) : 1.f;
-          float p[8], psum = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            p[e] = live ? exp2f(sv[e] - m_new) : 0.f;
-            psum += p[e];
-          }
-          l_run[rb] = l_run[rb] * alpha + psum;
-          m_run[rb] = m_new;
+          const float alpha = __builtin_amdgcn_exp2f((m_run[rb] - m_new) * a.scale_log2);
+          l_run[rb] *= alpha;
 #pragma unroll
           for (int nd = 0; nd < ND; ++nd) o[nd][rb] *= alpha;
+          m_run[rb] = m_new;
+        }
+        const float mc = m_run[rb] * a.scale_log2;
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(sv[e], a.scale_log2, -mc));
+        l_run[rb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        if constexpr (T::code == PA_F16) {
+          uint32_t w[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = pack_f16x2(p[2 * e], p[2 * e + 1]);
+          pb[rb] = u32x4{w[0], w[1], w[2], w[3]};
+        } else {
+          uint32_t w[4], wl[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t h = pack_bf16x2(p[2 * e], p[2 * e + 1]);
+            w[e] = h;
+            wl[e] = pack_bf16x2(p[2 * e] - __uint_as_float(h << 16), p[2 * e + 1] - __uint_as_float(h & 0xffff0000u));
+          }
+          pb[rb] = u32x4{w[0], w[1], w[2], w[3]};
+          pl[rb] = u32x4{wl[0], wl[1], wl[2], wl[3]};
+        }
+      }
+      // O^T += V^T P^T, V^T via transpose reads of the row-major V tile
+      const int tr_r = r16 >> 2, tr_q = r16 & 3;
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd) {
+        const i16x4 v0 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&v_lds[buf][4 * c + tr_r][16 * nd + 4 * tr_q]));
+        const i16x4 v1 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&v_lds[buf][16 + 4 * c + tr_r][16 * nd + 4 * tr_q]));
+        const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
+        const u32x4 va = u32x4{w0.x, w0.y, w1.x, w1.y};
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
           if constexpr (T::code == PA_F16) {
-            uint32_t w[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = pack2(narrow<F16>(p[2 * e]), narrow<F16>(p[2 * e + 1]));
-            pb[rb] = u32x4{w[0], w[1], w[2], w[3]};
+            o[nd][rb] = mfma_16x16x32<F16>(va, pb[rb], o[nd][rb]);
           } else {
-            uint32_t w[4], wl[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const uint32_t h0 = narrow<BF16>(p[2 * e]), h1 = narrow<BF16>(p[2 * e + 1]);
-              const float r0 = p[2 * e] - __uint_as_float(h0 << 16), r1 = p[2 * e + 1] - __uint_as_float(h1 << 16);
-              w[e] = pack2(h0, h1);
-              wl[e] = pack2(narrow<BF16>(r0), narrow<BF16>(r1));
-            }
-            pb[rb] = u32x4{w[0], w[1], w[2], w[3]};
-            pl[rb] = u32x4{wl[0], wl[1], wl[2], wl[3]};
-          }
-        }
-        // O^T += V^T P^T, V^T via transpose reads of the row-major V tile
-        const int tr_r = r16 >> 2, tr_q = r16 & 3;
-#pragma unroll
-        for (int nd = 0; nd < ND; ++nd) {
-          const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(&v_lds[buf][4 * c + tr_r][16 * nd + 4 * tr_q]));
-          const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(&v_lds[buf][16 + 4 * c + tr_r][16 * nd + 4 * tr_q]));
-          const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
-          const u32x4 va = u32x4{w0.x, w0.y, w1.x, w1.y};
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb) {
-            if constexpr (T::code == PA_F16) {
-              o[nd][rb] = mfma_16x16x32<F16>(va, pb[rb], o[nd][rb]);
-            } else {
-              o[nd][rb] = mfma_16x16x32<BF16>(va, pb[rb], o[nd][rb]);
-              o[nd][rb] = mfma_16x16x32<BF16>(va, pl[rb], o[nd][rb]);
-            }
+            o[nd][rb] = mfma_16x16x32<BF16>(va, pb[rb], o[nd][rb]);
+            o[nd][rb] = mfma_16x16x32<BF16>(va, pl[rb], o[nd][rb]);
           }
         }
       }
-      if (more) {
-        stash(buf ^ 1);
-        __syncthreads();
-        buf ^= 1;
+    };
+
+    // Software pipeline: while tile i is computed from LDS, tile i + 1 waits in
+    // registers and the loads of tile i + 2 are in flight.
+    Regs RA, RB;
+    fetch(0, RA);
+    if (num_tiles > 1) fetch(1, RB);
+    stash(RA, 0, 0);
+    __syncthreads();
+    // one step: compute tile i, refill `next` with tile i + 2, publish `held` (tile i+1)
+    auto step = [&](int i, Regs& next, Regs& held) {
+      if (i + 2 < num_tiles) fetch(i + 2, next);
+      compute(i, i & 1);
+      if (i + 1 < num_tiles) {
+        stash(held, i + 1, (i + 1) & 1);
+        lds_barrier();
       }
+    };
+    int i = 0;
+    for (; i + 1 < num_tiles; i += 2) {
+      step(i, RA, RB);
+      step(i + 1, RB, RA);
     }
+    if (i < num_tiles) step(i, RA, RB);
   }
 
   // --- finish: sum the lane groups' exp-sums, normalise, write ---------------------
@@ -328,17 +428,18 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
         *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + obase + d0) = v;
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) store_as(a.out, a.out_dtype, obase + d0 + i, v[i]);
+        for (int ii = 0; ii < 4; ++ii) store_as(a.out, a.out_dtype, obase + d0 + ii, v[ii]);
       }
     }
     if (a.lse != nullptr && c == 0)
-      a.lse[(int64_t)row_head[rb] * a.num_tokens + row_tok[rb]] = l > 0.f ? (m_run[rb] + log2f(l)) * kLn2 : -INFINITY;
+      a.lse[(int64_t)row_head[rb] * a.num_tokens + row_tok[rb]] =
+          l > 0.f ? (m_run[rb] * a.scale_log2 + log2f(l)) * kLn2 : -INFINITY;
   }
 }
 
 template <typename T>
 hipError_t launch_prefill_typed(const PrefillArgs& a, int dk, int dv, dim3 grid, hipStream_t stream) {
-  const dim3 block(256);
+  const dim3 block(kPrefillThreads);
   if (dk == 128 && dv == 128)
     hipLaunchKernelGGL((prefill_kernel<T, 128, 128>), grid, block, 0, stream, a);
   else if (dk == 192 && dv == 128)
