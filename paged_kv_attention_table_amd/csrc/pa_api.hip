@@ -33,6 +33,30 @@ bool prefill_supported(int dtype, int dk, int dv, int group) {
   return dims && group >= 1 && group <= kPrefillRows;
 }
 
+hipError_t launch_decode_bf16(const RowsArgs& a, int block_shift, int dk, int dv, dim3 grid, hipStream_t stream);
+hipError_t launch_decode_f16(const RowsArgs& a, int block_shift, int dk, int dv, dim3 grid, hipStream_t stream);
+
+// The MFMA decode kernel: f16 / bf16, a power-of-two block size that is a multiple
+// of 16, up to 16 q heads per kv head.
+bool decode_mfma_supported(int dtype, int dk, int dv, int group, int block_size) {
+  if (dtype != PA_BF16 && dtype != PA_F16) return false;
+  const bool dims = dk == 128 && dv == 128;
+  const bool pow2 = block_size >= 16 && (block_size & (block_size - 1)) == 0;
+  return dims && pow2 && group >= 1 && group <= 16;
+}
+
+// Row kernel launch: the MFMA decode kernel when it supports the shape, else the
+// general per-row kernel.
+hipError_t launch_row_kernel(const RowsArgs& a, int dtype, int dk, int dv, dim3 grid, hipStream_t stream) {
+  if (decode_mfma_supported(dtype, dk, dv, a.group, a.block_size)) {
+    int shift = 0;
+    while ((1 << shift) < a.block_size) ++shift;
+    return dtype == PA_BF16 ? launch_decode_bf16(a, shift, dk, dv, grid, stream)
+                            : launch_decode_f16(a, shift, dk, dv, grid, stream);
+  }
+  return launch_rows(a, dtype, dk, dv, grid, stream);
+}
+
 bool rows_supported(int dtype, int dk, int dv, int group) {
   if (dtype != PA_F32 && dtype != PA_F16 && dtype != PA_BF16) return false;
   const bool dims = (dk == dv && (dk == 32 || dk == 64 || dk == 128 || dk == 256)) || (dk == 192 && dv == 128);
@@ -195,7 +219,7 @@ int pa_decode(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
   a.tmp_out = tmp_out;
   a.status = status;
   const dim3 grid((unsigned)num_seqs, (unsigned)pool->num_kv_heads, (unsigned)(partition_size > 0 ? max_partitions : 1));
-  st = from_hip(launch_rows(a, pool->dtype, pool->head_dim_k, pool->head_dim_v, grid, s));
+  st = from_hip(launch_row_kernel(a, pool->dtype, pool->head_dim_k, pool->head_dim_v, grid, s));
   if (st != PA_OK || partition_size == 0) return st;
 
   ReduceArgs r = {};
@@ -288,7 +312,7 @@ int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
     // every token through the per-row kernel
     a.single_token_seqs = 0;
     const dim3 grid((unsigned)num_tokens, (unsigned)pool->num_kv_heads, 1);
-    return from_hip(launch_rows(a, pool->dtype, pool->head_dim_k, pool->head_dim_v, grid, s));
+    return from_hip(launch_row_kernel(a, pool->dtype, pool->head_dim_k, pool->head_dim_v, grid, s));
   }
   // sequences with several tokens: tiled MFMA kernel; single tokens: per-row kernel
   PrefillArgs p = {};
@@ -318,13 +342,15 @@ int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
   p.causal = causal ? 1 : 0;
   p.window = sliding_window;
   p.status = status;
-  const unsigned tiles = (unsigned)((max_query_len + p.tokens_per_tile - 1) / p.tokens_per_tile);
-  st = from_hip(launch_prefill(p, pool->dtype, pool->head_dim_k, pool->head_dim_v,
-                               dim3(tiles, (unsigned)num_seqs, (unsigned)pool->num_kv_heads), s));
+  p.tiles_per_seq = (max_query_len + p.tokens_per_tile - 1) / p.tokens_per_tile;
+  const int64_t groups8 = ((int64_t)num_seqs * pool->num_kv_heads + 7) / 8 * 8;
+  const int64_t wgs = groups8 * p.tiles_per_seq;
+  if (wgs > 0x7fffffffLL) return PA_EUNSUPPORTED;
+  st = from_hip(launch_prefill(p, pool->dtype, pool->head_dim_k, pool->head_dim_v, dim3((unsigned)wgs), s));
   if (st != PA_OK || !rows_take_singles) return st;
   a.single_token_seqs = 1;
   const dim3 grid((unsigned)num_seqs, (unsigned)pool->num_kv_heads, 1);
-  return from_hip(launch_rows(a, pool->dtype, pool->head_dim_k, pool->head_dim_v, grid, s));
+  return from_hip(launch_row_kernel(a, pool->dtype, pool->head_dim_k, pool->head_dim_v, grid, s));
 }
 
 int pa_merge_states(void* out, float* out_lse, const void* prefix_out, const float* prefix_lse,

@@ -53,6 +53,7 @@ struct PrefillArgs {
   int group;
   int block_shift;      // log2(block_size) when it is a power of two, else -1
   int tokens_per_tile;  // 256 / group (rounded down)
+  int tiles_per_seq;    // ceil(max_query_len / tokens_per_tile)
   int min_q_len;        // sequences with fewer tokens are left to the per-row kernel
   float scale_log2;
   int causal;
@@ -118,9 +119,17 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_kernel(const Prefi
   __shared__ int range_lo, range_hi;
 
   if (status_failed(a.status)) return;
-  // Tiles run last-first: under a causal mask the later tiles see more keys, so
-  // the longest workgroups start first.
-  const int tile = gridDim.x - 1 - blockIdx.x, s = blockIdx.y, g = blockIdx.z;
+  // XCD-aware 1-D grid.  Workgroup L runs on XCD L % 8 (the dispatcher deals
+  // workgroups round-robin over the 8 XCDs); all query tiles of one (sequence, kv
+  // head) group get the same L % 8, so they share that XCD's L2 for the group's
+  // K/V, and consecutive groups rotate over the XCDs.  Tiles run last-first: under
+  // a causal mask the later tiles see more keys, so the longest workgroups start
+  // first.
+  const int TPS = a.tiles_per_seq;
+  const int L = blockIdx.x, xcd = L & 7, q8 = L >> 3;
+  const int grp = (q8 / TPS) * 8 + xcd;
+  if (grp >= a.num_seqs * a.num_kv_heads) return;
+  const int tile = TPS - 1 - q8 % TPS, s = grp / a.num_kv_heads, g = grp % a.num_kv_heads;
   const int q0 = a.query_start_loc[s];
   const int q_len = a.query_start_loc[s + 1] - q0;
   const int TPT = a.tokens_per_tile;
