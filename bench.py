@@ -3,16 +3,25 @@
 Default line: the batched decode workload (64 sequences, lengths uniform in
 [512, 4096], 32 q heads / 8 kv heads, head dim 128, block size 16, f16 K/V, 8 forks
 sharing a 256-token prefix).  One step = pa_write_kv of the 64 new tokens + pa_decode
-(split-KV, partitions of 512 positions, then the log-sum-exp reduce).  The value is
-decode KV bytes per second: sum over sequences and kv heads of the visible positions
-times (head_dim_k + head_dim_v) * 2 bytes, divided by the step time.
+(unsplit by default: one kernel launch).  The value is decode KV bytes per second:
+sum over sequences and kv heads of the visible positions times
+(head_dim_k + head_dim_v) * 2 bytes, divided by the wall time of a step.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|long|varlen|mla]
+                    [--partition-size P] [--no-cpu-baseline] [--copy-calibration] [--sweep]
 
-Prints one JSON line.  The roofline object times the decode call alone with HIP
-events on its stream, with a 512 MiB buffer rewritten between launches so that the
-pool is read from HBM; the cpu_baseline object times the CPU oracle on the same
-workload on the host cores.
+Prints one JSON line.  The roofline object divides the same algorithmic bytes (or
+flops) by the attention call's average duration, taken from HIP events recorded on
+its stream around every call of the timed loop.  Its traffic field is the HBM bytes
+per launch that rocprofv3's FETCH_SIZE and WRITE_SIZE counters gave for the kernel,
+scaled by what the counters read for a copy of known size; it is read from
+profiles/traffic.md and reported only while the kernel's source hash still matches
+the one recorded there.  The cpu_baseline object times the CPU oracle on a bounded
+sample of the same workload on the host cores.  --copy-calibration appends, after
+the timed region, three launches of a 1 GiB elementwise copy (torch.neg) that the
+counter runs use as the known-size reference.  --sweep (decode workloads) adds, after
+the timed region, each partition size in {0, 512, 1024} and the cost of device
+validation, each as the median of 20 calls with the caches flushed between calls.
 """
 from __future__ import annotations
 
@@ -21,6 +30,8 @@ import json
 import math
 import os
 import sys
+import hashlib
+import re
 import time
 
 import numpy as np
@@ -42,7 +53,81 @@ def parse():
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--sweep", action="store_true")
     return ap.parse_args()
+
+
+CSRC = os.path.join(ROOT, "paged_kv_attention_table_amd", "csrc")
+KERNEL_SOURCES = {"decode_mfma_kernel": ("pa_decode.h", "pa_common.h", "pa_misc.hip"),
+                  "prefill_kernel": ("pa_prefill.h", "pa_common.h")}
+
+
+def kernel_source_hash(kernel):
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_lookup(kernel, workload, partition_size):
+    """HBM bytes per launch (read, write) recorded in profiles/traffic.md for this
+    kernel, workload and partition size, or None when absent or when the kernel's
+    sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.md")
+    if not os.path.exists(path):
+        return None
+    want = kernel_source_hash(kernel)
+    for line in open(path):
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) < 6 or cells[0] != kernel:
+            continue
+        if cells[1] == workload and cells[2] == str(partition_size) and cells[3] == want:
+            try:
+                return int(cells[4]), int(cells[5])
+            except ValueError:
+                return None
+    return None
+
+
+def copy_calibration():
+    """A 1 GiB elementwise copy (read 1 GiB, write 1 GiB), three launches: the
+    known-size reference for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def host_cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def timed_loop(steps, pre, call):
+    """Runs pre(); call() per step.  Returns (wall ms per step, average and median
+    event duration of call() in ms), with events recorded on the current stream."""
+    import torch
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s, e in evs:
+        pre()
+        s.record()
+        call()
+        e.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    durs = [s.elapsed_time(e) for s, e in evs]
+    return wall, float(np.mean(durs)), float(np.median(durs))
 
 
 def dev(a, dtype=None):
@@ -84,28 +169,38 @@ def time_calls(fn, reps, flush=None):
 
 
 def cpu_baseline_decode(w, budget_s):
-    """The oracle (as it stands) on a bounded prefix of the sequences, all host cores."""
+    """The oracle (as it stands) on a bounded sample of the workload, all host cores:
+    the first sequences (as many as fit the budget in one call), the call repeated
+    until about budget_s seconds of host time have passed."""
     from oracle import oracle as orc_mod
 
     orc = orc_mod.get()
-    threads = os.cpu_count() or 1
+    threads = host_cores()
     kp, vp = w.k_pool.copy(), w.v_pool.copy()
     orc.write_kv(kp, vp, w.dtype, w.k_new, w.v_new, w.slot_mapping)
     S = w.num_seqs
-    take = S
-    # calibrate on 4 sequences, then size the sample to the budget
+
+    def call(n):
+        orc.decode(kp, vp, w.dtype, w.q[:n], w.dtype, w.block_tables[:n], w.seq_lens[:n], w.scale,
+                   threads=threads)
+
     t0 = time.perf_counter()
-    orc.decode(kp, vp, w.dtype, w.q[:4], w.dtype, w.block_tables[:4], w.seq_lens[:4], w.scale, threads=threads)
-    per_seq = (time.perf_counter() - t0) / 4
-    take = int(max(4, min(S, budget_s / max(per_seq, 1e-9))))
+    call(min(S, 4))
+    per_seq = (time.perf_counter() - t0) / min(S, 4)
+    take = int(max(1, min(S, budget_s / max(per_seq, 1e-9))))
+    reps = 0
     t0 = time.perf_counter()
-    orc.decode(kp, vp, w.dtype, w.q[:take], w.dtype, w.block_tables[:take], w.seq_lens[:take], w.scale,
-               threads=threads)
-    dt = time.perf_counter() - t0
+    while True:
+        call(take)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= budget_s or dt + dt / reps > 1.5 * budget_s:
+            break
     eb = 4 if w.dtype == "f32" else 2
-    nbytes = int(w.seq_lens[:take].astype(np.int64).sum()) * w.num_kv_heads * (w.dk + w.dv) * eb
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {take} of {S} sequences, whole decode call (gather + two-pass fp64), {dt:.2f} s"}
+    nbytes = int(w.seq_lens[:take].astype(np.int64).sum()) * w.num_kv_heads * (w.dk + w.dv) * eb * reps
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {take} of {S} sequences, whole oracle decode call (gather + two-pass fp64) "
+                      f"repeated {reps} times, {dt:.1f} s"}
 
 
 def varlen_flops(w):
@@ -152,9 +247,10 @@ def run_prefill(args):
             pa_varlen(kp, vp, q, out, qsl, lens, pos, tables, max_q, w.scale, causal=True,
                       sliding_window=w.sliding_window, lse=lse)
 
-        def step():
+        def write():
             pa_write_kv(kp, vp, k_new, v_new, slots)
-            attn()
+
+        kernel_label = "pa_varlen call (prefill tile kernel + single-token row kernel)"
         name, dtype = w.name, w.dtype
         cfg = {"workload": name, "prefill_seqs": 4, "decode_seqs": 12, "num_tokens": w.num_tokens,
                "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.dk,
@@ -174,22 +270,21 @@ def run_prefill(args):
         def attn():
             plan.run(kp, vp, q, out, lse)
 
-        def step():
+        def write():
             pa_write_kv(kp, vp, k_new, v_new, slots)
-            attn()
+
+        kernel_label = "chunked prefill (pa_varlen per context chunk + causal new tokens + pa_merge_states)"
         name, dtype = cp.name, cp.dtype
         cfg = {"workload": name, "requests": int(cp.ctx_lens.size), "num_tokens": cp.num_tokens,
                "num_heads": cp.num_heads, "head_dim_k": cp.dk, "head_dim_v": cp.dv, "chunk": cp.chunk,
                "step": "pa_write_kv + chunked pa_varlen + pa_merge_states"}
+    def step():
+        write()
+        attn()
+
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    avg_ms, med_ms = time_calls(attn, max(10, args.steps // 2))
+    ms, avg_ms, med_ms = timed_loop(args.steps, write, attn)
     value = flops / (ms * 1e-3) / 1e12
     achieved = flops / (avg_ms * 1e-3) / 1e12
     line = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -197,14 +292,16 @@ def run_prefill(args):
             "vs_baseline": None, "dtype": dtype, "data": "synthetic", "config": dict(cfg, flops_per_step=flops),
             "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                         "avg_ms": round(avg_ms, 5), "median_ms": round(med_ms, 5)}}
+                         "kernel": kernel_label, "avg_ms": round(avg_ms, 5), "median_ms": round(med_ms, 5)}}
+    if args.copy_calibration:
+        copy_calibration()
     print(json.dumps(line), flush=True)
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1 (no multi-GPU path)"}))
         sys.exit(2)
     import torch
 
@@ -214,54 +311,79 @@ def main():
     if args.workload in ("varlen", "mla"):
         return run_prefill(args)
     w = W.config2() if args.workload == "decode" else W.config3()
-    P = args.partition_size if args.partition_size is not None else 512
+    if args.partition_size is not None:
+        P = args.partition_size
+    else:
+        P = 0 if args.workload == "decode" else 512
     kp, vp = dev(w.k_pool, w.dtype), dev(w.v_pool, w.dtype)
     q = dev(w.q, w.dtype)
     tables, lens = dev(w.block_tables), dev(w.seq_lens)
     k_new, v_new, slots = dev(w.k_new, w.dtype), dev(w.v_new, w.dtype), dev(w.slot_mapping)
     S, H = w.num_seqs, w.num_heads
     out = torch.empty((S, H, w.dv), device="cuda")
-    pmax = max(1, -(-int(w.seq_lens.max()) // P)) if P else 0
-    ws = (torch.empty((S, H, pmax), device="cuda"), torch.empty((S, H, pmax), device="cuda"),
-          torch.empty((S, H, pmax, w.dv), device="cuda")) if P else (None, None, None)
+    max_len = int(w.seq_lens.max())
 
-    def decode():
-        pa_decode(kp, vp, q, out, tables, lens, w.scale, sliding_window=w.sliding_window, partition_size=P,
-                  max_logits=ws[0], exp_sums=ws[1], tmp_out=ws[2])
+    def workspace(p):
+        if not p:
+            return None, None, None
+        pmax = -(-max_len // p)
+        return (torch.empty((S, H, pmax), device="cuda"), torch.empty((S, H, pmax), device="cuda"),
+                torch.empty((S, H, pmax, w.dv), device="cuda"))
 
-    def step():
+    ws = workspace(P)
+
+    def decode(p=P, buf=ws, status=None):
+        pa_decode(kp, vp, q, out, tables, lens, w.scale, sliding_window=w.sliding_window, partition_size=p,
+                  max_logits=buf[0], exp_sums=buf[1], tmp_out=buf[2], status=status)
+
+    def write():
         pa_write_kv(kp, vp, k_new, v_new, slots)
-        decode()
 
     for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = wall * 1e3 / args.steps
+        write()
+        decode()
+    ms, avg_ms, med_ms = timed_loop(args.steps, write, decode)
     nbytes = decode_bytes(w)
     value = nbytes / (ms * 1e-3) / 1e9
-
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-    flush = lambda: scratch.fill_(1)
-    avg_ms, med_ms = time_calls(decode, max(10, args.steps // 2), flush=flush)
     achieved = nbytes / (avg_ms * 1e-3) / 1e9
 
+    kernel = "decode_mfma_kernel"
+    roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": kernel + ("" if P == 0 else " + partition reduce_kernel"),
+            "bytes_per_launch": nbytes, "avg_ms": round(avg_ms, 5), "median_ms": round(med_ms, 5)}
+    t = traffic_lookup(kernel, w.name, P)
+    if t is not None:
+        roof["traffic"] = t[0] + t[1]
+        roof["traffic_read"], roof["traffic_write"] = t
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": w.name, "num_seqs": S, "seq_lens": [int(w.seq_lens.min()), int(w.seq_lens.max())],
+        "config": {"workload": w.name, "num_seqs": S, "seq_lens": [int(w.seq_lens.min()), max_len],
                    "num_heads": H, "num_kv_heads": w.num_kv_heads, "head_dim": w.dk, "block_size": w.block_size,
                    "partition_size": P, "kv_bytes_per_step": nbytes, "step": "pa_write_kv + pa_decode"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "pa_decode (per-partition kernel + reduce)", "avg_ms": round(avg_ms, 5),
-                     "median_ms": round(med_ms, 5)},
+        "roofline": roof,
     }
+    if args.sweep:
+        # context, after the timed region: each partition size, and the cost of device
+        # validation (status word); median of 20 calls with a 512 MiB write between
+        # calls so that the pool is read from HBM
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        flush = lambda: scratch.fill_(1)
+        sweep = {}
+        for p in (0, 512, 1024):
+            buf = ws if p == P else workspace(p)
+            _, med = time_calls(lambda: decode(p, buf), 20, flush=flush)
+            sweep[str(p)] = round(nbytes / (med * 1e-3) / 1e9, 1)
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        _, med_plain = time_calls(decode, 20, flush=flush)
+        _, med_status = time_calls(lambda: decode(status=status), 20, flush=flush)
+        if int(status.item()) != 0:
+            raise RuntimeError(f"device validation reported status {int(status.item())}")
+        line["sweep"] = {"cold_gbs_by_partition_size": sweep, "validation_ms": round(med_status - med_plain, 5)}
+    if args.copy_calibration:
+        copy_calibration()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_decode(w, args.cpu_budget_s)
     print(json.dumps(line), flush=True)

@@ -43,7 +43,8 @@ def test_write_kv_bit_exact(orc, name):
 
 
 CASES = [("config1", 0), ("config2-small", 0), ("config2-small", 512), ("config2-small", 32), ("config2-small", 16),
-         ("config3-small", 512), ("config3-small", 0), ("config2", 512), ("config2", 0), ("config3", 512)]
+         ("config3-small", 512), ("config3-small", 0), ("config2", 512), ("config2", 0), ("config2", 1024),
+         ("config3", 512)]
 
 
 @pytest.mark.parametrize("name,P", CASES, ids=[f"{n}-P{p}" for n, p in CASES])
