@@ -21,7 +21,7 @@
 //     caches and as bf16 high + low parts for bf16 caches;
 //   * keeps a reference max per head that moves (rescaling O and l) only when a
 //     tile's max exceeds it by more than 2^8.
-// Loads are software-pipelined one tile ahead, and the block ids of a wave's tiles
+// Loads are software-pipelined two tiles ahead, and the block ids of a wave's tiles
 // are fetched up to 64 at a time with one vector load and broadcast per tile, so
 // no K/V load waits on a table lookup.  Requires a power-of-two block size that is
 // a multiple of 16 (a tile then lies inside one block) and head dims of 128.
@@ -37,7 +37,6 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
-constexpr int kDecodeWaves = 4;
 constexpr int kLoadNT = 2;  // cache-policy bits of the direct-to-LDS loads: non-temporal
 
 template <typename T>
@@ -53,7 +52,8 @@ __device__ __forceinline__ f32x4 mfma_16x16x16<F16>(u32x2 a, u32x2 b, f32x4 c) {
                                                0);
 }
 
-// Which sequence and which visible range a row workgroup covers; false: nothing to do.
+// Which sequence and which visible range a row workgroup covers (partition `part`
+// of it in split mode); false: nothing to do.
 __device__ __forceinline__ bool decode_row_range(const RowsArgs& a, int row, int part, int& s, int64_t& q_row, int& n,
                                                  int& lo, int& hi) {
   q_row = row;
@@ -99,10 +99,14 @@ __device__ __forceinline__ bool decode_row_range(const RowsArgs& a, int row, int
   return true;
 }
 
-template <typename T, int DK>
-__global__ __launch_bounds__(kDecodeWaves * 64) void decode_mfma_kernel(const RowsArgs a, int block_shift) {
+// NW waves per workgroup.  WP = false: the workgroup answers one (row, kv head[,
+// partition]); its waves take the range's tiles round-robin and merge their states
+// through LDS at the end.  WP = true (split, one wave): the wave answers one (row,
+// kv head, partition) alone and writes the partition's state from registers.
+template <typename T, int DK, int NW, bool WP>
+__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, int block_shift, uint32_t grid_rows) {
+  static_assert(!WP || NW == 1, "split mode runs one wave per workgroup");
   constexpr int DV = 128;        // V rows of 256 bytes: 16 lanes x 16 bytes
-  constexpr int NW = kDecodeWaves;
   constexpr int KCH = DK / 32;   // 16-byte K chunks per lane
   constexpr int ND = DV / 16;    // 16-wide d blocks of O^T
   // A tile's V arrives by direct global->LDS loads: load ii (0..3) writes
@@ -119,6 +123,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_mfma_kernel(const Ro
   constexpr int KBLK = 1024;                // one load: 4 rows x 256 bytes
   constexpr int KBUF = 4 * KPIECES * KBLK;  // a tile's K
   static_assert(KROWB % 256 == 0, "K rows of whole 256-byte pieces");
+  constexpr int kTileLoads = 4 * KPIECES + 4;  // load instructions per tile and wave
   struct Merge {
     float m[NW][16];
     float l[NW][16];
@@ -135,12 +140,19 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_mfma_kernel(const Ro
   } sh;
 
   if (status_failed(a.status)) return;
-  const int row = blockIdx.x, g = blockIdx.y, part = blockIdx.z;
+  // 1-D grid, kv head fastest: the workgroups of one row's kv heads are dispatched
+  // together and stream the same blocks (each head's rows are interleaved with the
+  // others' in every slot) at about the same time.
+  const uint32_t wg = blockIdx.x, hkv_u = (uint32_t)a.num_kv_heads;
+  const int g = (int)(wg % hkv_u);
+  const int row = (int)((wg / hkv_u) % grid_rows);
+  const int pz = (int)(wg / (hkv_u * grid_rows));
   int s, n, lo, hi;
   int64_t q_row;
-  if (!decode_row_range(a, row, part, s, q_row, n, lo, hi)) return;
+  if (!decode_row_range(a, row, pz, s, q_row, n, lo, hi)) return;  // uniform per workgroup
 
   const int lane = lane_id(), wave = threadIdx.x / kWave;
+
   const int c = lane >> 4, r16 = lane & 15;
   const int G = a.group, hkv = a.num_kv_heads, b = a.block_size;
   const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks;
@@ -156,23 +168,40 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_mfma_kernel(const Ro
 #pragma unroll
     for (int u = 0; u < KCH; ++u)
       qb[u] = r16 < G ? *reinterpret_cast<const u32x4*>(qrow + (4 * u + c) * 8) : u32x4{0u, 0u, 0u, 0u};
+    // take the q loads' wait here, before any K/V load is in flight; otherwise the
+    // compiler guards the loop's first use of qb with a full vmcnt(0) every tile
+#pragma unroll
+    for (int u = 0; u < KCH; ++u) asm volatile("" ::"v"(qb[u]));
   }
-  // Zero this wave's V buffers: slots past the sequence are never loaded, and their
-  // rows (multiplied by p = 0) must hold finite values.
-  {
-    u32x4* z = reinterpret_cast<u32x4*>(sh.t.v[wave][0]);
-    for (int x = lane; x < 2 * VBUF / 16; x += kWave) z[x] = u32x4{0u, 0u, 0u, 0u};
-  }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // zeros land before any load into LDS
-
   f32x4 o[ND];
+  float m_run, m_true, l_run;  // reference max, true max (raw score units), exp-sum share
 #pragma unroll
   for (int nd = 0; nd < ND; ++nd) o[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -kHugeScore;  // reference max for head r16 (raw score units)
-  float m_true = -INFINITY;   // true max of the scores seen, head r16
-  float l_run = 0.f;          // this lane group's share of the exp-sum
+  m_run = -kHugeScore;
+  m_true = -INFINITY;
+  l_run = 0.f;
 
-  const int my_first = (lo >> 4) + wave;
+  // Split, one wave: the partition's state -- (true max, exp-sum against it,
+  // normalised output) -- straight from registers.  Lane (head r16, group c) holds output
+  // elements 16 nd + 4 c + ii of head r16.
+  auto write_state = [&](int p) {
+    float l = l_run;
+    l += shfl_xor(l, 16);
+    l += shfl_xor(l, 32);
+    if (r16 < G) {
+      const int64_t pi = ((int64_t)s * a.num_heads + g * G + r16) * a.max_partitions + p;
+      const float inv = l > 0.f ? 1.0f / l : 0.f;
+      float* dst = a.tmp_out + pi * DV + 4 * c;
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd) *reinterpret_cast<f32x4*>(dst + 16 * nd) = o[nd] * inv;
+      if (c == 0) {
+        a.max_logits[pi] = l > 0.f ? m_true * a.scale_log2 * kLn2 : -INFINITY;
+        a.exp_sums[pi] = l > 0.f ? l * __builtin_amdgcn_exp2f((m_run - m_true) * a.scale_log2) : 0.f;
+      }
+    }
+  };
+
+  const int my_first = (lo >> 4) + wave;  // this wave's tiles: my_first + NW * i, i < my_tiles
   const int last = (hi - 1) >> 4;
   const int my_tiles = (lo < hi && last >= my_first) ? (last - my_first) / NW + 1 : 0;
 
@@ -188,8 +217,10 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_mfma_kernel(const Ro
   // data is streamed once).  Load ii writes positions ii + 4c'' (c'' = lane / 16)
   // as contiguous 256-byte rows, one 16-byte piece per lane; for K the piece a lane
   // fetches is swizzled: LDS chunk slot of logical chunk k in row c'' of load ii is
-  // k ^ 4c'' ^ ii (within the 256-byte piece).  Slots past the sequence are not
-  // loaded.
+  // k ^ 4c'' ^ ii (within the 256-byte piece).  Positions past the sequence read
+  // the sequence's last position instead (finite data, in the same block; their
+  // scores are masked), so every tile issues exactly kTileLoads loads and a
+  // counted wait can tell tiles apart.
   auto fetch = [&](int i) {
     const int t0 = (my_first + NW * i) << 4;
     const int blk = __builtin_amdgcn_readlane(ids, i & 63);
@@ -198,46 +229,74 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_mfma_kernel(const Ro
     const char* vt = vbase + slot0 * vrow + r16 * 16;
     char* kl = sh.t.k[wave][i & 1];
     char* vl = sh.t.v[wave][i & 1];
+    const int lim = n - 1 - t0;  // >= 0: every tile starts inside the sequence
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
-      if (t0 + ii + 4 * c < n) {
-        const int kchunk = r16 ^ (4 * c) ^ ii;
+      const int rr = ii + 4 * c < lim ? ii + 4 * c : lim;
+      const int kchunk = r16 ^ (4 * c) ^ ii;
 #pragma unroll
-        for (int pc = 0; pc < KPIECES; ++pc)
-          __builtin_amdgcn_global_load_lds(kt + (ii + 4 * c) * krow + pc * 256 + kchunk * 16,
-                                           (__attribute__((address_space(3))) void*)(kl + (pc * 4 + ii) * KBLK), 16, 0,
-                                           kLoadNT);
-        __builtin_amdgcn_global_load_lds(vt + (ii + 4 * c) * vrow, (__attribute__((address_space(3))) void*)(vl + ii * VBLK),
-                                         16, 0, kLoadNT);
-      }
+      for (int pc = 0; pc < KPIECES; ++pc)
+        __builtin_amdgcn_global_load_lds(kt + rr * krow + pc * 256 + kchunk * 16,
+                                         (__attribute__((address_space(3))) void*)(kl + (pc * 4 + ii) * KBLK), 16, 0,
+                                         kLoadNT);
+      __builtin_amdgcn_global_load_lds(vt + rr * vrow, (__attribute__((address_space(3))) void*)(vl + ii * VBLK), 16,
+                                       0, kLoadNT);
     }
   };
-  // one tile: its K operands and transpose reads of V first (so that no wait covers
-  // the next tile's loads), then the next tile's loads, then S, softmax and PV.
+  // one tile: wait for its loads (tile i + 1's may stay in flight), copy its K
+  // operands and transposed V from LDS into registers, refill the freed buffer with
+  // tile i + 2, then S, softmax and PV from registers.  Two tiles per wave are in
+  // flight while one is computed.
   auto step = [&](int i) {
     const int t0 = (my_first + NW * i) << 4;
     const char* kl = sh.t.k[wave][i & 1];
     const char* lb = sh.t.v[wave][i & 1];
-    // Tile i's loads (issued one step earlier) must have landed before its K and V
-    // are read back from LDS; the waits are explicit because the direct-to-LDS
-    // loads are not otherwise ordered with these reads, and the clobbers keep tile
-    // i+1's loads from being hoisted above them.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // The waits are explicit because the direct-to-LDS loads are not otherwise
+    // ordered with the LDS reads below; the clobbers keep later loads from being
+    // hoisted above them.  Vector-memory counts retire in order, so with tile
+    // i + 1's kTileLoads loads issued after tile i's, "at most kTileLoads
+    // outstanding" means tile i has landed.
+    if (i + 1 < my_tiles)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kTileLoads) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // The LDS reads are issued as inline asm and their results are tied to the
+    // lgkmcnt wait below: the compiler would otherwise guard reads of memory that
+    // direct loads write with a full vmcnt(0) wait, draining tile i + 1's loads.
+    const uint32_t kl_a = lds_addr(kl), lb_a = lds_addr(lb);
     u32x4 kc[KCH];
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
       // logical chunk 4u + c of position r16 = 4 * row + block
       const int kk = 4 * u + c, piece = kk >> 4, chunk = (kk & 15) ^ (4 * tr_r) ^ tr_q;
-      kc[u] = *reinterpret_cast<const u32x4*>(kl + (piece * 4 + tr_q) * KBLK + tr_r * 256 + chunk * 16);
+      asm volatile("ds_read_b128 %0, %1" : "=v"(kc[u]) : "v"(kl_a + (piece * 4 + tr_q) * KBLK + tr_r * 256 + chunk * 16));
     }
     u32x2 va[ND];
-#pragma unroll
-    for (int nd = 0; nd < ND; ++nd)
-      va[nd] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                            (lds_i16x4*)(lb + tr_r * VBLK + c * 256 + (16 * nd + 4 * tr_q) * 2)));
-    asm volatile("" ::: "memory");
-    if ((i & 63) == 63 && i + 1 < my_tiles) load_ids(i + 1);
-    if (i + 1 < my_tiles) fetch(i + 1);
+    const uint32_t va_a = lb_a + tr_r * VBLK + c * 256 + 4 * tr_q * 2;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:32\n\t"
+        "ds_read_b64_tr_b16 %2, %8 offset:64\n\t"
+        "ds_read_b64_tr_b16 %3, %8 offset:96\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:128\n\t"
+        "ds_read_b64_tr_b16 %5, %8 offset:160\n\t"
+        "ds_read_b64_tr_b16 %6, %8 offset:192\n\t"
+        "ds_read_b64_tr_b16 %7, %8 offset:224"
+        : "=&v"(va[0]), "=&v"(va[1]), "=&v"(va[2]), "=&v"(va[3]), "=&v"(va[4]), "=&v"(va[5]), "=&v"(va[6]),
+          "=&v"(va[7])
+        : "v"(va_a));
+    // the reads of buffer i & 1 complete (and their registers are valid) before
+    // tile i + 2's loads may overwrite it
+    static_assert(KCH == 4 && ND == 8, "operand wait below lists 4 K and 8 V registers");
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(kc[0]), "+v"(kc[1]), "+v"(kc[2]), "+v"(kc[3]), "+v"(va[0]), "+v"(va[1]), "+v"(va[2]),
+                   "+v"(va[3]), "+v"(va[4]), "+v"(va[5]), "+v"(va[6]), "+v"(va[7])
+                 :
+                 : "memory");
+    if (i + 2 < my_tiles) {
+      if (((i + 2) & 63) == 0) load_ids(i + 2);
+      fetch(i + 2);
+    }
 
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -288,13 +347,18 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_mfma_kernel(const Ro
   if (my_tiles > 0) {
     load_ids(0);
     fetch(0);
+    if (my_tiles > 1) fetch(1);
   }
   for (int i = 0; i < my_tiles; ++i) step(i);
+  if constexpr (WP) {
+    write_state(pz);  // (-inf, 0, 0) when the window leaves the partition empty
+    return;
+  }
 
-  // --- merge: lane groups (exp-sum only; O^T is complete per wave), then waves ----
+  // --- merge of the waves' states (O^T is complete per wave) ----
   l_run += shfl_xor(l_run, 16);
   l_run += shfl_xor(l_run, 32);
-  __syncthreads();  // the V buffers become the merge area
+  __syncthreads();  // the tile buffers become the merge area
   if (lane < 16) {
     sh.r.m[wave][lane] = m_run;
     sh.r.l[wave][lane] = l_run;
@@ -329,7 +393,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_mfma_kernel(const Ro
       if (a.lse != nullptr && d == 0)
         a.lse[(int64_t)hq * a.num_rows + q_row] = L > 0.f ? (M * a.scale_log2 + log2f(L)) * kLn2 : -INFINITY;
     } else {
-      const int64_t pi = ((int64_t)s * a.num_heads + hq) * a.max_partitions + part;
+      const int64_t pi = ((int64_t)s * a.num_heads + hq) * a.max_partitions + pz;
       a.tmp_out[pi * DV + d] = out_v;
       if (d == 0) {
         a.max_logits[pi] = L > 0.f ? M * a.scale_log2 * kLn2 : -INFINITY;
@@ -339,13 +403,29 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_mfma_kernel(const Ro
   }
 }
 
+constexpr int kWholeWaves = 8;  // waves per workgroup, unsplit: a whole row per workgroup
+constexpr int kPartWaves = 4;   // waves per workgroup, split with few partitions
+// Split mode with at least this many (row, kv head, partition) items: one wave per
+// workgroup and partition.  Fewer items: kPartWaves waves share each partition, so
+// that every CU still gets enough waves.
+constexpr int64_t kOneWaveItems = 8192;
+
+// `grid` is (rows, kv heads, partitions); the kernel takes it flattened.
 template <typename T>
 hipError_t launch_decode_typed(const RowsArgs& a, int block_shift, int dk, int dv, dim3 grid, hipStream_t stream) {
-  const dim3 block(kDecodeWaves * 64);
-  if (dk == 128 && dv == 128)
-    hipLaunchKernelGGL((decode_mfma_kernel<T, 128>), grid, block, 0, stream, a, block_shift);
+  if ((int)grid.y != a.num_kv_heads || dk != 128 || dv != 128) return hipErrorInvalidValue;
+  const uint32_t rows = grid.x;
+  const uint64_t n = (uint64_t)grid.x * grid.y * grid.z;
+  if (n > 0xffffffffull) return hipErrorInvalidValue;
+  if (a.partition_size > 0 && (int64_t)n >= kOneWaveItems)
+    hipLaunchKernelGGL((decode_mfma_kernel<T, 128, 1, true>), dim3((uint32_t)n), dim3(64), 0, stream, a, block_shift,
+                       rows);
+  else if (a.partition_size > 0)
+    hipLaunchKernelGGL((decode_mfma_kernel<T, 128, kPartWaves, false>), dim3((uint32_t)n), dim3(kPartWaves * 64), 0,
+                       stream, a, block_shift, rows);
   else
-    return hipErrorInvalidValue;
+    hipLaunchKernelGGL((decode_mfma_kernel<T, 128, kWholeWaves, false>), dim3((uint32_t)n), dim3(kWholeWaves * 64), 0,
+                       stream, a, block_shift, rows);
   return hipGetLastError();
 }
 

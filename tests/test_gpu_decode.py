@@ -47,22 +47,25 @@ CASES = [("config1", 0), ("config2-small", 0), ("config2-small", 512), ("config2
          ("config3", 512)]
 
 
-@pytest.mark.parametrize("name,P", CASES, ids=[f"{n}-P{p}" for n, p in CASES])
-def test_decode_parity(orc, name, P):
+def check_decode(orc, name, P, pmax=None, window=None):
+    """GPU decode (and, when split, every used partition state) against the oracle;
+    partition entries past each sequence's context must stay untouched."""
     w = workload(name)
     d = OnDevice(w)
     kp, vp = d.host_pools_after_write(orc)
-    pmax = w.max_partitions if (P and P == w.partition_size and w.max_partitions) else None
-    out, ws = run_decode(d, P, pmax)
+    if pmax is None and P and P == w.partition_size and w.max_partitions:
+        pmax = w.max_partitions
+    win = w.sliding_window if window is None else window
+    out, ws = run_decode(d, P, pmax, sliding_window=win)
     st, ref, _ = orc.decode(kp, vp, w.dtype, w.q, w.dtype, w.block_tables, w.seq_lens, w.scale,
-                            sliding_window=w.sliding_window, threads=threads())
+                            sliding_window=win, threads=threads())
     assert st == 0
     tol = TOL[w.dtype]
     assert_close(host(out), ref, tol, f"{name} out")
     if P:
         pmax = ws[0].shape[-1]
         st, rml, res, rto = orc.decode(kp, vp, w.dtype, w.q, w.dtype, w.block_tables, w.seq_lens, w.scale,
-                                       sliding_window=w.sliding_window, partition_size=P, max_partitions=pmax,
+                                       sliding_window=win, partition_size=P, max_partitions=pmax,
                                        threads=threads())
         assert st == 0
         ml, es, to = host(ws[0]), host(ws[1]), host(ws[2])
@@ -74,6 +77,24 @@ def test_decode_parity(orc, name, P):
         assert np.all((res[used] == 0) == (es[used] == 0)) and rel.max() <= tol, rel.max()
         assert_close(to, rto, tol, "tmp_out", mask=used)
         assert np.all(np.isnan(ml[~used])) and np.all(np.isnan(to[~used])), "partitions past the context written"
+
+
+@pytest.mark.parametrize("name,P", CASES, ids=[f"{n}-P{p}" for n, p in CASES])
+def test_decode_parity(orc, name, P):
+    check_decode(orc, name, P)
+
+
+# An oversized max_partitions gives the launcher enough (row, kv head, partition)
+# items to run one wave per partition (the layout the long-context workload uses) on
+# small inputs: most partitions lie past the context and must stay untouched, and
+# the window empties some partitions wholly.
+ONE_WAVE = [("config2-small", 16, 4096, 0), ("config2-small", 16, 4096, 100), ("config3-small", 64, 2048, 0),
+           ("config3-small", 32, 1000, 700)]
+
+
+@pytest.mark.parametrize("name,P,pmax,win", ONE_WAVE, ids=[f"{n}-P{p}-pmax{m}-w{w}" for n, p, m, w in ONE_WAVE])
+def test_decode_one_wave_partitions(orc, name, P, pmax, win):
+    check_decode(orc, name, P, pmax=pmax, window=win)
 
 
 def test_decode_window_and_out_dtype(orc):
