@@ -17,7 +17,8 @@
  *   - A query at position pos of a sequence of seq_len tokens sees positions
  *     [start, end): end = pos + 1 when causal, else seq_len; start = max(0, end -
  *     sliding_window) when sliding_window > 0, else 0.  Scores are
- *     scale * <q, k_j>, normalised by softmax over the visible positions.
+ *     scale * <q, k_j>, normalised by softmax over the visible positions; scale
+ *     must be finite and > 0 (else PA_EINVAL).
  *   - lse arrays are float32 [num_heads, tokens] in natural log; a row that sees no
  *     position has output 0 and lse -inf ("cpu_mla_prefill.cpp", MlaPrefillAttention).
  *

@@ -186,8 +186,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
   // elements 16 nd + 4 c + ii of head r16.
   auto write_state = [&](int p) {
     float l = l_run;
-    l += shfl_xor(l, 16);
-    l += shfl_xor(l, 32);
+    l = sum_over_groups(l);
     if (r16 < G) {
       const int64_t pi = ((int64_t)s * a.num_heads + g * G + r16) * a.max_partitions + p;
       const float inv = l > 0.f ? 1.0f / l : 0.f;
@@ -310,8 +309,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
       }
     }
     float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    mx = fmaxf(mx, shfl_xor(mx, 16));
-    mx = fmaxf(mx, shfl_xor(mx, 32));
+    mx = max_over_groups(mx);
     m_true = fmaxf(m_true, mx);
     if (__any((mx - m_run) * a.scale_log2 > kRescaleLog2)) {
       const float m_new = fmaxf(m_run, mx);
@@ -356,8 +354,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
   }
 
   // --- merge of the waves' states (O^T is complete per wave) ----
-  l_run += shfl_xor(l_run, 16);
-  l_run += shfl_xor(l_run, 32);
+  l_run = sum_over_groups(l_run);
   __syncthreads();  // the tile buffers become the merge area
   if (lane < 16) {
     sh.r.m[wave][lane] = m_run;

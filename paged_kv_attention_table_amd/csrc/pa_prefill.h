@@ -24,6 +24,8 @@
 // are stored as zeros in LDS, so unwritten pool slots never reach the product.
 #pragma once
 
+#include <type_traits>
+
 #include "pa_common.h"
 #include "pa_internal.h"
 
@@ -90,6 +92,27 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
 }
 
+// Eight bf16 values to f16 (round to nearest even), tracking the largest magnitude
+// seen: exact for |v| in [2^-14, 65504] (f16 holds bf16's 8-bit significands there),
+// below 2^-14 the f16 subnormals keep an absolute error under 2^-25.
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 x, float& vmax) {
+  u32x4 y;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float lo = __uint_as_float(x[e] << 16), hi = __uint_as_float(x[e] & 0xffff0000u);
+    vmax = fmaxf(vmax, fmaxf(fabsf(lo), fabsf(hi)));
+    y[e] = pack_f16x2(lo, hi);
+  }
+  return y;
+}
+
+// max(a, b, c) in one instruction (no canonicalising copies of the operands).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 constexpr float kRescaleLog2 = 8.0f;  // move the reference max only past 2^8
 constexpr float kHugeScore = 1.0e30f;
 
@@ -116,7 +139,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_kernel(const Prefi
 
   __shared__ __align__(16) uint16_t k_lds[2][KT][KROW];
   __shared__ __align__(16) uint16_t v_lds[2][KT][VROW];
-  __shared__ int range_lo, range_hi;
+  __shared__ int range_lo, range_hi, v_out_of_range;
 
   if (status_failed(a.status)) return;
   // XCD-aware 1-D grid.  Workgroup L runs on XCD L % 8 (the dispatcher deals
@@ -145,6 +168,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_kernel(const Prefi
   if (tid == 0) {
     range_lo = 0x7fffffff;
     range_hi = 0;
+    v_out_of_range = 0;
   }
 
   // --- this lane's two rows (one per 16-row block) --------------------------------
@@ -194,83 +218,115 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_kernel(const Prefi
   const int klo = range_lo, khi = range_hi;
 
   f32x4 o[ND][2];
-#pragma unroll
-  for (int nd = 0; nd < ND; ++nd)
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) o[nd][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // Finite start for the reference max: rows that see nothing keep l = 0, and no
-  // -inf - -inf ever occurs.
-  float m_run[2] = {-kHugeScore, -kHugeScore};
-  float l_run[2] = {0.f, 0.f};
+  float m_run[2], l_run[2];
+  float vmax = 0.f;  // largest |V| this thread staged as f16 (bf16 caches)
 
-  if (klo < khi) {
+  // Loop-invariant share of this thread in every tile's loads.  A tile's K (V)
+  // chunks are dealt so that each wave's 64 lanes fall in one 16-key half of the
+  // tile (a half is 16 * KCH chunks, a multiple of 64): the half -- hence the block
+  // and the base address -- is wave-uniform, and a lane adds its fixed offset (key
+  // within the half, chunk) to it.
+  constexpr int KHALF = 16 * KCH, VHALF = 16 * VCH;
+  constexpr int KN = (2 * KHALF + NTH - 1) / NTH, VN = (2 * VHALF + NTH - 1) / NTH;
+  static_assert(KHALF % kWave == 0 && VHALF % kWave == 0, "tile halves of whole waves");
+  static_assert(KN == Regs::KN && VN == Regs::VN, "register share of a tile");
+  const int hkv = a.num_kv_heads, b = a.block_size;
+  const int64_t krow_bytes = (int64_t)hkv * DK * 2, vrow_bytes = (int64_t)hkv * DV * 2;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t k_gofs[KN], k_lofs[KN], v_gofs[VN], v_lofs[VN];
+  int k_key[KN], v_key[VN];
+  bool k_on[KN], v_on[VN], k_hi[KN], v_hi[VN];  // wave-uniform
+#pragma unroll
+  for (int u = 0; u < KN; ++u) {
+    const int w0 = wave_u * kWave + NTH * u;  // the wave's first chunk index
+    k_on[u] = w0 < 2 * KHALF;
+    k_hi[u] = w0 >= KHALF;
+    const int within = (tid + NTH * u) % KHALF, key16 = within / KCH, ch = within % KCH;
+    k_key[u] = (k_hi[u] ? 16 : 0) + key16;
+    k_gofs[u] = (uint32_t)(key16 * krow_bytes + ch * 16);
+    k_lofs[u] = (uint32_t)((k_key[u] * KROW + ch * 8) * 2);
+  }
+#pragma unroll
+  for (int u = 0; u < VN; ++u) {
+    const int w0 = wave_u * kWave + NTH * u;
+    v_on[u] = w0 < 2 * VHALF;
+    v_hi[u] = w0 >= VHALF;
+    const int within = (tid + NTH * u) % VHALF, key16 = within / VCH, ch = within % VCH;
+    v_key[u] = (v_hi[u] ? 16 : 0) + key16;
+    v_gofs[u] = (uint32_t)(key16 * vrow_bytes + ch * 16);
+    v_lofs[u] = (uint32_t)((v_key[u] * VROW + ch * 8) * 2);
+  }
+
+  // The whole key loop.  EXACT = false with a bf16 cache stages V as f16 and runs
+  // PV on f16 MFMA with P in f16; EXACT = true keeps V in bf16 and splits P into
+  // bf16 high and low parts (two MFMAs).  f16 caches always take the f16 path.
+  auto run = [&](auto exact_tag) {
+    constexpr bool EXACT = decltype(exact_tag)::value;
+    constexpr bool F16PV = T::code == PA_F16 || !EXACT;
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) o[nd][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Reference max per row, in raw score units, with its scaled value and the
+    // threshold past which it must move: a score s gives p = 2^((s - m) c) with
+    // c = scale * log2(e), one fma and one v_exp; m only moves (rescaling O and l)
+    // when a score exceeds it by more than 2^8 in p, so p stays below 256, which
+    // f16 / bf16 and the fp32 accumulators hold as well, and O / l is unchanged.
+    // The finite start makes the first visible tile move it; rows that see nothing
+    // keep l = 0, and no -inf - -inf ever occurs.
+    const float c2 = a.scale_log2;
+    const float thr = kRescaleLog2 / c2;
+    float mc[2], m_thr[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      m_run[rb] = -kHugeScore;
+      l_run[rb] = 0.f;
+      mc[rb] = m_run[rb] * c2;
+      m_thr[rb] = m_run[rb] + thr;
+    }
+    if (klo >= khi) return;
     const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks;
-    const char* kbase = static_cast<const char*>(a.k_pool);
-    const char* vbase = static_cast<const char*>(a.v_pool);
-    const int hkv = a.num_kv_heads, b = a.block_size;
+    const char* kbase = static_cast<const char*>(a.k_pool) + (int64_t)g * DK * 2;
+    const char* vbase = static_cast<const char*>(a.v_pool) + (int64_t)g * DV * 2;
     const int t_first = klo & ~(KT - 1);
     const int num_tiles = (khi - t_first + KT - 1) / KT;
+    char* const k_lds_b = reinterpret_cast<char*>(&k_lds[0][0][0]);
+    char* const v_lds_b = reinterpret_cast<char*>(&v_lds[0][0][0]);
 
-    // Addresses.  When the block size is a power of two of at least 16, a 32-key
-    // tile aligned to 32 positions spans at most two blocks: their ids are read
-    // with wave-uniform scalar loads (counted apart from the vector loads, so the
-    // K/V prefetches of earlier tiles are not waited for) and turned into two row
-    // base pointers; each thread then adds a fixed in-block offset.  Keys past the
-    // visible range are loaded from valid (clamped) blocks and zeroed when stashed.
-    // Other block sizes look ids up per key.
-    const bool tile_ids = a.block_shift >= 4;
+    // Bases of a tile's two halves.  The block size is a power of two of at least
+    // 16, so a 32-key tile aligned to 32 positions lies in one block (b >= 32) or in
+    // two (b = 16, one per half).  The ids are read with scalar loads (counted
+    // apart from the vector loads, so the prefetches of earlier tiles are not
+    // waited for), and the code that issues loads has no branches, so the compiler
+    // counts every tile's loads exactly.  Keys past the visible range are loaded
+    // from valid (clamped) blocks and zeroed when stashed.
     const int max_idx = a.max_blocks - 1;
-    const int64_t krow_bytes = (int64_t)hkv * DK * 2, vrow_bytes = (int64_t)hkv * DV * 2;
-    auto tile_bases = [&](int t0, const char*& k0, const char*& k1, const char*& v0, const char*& v1) {
+    auto tile_bases = [&](int t0, const char*& klo_p, const char*& khi_p, const char*& vlo_p, const char*& vhi_p) {
       const int i0 = __builtin_amdgcn_readfirstlane(t0 >> a.block_shift);
       const int i1 = i0 + 1 < max_idx ? i0 + 1 : max_idx;
-      int64_t b0 = table[i0], b1 = table[__builtin_amdgcn_readfirstlane(i1)];
+      int64_t b0 = load_scalar_i32(table + i0), b1 = load_scalar_i32(table + i1);
       b0 = b0 < 0 ? 0 : (b0 >= a.num_blocks ? a.num_blocks - 1 : b0);
       b1 = b1 < 0 ? 0 : (b1 >= a.num_blocks ? a.num_blocks - 1 : b1);
-      k0 = kbase + b0 * b * krow_bytes + (int64_t)g * DK * 2;
-      k1 = kbase + b1 * b * krow_bytes + (int64_t)g * DK * 2;
-      v0 = vbase + b0 * b * vrow_bytes + (int64_t)g * DV * 2;
-      v1 = vbase + b1 * b * vrow_bytes + (int64_t)g * DV * 2;
+      const int64_t r0 = b0 * b + (t0 & (b - 1));
+      // the second half: the next block when b = 16, else 16 rows further on
+      const int64_t r1 = b == 16 ? b1 * 16 : r0 + 16;
+      klo_p = kbase + r0 * krow_bytes;
+      vlo_p = vbase + r0 * vrow_bytes;
+      khi_p = kbase + r1 * krow_bytes;
+      vhi_p = vbase + r1 * vrow_bytes;
     };
-    // global -> registers for tile i
+    // global -> registers for tile i.  Every load is issued (lanes past the tile's
+    // chunks read inside the same block and are not stashed), so the loads per
+    // tile are a fixed count and the waits for a tile's registers leave the next
+    // tile's loads in flight.
     auto fetch = [&](int i, Regs& R) {
       const int t0 = t_first + i * KT;
-      if (tile_ids) {
-        const char *k0, *k1, *v0, *v1;
-        tile_bases(t0, k0, k1, v0, v1);
-        const int i0 = t0 >> a.block_shift;
+      const char *klo_p, *khi_p, *vlo_p, *vhi_p;
+      tile_bases(t0, klo_p, khi_p, vlo_p, vhi_p);
 #pragma unroll
-        for (int u = 0; u < Regs::KN; ++u) {
-          const int id = tid + NTH * u, key = (id < KT * KCH ? id : 0) / KCH, ch = id % KCH;
-          const int j = t0 + key;
-          const char* base = (j >> a.block_shift) == i0 ? k0 : k1;
-          R.k[u] = *reinterpret_cast<const u32x4*>(base + (j & (b - 1)) * krow_bytes + ch * 16);
-        }
+      for (int u = 0; u < KN; ++u) R.k[u] = *reinterpret_cast<const u32x4*>((k_hi[u] ? khi_p : klo_p) + k_gofs[u]);
 #pragma unroll
-        for (int u = 0; u < Regs::VN; ++u) {
-          const int id = tid + NTH * u, key = (id < KT * VCH ? id : 0) / VCH, ch = id % VCH;
-          const int j = t0 + key;
-          const char* base = (j >> a.block_shift) == i0 ? v0 : v1;
-          R.v[u] = *reinterpret_cast<const u32x4*>(base + (j & (b - 1)) * vrow_bytes + ch * 16);
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u < Regs::KN; ++u) {
-          const int id = tid + NTH * u, key = (id < KT * KCH ? id : 0) / KCH, ch = id % KCH;
-          int j = t0 + key;
-          j = j < klo ? klo : (j >= khi ? khi - 1 : j);
-          const int64_t slot = slot_fast(table, j, b, a.block_shift, a.num_blocks);
-          R.k[u] = *reinterpret_cast<const u32x4*>(kbase + slot * krow_bytes + (int64_t)g * DK * 2 + ch * 16);
-        }
-#pragma unroll
-        for (int u = 0; u < Regs::VN; ++u) {
-          const int id = tid + NTH * u, key = (id < KT * VCH ? id : 0) / VCH, ch = id % VCH;
-          int j = t0 + key;
-          j = j < klo ? klo : (j >= khi ? khi - 1 : j);
-          const int64_t slot = slot_fast(table, j, b, a.block_shift, a.num_blocks);
-          R.v[u] = *reinterpret_cast<const u32x4*>(vbase + slot * vrow_bytes + (int64_t)g * DV * 2 + ch * 16);
-        }
-      }
+      for (int u = 0; u < VN; ++u) R.v[u] = *reinterpret_cast<const u32x4*>((v_hi[u] ? vhi_p : vlo_p) + v_gofs[u]);
     };
     // registers -> LDS buffer, zeros for keys outside [klo, khi) on edge tiles
     auto stash = [&](const Regs& R, int i, int buf) {
@@ -278,20 +334,25 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_kernel(const Prefi
       const bool edge = t0 < klo || t0 + KT > khi;
       const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int u = 0; u < Regs::KN; ++u) {
-        const int id = tid + NTH * u, key = id / KCH, ch = id % KCH;
-        const int j = t0 + key;
+      for (int u = 0; u < KN; ++u) {
+        if (!k_on[u]) continue;
         u32x4 x = R.k[u];
-        if (edge && (j < klo || j >= khi)) x = zero;
-        if (id < KT * KCH) *reinterpret_cast<u32x4*>(&k_lds[buf][key][ch * 8]) = x;
+        if (edge) {
+          const int j = t0 + k_key[u];
+          if (j < klo || j >= khi) x = zero;
+        }
+        *reinterpret_cast<u32x4*>(k_lds_b + buf * sizeof(k_lds[0]) + k_lofs[u]) = x;
       }
 #pragma unroll
-      for (int u = 0; u < Regs::VN; ++u) {
-        const int id = tid + NTH * u, key = id / VCH, ch = id % VCH;
-        const int j = t0 + key;
+      for (int u = 0; u < VN; ++u) {
+        if (!v_on[u]) continue;
         u32x4 x = R.v[u];
-        if (edge && (j < klo || j >= khi)) x = zero;
-        if (id < KT * VCH) *reinterpret_cast<u32x4*>(&v_lds[buf][key][ch * 8]) = x;
+        if (edge) {
+          const int j = t0 + v_key[u];
+          if (j < klo || j >= khi) x = zero;
+        }
+        if constexpr (T::code == PA_BF16 && !EXACT) x = bf16x8_to_f16x8(x, vmax);
+        *reinterpret_cast<u32x4*>(v_lds_b + buf * sizeof(v_lds[0]) + v_lofs[u]) = x;
       }
     };
     // one key tile from LDS buffer `buf`
@@ -314,12 +375,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_kernel(const Prefi
           for (int rb = 0; rb < 2; ++rb) sc[kb][rb] = mfma_16x16x32<T>(ka, qb[rb][kk], sc[kb][rb]);
         }
       }
-      // Online softmax per row, in raw score units: p = 2^((s - m) * c) with
-      // c = scale * log2(e), one fma and one v_exp per score.  The reference max m
-      // is only moved (and O, l rescaled) when the tile max exceeds it by more than
-      // 2^8 in p; otherwise p may exceed 1 by up to 256, which f16 / bf16 and the
-      // fp32 accumulators hold exactly as well, and O / l is unchanged.  Tiles that
-      // lie inside every row's visible range skip the masking.
+      // Tiles inside every row's visible range skip the masking.
       bool inside = true;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) inside &= !row_ok[rb] || (vis_lo[rb] <= t0 && vis_hi[rb] >= t0 + KT);
@@ -341,23 +397,23 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_kernel(const Prefi
               if (j < vis_lo[rb] || j >= vis_hi[rb]) sv[kb * 4 + ii] = -INFINITY;
             }
         }
-        float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-        mx = fmaxf(mx, shfl_xor(mx, 16));
-        mx = fmaxf(mx, shfl_xor(mx, 32));
-        if (__any((mx - m_run[rb]) * a.scale_log2 > kRescaleLog2)) {
-          const float m_new = fmaxf(m_run[rb], mx);
-          const float alpha = __builtin_amdgcn_exp2f((m_run[rb] - m_new) * a.scale_log2);
+        // this lane's max; the row-wide max is only formed when the reference must move
+        const float lm = max3f(max3f(sv[0], sv[1], sv[2]), max3f(sv[3], sv[4], sv[5]), max3f(sv[6], sv[7], sv[7]));
+        if (__any(lm > m_thr[rb])) {
+          const float m_new = fmaxf(m_run[rb], max_over_groups(lm));
+          const float alpha = __builtin_amdgcn_exp2f((m_run[rb] - m_new) * c2);
           l_run[rb] *= alpha;
 #pragma unroll
           for (int nd = 0; nd < ND; ++nd) o[nd][rb] *= alpha;
           m_run[rb] = m_new;
+          mc[rb] = m_new * c2;
+          m_thr[rb] = m_new + thr;
         }
-        const float mc = m_run[rb] * a.scale_log2;
         float p[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(sv[e], a.scale_log2, -mc));
+        for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(sv[e], c2, -mc[rb]));
         l_run[rb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-        if constexpr (T::code == PA_F16) {
+        if constexpr (F16PV) {
           uint32_t w[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) w[e] = pack_f16x2(p[2 * e], p[2 * e + 1]);
@@ -386,7 +442,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_kernel(const Prefi
         const u32x4 va = u32x4{w0.x, w0.y, w1.x, w1.y};
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
-          if constexpr (T::code == PA_F16) {
+          if constexpr (F16PV) {
             o[nd][rb] = mfma_16x16x32<F16>(va, pb[rb], o[nd][rb]);
           } else {
             o[nd][rb] = mfma_16x16x32<BF16>(va, pb[rb], o[nd][rb]);
@@ -418,14 +474,23 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_kernel(const Prefi
       step(i + 1, RB, RA);
     }
     if (i < num_tiles) step(i, RA, RB);
+  };
+  if constexpr (T::code == PA_BF16) {
+    run(std::false_type{});
+    // a V value beyond f16's range anywhere in the staged tiles: this workgroup's
+    // rows again, exactly
+    if (vmax > 65504.f) v_out_of_range = 1;
+    __syncthreads();
+    if (v_out_of_range) run(std::true_type{});
+  } else {
+    run(std::false_type{});
   }
 
   // --- finish: sum the lane groups' exp-sums, normalise, write ---------------------
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     float l = l_run[rb];
-    l += shfl_xor(l, 16);
-    l += shfl_xor(l, 32);
+    l = sum_over_groups(l);
     if (!row_ok[rb]) continue;
     const float inv = l > 0.f ? 1.0f / l : 0.f;
     const int64_t obase = (row_tok[rb] * a.num_heads + row_head[rb]) * (int64_t)DV;

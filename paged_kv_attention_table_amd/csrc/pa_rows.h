@@ -178,8 +178,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const RowsArgs a) {
         sv[i] = (j >= lo && j < hi) ? sc[i] * a.scale_log2 : -INFINITY;
         mx = fmaxf(mx, sv[i]);
       }
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
+      mx = max_over_groups(mx);
       const float m_new = fmaxf(m_run, mx);
       const bool live = m_new != -INFINITY;
       const float alpha = live ? exp2f(m_run - m_new) : 1.f;
@@ -218,14 +217,12 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const RowsArgs a) {
   }
 
   // --- merge the four lane groups (different positions, same heads) -------------
-  l_run += shfl_xor(l_run, 16);
-  l_run += shfl_xor(l_run, 32);
+  l_run = sum_over_groups(l_run);
 #pragma unroll
   for (int h = 0; h < GMAX; ++h)
 #pragma unroll
     for (int e = 0; e < VE; ++e) {
-      acc[h][e] += shfl_xor(acc[h][e], 16);
-      acc[h][e] += shfl_xor(acc[h][e], 32);
+      acc[h][e] = sum_over_groups(acc[h][e]);
     }
   if (lane < 16) {
     red_m[wave][lane] = m_run;

@@ -97,6 +97,16 @@ def test_varlen_host_checks():
                          5, 0.1, 1, 0, None, None) == binding.PA_ESHAPE
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.125, float("inf"), float("nan")])
+def test_scale_must_be_positive_and_finite(scale):
+    lib = binding.load()
+    p = ctypes.byref(_pool())
+    assert lib.pa_decode(p, FAKE, binding.PA_F16, FAKE, binding.PA_F32, FAKE, 4, FAKE, 2, 4, scale, 0, 0, 0, None,
+                         None, None, None, None) == binding.PA_EINVAL
+    assert lib.pa_varlen(p, FAKE, binding.PA_F16, FAKE, binding.PA_F32, None, FAKE, FAKE, FAKE, FAKE, 4, 2, 10, 8,
+                         4, scale, 1, 0, None, None) == binding.PA_EINVAL
+
+
 def test_write_and_merge_host_checks():
     lib = binding.load()
     p = ctypes.byref(_pool())

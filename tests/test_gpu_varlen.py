@@ -80,6 +80,29 @@ def test_varlen_small_shapes(orc, case):
     assert_close(host(lse), rlse, TOL[dtype], "lse")
 
 
+def test_varlen_bf16_values_beyond_f16(orc):
+    """bf16 V entries far beyond f16's range: the prefill kernel stages bf16 V as f16
+    for its PV product, and workgroups that meet such a value redo their rows with
+    bf16 V, so results stay finite and within the bound relative to their size."""
+    import dataclasses
+
+    w = workload("config4-small")
+    vals = (w.v_new.astype(np.uint32) << 16).view(np.float32).copy()
+    starts = w.query_start_loc[:-1]
+    vals[starts] *= np.float32(3.0e5)  # the first new token of every sequence, all heads and dims
+    big = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    w2 = dataclasses.replace(w, v_new=big)
+    d = OnDevice(w2)
+    out, lse = run_varlen(d)
+    ref, rlse = oracle_varlen(orc, d)
+    g = host(out).astype(np.float64)
+    assert np.all(np.isfinite(g))
+    err = np.abs(g - ref) / np.maximum(1.0, np.abs(ref))
+    assert err.max() <= TOL[w.dtype], err.max()
+    assert np.abs(ref).max() > 1e3  # the large values do reach the outputs
+    assert_close(host(lse), rlse, TOL[w.dtype], "lse")
+
+
 def test_varlen_empty_context_rows(orc):
     """Non-causal rows of a sequence with no cached positions: out 0, lse -inf."""
     w = W.make_paged("empty", 611, dtype="bf16", block_size=16, num_heads=4, num_kv_heads=2, dk=64, dv=64,
