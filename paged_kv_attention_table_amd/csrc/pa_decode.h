@@ -21,7 +21,8 @@
 //     caches and as bf16 high + low parts for bf16 caches;
 //   * keeps a reference max per head that moves (rescaling O and l) only when a
 //     tile's max exceeds it by more than 2^8.
-// Loads are software-pipelined two tiles ahead, and the block ids of a wave's tiles
+// Loads are software-pipelined NB tiles ahead (NB LDS buffers per wave, each refilled
+// as soon as its tile has been copied into registers), and the block ids of a wave's tiles
 // are fetched up to 64 at a time with one vector load and broadcast per tile, so
 // no K/V load waits on a table lookup.  Requires a power-of-two block size that is
 // a multiple of 16 (a tile then lies inside one block) and head dims of 128.
@@ -103,9 +104,10 @@ __device__ __forceinline__ bool decode_row_range(const RowsArgs& a, int row, int
 // partition]); its waves take the range's tiles round-robin and merge their states
 // through LDS at the end.  WP = true (split, one wave): the wave answers one (row,
 // kv head, partition) alone and writes the partition's state from registers.
-template <typename T, int DK, int NW, bool WP>
+template <typename T, int DK, int NW, bool WP, int NB>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, int block_shift, uint32_t grid_rows) {
   static_assert(!WP || NW == 1, "split mode runs one wave per workgroup");
+  static_assert(NB >= 2 && NB <= 4, "2 to 4 tile buffers per wave");
   constexpr int DV = 128;        // V rows of 256 bytes: 16 lanes x 16 bytes
   constexpr int KCH = DK / 32;   // 16-byte K chunks per lane
   constexpr int ND = DV / 16;    // 16-wide d blocks of O^T
@@ -131,8 +133,8 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
   };
   __shared__ float true_max[NW][16];
   struct Tiles {
-    char k[NW][2][KBUF];
-    char v[NW][2][VBUF];
+    char k[NW][NB][KBUF];
+    char v[NW][NB][VBUF];
   };
   __shared__ __align__(16) union {
     Tiles t;
@@ -212,7 +214,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
     const int id = table[idx];
     ids = id < 0 ? 0 : (id >= a.num_blocks ? (int)(a.num_blocks - 1) : id);
   };
-  // K and V of tile i into LDS buffer i & 1 by direct loads (non-temporal: the
+  // K and V of tile i into LDS buffer i % NB by direct loads (non-temporal: the
   // data is streamed once).  Load ii writes positions ii + 4c'' (c'' = lane / 16)
   // as contiguous 256-byte rows, one 16-byte piece per lane; for K the piece a lane
   // fetches is swizzled: LDS chunk slot of logical chunk k in row c'' of load ii is
@@ -226,8 +228,8 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
     const int64_t slot0 = (int64_t)blk * b + (t0 & (b - 1));
     const char* kt = kbase + slot0 * krow;
     const char* vt = vbase + slot0 * vrow + r16 * 16;
-    char* kl = sh.t.k[wave][i & 1];
-    char* vl = sh.t.v[wave][i & 1];
+    char* kl = sh.t.k[wave][i % NB];
+    char* vl = sh.t.v[wave][i % NB];
     const int lim = n - 1 - t0;  // >= 0: every tile starts inside the sequence
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
@@ -242,20 +244,25 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
                                        0, kLoadNT);
     }
   };
-  // one tile: wait for its loads (tile i + 1's may stay in flight), copy its K
+  // one tile: wait for its loads (the later tiles' may stay in flight), copy its K
   // operands and transposed V from LDS into registers, refill the freed buffer with
-  // tile i + 2, then S, softmax and PV from registers.  Two tiles per wave are in
+  // tile i + NB, then S, softmax and PV from registers.  NB tiles per wave are in
   // flight while one is computed.
   auto step = [&](int i) {
     const int t0 = (my_first + NW * i) << 4;
-    const char* kl = sh.t.k[wave][i & 1];
-    const char* lb = sh.t.v[wave][i & 1];
+    const char* kl = sh.t.k[wave][i % NB];
+    const char* lb = sh.t.v[wave][i % NB];
     // The waits are explicit because the direct-to-LDS loads are not otherwise
     // ordered with the LDS reads below; the clobbers keep later loads from being
-    // hoisted above them.  Vector-memory counts retire in order, so with tile
-    // i + 1's kTileLoads loads issued after tile i's, "at most kTileLoads
-    // outstanding" means tile i has landed.
-    if (i + 1 < my_tiles)
+    // hoisted above them.  Vector-memory counts retire in order, so with the
+    // kTileLoads loads of each of `ahead` later tiles issued after tile i's, "at most
+    // ahead * kTileLoads outstanding" means tile i has landed.
+    const int ahead = my_tiles - 1 - i;  // tiles issued after tile i, up to NB - 1
+    if (NB >= 4 && ahead >= 3)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * kTileLoads) : "memory");
+    else if (NB >= 3 && ahead >= 2)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kTileLoads) : "memory");
+    else if (ahead >= 1)
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kTileLoads) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -284,17 +291,17 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
         : "=&v"(va[0]), "=&v"(va[1]), "=&v"(va[2]), "=&v"(va[3]), "=&v"(va[4]), "=&v"(va[5]), "=&v"(va[6]),
           "=&v"(va[7])
         : "v"(va_a));
-    // the reads of buffer i & 1 complete (and their registers are valid) before
-    // tile i + 2's loads may overwrite it
+    // the reads of buffer i % NB complete (and their registers are valid) before
+    // tile i + NB's loads may overwrite it
     static_assert(KCH == 4 && ND == 8, "operand wait below lists 4 K and 8 V registers");
     asm volatile("s_waitcnt lgkmcnt(0)"
                  : "+v"(kc[0]), "+v"(kc[1]), "+v"(kc[2]), "+v"(kc[3]), "+v"(va[0]), "+v"(va[1]), "+v"(va[2]),
                    "+v"(va[3]), "+v"(va[4]), "+v"(va[5]), "+v"(va[6]), "+v"(va[7])
                  :
                  : "memory");
-    if (i + 2 < my_tiles) {
-      if (((i + 2) & 63) == 0) load_ids(i + 2);
-      fetch(i + 2);
+    if (i + NB < my_tiles) {
+      if (((i + NB) & 63) == 0) load_ids(i + NB);
+      fetch(i + NB);
     }
 
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
@@ -344,8 +351,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
 
   if (my_tiles > 0) {
     load_ids(0);
-    fetch(0);
-    if (my_tiles > 1) fetch(1);
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      if (j < my_tiles) fetch(j);
   }
   for (int i = 0; i < my_tiles; ++i) step(i);
   if constexpr (WP) {
@@ -400,8 +408,13 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
   }
 }
 
-constexpr int kWholeWaves = 8;  // waves per workgroup, unsplit: a whole row per workgroup
-constexpr int kPartWaves = 4;   // waves per workgroup, split with few partitions
+// Waves per workgroup and tile buffers per wave.  Loads in flight per CU are bounded
+// by LDS (a buffer holds a tile from load issue until its copy into registers):
+// unsplit, 6 waves x 3 buffers = 146 KB, one workgroup per CU; split with few
+// partitions, 4 waves x 2 buffers, two per CU; one-wave split, 3 buffers, six per CU.
+constexpr int kWholeWaves = 6, kWholeBufs = 3;
+constexpr int kPartWaves = 4, kPartBufs = 2;
+constexpr int kOneWaveBufs = 3;
 // Split mode with at least this many (row, kv head, partition) items: one wave per
 // workgroup and partition.  Fewer items: kPartWaves waves share each partition, so
 // that every CU still gets enough waves.
@@ -415,13 +428,13 @@ hipError_t launch_decode_typed(const RowsArgs& a, int block_shift, int dk, int d
   const uint64_t n = (uint64_t)grid.x * grid.y * grid.z;
   if (n > 0xffffffffull) return hipErrorInvalidValue;
   if (a.partition_size > 0 && (int64_t)n >= kOneWaveItems)
-    hipLaunchKernelGGL((decode_mfma_kernel<T, 128, 1, true>), dim3((uint32_t)n), dim3(64), 0, stream, a, block_shift,
+    hipLaunchKernelGGL((decode_mfma_kernel<T, 128, 1, true, kOneWaveBufs>), dim3((uint32_t)n), dim3(64), 0, stream, a, block_shift,
                        rows);
   else if (a.partition_size > 0)
-    hipLaunchKernelGGL((decode_mfma_kernel<T, 128, kPartWaves, false>), dim3((uint32_t)n), dim3(kPartWaves * 64), 0,
+    hipLaunchKernelGGL((decode_mfma_kernel<T, 128, kPartWaves, false, kPartBufs>), dim3((uint32_t)n), dim3(kPartWaves * 64), 0,
                        stream, a, block_shift, rows);
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<T, 128, kWholeWaves, false>), dim3((uint32_t)n), dim3(kWholeWaves * 64), 0,
+    hipLaunchKernelGGL((decode_mfma_kernel<T, 128, kWholeWaves, false, kWholeBufs>), dim3((uint32_t)n), dim3(kWholeWaves * 64), 0,
                        stream, a, block_shift, rows);
   return hipGetLastError();
 }

@@ -3,12 +3,12 @@
 // semantics; the online softmax of "Paged attention for decode in C", section 2.2,
 // applied per key tile).
 //
-// Workgroup = (query tile, sequence, kv head g): 256 rows, each a (token, q head)
-// pair of the group, 8 waves of 32 rows (two 16-row blocks).  Key tiles of 32
-// positions aligned to absolute positions are gathered through the block table:
-// global loads for tile t+2 are issued into one of two register sets while tile t
-// is computed from one of two LDS buffers, so each load has two tiles of compute to
-// arrive; the 256 rows share every K/V byte brought in.
+// Workgroup = (query tile, sequence, kv head g): 128 rows, each a (token, q head)
+// pair of the group, 4 waves of 32 rows (two 16-row blocks); two workgroups share a
+// CU.  Key tiles of 32 positions aligned to absolute positions are gathered through
+// the block table: global loads for tile t+2 are issued into one of two register
+// sets while tile t is computed from one of two LDS buffers, so each load has two
+// tiles of compute to arrive; the 128 rows share every K/V byte brought in.
 //   S^T[key][row] = K_tile . Q^T  -- 16x16x32 MFMA; A = K rows read from LDS with
 //                                    16-byte reads, B = the rows' q, kept in VGPRs.
 //   O^T[d][row]  += V^T . P^T     -- 16x16x32 MFMA; A = V^T obtained from the
@@ -17,9 +17,11 @@
 //                                    which are already in the B layout because
 //                                    S^T's accumulator holds 4 keys x 1 row per lane.
 // Each lane therefore owns one row in both products, so the running max, exp-sum
-// and the rescale of O stay in registers.  Probabilities enter the PV product as
-// f16 for f16 caches; for bf16 caches they are split into bf16 high and low parts
-// (two MFMAs) so that the rounding of P stays far below the accuracy bound.
+// and the rescale of O stay in registers.  The PV product runs in f16: f16 caches
+// as they are, bf16 caches with V converted to f16 as it is staged in LDS (exact
+// over f16's range); a workgroup that meets a bf16 V value beyond that range redoes
+// its rows with bf16 V and P split into bf16 high and low parts (two MFMAs), which
+// keeps the rounding of P far below the accuracy bound.
 // Keys outside a row's visible range get score -inf; K/V slots past the sequence
 // are stored as zeros in LDS, so unwritten pool slots never reach the product.
 #pragma once
@@ -54,7 +56,7 @@ struct PrefillArgs {
   int num_heads;
   int group;
   int block_shift;      // log2(block_size) when it is a power of two, else -1
-  int tokens_per_tile;  // 256 / group (rounded down)
+  int tokens_per_tile;  // kPrefillRows / group (rounded down)
   int tiles_per_seq;    // ceil(max_query_len / tokens_per_tile)
   int min_q_len;        // sequences with fewer tokens are left to the per-row kernel
   float scale_log2;
@@ -63,8 +65,10 @@ struct PrefillArgs {
   const int32_t* status;
 };
 
-constexpr int kPrefillRows = 256;
-constexpr int kPrefillThreads = 512;
+// 128 rows (4 waves x 32) per workgroup: two workgroups fit on a CU (registers and
+// LDS), so one's Q load, pipeline fill and epilogue overlap the other's key loop.
+constexpr int kPrefillRows = 128;
+constexpr int kPrefillThreads = 256;
 constexpr int kPrefillKeys = 32;
 
 template <typename T>
@@ -127,7 +131,7 @@ struct TileRegs {
 };
 
 template <typename T, int DK, int DV>
-__global__ __launch_bounds__(kPrefillThreads, 1) void prefill_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const PrefillArgs a) {
   constexpr int KT = kPrefillKeys;
   constexpr int NTH = kPrefillThreads;
   constexpr int KPAD = 16;  // elements of padding per LDS row (32 bytes)
