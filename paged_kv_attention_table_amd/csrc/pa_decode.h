@@ -408,13 +408,14 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
   }
 }
 
-// Waves per workgroup and tile buffers per wave.  Loads in flight per CU are bounded
-// by LDS (a buffer holds a tile from load issue until its copy into registers):
-// unsplit, 6 waves x 3 buffers = 146 KB, one workgroup per CU; split with few
-// partitions, 4 waves x 2 buffers, two per CU; one-wave split, 3 buffers, six per CU.
-constexpr int kWholeWaves = 6, kWholeBufs = 3;
+// Waves per workgroup and tile buffers per wave.  A buffer holds a tile from load
+// issue until its copy into registers, so LDS bounds the loads in flight per CU:
+// unsplit, 8 waves x 2 buffers = 130 KB, one workgroup per CU; split with few
+// partitions, 4 waves x 2 buffers, two per CU; one-wave split, 2 buffers.  Deeper
+// rings (6 waves x 3, 4 x 4) measured no faster.
+constexpr int kWholeWaves = 8, kWholeBufs = 2;
 constexpr int kPartWaves = 4, kPartBufs = 2;
-constexpr int kOneWaveBufs = 3;
+constexpr int kOneWaveBufs = 2;
 // Split mode with at least this many (row, kv head, partition) items: one wave per
 // workgroup and partition.  Fewer items: kPartWaves waves share each partition, so
 // that every CU still gets enough waves.
