@@ -218,11 +218,36 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
         qb[rb][kk] = u32x4{0u, 0u, 0u, 0u};
     }
   }
+  // take the q loads' wait here, before any untracked K/V load is issued
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) asm volatile("" ::"v"(qb[rb][kk]));
   __syncthreads();
   const int klo = range_lo, khi = range_hi;
+  // Wave-uniform bounds of the rows' visible ranges, for the per-tile tests:
+  // [w_lo_min, w_hi_max) covers every non-empty range of this wave's rows, and a
+  // tile inside [w_lo_max, w_hi_min) is seen whole by every row.
+  int w_lo_min = 0x7fffffff, w_hi_max = 0, w_lo_max = 0, w_hi_min = 0x7fffffff;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    if (vis_lo[rb] < vis_hi[rb]) {
+      w_lo_min = min(w_lo_min, vis_lo[rb]);
+      w_hi_max = max(w_hi_max, vis_hi[rb]);
+    }
+    if (row_ok[rb]) {
+      w_lo_max = max(w_lo_max, vis_lo[rb]);
+      w_hi_min = min(w_hi_min, vis_hi[rb]);
+    }
+  }
+  w_lo_min = wave_min_i32(w_lo_min);
+  w_hi_max = wave_max_i32(w_hi_max);
+  w_lo_max = wave_max_i32(w_lo_max);
+  w_hi_min = wave_min_i32(w_hi_min);
 
   f32x4 o[ND][2];
-  float m_run[2], l_run[2];
+  float m_run[2];
+  f32x4 l_acc[2];  // exp-sums, formed by the PV MFMA against a block of ones: 4 equal values
   float vmax = 0.f;  // largest |V| this thread staged as f16 (bf16 caches)
 
   // Loop-invariant share of this thread in every tile's loads.  A tile's K (V)
@@ -284,7 +309,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       m_run[rb] = -kHugeScore;
-      l_run[rb] = 0.f;
+      l_acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
       mc[rb] = m_run[rb] * c2;
       m_thr[rb] = m_run[rb] + thr;
     }
@@ -319,18 +344,31 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
       khi_p = kbase + r1 * krow_bytes;
       vhi_p = vbase + r1 * vrow_bytes;
     };
-    // global -> registers for tile i.  Every load is issued (lanes past the tile's
-    // chunks read inside the same block and are not stashed), so the loads per
-    // tile are a fixed count and the waits for a tile's registers leave the next
-    // tile's loads in flight.
+    // global -> registers for tile i: exactly KN + VN loads (lanes past the tile's
+    // chunks read inside the same block and are not stashed), issued untracked so
+    // that the compiler's waits never drain the pipeline; `settle` below waits for
+    // them explicitly.
     auto fetch = [&](int i, Regs& R) {
       const int t0 = t_first + i * KT;
       const char *klo_p, *khi_p, *vlo_p, *vhi_p;
       tile_bases(t0, klo_p, khi_p, vlo_p, vhi_p);
 #pragma unroll
-      for (int u = 0; u < KN; ++u) R.k[u] = *reinterpret_cast<const u32x4*>((k_hi[u] ? khi_p : klo_p) + k_gofs[u]);
+      for (int u = 0; u < KN; ++u) R.k[u] = load16_untracked(k_hi[u] ? khi_p : klo_p, k_gofs[u]);
 #pragma unroll
-      for (int u = 0; u < VN; ++u) R.v[u] = *reinterpret_cast<const u32x4*>((v_hi[u] ? vhi_p : vlo_p) + v_gofs[u]);
+      for (int u = 0; u < VN; ++u) R.v[u] = load16_untracked(v_hi[u] ? vhi_p : vlo_p, v_gofs[u]);
+    };
+    // Wait until the registers of a tile have landed: vector-memory counts retire
+    // in order, so with one later tile's KN + VN loads issued after them (`later`),
+    // "at most KN + VN outstanding" is enough; with none, all must have landed.
+    auto settle = [&](Regs& R, bool later) {
+      if (later)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KN + VN) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int u = 0; u < KN; ++u) tie_reg(R.k[u]);
+#pragma unroll
+      for (int u = 0; u < VN; ++u) tie_reg(R.v[u]);
     };
     // registers -> LDS buffer, zeros for keys outside [klo, khi) on edge tiles
     auto stash = [&](const Regs& R, int i, int buf) {
@@ -340,32 +378,31 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
 #pragma unroll
       for (int u = 0; u < KN; ++u) {
         if (!k_on[u]) continue;
-        u32x4 x = R.k[u];
+        u32x4* dst = reinterpret_cast<u32x4*>(k_lds_b + buf * sizeof(k_lds[0]) + k_lofs[u]);
+        *dst = R.k[u];
         if (edge) {
           const int j = t0 + k_key[u];
-          if (j < klo || j >= khi) x = zero;
+          if (j < klo || j >= khi) *dst = zero;  // the later write of this lane wins
         }
-        *reinterpret_cast<u32x4*>(k_lds_b + buf * sizeof(k_lds[0]) + k_lofs[u]) = x;
       }
 #pragma unroll
       for (int u = 0; u < VN; ++u) {
         if (!v_on[u]) continue;
-        u32x4 x = R.v[u];
+        u32x4* dst = reinterpret_cast<u32x4*>(v_lds_b + buf * sizeof(v_lds[0]) + v_lofs[u]);
+        if constexpr (T::code == PA_BF16 && !EXACT)
+          *dst = bf16x8_to_f16x8(R.v[u], vmax);
+        else
+          *dst = R.v[u];
         if (edge) {
           const int j = t0 + v_key[u];
-          if (j < klo || j >= khi) x = zero;
+          if (j < klo || j >= khi) *dst = zero;
         }
-        if constexpr (T::code == PA_BF16 && !EXACT) x = bf16x8_to_f16x8(x, vmax);
-        *reinterpret_cast<u32x4*>(v_lds_b + buf * sizeof(v_lds[0]) + v_lofs[u]) = x;
       }
     };
     // one key tile from LDS buffer `buf`
     auto compute = [&](int i, int buf) {
       const int t0 = t_first + i * KT;
-      bool mine = false;
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) mine |= (vis_lo[rb] < t0 + KT) && (vis_hi[rb] > t0) && (vis_lo[rb] < vis_hi[rb]);
-      if (!__any(mine)) return;
+      if (!(t0 < w_hi_max && t0 + KT > w_lo_min)) return;  // no row of this wave sees the tile
       // S^T for two 16-key blocks and both row blocks
       f32x4 sc[2][2];
 #pragma unroll
@@ -380,10 +417,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
         }
       }
       // Tiles inside every row's visible range skip the masking.
-      bool inside = true;
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) inside &= !row_ok[rb] || (vis_lo[rb] <= t0 && vis_hi[rb] >= t0 + KT);
-      const bool masked = !__all(inside);
+      const bool masked = !(w_lo_max <= t0 && w_hi_min >= t0 + KT);  // some row sees only part of it
       u32x4 pb[2], pl[2];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
@@ -393,6 +427,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
 #pragma unroll
           for (int ii = 0; ii < 4; ++ii) sv[kb * 4 + ii] = sc[kb][rb][ii];
         if (masked) {
+          asm volatile("");  // keep this a branch: edge tiles only
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -406,7 +441,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
         if (__any(lm > m_thr[rb])) {
           const float m_new = fmaxf(m_run[rb], max_over_groups(lm));
           const float alpha = __builtin_amdgcn_exp2f((m_run[rb] - m_new) * c2);
-          l_run[rb] *= alpha;
+          l_acc[rb] *= alpha;
 #pragma unroll
           for (int nd = 0; nd < ND; ++nd) o[nd][rb] *= alpha;
           m_run[rb] = m_new;
@@ -416,7 +451,6 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
         float p[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(sv[e], c2, -mc[rb]));
-        l_run[rb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         if constexpr (F16PV) {
           uint32_t w[4];
 #pragma unroll
@@ -454,6 +488,20 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
           }
         }
       }
+      // exp-sums: the same product against a V^T block of ones sums each row's
+      // probabilities over the tile's 32 keys, across the lanes that hold them --
+      // the same rounded values that enter O
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        if constexpr (F16PV) {
+          constexpr uint32_t one2 = 0x3C003C00u;  // two f16 ones
+          l_acc[rb] = mfma_16x16x32<F16>(u32x4{one2, one2, one2, one2}, pb[rb], l_acc[rb]);
+        } else {
+          constexpr uint32_t one2 = 0x3F803F80u;  // two bf16 ones
+          l_acc[rb] = mfma_16x16x32<BF16>(u32x4{one2, one2, one2, one2}, pb[rb], l_acc[rb]);
+          l_acc[rb] = mfma_16x16x32<BF16>(u32x4{one2, one2, one2, one2}, pl[rb], l_acc[rb]);
+        }
+      }
     };
 
     // Software pipeline: while tile i is computed from LDS, tile i + 1 waits in
@@ -461,6 +509,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
     Regs RA, RB;
     fetch(0, RA);
     if (num_tiles > 1) fetch(1, RB);
+    settle(RA, num_tiles > 1);
     stash(RA, 0, 0);
     __syncthreads();
     // one step: compute tile i, refill `next` with tile i + 2, publish `held` (tile i+1)
@@ -468,6 +517,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
       if (i + 2 < num_tiles) fetch(i + 2, next);
       compute(i, i & 1);
       if (i + 1 < num_tiles) {
+        settle(held, i + 2 < num_tiles);
         stash(held, i + 1, (i + 1) & 1);
         lds_barrier();
       }
@@ -490,11 +540,10 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
     run(std::false_type{});
   }
 
-  // --- finish: sum the lane groups' exp-sums, normalise, write ---------------------
+  // --- finish: normalise, write ---------------------------------------------------
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    float l = l_run[rb];
-    l = sum_over_groups(l);
+    const float l = l_acc[rb][0];
     if (!row_ok[rb]) continue;
     const float inv = l > 0.f ? 1.0f / l : 0.f;
     const int64_t obase = (row_tok[rb] * a.num_heads + row_head[rb]) * (int64_t)DV;
