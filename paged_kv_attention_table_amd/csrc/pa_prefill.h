@@ -21,7 +21,8 @@
 // as they are, bf16 caches with V converted to f16 as it is staged in LDS (exact
 // over f16's range); a workgroup that meets a bf16 V value beyond that range redoes
 // its rows with bf16 V and P split into bf16 high and low parts (two MFMAs), which
-// keeps the rounding of P far below the accuracy bound.
+// keeps the rounding of P far below the accuracy bound; such a value shows as a
+// non-finite output of the f16 pass.
 // Keys outside a row's visible range get score -inf; K/V slots past the sequence
 // are stored as zeros in LDS, so unwritten pool slots never reach the product.
 #pragma once
@@ -96,17 +97,13 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
 }
 
-// Eight bf16 values to f16 (round to nearest even), tracking the largest magnitude
-// seen: exact for |v| in [2^-14, 65504] (f16 holds bf16's 8-bit significands there),
-// below 2^-14 the f16 subnormals keep an absolute error under 2^-25.
-__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 x, float& vmax) {
+// Eight bf16 values to f16 (round to nearest even): exact for |v| in [2^-14, 65504]
+// (f16 holds bf16's 8-bit significands there); below 2^-14 the f16 subnormals keep
+// an absolute error under 2^-25; beyond 65504 the result is inf.
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 x) {
   u32x4 y;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float lo = __uint_as_float(x[e] << 16), hi = __uint_as_float(x[e] & 0xffff0000u);
-    vmax = fmaxf(vmax, fmaxf(fabsf(lo), fabsf(hi)));
-    y[e] = pack_f16x2(lo, hi);
-  }
+  for (int e = 0; e < 4; ++e) y[e] = pack_f16x2(__uint_as_float(x[e] << 16), __uint_as_float(x[e] & 0xffff0000u));
   return y;
 }
 
@@ -248,7 +245,6 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
   f32x4 o[ND][2];
   float m_run[2];
   f32x4 l_acc[2];  // exp-sums, formed by the PV MFMA against a block of ones: 4 equal values
-  float vmax = 0.f;  // largest |V| this thread staged as f16 (bf16 caches)
 
   // Loop-invariant share of this thread in every tile's loads.  A tile's K (V)
   // chunks are dealt so that each wave's 64 lanes fall in one 16-key half of the
@@ -390,7 +386,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
         if (!v_on[u]) continue;
         u32x4* dst = reinterpret_cast<u32x4*>(v_lds_b + buf * sizeof(v_lds[0]) + v_lofs[u]);
         if constexpr (T::code == PA_BF16 && !EXACT)
-          *dst = bf16x8_to_f16x8(R.v[u], vmax);
+          *dst = bf16x8_to_f16x8(R.v[u]);
         else
           *dst = R.v[u];
         if (edge) {
@@ -531,9 +527,16 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
   };
   if constexpr (T::code == PA_BF16) {
     run(std::false_type{});
-    // a V value beyond f16's range anywhere in the staged tiles: this workgroup's
-    // rows again, exactly
-    if (vmax > 65504.f) v_out_of_range = 1;
+    // A V value beyond f16's range became inf in the staged tile, which makes every
+    // output it reaches inf or NaN (NaN where p = 0): any non-finite output of this
+    // workgroup means its rows are done again, exactly, with bf16 V.  (Inputs that
+    // are themselves inf or NaN take the exact path too; it gives the same result.)
+    float sum = 0.f;
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) sum += (o[nd][rb][0] + o[nd][rb][1]) + (o[nd][rb][2] + o[nd][rb][3]);
+    if (!__builtin_isfinite(sum)) v_out_of_range = 1;
     __syncthreads();
     if (v_out_of_range) run(std::true_type{});
   } else {
