@@ -147,13 +147,32 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
   // others' in every slot) at about the same time.
   const uint32_t wg = blockIdx.x, hkv_u = (uint32_t)a.num_kv_heads;
   const int g = (int)(wg % hkv_u);
-  const int row = (int)((wg / hkv_u) % grid_rows);
+  int row = (int)((wg / hkv_u) % grid_rows);
   const int pz = (int)(wg / (hkv_u * grid_rows));
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  if (a.query_start_loc == nullptr && a.partition_size == 0 && grid_rows <= (uint32_t)kWave) {
+    // Unsplit decode of at most 64 rows: the r-th workgroup group takes the row with
+    // the r-th longest visible range (ties by index), so the longest rows start first
+    // and the last workgroups to be dispatched are the shortest.
+    const int S = (int)grid_rows, cap = a.max_blocks * a.block_size;
+    int len = -1;
+    if (lane < S) {
+      int nl = a.seq_lens[lane];
+      nl = nl < 0 ? 0 : (nl > cap ? cap : nl);
+      len = a.window > 0 && nl > a.window ? a.window : nl;
+    }
+    int rank = 0;
+    for (int r = 0; r < S; ++r) {
+      const int lr = __builtin_amdgcn_readlane(len, r);
+      rank += (lr > len) || (lr == len && r < lane);
+    }
+    const uint64_t hit = __ballot(lane < S && rank == row);
+    row = hit ? __builtin_ctzll(hit) : row;
+  }
   int s, n, lo, hi;
   int64_t q_row;
   if (!decode_row_range(a, row, pz, s, q_row, n, lo, hi)) return;  // uniform per workgroup
 
-  const int lane = lane_id(), wave = threadIdx.x / kWave;
 
   const int c = lane >> 4, r16 = lane & 15;
   const int G = a.group, hkv = a.num_kv_heads, b = a.block_size;
