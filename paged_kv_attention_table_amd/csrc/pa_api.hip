@@ -27,13 +27,15 @@ hipError_t launch_prefill(const PrefillArgs& a, int dtype, int dk, int dv, dim3 
   return hipErrorInvalidValue;
 }
 
-// The tiled prefill kernel: f16 / bf16, these head dims, and a power-of-two block
-// size of at least 16 (a 32-key tile then spans at most two blocks, one per half).
-bool prefill_supported(int dtype, int dk, int dv, int group, int block_size) {
+// The tiled prefill kernel: f16 / bf16, these head dims, a power-of-two block size
+// of at least 16 (a 32-key tile then spans at most two blocks, one per half), and
+// a pool of fewer than 2^32 rows (the kernel forms row indices in 32 bits).
+bool prefill_supported(int dtype, int dk, int dv, int group, int block_size, int64_t num_blocks) {
   if (dtype != PA_BF16 && dtype != PA_F16) return false;
   const bool dims = (dk == 128 && dv == 128) || (dk == 192 && dv == 128) || (dk == 64 && dv == 64);
   const bool pow2 = block_size >= 16 && (block_size & (block_size - 1)) == 0;
-  return dims && pow2 && group >= 1 && group <= kPrefillRows;
+  const bool rows32 = num_blocks * (int64_t)block_size <= 0xffffffffLL;
+  return dims && pow2 && rows32 && group >= 1 && group <= kPrefillRows;
 }
 
 hipError_t launch_decode_bf16(const RowsArgs& a, int block_shift, int dk, int dv, dim3 grid, hipStream_t stream);
@@ -260,7 +262,7 @@ int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
   if (out_dtype != PA_F32 && out_dtype != q_dtype) return PA_EUNSUPPORTED;
   const int group = num_heads / pool->num_kv_heads;
   if (!rows_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group) &&
-      !prefill_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group, pool->block_size))
+      !prefill_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group, pool->block_size, pool->num_blocks))
     return PA_EUNSUPPORTED;
   if (!isfinite(scale) || !(scale > 0.f)) return PA_EINVAL;
   if (num_tokens > 0x7fffffffLL || num_seqs > 65535) return PA_EUNSUPPORTED;
@@ -311,7 +313,7 @@ int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
   a.max_partitions = 1;
   a.status = status;
 
-  if (!prefill_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group, pool->block_size) || max_query_len <= 1) {
+  if (!prefill_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group, pool->block_size, pool->num_blocks) || max_query_len <= 1) {
     // every token through the per-row kernel
     a.single_token_seqs = 0;
     const dim3 grid((unsigned)num_tokens, (unsigned)pool->num_kv_heads, 1);

@@ -111,7 +111,7 @@ struct MergeArgs {
 hipError_t launch_rows(const RowsArgs& a, int dtype, int dk, int dv, dim3 grid, hipStream_t stream);
 struct PrefillArgs;
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int dk, int dv, dim3 grid, hipStream_t stream);
-bool prefill_supported(int dtype, int dk, int dv, int group, int block_size);
+bool prefill_supported(int dtype, int dk, int dv, int group, int block_size, int64_t num_blocks);
 hipError_t launch_validate(const ValidateArgs& a, hipStream_t stream);
 hipError_t launch_write(const WriteArgs& a, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);

@@ -256,7 +256,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
   static_assert(KHALF % kWave == 0 && VHALF % kWave == 0, "tile halves of whole waves");
   static_assert(KN == Regs::KN && VN == Regs::VN, "register share of a tile");
   const int hkv = a.num_kv_heads, b = a.block_size;
-  const int64_t krow_bytes = (int64_t)hkv * DK * 2, vrow_bytes = (int64_t)hkv * DV * 2;
+  const uint32_t krow_bytes = (uint32_t)hkv * DK * 2, vrow_bytes = (uint32_t)hkv * DV * 2;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   uint32_t k_gofs[KN], k_lofs[KN], v_gofs[VN], v_lofs[VN];
   int k_key[KN], v_key[VN];
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
     k_hi[u] = w0 >= KHALF;
     const int within = (tid + NTH * u) % KHALF, key16 = within / KCH, ch = within % KCH;
     k_key[u] = (k_hi[u] ? 16 : 0) + key16;
-    k_gofs[u] = (uint32_t)(key16 * krow_bytes + ch * 16);
+    k_gofs[u] = (uint32_t)key16 * krow_bytes + (uint32_t)(ch * 16);
     k_lofs[u] = (uint32_t)((k_key[u] * KROW + ch * 8) * 2);
   }
 #pragma unroll
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
     v_hi[u] = w0 >= VHALF;
     const int within = (tid + NTH * u) % VHALF, key16 = within / VCH, ch = within % VCH;
     v_key[u] = (v_hi[u] ? 16 : 0) + key16;
-    v_gofs[u] = (uint32_t)(key16 * vrow_bytes + ch * 16);
+    v_gofs[u] = (uint32_t)key16 * vrow_bytes + (uint32_t)(ch * 16);
     v_lofs[u] = (uint32_t)((v_key[u] * VROW + ch * 8) * 2);
   }
 
@@ -318,27 +318,32 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
     char* const k_lds_b = reinterpret_cast<char*>(&k_lds[0][0][0]);
     char* const v_lds_b = reinterpret_cast<char*>(&v_lds[0][0][0]);
 
-    // Bases of a tile's two halves.  The block size is a power of two of at least
-    // 16, so a 32-key tile aligned to 32 positions lies in one block (b >= 32) or in
-    // two (b = 16, one per half).  The ids are read with scalar loads (counted
-    // apart from the vector loads, so the prefetches of earlier tiles are not
-    // waited for), and the code that issues loads has no branches, so the compiler
-    // counts every tile's loads exactly.  Keys past the visible range are loaded
-    // from valid (clamped) blocks and zeroed when stashed.
-    const int max_idx = a.max_blocks - 1;
+    // Bases of a tile's two 16-key halves.  The block size is a power of two of at
+    // least 16, so each half lies in one block: the block of its first key (the
+    // same block for both halves when b >= 32).  The ids are read with scalar loads
+    // (counted apart from the vector loads, so the prefetches of earlier tiles are
+    // not waited for), and the code that issues loads has no branches, so the
+    // compiler counts every tile's loads exactly.  Keys past the visible range are
+    // loaded from valid (clamped) blocks and zeroed when stashed.  Pool rows fit 32
+    // bits (the host sends larger pools elsewhere).
+    const int max_idx = a.max_blocks - 1, last_block = (int)(a.num_blocks - 1);
     auto tile_bases = [&](int t0, const char*& klo_p, const char*& khi_p, const char*& vlo_p, const char*& vhi_p) {
-      const int i0 = __builtin_amdgcn_readfirstlane(t0 >> a.block_shift);
-      const int i1 = i0 + 1 < max_idx ? i0 + 1 : max_idx;
-      int64_t b0 = load_scalar_i32(table + i0), b1 = load_scalar_i32(table + i1);
-      b0 = b0 < 0 ? 0 : (b0 >= a.num_blocks ? a.num_blocks - 1 : b0);
-      b1 = b1 < 0 ? 0 : (b1 >= a.num_blocks ? a.num_blocks - 1 : b1);
-      const int64_t r0 = b0 * b + (t0 & (b - 1));
-      // the second half: the next block when b = 16, else 16 rows further on
-      const int64_t r1 = b == 16 ? b1 * 16 : r0 + 16;
-      klo_p = kbase + r0 * krow_bytes;
-      vlo_p = vbase + r0 * vrow_bytes;
-      khi_p = kbase + r1 * krow_bytes;
-      vhi_p = vbase + r1 * vrow_bytes;
+      const int u0 = __builtin_amdgcn_readfirstlane(t0), u1 = u0 + 16;
+      const int i0 = min(u0 >> a.block_shift, max_idx), i1 = min(u1 >> a.block_shift, max_idx);
+      int b0, b1;
+      load_scalar_i32x2(table, (uint32_t)i0 * 4u, (uint32_t)i1 * 4u, b0, b1);
+      b0 = min(max(b0, 0), last_block);
+      b1 = min(max(b1, 0), last_block);
+      const uint32_t r0 = ((uint32_t)b0 << a.block_shift) | (uint32_t)(u0 & (b - 1));
+      const uint32_t r1 = ((uint32_t)b1 << a.block_shift) | (uint32_t)(u1 & (b - 1));
+      klo_p = kbase + (uint64_t)r0 * krow_bytes;
+      khi_p = kbase + (uint64_t)r1 * krow_bytes;
+      vlo_p = vbase + (uint64_t)r0 * vrow_bytes;
+      vhi_p = vbase + (uint64_t)r1 * vrow_bytes;
+      pin_sgpr(klo_p);
+      pin_sgpr(khi_p);
+      pin_sgpr(vlo_p);
+      pin_sgpr(vhi_p);
     };
     // global -> registers for tile i: exactly KN + VN loads (lanes past the tile's
     // chunks read inside the same block and are not stashed), issued untracked so
@@ -348,10 +353,17 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
       const int t0 = t_first + i * KT;
       const char *klo_p, *khi_p, *vlo_p, *vhi_p;
       tile_bases(t0, klo_p, khi_p, vlo_p, vhi_p);
+      // (the half of slot u is the same for every wave except for at most one u)
 #pragma unroll
-      for (int u = 0; u < KN; ++u) R.k[u] = load16_untracked(k_hi[u] ? khi_p : klo_p, k_gofs[u]);
+      for (int u = 0; u < KN; ++u) {
+        const char* p = NTH * u + NTH <= KHALF ? klo_p : NTH * u >= KHALF ? khi_p : k_hi[u] ? khi_p : klo_p;
+        R.k[u] = load16_untracked(p, k_gofs[u]);
+      }
 #pragma unroll
-      for (int u = 0; u < VN; ++u) R.v[u] = load16_untracked(v_hi[u] ? vhi_p : vlo_p, v_gofs[u]);
+      for (int u = 0; u < VN; ++u) {
+        const char* p = NTH * u + NTH <= VHALF ? vlo_p : NTH * u >= VHALF ? vhi_p : v_hi[u] ? vhi_p : vlo_p;
+        R.v[u] = load16_untracked(p, v_gofs[u]);
+      }
     };
     // Wait until the registers of a tile have landed: vector-memory counts retire
     // in order, so with one later tile's KN + VN loads issued after them (`later`),
@@ -366,33 +378,43 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
 #pragma unroll
       for (int u = 0; u < VN; ++u) tie_reg(R.v[u]);
     };
-    // registers -> LDS buffer, zeros for keys outside [klo, khi) on edge tiles
+    // registers -> LDS buffer, zeros for keys outside [klo, khi) on edge tiles.  A
+    // slot u is used by every wave when the tile's chunks fill it (always so for
+    // these head dims).
     auto stash = [&](const Regs& R, int i, int buf) {
       const int t0 = t_first + i * KT;
       const bool edge = t0 < klo || t0 + KT > khi;
       const u32x4 zero = {0u, 0u, 0u, 0u};
+      auto put = [&](bool masking) {
 #pragma unroll
-      for (int u = 0; u < KN; ++u) {
-        if (!k_on[u]) continue;
-        u32x4* dst = reinterpret_cast<u32x4*>(k_lds_b + buf * sizeof(k_lds[0]) + k_lofs[u]);
-        *dst = R.k[u];
-        if (edge) {
-          const int j = t0 + k_key[u];
-          if (j < klo || j >= khi) *dst = zero;  // the later write of this lane wins
+        for (int u = 0; u < KN; ++u) {
+          if (!(NTH * u + NTH <= 2 * KHALF || k_on[u])) continue;
+          u32x4* dst = reinterpret_cast<u32x4*>(k_lds_b + buf * sizeof(k_lds[0]) + k_lofs[u]);
+          u32x4 x = R.k[u];
+          if (masking) {
+            const int j = t0 + k_key[u];
+            if (j < klo || j >= khi) x = zero;
+          }
+          *dst = x;
         }
-      }
 #pragma unroll
-      for (int u = 0; u < VN; ++u) {
-        if (!v_on[u]) continue;
-        u32x4* dst = reinterpret_cast<u32x4*>(v_lds_b + buf * sizeof(v_lds[0]) + v_lofs[u]);
-        if constexpr (T::code == PA_BF16 && !EXACT)
-          *dst = bf16x8_to_f16x8(R.v[u]);
-        else
-          *dst = R.v[u];
-        if (edge) {
-          const int j = t0 + v_key[u];
-          if (j < klo || j >= khi) *dst = zero;
+        for (int u = 0; u < VN; ++u) {
+          if (!(NTH * u + NTH <= 2 * VHALF || v_on[u])) continue;
+          u32x4* dst = reinterpret_cast<u32x4*>(v_lds_b + buf * sizeof(v_lds[0]) + v_lofs[u]);
+          u32x4 x = R.v[u];
+          if constexpr (T::code == PA_BF16 && !EXACT) x = bf16x8_to_f16x8(x);
+          if (masking) {
+            const int j = t0 + v_key[u];
+            if (j < klo || j >= khi) x = zero;
+          }
+          *dst = x;
         }
+      };
+      if (edge) {
+        asm volatile("");  // keep the two copies apart: edge tiles only
+        put(true);
+      } else {
+        put(false);
       }
     };
     // one key tile from LDS buffer `buf`
@@ -402,15 +424,18 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
       // S^T for two 16-key blocks and both row blocks
       f32x4 sc[2][2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) sc[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
-          const u32x4 ka = *reinterpret_cast<const u32x4*>(&k_lds[buf][kb * 16 + r16][32 * kk + 8 * c]);
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        u32x4 ka[2];
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb) sc[kb][rb] = mfma_16x16x32<T>(ka, qb[rb][kk], sc[kb][rb]);
-        }
+        for (int kb = 0; kb < 2; ++kb) ka[kb] = *reinterpret_cast<const u32x4*>(&k_lds[buf][kb * 16 + r16][32 * kk + 8 * c]);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) sc[kb][rb] = mfma_16x16x32<T>(ka[kb], qb[rb][kk], sc[kb][rb]);
       }
       // Tiles inside every row's visible range skip the masking.
       const bool masked = !(w_lo_max <= t0 && w_hi_min >= t0 + KT);  // some row sees only part of it
