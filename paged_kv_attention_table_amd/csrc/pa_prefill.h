@@ -137,6 +137,9 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
   constexpr int KCH = Regs::KCH, VCH = Regs::VCH;
   constexpr int KSTEPS = DK / 32;
   constexpr int ND = DV / 16;
+  // Overlap S^T of the next key tile with the softmax of this one where the
+  // registers allow a second S^T (head dim 128).
+  constexpr bool PIPE = DK == 128;
 
   __shared__ __align__(16) uint16_t k_lds[2][KT][KROW];
   __shared__ __align__(16) uint16_t v_lds[2][KT][VROW];
@@ -318,56 +321,57 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
     char* const k_lds_b = reinterpret_cast<char*>(&k_lds[0][0][0]);
     char* const v_lds_b = reinterpret_cast<char*>(&v_lds[0][0][0]);
 
-    // Bases of a tile's two 16-key halves.  The block size is a power of two of at
-    // least 16, so each half lies in one block: the block of its first key (the
+    // Pool rows of a tile's two 16-key halves.  The block size is a power of two of
+    // at least 16, so each half lies in one block: the block of its first key (the
     // same block for both halves when b >= 32).  The ids are read with scalar loads
     // (counted apart from the vector loads, so the prefetches of earlier tiles are
-    // not waited for), and the code that issues loads has no branches, so the
-    // compiler counts every tile's loads exactly.  Keys past the visible range are
-    // loaded from valid (clamped) blocks and zeroed when stashed.  Pool rows fit 32
-    // bits (the host sends larger pools elsewhere).
+    // not waited for).  Keys past the visible range are loaded from valid (clamped)
+    // blocks and zeroed when stashed.  Pool rows fit 32 bits (the host sends larger
+    // pools elsewhere).
     const int max_idx = a.max_blocks - 1, last_block = (int)(a.num_blocks - 1);
-    auto tile_bases = [&](int t0, const char*& klo_p, const char*& khi_p, const char*& vlo_p, const char*& vhi_p) {
-      const int u0 = __builtin_amdgcn_readfirstlane(t0), u1 = u0 + 16;
+    struct Rows {
+      uint32_t lo, hi;
+    };
+    auto tile_rows = [&](int i) -> Rows {
+      const int u0 = __builtin_amdgcn_readfirstlane(t_first + i * KT), u1 = u0 + 16;
       const int i0 = min(u0 >> a.block_shift, max_idx), i1 = min(u1 >> a.block_shift, max_idx);
       int b0, b1;
       load_scalar_i32x2(table, (uint32_t)i0 * 4u, (uint32_t)i1 * 4u, b0, b1);
       b0 = min(max(b0, 0), last_block);
       b1 = min(max(b1, 0), last_block);
-      const uint32_t r0 = ((uint32_t)b0 << a.block_shift) | (uint32_t)(u0 & (b - 1));
-      const uint32_t r1 = ((uint32_t)b1 << a.block_shift) | (uint32_t)(u1 & (b - 1));
-      klo_p = kbase + (uint64_t)r0 * krow_bytes;
-      khi_p = kbase + (uint64_t)r1 * krow_bytes;
-      vlo_p = vbase + (uint64_t)r0 * vrow_bytes;
-      vhi_p = vbase + (uint64_t)r1 * vrow_bytes;
-      pin_sgpr(klo_p);
-      pin_sgpr(khi_p);
-      pin_sgpr(vlo_p);
-      pin_sgpr(vhi_p);
+      return Rows{((uint32_t)b0 << a.block_shift) | (uint32_t)(u0 & (b - 1)),
+                  ((uint32_t)b1 << a.block_shift) | (uint32_t)(u1 & (b - 1))};
     };
-    // global -> registers for tile i: exactly KN + VN loads (lanes past the tile's
-    // chunks read inside the same block and are not stashed), issued untracked so
-    // that the compiler's waits never drain the pipeline; `settle` below waits for
-    // them explicitly.
-    auto fetch = [&](int i, Regs& R) {
-      const int t0 = t_first + i * KT;
-      const char *klo_p, *khi_p, *vlo_p, *vhi_p;
-      tile_bases(t0, klo_p, khi_p, vlo_p, vhi_p);
-      // (the half of slot u is the same for every wave except for at most one u)
+    // global -> registers: the K or V share of one tile, KN or VN loads (lanes past
+    // the tile's chunks read inside the same block and are not stashed), issued
+    // untracked so that the compiler's waits never drain the pipeline; `settle`
+    // below waits for them explicitly.  The half of slot u is the same for every
+    // wave except for at most one u.
+    auto fetch_k = [&](Rows r, Regs& R) {
+      const char* lo_p = kbase + (uint64_t)r.lo * krow_bytes;
+      const char* hi_p = kbase + (uint64_t)r.hi * krow_bytes;
+      pin_sgpr(lo_p);
+      pin_sgpr(hi_p);
 #pragma unroll
       for (int u = 0; u < KN; ++u) {
-        const char* p = NTH * u + NTH <= KHALF ? klo_p : NTH * u >= KHALF ? khi_p : k_hi[u] ? khi_p : klo_p;
+        const char* p = NTH * u + NTH <= KHALF ? lo_p : NTH * u >= KHALF ? hi_p : k_hi[u] ? hi_p : lo_p;
         R.k[u] = load16_untracked(p, k_gofs[u]);
       }
+    };
+    auto fetch_v = [&](Rows r, Regs& R) {
+      const char* lo_p = vbase + (uint64_t)r.lo * vrow_bytes;
+      const char* hi_p = vbase + (uint64_t)r.hi * vrow_bytes;
+      pin_sgpr(lo_p);
+      pin_sgpr(hi_p);
 #pragma unroll
       for (int u = 0; u < VN; ++u) {
-        const char* p = NTH * u + NTH <= VHALF ? vlo_p : NTH * u >= VHALF ? vhi_p : v_hi[u] ? vhi_p : vlo_p;
+        const char* p = NTH * u + NTH <= VHALF ? lo_p : NTH * u >= VHALF ? hi_p : v_hi[u] ? hi_p : lo_p;
         R.v[u] = load16_untracked(p, v_gofs[u]);
       }
     };
-    // Wait until the registers of a tile have landed: vector-memory counts retire
-    // in order, so with one later tile's KN + VN loads issued after them (`later`),
-    // "at most KN + VN outstanding" is enough; with none, all must have landed.
+    // Wait until a register set has landed: vector-memory counts retire in order,
+    // so with one later set's KN + VN loads issued after it (`later`), "at most
+    // KN + VN outstanding" is enough; with none, all must have landed.
     auto settle = [&](Regs& R, bool later) {
       if (later)
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KN + VN) : "memory");
@@ -378,33 +382,36 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
 #pragma unroll
       for (int u = 0; u < VN; ++u) tie_reg(R.v[u]);
     };
-    // registers -> LDS buffer, zeros for keys outside [klo, khi) on edge tiles.  A
-    // slot u is used by every wave when the tile's chunks fill it (always so for
-    // these head dims).
-    auto stash = [&](const Regs& R, int i, int buf) {
-      const int t0 = t_first + i * KT;
-      const bool edge = t0 < klo || t0 + KT > khi;
+    // registers -> LDS: K of tile ik into buffer kb (when put_k) and V of tile iv
+    // into buffer vb, zeros for keys outside [klo, khi) on edge tiles.  A slot u is
+    // used by every wave when the tile's chunks fill it (always so for these head
+    // dims).
+    auto stash = [&](const Regs& R, bool put_k, int ik, int kb, int iv, int vb) {
+      const int tk = t_first + ik * KT, tv = t_first + iv * KT;
+      const bool edge = tk < klo || tk + KT > khi || tv < klo || tv + KT > khi;
       const u32x4 zero = {0u, 0u, 0u, 0u};
       auto put = [&](bool masking) {
+        if (put_k) {
 #pragma unroll
-        for (int u = 0; u < KN; ++u) {
-          if (!(NTH * u + NTH <= 2 * KHALF || k_on[u])) continue;
-          u32x4* dst = reinterpret_cast<u32x4*>(k_lds_b + buf * sizeof(k_lds[0]) + k_lofs[u]);
-          u32x4 x = R.k[u];
-          if (masking) {
-            const int j = t0 + k_key[u];
-            if (j < klo || j >= khi) x = zero;
+          for (int u = 0; u < KN; ++u) {
+            if (!(NTH * u + NTH <= 2 * KHALF || k_on[u])) continue;
+            u32x4* dst = reinterpret_cast<u32x4*>(k_lds_b + kb * sizeof(k_lds[0]) + k_lofs[u]);
+            u32x4 x = R.k[u];
+            if (masking) {
+              const int j = tk + k_key[u];
+              if (j < klo || j >= khi) x = zero;
+            }
+            *dst = x;
           }
-          *dst = x;
         }
 #pragma unroll
         for (int u = 0; u < VN; ++u) {
           if (!(NTH * u + NTH <= 2 * VHALF || v_on[u])) continue;
-          u32x4* dst = reinterpret_cast<u32x4*>(v_lds_b + buf * sizeof(v_lds[0]) + v_lofs[u]);
+          u32x4* dst = reinterpret_cast<u32x4*>(v_lds_b + vb * sizeof(v_lds[0]) + v_lofs[u]);
           u32x4 x = R.v[u];
           if constexpr (T::code == PA_BF16 && !EXACT) x = bf16x8_to_f16x8(x);
           if (masking) {
-            const int j = t0 + v_key[u];
+            const int j = tv + v_key[u];
             if (j < klo || j >= khi) x = zero;
           }
           *dst = x;
@@ -417,12 +424,8 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
         put(false);
       }
     };
-    // one key tile from LDS buffer `buf`
-    auto compute = [&](int i, int buf) {
-      const int t0 = t_first + i * KT;
-      if (!(t0 < w_hi_max && t0 + KT > w_lo_min)) return;  // no row of this wave sees the tile
-      // S^T for two 16-key blocks and both row blocks
-      f32x4 sc[2][2];
+    // S^T of key tile i (from K buffer `buf`) for two 16-key blocks and both row blocks
+    auto qk = [&](int buf, f32x4 (&sc)[2][2]) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -437,16 +440,15 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb) sc[kb][rb] = mfma_16x16x32<T>(ka[kb], qb[rb][kk], sc[kb][rb]);
       }
+    };
+    // First half of the softmax of tile i: masking (edge tiles, and tiles no row of
+    // this wave sees, which end up all masked), and the move of the reference max.
+    auto soft_max = [&](int i, f32x4 (&sc)[2][2]) {
+      const int t0 = t_first + i * KT;
       // Tiles inside every row's visible range skip the masking.
       const bool masked = !(w_lo_max <= t0 && w_hi_min >= t0 + KT);  // some row sees only part of it
-      u32x4 pb[2], pl[2];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        float sv[8];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) sv[kb * 4 + ii] = sc[kb][rb][ii];
         if (masked) {
           asm volatile("");  // keep this a branch: edge tiles only
 #pragma unroll
@@ -454,11 +456,13 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
               const int j = t0 + kb * 16 + 4 * c + ii;
-              if (j < vis_lo[rb] || j >= vis_hi[rb]) sv[kb * 4 + ii] = -INFINITY;
+              if (j < vis_lo[rb] || j >= vis_hi[rb]) sc[kb][rb][ii] = -INFINITY;
             }
         }
         // this lane's max; the row-wide max is only formed when the reference must move
-        const float lm = max3f(max3f(sv[0], sv[1], sv[2]), max3f(sv[3], sv[4], sv[5]), max3f(sv[6], sv[7], sv[7]));
+        const float lm = max3f(max3f(sc[0][rb][0], sc[0][rb][1], sc[0][rb][2]),
+                               max3f(sc[0][rb][3], sc[1][rb][0], sc[1][rb][1]),
+                               max3f(sc[1][rb][2], sc[1][rb][3], sc[1][rb][3]));
         if (__any(lm > m_thr[rb])) {
           const float m_new = fmaxf(m_run[rb], max_over_groups(lm));
           const float alpha = __builtin_amdgcn_exp2f((m_run[rb] - m_new) * c2);
@@ -469,9 +473,19 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
           mc[rb] = m_new * c2;
           m_thr[rb] = m_new + thr;
         }
+      }
+    };
+    // Second half: probabilities, and O^T += V^T P^T from V buffer `buf` (V^T via
+    // transpose reads of the row-major V tile), with the exp-sums.
+    auto soft_pv = [&](int buf, const f32x4 (&sc)[2][2]) {
+      u32x4 pb[2], pl[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
         float p[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(sv[e], c2, -mc[rb]));
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) p[kb * 4 + ii] = __builtin_amdgcn_exp2f(fmaf(sc[kb][rb][ii], c2, -mc[rb]));
         if constexpr (F16PV) {
           uint32_t w[4];
 #pragma unroll
@@ -489,7 +503,6 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
           pl[rb] = u32x4{wl[0], wl[1], wl[2], wl[3]};
         }
       }
-      // O^T += V^T P^T, V^T via transpose reads of the row-major V tile
       const int tr_r = r16 >> 2, tr_q = r16 & 3;
 #pragma unroll
       for (int nd = 0; nd < ND; ++nd) {
@@ -525,30 +538,108 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
       }
     };
 
-    // Software pipeline: while tile i is computed from LDS, tile i + 1 waits in
-    // registers and the loads of tile i + 2 are in flight.
-    Regs RA, RB;
-    fetch(0, RA);
-    if (num_tiles > 1) fetch(1, RB);
-    settle(RA, num_tiles > 1);
-    stash(RA, 0, 0);
-    __syncthreads();
-    // one step: compute tile i, refill `next` with tile i + 2, publish `held` (tile i+1)
-    auto step = [&](int i, Regs& next, Regs& held) {
-      if (i + 2 < num_tiles) fetch(i + 2, next);
-      compute(i, i & 1);
-      if (i + 1 < num_tiles) {
-        settle(held, i + 2 < num_tiles);
-        stash(held, i + 1, (i + 1) & 1);
+    if constexpr (PIPE) {
+      // Software pipeline over key tiles.  Step i finishes tile i -- its softmax and
+      // PV product, from S^T formed in the step before -- while it forms S^T of tile
+      // i + 1, so the MFMAs of one overlap the vector work of the other.  K therefore
+      // reaches LDS a step ahead of V: step i issues the loads of K(i+3) and V(i+2)
+      // into one register set, and ends by stashing the set issued a step earlier,
+      // K(i+2) and V(i+1) (tile j in buffers j & 1), behind one barrier.  Loads past
+      // the last tile are clamped to it and not stashed.  The pool rows of a tile are
+      // read with its K loads and kept for its V loads a step later.
+      const int last = num_tiles - 1;
+      Regs RA, RB;
+      Rows rows_v = tile_rows(0);  // rows of the tile whose V is loaded next
+      auto issue = [&](int i, Regs& R) {  // the set of step i: K(i+3), V(i+2), clamped
+        const Rows rk = tile_rows(min(i + 3, last));
+        fetch_k(rk, R);
+        fetch_v(rows_v, R);
+        rows_v = rk;
+      };
+      // prologue: the sets of steps -3 (K0 and V0 again), -2 (K1, V0), -1 (K2, V1)
+      {
+        fetch_k(rows_v, RA);
+        fetch_v(rows_v, RA);
+        const Rows r1 = tile_rows(min(1, last));
+        fetch_k(r1, RB);
+        fetch_v(rows_v, RB);
+        rows_v = r1;
+        settle(RA, true);
+        stash(RA, true, 0, 0, 0, 0);
+        issue(-1, RA);
+        settle(RB, true);
+        stash(RB, last >= 1, min(1, last), 1, 0, 0);
         lds_barrier();
       }
-    };
-    int i = 0;
-    for (; i + 1 < num_tiles; i += 2) {
-      step(i, RA, RB);
-      step(i + 1, RB, RA);
+      f32x4 sc[2][2];
+      qk(0, sc);
+      // one step: `next` takes the set of step i, `held` (the set of step i - 1) is stashed
+      auto step = [&](int i, Regs& next, Regs& held, auto more_tag) {
+        constexpr bool MORE = decltype(more_tag)::value;  // i + 1 < num_tiles
+        if (i + 2 < num_tiles) issue(i, next);
+        soft_max(i, sc);
+        f32x4 sn[2][2];
+        if constexpr (MORE) qk((i + 1) & 1, sn);
+        soft_pv(i & 1, sc);
+        if constexpr (MORE) {
+          settle(held, i + 2 < num_tiles);
+          stash(held, i + 2 < num_tiles, i + 2, i & 1, i + 1, (i + 1) & 1);
+          lds_barrier();
+  #pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+  #pragma unroll
+            for (int rb = 0; rb < 2; ++rb) sc[kb][rb] = sn[kb][rb];
+        }
+      };
+      int i = 0;
+      for (; i + 2 < num_tiles; i += 2) {
+        step(i, RB, RA, std::true_type{});
+        step(i + 1, RA, RB, std::true_type{});
+      }
+      if (i + 1 < num_tiles) {
+        step(i, RB, RA, std::true_type{});
+        step(i + 1, RA, RB, std::false_type{});
+      } else {
+        step(i, RB, RA, std::false_type{});
+      }
+    } else {
+      // One tile after another (head dims whose registers leave no room for a second
+      // S^T): while tile i is computed from LDS, tile i + 1 waits in registers and
+      // the loads of tile i + 2 are in flight.
+      Regs RA, RB;
+      auto fetch = [&](int i, Regs& R) {
+        const Rows r = tile_rows(i);
+        fetch_k(r, R);
+        fetch_v(r, R);
+      };
+      fetch(0, RA);
+      if (num_tiles > 1) fetch(1, RB);
+      settle(RA, num_tiles > 1);
+      stash(RA, true, 0, 0, 0, 0);
+      lds_barrier();
+      // one step: compute tile i, refill `next` with tile i + 2, publish `held` (tile i+1)
+      auto step = [&](int i, Regs& next, Regs& held) {
+        if (i + 2 < num_tiles) fetch(i + 2, next);
+        const int t0 = t_first + i * KT;
+        if (t0 < w_hi_max && t0 + KT > w_lo_min) {  // some row of this wave sees the tile
+          f32x4 sc[2][2];
+          qk(i & 1, sc);
+          soft_max(i, sc);
+          soft_pv(i & 1, sc);
+        }
+        if (i + 1 < num_tiles) {
+          settle(held, i + 2 < num_tiles);
+          stash(held, true, i + 1, (i + 1) & 1, i + 1, (i + 1) & 1);
+          lds_barrier();
+        }
+      };
+      int i = 0;
+      for (; i + 1 < num_tiles; i += 2) {
+        step(i, RA, RB);
+        step(i + 1, RB, RA);
+      }
+      if (i < num_tiles) step(i, RA, RB);
     }
-    if (i < num_tiles) step(i, RA, RB);
   };
   if constexpr (T::code == PA_BF16) {
     run(std::false_type{});
