@@ -117,13 +117,13 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 constexpr float kRescaleLog2 = 8.0f;  // move the reference max only past 2^8
 constexpr float kHugeScore = 1.0e30f;
 
-// Per-thread share of one K/V tile, in 16-byte chunks.
+// Per-thread share of one key tile: K goes straight to LDS (KN direct 16-byte
+// loads), V through registers (VN 16-byte chunks).
 template <int DK, int DV>
 struct TileRegs {
-  static constexpr int KCH = DK / 8, VCH = DV / 8;  // chunks per position
-  static constexpr int KN = (kPrefillKeys * KCH + kPrefillThreads - 1) / kPrefillThreads;
-  static constexpr int VN = (kPrefillKeys * VCH + kPrefillThreads - 1) / kPrefillThreads;
-  u32x4 k[KN];
+  static constexpr int KCH = DK / 8, VCH = DV / 8;  // 16-byte chunks per position
+  static constexpr int KN = kPrefillKeys * KCH / kPrefillThreads;
+  static constexpr int VN = kPrefillKeys * VCH / kPrefillThreads;
   u32x4 v[VN];
 };
 
@@ -131,18 +131,23 @@ template <typename T, int DK, int DV>
 __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const PrefillArgs a) {
   constexpr int KT = kPrefillKeys;
   constexpr int NTH = kPrefillThreads;
-  constexpr int KPAD = 16;  // elements of padding per LDS row (32 bytes)
-  constexpr int KROW = DK + KPAD, VROW = DV + KPAD;
+  constexpr int VPAD = 16;  // elements of padding per V row in LDS (32 bytes)
+  constexpr int VROW = DV + VPAD;
+  constexpr int NBUF = 3;  // LDS ring depth, in key tiles
   using Regs = TileRegs<DK, DV>;
   constexpr int KCH = Regs::KCH, VCH = Regs::VCH;
   constexpr int KSTEPS = DK / 32;
   constexpr int ND = DV / 16;
   // Overlap S^T of the next key tile with the softmax of this one where the
-  // registers allow a second S^T (head dim 128).
+  // registers allow a second S^T without spilling (head dim 128).
   constexpr bool PIPE = DK == 128;
 
-  __shared__ __align__(16) uint16_t k_lds[2][KT][KROW];
-  __shared__ __align__(16) uint16_t v_lds[2][KT][VROW];
+  // K rows sit unpadded, chunk ch of key row r in 16-byte slot ch ^ ksw(r): with
+  // 256-byte rows the 16 rows one read touches get 16 distinct slots of the bank
+  // space; with 128- or 384-byte rows consecutive rows alternate between its two
+  // 128-byte halves, and (r / 2) % 8 spreads eight of them over each half.
+  __shared__ __align__(16) uint16_t k_lds[NBUF][KT][DK];
+  __shared__ __align__(16) uint16_t v_lds[NBUF][KT][VROW];
   __shared__ int range_lo, range_hi, v_out_of_range;
 
   if (status_failed(a.status)) return;
@@ -244,6 +249,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
   w_hi_max = wave_max_i32(w_hi_max);
   w_lo_max = wave_max_i32(w_lo_max);
   w_hi_min = wave_min_i32(w_hi_min);
+  if (w_hi_min == 0x7fffffff) w_lo_max = 0x7fffffff;  // no row of the wave is real: mask every tile
 
   f32x4 o[ND][2];
   float m_run[2];
@@ -253,37 +259,39 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
   // chunks are dealt so that each wave's 64 lanes fall in one 16-key half of the
   // tile (a half is 16 * KCH chunks, a multiple of 64): the half -- hence the block
   // and the base address -- is wave-uniform, and a lane adds its fixed offset (key
-  // within the half, chunk) to it.
+  // within the half, chunk) to it.  K slot u of a thread is 16-byte position
+  // tid + NTH u of the tile in LDS (row-major, swizzled); its global chunk is the
+  // one the swizzle puts there.
   constexpr int KHALF = 16 * KCH, VHALF = 16 * VCH;
-  constexpr int KN = (2 * KHALF + NTH - 1) / NTH, VN = (2 * VHALF + NTH - 1) / NTH;
+  constexpr int KN = Regs::KN, VN = Regs::VN;
   static_assert(KHALF % kWave == 0 && VHALF % kWave == 0, "tile halves of whole waves");
-  static_assert(KN == Regs::KN && VN == Regs::VN, "register share of a tile");
+  static_assert(KN * NTH == 2 * KHALF && VN * NTH == 2 * VHALF, "whole loads per thread");
   const int hkv = a.num_kv_heads, b = a.block_size;
   const uint32_t krow_bytes = (uint32_t)hkv * DK * 2, vrow_bytes = (uint32_t)hkv * DV * 2;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  uint32_t k_gofs[KN], k_lofs[KN], v_gofs[VN], v_lofs[VN];
-  int k_key[KN], v_key[VN];
-  bool k_on[KN], v_on[VN], k_hi[KN], v_hi[VN];  // wave-uniform
+  auto ksw = [](int r) { return DK == 128 ? (r & 15) : ((r >> 1) & 7); };
+  uint32_t k_gofs[KN], v_gofs[VN], v_lofs[VN];
+  int v_key[VN];
+  bool k_hi[KN], v_hi[VN];  // wave-uniform
 #pragma unroll
   for (int u = 0; u < KN; ++u) {
-    const int w0 = wave_u * kWave + NTH * u;  // the wave's first chunk index
-    k_on[u] = w0 < 2 * KHALF;
-    k_hi[u] = w0 >= KHALF;
-    const int within = (tid + NTH * u) % KHALF, key16 = within / KCH, ch = within % KCH;
-    k_key[u] = (k_hi[u] ? 16 : 0) + key16;
-    k_gofs[u] = (uint32_t)key16 * krow_bytes + (uint32_t)(ch * 16);
-    k_lofs[u] = (uint32_t)((k_key[u] * KROW + ch * 8) * 2);
+    k_hi[u] = wave_u * kWave + NTH * u >= KHALF;
+    const int pos = tid + NTH * u, row = pos / KCH, ch = (pos % KCH) ^ ksw(row);
+    k_gofs[u] = (uint32_t)(row & 15) * krow_bytes + (uint32_t)(ch * 16);
   }
 #pragma unroll
   for (int u = 0; u < VN; ++u) {
-    const int w0 = wave_u * kWave + NTH * u;
-    v_on[u] = w0 < 2 * VHALF;
-    v_hi[u] = w0 >= VHALF;
+    v_hi[u] = wave_u * kWave + NTH * u >= VHALF;
     const int within = (tid + NTH * u) % VHALF, key16 = within / VCH, ch = within % VCH;
     v_key[u] = (v_hi[u] ? 16 : 0) + key16;
     v_gofs[u] = (uint32_t)key16 * vrow_bytes + (uint32_t)(ch * 16);
     v_lofs[u] = (uint32_t)((v_key[u] * VROW + ch * 8) * 2);
   }
+  // byte offsets of this lane's K reads in a tile: row kb * 16 + r16 (the kb term is
+  // added as a constant), logical chunk 4 kk + c
+  uint32_t k_rd[KSTEPS];
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) k_rd[kk] = (uint32_t)(r16 * DK * 2 + (((4 * kk + c) ^ ksw(r16)) * 16));
 
   // The whole key loop.  EXACT = false with a bf16 cache stages V as f16 and runs
   // PV on f16 MFMA with P in f16; EXACT = true keeps V in bf16 and splits P into
@@ -318,7 +326,6 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
     const char* vbase = static_cast<const char*>(a.v_pool) + (int64_t)g * DV * 2;
     const int t_first = klo & ~(KT - 1);
     const int num_tiles = (khi - t_first + KT - 1) / KT;
-    char* const k_lds_b = reinterpret_cast<char*>(&k_lds[0][0][0]);
     char* const v_lds_b = reinterpret_cast<char*>(&v_lds[0][0][0]);
 
     // Pool rows of a tile's two 16-key halves.  The block size is a power of two of
@@ -342,20 +349,22 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
       return Rows{((uint32_t)b0 << a.block_shift) | (uint32_t)(u0 & (b - 1)),
                   ((uint32_t)b1 << a.block_shift) | (uint32_t)(u1 & (b - 1))};
     };
-    // global -> registers: the K or V share of one tile, KN or VN loads (lanes past
-    // the tile's chunks read inside the same block and are not stashed), issued
-    // untracked so that the compiler's waits never drain the pipeline; `settle`
-    // below waits for them explicitly.  The half of slot u is the same for every
-    // wave except for at most one u.
-    auto fetch_k = [&](Rows r, Regs& R) {
+    // global -> LDS: the K share of one tile, KN direct loads into LDS buffer `buf`
+    // (wave w's load u fills 16-byte positions NTH u + 64 w ..+ 63 of the tile, one
+    // per lane); global -> registers: the V share, VN loads.  All are issued
+    // untracked, so that the compiler's waits never drain the pipeline; the loop
+    // waits for them explicitly.  The half of slot u is the same for every wave
+    // except for at most one u.
+    auto dma_k = [&](Rows r, int buf) {
       const char* lo_p = kbase + (uint64_t)r.lo * krow_bytes;
       const char* hi_p = kbase + (uint64_t)r.hi * krow_bytes;
       pin_sgpr(lo_p);
       pin_sgpr(hi_p);
+      const uint32_t lds0 = lds_addr(&k_lds[buf][0][0]) + (uint32_t)wave_u * kWave * 16;
 #pragma unroll
       for (int u = 0; u < KN; ++u) {
         const char* p = NTH * u + NTH <= KHALF ? lo_p : NTH * u >= KHALF ? hi_p : k_hi[u] ? hi_p : lo_p;
-        R.k[u] = load16_untracked(p, k_gofs[u]);
+        load16_to_lds_untracked(p, k_gofs[u], lds0 + (uint32_t)(NTH * u * 16));
       }
     };
     auto fetch_v = [&](Rows r, Regs& R) {
@@ -369,44 +378,23 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
         R.v[u] = load16_untracked(p, v_gofs[u]);
       }
     };
-    // Wait until a register set has landed: vector-memory counts retire in order,
-    // so with one later set's KN + VN loads issued after it (`later`), "at most
-    // KN + VN outstanding" is enough; with none, all must have landed.
-    auto settle = [&](Regs& R, bool later) {
-      if (later)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KN + VN) : "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-#pragma unroll
-      for (int u = 0; u < KN; ++u) tie_reg(R.k[u]);
+    // Wait until everything but the last KN loads (one tile's K, issued after the
+    // V loads of the same step) has landed, then order the V registers after it.
+    auto settle = [&](Regs& R) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KN) : "memory");
 #pragma unroll
       for (int u = 0; u < VN; ++u) tie_reg(R.v[u]);
     };
-    // registers -> LDS: K of tile ik into buffer kb (when put_k) and V of tile iv
-    // into buffer vb, zeros for keys outside [klo, khi) on edge tiles.  A slot u is
-    // used by every wave when the tile's chunks fill it (always so for these head
-    // dims).
-    auto stash = [&](const Regs& R, bool put_k, int ik, int kb, int iv, int vb) {
-      const int tk = t_first + ik * KT, tv = t_first + iv * KT;
-      const bool edge = tk < klo || tk + KT > khi || tv < klo || tv + KT > khi;
+    // registers -> LDS: V of tile iv into buffer vb, zeros for keys outside
+    // [klo, khi) on edge tiles.  (K is not cleared: scores of keys outside a row's
+    // range are replaced by -inf, whatever the bytes hold.)
+    auto stash_v = [&](const Regs& R, int iv, int vb) {
+      const int tv = t_first + iv * KT;
+      const bool edge = tv < klo || tv + KT > khi;
       const u32x4 zero = {0u, 0u, 0u, 0u};
       auto put = [&](bool masking) {
-        if (put_k) {
-#pragma unroll
-          for (int u = 0; u < KN; ++u) {
-            if (!(NTH * u + NTH <= 2 * KHALF || k_on[u])) continue;
-            u32x4* dst = reinterpret_cast<u32x4*>(k_lds_b + kb * sizeof(k_lds[0]) + k_lofs[u]);
-            u32x4 x = R.k[u];
-            if (masking) {
-              const int j = tk + k_key[u];
-              if (j < klo || j >= khi) x = zero;
-            }
-            *dst = x;
-          }
-        }
 #pragma unroll
         for (int u = 0; u < VN; ++u) {
-          if (!(NTH * u + NTH <= 2 * VHALF || v_on[u])) continue;
           u32x4* dst = reinterpret_cast<u32x4*>(v_lds_b + vb * sizeof(v_lds[0]) + v_lofs[u]);
           u32x4 x = R.v[u];
           if constexpr (T::code == PA_BF16 && !EXACT) x = bf16x8_to_f16x8(x);
@@ -424,7 +412,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
         put(false);
       }
     };
-    // S^T of key tile i (from K buffer `buf`) for two 16-key blocks and both row blocks
+    // S^T of a key tile (from K buffer `buf`) for two 16-key blocks and both row blocks
     auto qk = [&](int buf, f32x4 (&sc)[2][2]) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -434,7 +422,8 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
       for (int kk = 0; kk < KSTEPS; ++kk) {
         u32x4 ka[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) ka[kb] = *reinterpret_cast<const u32x4*>(&k_lds[buf][kb * 16 + r16][32 * kk + 8 * c]);
+        for (int kb = 0; kb < 2; ++kb)
+          ka[kb] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(&k_lds[buf][kb * 16][0]) + k_rd[kk]);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -538,108 +527,79 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
       }
     };
 
+    // Software pipeline over key tiles, in rings of NBUF LDS buffers (tile j in
+    // buffer j % NBUF).  Step i loads V(i+1) into registers and K(i+KA) straight
+    // into LDS, finishes tile i, and ends by stashing V(i+1) behind one barrier.
+    // With PIPE, step i finishes tile i -- its softmax and PV product, from S^T
+    // formed in the step before -- while it forms S^T of tile i + 1, so the MFMAs
+    // of one overlap the vector work of the other; K then runs KA = 3 tiles ahead
+    // (buffer i % NBUF held K(i), last read in step i - 1), else KA = 2 (buffer
+    // (i + 2) % NBUF held K(i - 1)).  Loads past the last tile are clamped to it.
+    constexpr int KA = PIPE ? 3 : 2;
+    const int last = num_tiles - 1;
+    Regs RV;
+    Rows rq[NBUF];  // pool rows of tile j in rq[j % NBUF], from its K load on
+    rq[0] = tile_rows(0);
+    fetch_v(rq[0], RV);
+#pragma unroll
+    for (int j = 0; j < KA; ++j) {
+      if (j > 0) rq[j] = tile_rows(min(j, last));
+      dma_k(rq[j], j);
+    }
+    settle(RV);  // V0 and K0 .. K(KA-2) have landed
+    stash_v(RV, 0, 0);
+    lds_barrier();
+    f32x4 sc[2][2];
     if constexpr (PIPE) {
-      // Software pipeline over key tiles.  Step i finishes tile i -- its softmax and
-      // PV product, from S^T formed in the step before -- while it forms S^T of tile
-      // i + 1, so the MFMAs of one overlap the vector work of the other.  K therefore
-      // reaches LDS a step ahead of V: step i issues the loads of K(i+3) and V(i+2)
-      // into one register set, and ends by stashing the set issued a step earlier,
-      // K(i+2) and V(i+1) (tile j in buffers j & 1), behind one barrier.  Loads past
-      // the last tile are clamped to it and not stashed.  The pool rows of a tile are
-      // read with its K loads and kept for its V loads a step later.
-      const int last = num_tiles - 1;
-      Regs RA, RB;
-      Rows rows_v = tile_rows(0);  // rows of the tile whose V is loaded next
-      auto issue = [&](int i, Regs& R) {  // the set of step i: K(i+3), V(i+2), clamped
-        const Rows rk = tile_rows(min(i + 3, last));
-        fetch_k(rk, R);
-        fetch_v(rows_v, R);
-        rows_v = rk;
-      };
-      // prologue: the sets of steps -3 (K0 and V0 again), -2 (K1, V0), -1 (K2, V1)
-      {
-        fetch_k(rows_v, RA);
-        fetch_v(rows_v, RA);
-        const Rows r1 = tile_rows(min(1, last));
-        fetch_k(r1, RB);
-        fetch_v(rows_v, RB);
-        rows_v = r1;
-        settle(RA, true);
-        stash(RA, true, 0, 0, 0, 0);
-        issue(-1, RA);
-        settle(RB, true);
-        stash(RB, last >= 1, min(1, last), 1, 0, 0);
-        lds_barrier();
-      }
-      f32x4 sc[2][2];
       qk(0, sc);
-      // one step: `next` takes the set of step i, `held` (the set of step i - 1) is stashed
-      auto step = [&](int i, Regs& next, Regs& held, auto more_tag) {
-        constexpr bool MORE = decltype(more_tag)::value;  // i + 1 < num_tiles
-        if (i + 2 < num_tiles) issue(i, next);
+      lds_barrier();  // every wave is past K0 before step 0 reloads its buffer
+    }
+    // one step on tile i in buffer B = i % NBUF; `more`: i + 1 < num_tiles
+    auto step = [&](int i, auto slot_tag, auto more) {
+      constexpr int B = decltype(slot_tag)::value, B1 = (B + 1) % NBUF, BK = (B + KA) % NBUF;
+      if (more) {
+        fetch_v(rq[B1], RV);
+        rq[BK] = tile_rows(min(i + KA, last));
+        dma_k(rq[BK], BK);
+      }
+      if constexpr (PIPE) {
         soft_max(i, sc);
         f32x4 sn[2][2];
-        if constexpr (MORE) qk((i + 1) & 1, sn);
-        soft_pv(i & 1, sc);
-        if constexpr (MORE) {
-          settle(held, i + 2 < num_tiles);
-          stash(held, i + 2 < num_tiles, i + 2, i & 1, i + 1, (i + 1) & 1);
-          lds_barrier();
-  #pragma unroll
+        if (more) qk(B1, sn);
+        soft_pv(B, sc);
+        if (more) {
+#pragma unroll
           for (int kb = 0; kb < 2; ++kb)
-  #pragma unroll
+#pragma unroll
             for (int rb = 0; rb < 2; ++rb) sc[kb][rb] = sn[kb][rb];
         }
-      };
-      int i = 0;
-      for (; i + 2 < num_tiles; i += 2) {
-        step(i, RB, RA, std::true_type{});
-        step(i + 1, RA, RB, std::true_type{});
-      }
-      if (i + 1 < num_tiles) {
-        step(i, RB, RA, std::true_type{});
-        step(i + 1, RA, RB, std::false_type{});
       } else {
-        step(i, RB, RA, std::false_type{});
-      }
-    } else {
-      // One tile after another (head dims whose registers leave no room for a second
-      // S^T): while tile i is computed from LDS, tile i + 1 waits in registers and
-      // the loads of tile i + 2 are in flight.
-      Regs RA, RB;
-      auto fetch = [&](int i, Regs& R) {
-        const Rows r = tile_rows(i);
-        fetch_k(r, R);
-        fetch_v(r, R);
-      };
-      fetch(0, RA);
-      if (num_tiles > 1) fetch(1, RB);
-      settle(RA, num_tiles > 1);
-      stash(RA, true, 0, 0, 0, 0);
-      lds_barrier();
-      // one step: compute tile i, refill `next` with tile i + 2, publish `held` (tile i+1)
-      auto step = [&](int i, Regs& next, Regs& held) {
-        if (i + 2 < num_tiles) fetch(i + 2, next);
         const int t0 = t_first + i * KT;
         if (t0 < w_hi_max && t0 + KT > w_lo_min) {  // some row of this wave sees the tile
-          f32x4 sc[2][2];
-          qk(i & 1, sc);
+          qk(B, sc);
           soft_max(i, sc);
-          soft_pv(i & 1, sc);
+          soft_pv(B, sc);
         }
-        if (i + 1 < num_tiles) {
-          settle(held, i + 2 < num_tiles);
-          stash(held, true, i + 1, (i + 1) & 1, i + 1, (i + 1) & 1);
-          lds_barrier();
-        }
-      };
-      int i = 0;
-      for (; i + 1 < num_tiles; i += 2) {
-        step(i, RA, RB);
-        step(i + 1, RB, RA);
       }
-      if (i < num_tiles) step(i, RA, RB);
+      if (more) {
+        settle(RV);
+        stash_v(RV, i + 1, B1);
+        lds_barrier();
+      }
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    int i = 0;
+    for (; i + NBUF < num_tiles; i += NBUF) {
+      step(i, S0{}, std::true_type{});
+      step(i + 1, S1{}, std::true_type{});
+      step(i + 2, S2{}, std::true_type{});
     }
+    step(i, S0{}, i + 1 < num_tiles);
+    if (i + 1 < num_tiles) step(i + 1, S1{}, i + 2 < num_tiles);
+    if (i + 2 < num_tiles) step(i + 2, S2{}, false);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // clamped loads past the last tile
   };
   if constexpr (T::code == PA_BF16) {
     run(std::false_type{});
