@@ -68,6 +68,29 @@ SMALL = [
 ]
 
 
+# Single-token sequences mixed with longer ones: singles first in the batch, short
+# and long contexts, a window that cuts a long context down, and a batch of more
+# than 64 sequences.
+SINGLES = [
+    ("bf16", 32, 8, 128, 128, [(3000, 1), (1500, 1), (100, 40), (2047, 1), (2048, 1), (0, 1), (4000, 1), (50, 70)],
+     True, 0, 16),
+    ("bf16", 6, 6, 192, 128, [(3000, 1), (64, 64), (1200, 1), (2500, 1)], True, 1500, 16),
+    ("f16", 32, 8, 128, 128, [((37 * i) % 3100, 1) for i in range(68)] + [(10, 50), (200, 33)], True, 0, 32),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SINGLES)))
+def test_varlen_single_tokens_mixed_in(orc, case):
+    dtype, H, Hkv, dk, dv, segs, causal, window, b = SINGLES[case]
+    w = W.make_paged(f"singles{case}", 700 + case, dtype=dtype, block_size=b, num_heads=H, num_kv_heads=Hkv, dk=dk,
+                     dv=dv, segments=segs, causal=causal, sliding_window=window)
+    d = OnDevice(w)
+    out, lse = run_varlen(d)
+    ref, rlse = oracle_varlen(orc, d)
+    assert_close(host(out), ref, TOL[dtype], "out")
+    assert_close(host(lse), rlse, TOL[dtype], "lse")
+
+
 @pytest.mark.parametrize("case", range(len(SMALL)))
 def test_varlen_small_shapes(orc, case):
     dtype, H, Hkv, dk, dv, segs, causal, window, b = SMALL[case]
