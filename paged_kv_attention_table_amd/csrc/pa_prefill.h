@@ -138,9 +138,9 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
   constexpr int KCH = Regs::KCH, VCH = Regs::VCH;
   constexpr int KSTEPS = DK / 32;
   constexpr int ND = DV / 16;
-  // Overlap S^T of the next key tile with the softmax of this one where the
-  // registers allow a second S^T without spilling (head dim 128).
-  constexpr bool PIPE = DK == 128;
+  // Overlap S^T of the next key tile with the softmax of this one (head dims 128
+  // and 192; at 64 the single-tile loop keeps three workgroups per CU).
+  constexpr bool PIPE = DK >= 128;
 
   // K rows sit unpadded, chunk ch of key row r in 16-byte slot ch ^ ksw(r): with
   // 256-byte rows the 16 rows one read touches get 16 distinct slots of the bank
@@ -250,6 +250,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
   w_lo_max = wave_max_i32(w_lo_max);
   w_hi_min = wave_min_i32(w_hi_min);
   if (w_hi_min == 0x7fffffff) w_lo_max = 0x7fffffff;  // no row of the wave is real: mask every tile
+  const bool wave_live = w_hi_min != 0x7fffffff;  // some row of the wave is real
 
   f32x4 o[ND][2];
   float m_run[2];
@@ -492,6 +493,9 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
           pl[rb] = u32x4{wl[0], wl[1], wl[2], wl[3]};
         }
       }
+      // (pipelined: V reads stay below the P products; hoisted among them they push
+      // the loop past 256 VGPRs)
+      if constexpr (PIPE) __builtin_amdgcn_sched_barrier(0);
       const int tr_r = r16 >> 2, tr_q = r16 & 3;
 #pragma unroll
       for (int nd = 0; nd < ND; ++nd) {
@@ -554,15 +558,19 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
       qk(0, sc);
       lds_barrier();  // every wave is past K0 before step 0 reloads its buffer
     }
-    // one step on tile i in buffer B = i % NBUF; `more`: i + 1 < num_tiles
-    auto step = [&](int i, auto slot_tag, auto more) {
+    // one step on tile i in buffer B = i % NBUF; `more`: i + 1 < num_tiles; LIVE: the
+    // wave has a real row
+    auto step = [&](int i, auto slot_tag, auto more, auto live_tag) {
+      constexpr bool LIVE = decltype(live_tag)::value;
       constexpr int B = decltype(slot_tag)::value, B1 = (B + 1) % NBUF, BK = (B + KA) % NBUF;
       if (more) {
         fetch_v(rq[B1], RV);
         rq[BK] = tile_rows(min(i + KA, last));
         dma_k(rq[BK], BK);
       }
-      if constexpr (PIPE) {
+      if constexpr (!LIVE) {
+        // no real row in this wave: nothing to compute
+      } else if constexpr (PIPE) {
         soft_max(i, sc);
         f32x4 sn[2][2];
         if (more) qk(B1, sn);
@@ -590,15 +598,22 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
     using S2 = std::integral_constant<int, 2>;
-    int i = 0;
-    for (; i + NBUF < num_tiles; i += NBUF) {
-      step(i, S0{}, std::true_type{});
-      step(i + 1, S1{}, std::true_type{});
-      step(i + 2, S2{}, std::true_type{});
-    }
-    step(i, S0{}, i + 1 < num_tiles);
-    if (i + 1 < num_tiles) step(i + 1, S1{}, i + 2 < num_tiles);
-    if (i + 2 < num_tiles) step(i + 2, S2{}, false);
+    // waves with no real row only load, stash and meet the barriers
+    auto steps = [&](auto live) {
+      int i = 0;
+      for (; i + NBUF < num_tiles; i += NBUF) {
+        step(i, S0{}, std::true_type{}, live);
+        step(i + 1, S1{}, std::true_type{}, live);
+        step(i + 2, S2{}, std::true_type{}, live);
+      }
+      step(i, S0{}, i + 1 < num_tiles, live);
+      if (i + 1 < num_tiles) step(i + 1, S1{}, i + 2 < num_tiles, live);
+      if (i + 2 < num_tiles) step(i + 2, S2{}, false, live);
+    };
+    if (wave_live)
+      steps(std::true_type{});
+    else
+      steps(std::false_type{});
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // clamped loads past the last tile
   };
   if constexpr (T::code == PA_BF16) {
