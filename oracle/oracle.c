@@ -179,24 +179,28 @@ int orc_gather(const void* pool, int dtype, int64_t num_blocks, int block_size, 
 /* One query q[dk] against keys K[j * dk + d] and values V[j * dv + d] for the
  * visible positions lo <= j < hi.  Pass 1 forms each score scale * <q, k_j> and the
  * maximum m; pass 2 forms e_j = exp(s_j - m), l = sum e_j and a = sum e_j v_j.  The
- * output is a * (1 / l).  An empty range gives a zero output, m = -inf, l = 0.
- * s is scratch of at least hi - lo doubles.                                      */
+ * output is a * (1 / l).  An attention sink ("ManagedPagedAttention.cs",
+ * ForwardWithSinks) is one more position with score `sink` and a zero value: it
+ * enters the maximum and the exp-sum, not the numerator (sink = -inf: none).  An
+ * empty range without a sink gives a zero output, m = -inf, l = 0; with a sink, a
+ * zero output, m = sink, l = 1.  s is scratch of at least hi - lo doubles.        */
 static void attend(const double* q, const double* K, const double* V, int dk, int dv, int64_t lo,
-                   int64_t hi, double scale, double* s, double* out, double* m_out, double* l_out) {
+                   int64_t hi, double scale, double sink, double* s, double* out, double* m_out,
+                   double* l_out) {
   for (int d = 0; d < dv; ++d) out[d] = 0.0;
-  if (hi <= lo) {
-    *m_out = -INFINITY;
-    *l_out = 0.0;
-    return;
-  }
-  double m = -INFINITY;
+  double m = sink;
   for (int64_t j = lo; j < hi; ++j) {
     double dot = 0.0;
     for (int d = 0; d < dk; ++d) dot += q[d] * K[j * dk + d];
     s[j - lo] = scale * dot;
     if (s[j - lo] > m) m = s[j - lo];
   }
-  double l = 0.0;
+  if (m == -INFINITY) { /* nothing visible and no sink */
+    *m_out = -INFINITY;
+    *l_out = 0.0;
+    return;
+  }
+  double l = sink == -INFINITY ? 0.0 : exp(sink - m);
   for (int64_t j = lo; j < hi; ++j) {
     s[j - lo] = exp(s[j - lo] - m);
     l += s[j - lo];
@@ -224,7 +228,7 @@ int orc_attend_gathered(const double* q, const double* K, const double* V, int64
   double* s = (double*)malloc(sizeof(double) * (size_t)widest);
   for (int64_t r = 0; r < num_rows; ++r) {
     double m, l;
-    attend(q + r * dk, K, V, dk, dv, lo[r], hi[r], scale, s, out + r * dv, &m, &l);
+    attend(q + r * dk, K, V, dk, dv, lo[r], hi[r], scale, -INFINITY, s, out + r * dv, &m, &l);
     lse[r] = lse_of(m, l);
   }
   free(s);
@@ -262,6 +266,7 @@ struct attn_job {
   int causal;
   int sliding_window;
   const uint8_t* row_mask; /* [T * H], nullable: compute every row */
+  const double* sinks;     /* [H] sink logits, nullable: none */
   double* out;             /* [T, H, dv] */
   double* lse;             /* [H, T], nullable */
   /* split-KV outputs (partition_size > 0) */
@@ -325,7 +330,8 @@ static void attn_task(void* ctx, int64_t task) {
         qrow[d] = load_elem(job->q, job->q_dtype, (t * job->num_heads + h) * P->dk + d);
       if (job->partition_size <= 0) {
         double m, l;
-        attend(qrow, K, V, P->dk, P->dv, start, end, job->scale, sc, orow, &m, &l);
+        const double sink = job->sinks ? job->sinks[h] : -INFINITY;
+        attend(qrow, K, V, P->dk, P->dv, start, end, job->scale, sink, sc, orow, &m, &l);
         memcpy(job->out + (t * job->num_heads + h) * P->dv, orow, sizeof(double) * (size_t)P->dv);
         if (job->lse) job->lse[(int64_t)h * job->num_tokens + t] = lse_of(m, l);
       } else {
@@ -336,8 +342,8 @@ static void attn_task(void* ctx, int64_t task) {
           if (hi > n) hi = n;
           if (lo < start) lo = start;
           if (hi > end) hi = end;
-          double m, l;
-          attend(qrow, K, V, P->dk, P->dv, lo, hi, job->scale, sc, orow, &m, &l);
+          double m, l; /* partition states leave the sink to the reduction */
+          attend(qrow, K, V, P->dk, P->dv, lo, hi, job->scale, -INFINITY, sc, orow, &m, &l);
           int64_t idx = ((int64_t)s * job->num_heads + h) * job->max_partitions + p;
           job->max_logits[idx] = m;
           job->exp_sums[idx] = l;
@@ -390,7 +396,8 @@ int orc_varlen(const void* k_pool, const void* v_pool, int kv_dtype, int64_t num
                int num_heads, int64_t num_tokens, const int32_t* query_start_loc, int num_seqs,
                const int32_t* seq_lens, const int32_t* positions, const int32_t* block_tables,
                int max_blocks, double scale, int causal, int sliding_window,
-               const uint8_t* row_mask, double* out, double* lse, int num_threads) {
+               const uint8_t* row_mask, double* out, double* lse, const double* sinks,
+               int num_threads) {
   struct attn_job job;
   memset(&job, 0, sizeof job);
   job.pool.k = k_pool;
@@ -415,6 +422,7 @@ int orc_varlen(const void* k_pool, const void* v_pool, int kv_dtype, int64_t num
   job.causal = causal;
   job.sliding_window = sliding_window;
   job.row_mask = row_mask;
+  job.sinks = sinks;
   job.out = out;
   job.lse = lse;
   int st = check_job(&job);
@@ -436,7 +444,7 @@ int orc_decode(const void* k_pool, const void* v_pool, int kv_dtype, int64_t num
                int num_heads, const int32_t* block_tables, int max_blocks, const int32_t* seq_lens,
                int num_seqs, double scale, int sliding_window, int partition_size,
                int max_partitions, double* out, double* lse, double* max_logits,
-               double* exp_sums, double* tmp_out, int num_threads) {
+               double* exp_sums, double* tmp_out, const double* sinks, int num_threads) {
   if (num_seqs < 0) return ORC_EINVAL;
   for (int s = 0; s < num_seqs; ++s)
     if (seq_lens[s] < 1) return ORC_EINVAL;
@@ -483,6 +491,7 @@ int orc_decode(const void* k_pool, const void* v_pool, int kv_dtype, int64_t num
   job.max_logits = max_logits;
   job.exp_sums = exp_sums;
   job.tmp_out = tmp_out;
+  job.sinks = sinks;
   int st = check_job(&job);
   if (st == ORC_OK) parallel_for((int64_t)num_seqs * num_kv_heads, num_threads, attn_task, &job);
   free(pos);
@@ -492,10 +501,12 @@ int orc_decode(const void* k_pool, const void* v_pool, int kv_dtype, int64_t num
 
 /* Phase-2 reduction of decode partitions, for each (s, h) over p < ceil(n_s / P):
  * M = max_p m_p, w_p = l_p * exp(m_p - M), out = sum_p w_p o_p / sum_p w_p.
- * The o_p are the normalised partition outputs written by orc_decode.           */
+ * The o_p are the normalised partition outputs written by orc_decode.  A sink
+ * logit z_h (sinks nullable) joins once here, as a partition of weight exp(z_h - M)
+ * and zero output, with M taken over the z_h too.                               */
 int orc_reduce_partitions(const double* max_logits, const double* exp_sums, const double* tmp_out,
                           const int32_t* seq_lens, int num_seqs, int num_heads, int partition_size,
-                          int max_partitions, int dv, double* out) {
+                          int max_partitions, int dv, const double* sinks, double* out) {
   if (partition_size < 1) return ORC_EINVAL;
   for (int s = 0; s < num_seqs; ++s) {
     int64_t np = ((int64_t)seq_lens[s] + partition_size - 1) / partition_size;
@@ -503,12 +514,13 @@ int orc_reduce_partitions(const double* max_logits, const double* exp_sums, cons
     for (int h = 0; h < num_heads; ++h) {
       int64_t base = ((int64_t)s * num_heads + h) * max_partitions;
       double* o = out + ((int64_t)s * num_heads + h) * dv;
-      double M = -INFINITY;
+      const double sink = sinks ? sinks[h] : -INFINITY;
+      double M = sink;
       for (int64_t p = 0; p < np; ++p)
         if (max_logits[base + p] > M) M = max_logits[base + p];
       for (int d = 0; d < dv; ++d) o[d] = 0.0;
       if (M == -INFINITY) continue;
-      double total = 0.0;
+      double total = sink == -INFINITY ? 0.0 : exp(sink - M);
       for (int64_t p = 0; p < np; ++p) {
         if (exp_sums[base + p] == 0.0) continue;
         double w = exp_sums[base + p] * exp(max_logits[base + p] - M);

@@ -47,6 +47,15 @@ def _storage(a, dtype):
     return np.ascontiguousarray(a, dtype=NUMPY_STORAGE[dtype])
 
 
+def _sinks(sinks, num_heads):
+    """Sink logits as a contiguous float64 [H] array, or None."""
+    if sinks is None:
+        return None
+    a = np.ascontiguousarray(sinks, dtype=np.float64)
+    assert a.shape == (num_heads,)
+    return a
+
+
 def default_threads() -> int:
     return os.cpu_count() or 1
 
@@ -113,8 +122,9 @@ class Oracle:
     # -- varlen ----------------------------------------------------------------------
     def varlen(self, k_pool, v_pool, kv_dtype, q, q_dtype, query_start_loc, seq_lens, positions,
                block_tables, scale, causal, sliding_window, row_mask=None, threads=None,
-               out=None, lse=None):
-        """Returns (status, out [T, H, dv], lse [H, T]).  Rows outside row_mask stay NaN."""
+               out=None, lse=None, sinks=None):
+        """Returns (status, out [T, H, dv], lse [H, T]).  Rows outside row_mask stay NaN.
+        sinks: [H] sink logits (float64) or None."""
         k_pool = _storage(k_pool, kv_dtype)
         v_pool = _storage(v_pool, kv_dtype)
         nb, b, hkv, dk = k_pool.shape
@@ -136,12 +146,12 @@ class Oracle:
                                  dk, dv, _ptr(q), DTYPE_CODE[q_dtype], H, ctypes.c_int64(T), _ptr(qsl), S,
                                  _ptr(sl), _ptr(pos), _ptr(bt), max_blocks, ctypes.c_double(scale),
                                  int(bool(causal)), int(sliding_window), _ptr(mask), _ptr(out), _ptr(lse),
-                                 threads or default_threads())
+                                 _ptr(_sinks(sinks, H)), threads or default_threads())
         return st, out, lse
 
     # -- decode ----------------------------------------------------------------------
     def decode(self, k_pool, v_pool, kv_dtype, q, q_dtype, block_tables, seq_lens, scale,
-               sliding_window=0, partition_size=0, max_partitions=0, threads=None, out=None):
+               sliding_window=0, partition_size=0, max_partitions=0, threads=None, out=None, sinks=None):
         """Unsplit: (status, out [S, H, dv], lse [H, S]).
         Split (partition_size > 0): (status, max_logits, exp_sums, tmp_out), entries
         past each sequence's partition count NaN."""
@@ -163,7 +173,7 @@ class Oracle:
                                      hkv, dk, dv, _ptr(q), DTYPE_CODE[q_dtype], H, _ptr(bt), max_blocks,
                                      _ptr(sl), S, ctypes.c_double(scale), int(sliding_window),
                                      int(partition_size), int(max_partitions), _ptr(out), _ptr(lse),
-                                     None, None, None, thr)
+                                     None, None, None, _ptr(_sinks(sinks, H)), thr)
             return st, out, lse
         ml = np.full((S, H, max_partitions), np.nan, dtype=np.float64)
         es = np.full((S, H, max_partitions), np.nan, dtype=np.float64)
@@ -171,10 +181,11 @@ class Oracle:
         st = self.lib.orc_decode(_ptr(k_pool), _ptr(v_pool), DTYPE_CODE[kv_dtype], ctypes.c_int64(nb), b, hkv,
                                  dk, dv, _ptr(q), DTYPE_CODE[q_dtype], H, _ptr(bt), max_blocks, _ptr(sl), S,
                                  ctypes.c_double(scale), int(sliding_window), int(partition_size),
-                                 int(max_partitions), None, None, _ptr(ml), _ptr(es), _ptr(to), thr)
+                                 int(max_partitions), None, None, _ptr(ml), _ptr(es), _ptr(to),
+                                 _ptr(_sinks(sinks, H)), thr)
         return st, ml, es, to
 
-    def reduce_partitions(self, max_logits, exp_sums, tmp_out, seq_lens, partition_size):
+    def reduce_partitions(self, max_logits, exp_sums, tmp_out, seq_lens, partition_size, sinks=None):
         ml = np.ascontiguousarray(max_logits, dtype=np.float64)
         es = np.ascontiguousarray(exp_sums, dtype=np.float64)
         to = np.ascontiguousarray(tmp_out, dtype=np.float64)
@@ -182,7 +193,7 @@ class Oracle:
         S, H, pmax, dv = to.shape
         out = np.empty((S, H, dv), dtype=np.float64)
         st = self.lib.orc_reduce_partitions(_ptr(ml), _ptr(es), _ptr(to), _ptr(sl), S, H, int(partition_size),
-                                            pmax, dv, _ptr(out))
+                                            pmax, dv, _ptr(_sinks(sinks, H)), _ptr(out))
         if st:
             raise OracleError(st, "reduce_partitions")
         return out

@@ -14,7 +14,10 @@ oracle disagrees with what the pages or the mathematics fix:
   two halves of a context gives the whole, block permutations and batching change
   no bit;
 * the rejection rules of the decode page's section 2.6 and the merge edge rules of
-  the "cpu_mla_prefill.cpp" page (MergeAttnStates).
+  the "cpu_mla_prefill.cpp" page (MergeAttnStates);
+* attention sinks as defined by ForwardWithSinks ("ManagedPagedAttention.cs"): a
+  sink equals one more visible position with a zero value (checked against the
+  sink-free path on a pool that holds such a position), plus closed forms.
 
 The same functions run against deliberately broken builds of the oracle in
 test_oracle_mutants.py, which checks that each planted mistake fails at least one.
@@ -528,11 +531,96 @@ def pin_rejections(orc):
         assert np.array_equal(kp, case.k_pool, equal_nan=True) and np.array_equal(vp, case.v_pool, equal_nan=True)
 
 
+def _sink_position_case(rng, n_list, H, scale, target):
+    """One sequence per entry of n_list, with position 0 of each holding, per head h,
+    a key whose score against that sequence's query is target + h / 2 and a zero
+    value.  Returns (case, q, z) with z[s, h] the exact score of that key."""
+    lengths = [n + 1 for n in n_list]
+    case = Case(rng, lengths, H=H, Hkv=H, dk=16, dv=16, dtype="f32", b=4)
+    q = stored(rng.standard_normal((len(lengths), H, 16)), "f32")
+    z = np.empty((len(lengths), H))
+    for s in range(len(lengths)):
+        for h in range(H):
+            qh = q[s, h].astype(np.float64)
+            k0 = ((target + 0.5 * h) / (scale * float(qh @ qh)) * qh).astype(np.float32)
+            case.k_pool[case.tables[s, 0], 0, h] = k0
+            case.v_pool[case.tables[s, 0], 0, h] = 0.0
+            z[s, h] = scale * float(qh @ k0.astype(np.float64))
+    return case, q, z
+
+
+def pin_sink_is_a_zero_value_position(orc):
+    """An attention sink ("ManagedPagedAttention.cs", ForwardWithSinks) acts as one
+    more visible position whose score is the sink logit and whose value is zero:
+    decode with sink z_h over positions 1 .. n - 1 equals decode without sinks over
+    positions 0 .. n - 1 of the same pool, position 0 holding a key that scores z_h
+    and a zero value.  Checked unsplit, split (partitions and reduction) and through
+    the varlen entry, for sinks below, among and above the scores."""
+    rng = np.random.default_rng(21)
+    H, scale = 3, 0.25
+    for target in (-6.0, 0.4, 9.0):
+        case, q, z = _sink_position_case(rng, (1, 6, 13, 30), H, scale, target)
+        for s, n in enumerate(case.lengths):
+            one = case.tables[s:s + 1]
+            ref_st, ref, rlse = orc.decode(case.k_pool, case.v_pool, "f32", q[s:s + 1], "f32", one, [n], scale)
+            st, out, lse = orc.decode(case.k_pool, case.v_pool, "f32", q[s:s + 1], "f32", one, [n], scale,
+                                      sliding_window=n - 1, sinks=z[s])
+            assert ref_st == 0 and st == 0
+            np.testing.assert_allclose(out, ref, atol=1e-12, rtol=0)
+            np.testing.assert_allclose(lse, rlse, atol=1e-12, rtol=0)
+            P = 8
+            pm = (n + P - 1) // P
+            st, ml, es, to = orc.decode(case.k_pool, case.v_pool, "f32", q[s:s + 1], "f32", one, [n], scale,
+                                        sliding_window=n - 1, partition_size=P, max_partitions=pm, sinks=z[s])
+            assert st == 0
+            plain = orc.decode(case.k_pool, case.v_pool, "f32", q[s:s + 1], "f32", one, [n], scale,
+                               sliding_window=n - 1, partition_size=P, max_partitions=pm)
+            for x, y in zip((ml, es, to), plain[1:]):  # the states leave the sink to the reduction
+                assert np.array_equal(x, y, equal_nan=True)
+            red = orc.reduce_partitions(ml, es, to, [n], P, sinks=z[s])
+            np.testing.assert_allclose(red, ref, atol=1e-12, rtol=0)
+            st, vout, vlse = orc.varlen(case.k_pool, case.v_pool, "f32", q[s:s + 1], "f32", [0, 1], [n], [n - 1],
+                                        one, scale, True, n - 1, sinks=z[s])
+            assert st == 0
+            np.testing.assert_allclose(vout, ref, atol=1e-12, rtol=0)
+            np.testing.assert_allclose(vlse, rlse, atol=1e-12, rtol=0)
+
+
+def pin_sink_closed_forms(orc):
+    """A sink equal to the only visible score halves that key's value (lse = score +
+    ln 2); with nothing visible a sink gives a zero output and lse = the sink; sinks
+    of -inf change no bit of the sink-free result."""
+    rng = np.random.default_rng(22)
+    case = Case(rng, [9, 17], H=4, Hkv=2, dk=16, dv=16, dtype="f32", b=4)
+    q = stored(rng.standard_normal((2, 4, 16)), "f32")
+    for s, n in enumerate(case.lengths):
+        z = np.array([0.25 * float(q[s, h].astype(np.float64) @ case.K[s][n - 1, h // 2].astype(np.float64))
+                      for h in range(4)])
+        st, out, lse = orc.decode(case.k_pool, case.v_pool, "f32", q[s:s + 1], "f32", case.tables[s:s + 1], [n],
+                                  0.25, sliding_window=1, sinks=z)
+        assert st == 0
+        for h in range(4):
+            np.testing.assert_allclose(out[0, h], 0.5 * case.V[s][n - 1, h // 2].astype(np.float64), atol=1e-14,
+                                       rtol=0)
+            assert abs(lse[h, 0] - (z[h] + math.log(2.0))) < 1e-13
+    z = np.array([1.5, -2.0, 0.0, 7.25])
+    qv = stored(rng.standard_normal((3, 4, 16)), "f32")
+    st, out, lse = orc.varlen(case.k_pool, case.v_pool, "f32", qv, "f32", [0, 2, 3], [0, 17], None, case.tables,
+                              0.25, False, 0, sinks=z)
+    assert st == 0
+    assert np.all(out[:2] == 0.0) and np.array_equal(lse[:, 0], z) and np.array_equal(lse[:, 1], z)
+    none = np.full(4, -np.inf)
+    for kw in ({}, {"sliding_window": 5}):
+        a = orc.decode(case.k_pool, case.v_pool, "f32", q, "f32", case.tables, case.lengths, 0.25, **kw)
+        b = orc.decode(case.k_pool, case.v_pool, "f32", q, "f32", case.tables, case.lengths, 0.25, sinks=none, **kw)
+        assert a[0] == b[0] == 0 and np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2])
+
+
 PINS = [pin_hand_example, pin_hand_example_per_block, pin_hand_example_written_through_slots,
         pin_decode_matches_dense, pin_varlen_matches_dense, pin_empty_rows, pin_decoders,
         pin_permutation_invariance, pin_closed_forms, pin_partitions_reduce_to_unsplit,
         pin_merge_halves_equal_whole, pin_merge_edge_rules, pin_invariance, pin_write_kv_round_trip,
-        pin_rejections]
+        pin_rejections, pin_sink_is_a_zero_value_position, pin_sink_closed_forms]
 
 
 def run_all(path):

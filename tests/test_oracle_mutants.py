@@ -56,6 +56,13 @@ MUTANTS = {
         "for (int d = 0; d < head_dim; ++d) o[d] = load_elem(suffix_out, dtype, row + d);\n        if (out_lse) out_lse[li] = M;"),
     "merge_pass_through_off_by_one": ("if (t >= with_prefix) {", "if (t > with_prefix) {"),
     "merge_swapped_weights": ("load_elem(prefix_out, dtype, row + d) * (pw / sum)", "load_elem(prefix_out, dtype, row + d) * (sw / sum)"),
+    # attention sinks (ForwardWithSinks)
+    "sink_left_out_of_max": ("  double m = sink;\n", "  double m = -INFINITY;\n"),
+    "sink_left_out_of_sum": ("double l = sink == -INFINITY ? 0.0 : exp(sink - m);", "double l = 0.0;"),
+    "sink_counted_per_partition": (
+        "attend(qrow, K, V, P->dk, P->dv, lo, hi, job->scale, -INFINITY, sc, orow, &m, &l);",
+        "attend(qrow, K, V, P->dk, P->dv, lo, hi, job->scale, job->sinks ? job->sinks[h] : -INFINITY, sc, orow, &m, &l);"),
+    "reduce_without_sink": ("double total = sink == -INFINITY ? 0.0 : exp(sink - M);", "double total = 0.0;"),
 }
 
 
