@@ -20,8 +20,9 @@ the one recorded there.  The cpu_baseline object times the CPU oracle on a bound
 sample of the same workload on the host cores.  --copy-calibration appends, after
 the timed region, three launches of a 1 GiB elementwise copy (torch.neg) that the
 counter runs use as the known-size reference.  --sweep (decode workloads) adds, after
-the timed region, each partition size in {0, 512, 1024} and the cost of device
-validation, each as the median of 20 calls with the caches flushed between calls.
+the timed region, each partition size in {0, 512, 1024}, the cost of device
+validation and that of per-head attention sinks, each as the median of 20 calls with
+the caches flushed between calls.
 """
 from __future__ import annotations
 
@@ -332,9 +333,9 @@ def main():
 
     ws = workspace(P)
 
-    def decode(p=P, buf=ws, status=None):
+    def decode(p=P, buf=ws, status=None, sinks=None):
         pa_decode(kp, vp, q, out, tables, lens, w.scale, sliding_window=w.sliding_window, partition_size=p,
-                  max_logits=buf[0], exp_sums=buf[1], tmp_out=buf[2], status=status)
+                  max_logits=buf[0], exp_sums=buf[1], tmp_out=buf[2], status=status, sinks=sinks)
 
     def write():
         pa_write_kv(kp, vp, k_new, v_new, slots)
@@ -381,7 +382,11 @@ def main():
         _, med_status = time_calls(lambda: decode(status=status), 20, flush=flush)
         if int(status.item()) != 0:
             raise RuntimeError(f"device validation reported status {int(status.item())}")
-        line["sweep"] = {"cold_gbs_by_partition_size": sweep, "validation_ms": round(med_status - med_plain, 5)}
+        # attention sinks (one logit per q head) on the bench's own partition size
+        sinks = torch.linspace(-2.0, 2.0, w.num_heads, device="cuda")
+        _, med_sinks = time_calls(lambda: decode(sinks=sinks), 20, flush=flush)
+        line["sweep"] = {"cold_gbs_by_partition_size": sweep, "validation_ms": round(med_status - med_plain, 5),
+                         "sinks_ms": round(med_sinks - med_plain, 5)}
     if args.copy_calibration:
         copy_calibration()
     if not args.no_cpu_baseline:

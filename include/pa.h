@@ -106,13 +106,18 @@ int pa_write_kv(const pa_kv_pool* pool, const void* k_new, const void* v_new,
  * Device checks (with status): seq_len >= 1, ceil(seq_len / block_size) <=
  * max_blocks, the first ceil(seq_len / block_size) ids in [0, num_blocks), and
  * ceil(seq_len / partition_size) <= max_partitions.
+ * sinks [num_heads] float32 (device, nullable): per-head attention-sink logits
+ * (TensorSharp page, ForwardWithSinks): head h's softmax gains one more position of
+ * score sinks[h] and value zero, which takes probability mass and adds nothing to
+ * the output; -inf means no sink.  With partitions the workspaces stay sink-free and
+ * the sink joins in the combining step.
  * Supported: head_dim_k == head_dim_v in {32, 64, 128, 256}; num_heads /
  * num_kv_heads <= 16; any block_size. */
 int pa_decode(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out, int32_t out_dtype,
               const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
               int32_t num_seqs, int32_t num_heads, float scale, int32_t sliding_window,
               int32_t partition_size, int32_t max_partitions, float* max_logits, float* exp_sums,
-              float* tmp_out, int32_t* status, void* stream);
+              float* tmp_out, const float* sinks, int32_t* status, void* stream);
 
 /* Variable-length attention over many sequences in one call (TensorSharp page,
  * Forward; "cpu_mla_prefill.cpp", MlaPrefillAttention): prefill chunks and single
@@ -128,13 +133,18 @@ int pa_decode(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
  * == num_tokens; every token count <= max_query_len; seq_len >= 0;
  * ceil(seq_len / block_size) <= max_blocks with those ids in [0, num_blocks); when
  * causal, every position in [0, seq_len).
+ * sinks [num_heads] float32 (device, nullable): per-head attention-sink logits, as
+ * for pa_decode (TensorSharp page, ForwardWithSinks).  The lse then includes the
+ * sink's mass (a row that sees nothing gets out = 0 and lse = sinks[h]); when
+ * states of several calls are merged, give the sinks to one of them only.
  * Supported: (head_dim_k, head_dim_v) in {(32,32), (64,64), (128,128), (256,256),
  * (192,128)}; num_heads / num_kv_heads <= 16; any block_size. */
 int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out, int32_t out_dtype,
               float* lse, const int32_t* query_start_loc, const int32_t* seq_lens,
               const int32_t* positions, const int32_t* block_tables, int32_t max_blocks,
               int32_t num_seqs, int64_t num_tokens, int32_t max_query_len, int32_t num_heads,
-              float scale, int32_t causal, int32_t sliding_window, int32_t* status, void* stream);
+              float scale, int32_t causal, int32_t sliding_window, const float* sinks, int32_t* status,
+              void* stream);
 
 /* Merge two attention states over disjoint key sets ("cpu_mla_prefill.cpp",
  * MergeAttnStates).  prefix_out, suffix_out, out: [num_tokens, num_heads, head_dim] in

@@ -398,11 +398,18 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
     const int h = idx / DV, d = idx - h * DV;
     // Re-express every wave's (reference max, sums) against the true max M; the
     // factors are at most 1.
+    const int hq = g * G + h;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) M = fmaxf(M, true_max[w][h]);
+    // an attention sink (unsplit calls): one more position with score z (z / scale
+    // in raw units) and a zero value; split calls leave it to the reduction
+    const float zr =
+        (a.sinks != nullptr && a.partition_size == 0) ? a.sinks[hq] * (kLog2e / a.scale_log2) : -INFINITY;
+    M = fmaxf(M, zr);
     float L = 0.f, O = 0.f;
     if (M != -INFINITY) {
+      L = __builtin_amdgcn_exp2f((zr - M) * a.scale_log2);
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         const float f = __builtin_amdgcn_exp2f((sh.r.m[w][h] - M) * a.scale_log2);
@@ -411,7 +418,6 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
       }
     }
     const float out_v = L > 0.f ? O * (1.0f / L) : 0.f;
-    const int hq = g * G + h;
     if (a.partition_size == 0) {
       store_as(a.out, a.out_dtype, (q_row * a.num_heads + hq) * (int64_t)DV + d, out_v);
       if (a.lse != nullptr && d == 0)

@@ -37,6 +37,7 @@ struct RowsArgs {
   float* max_logits;
   float* exp_sums;
   float* tmp_out;
+  const float* sinks;  // [num_heads] sink logits, nullable; unsplit outputs only
   const int32_t* status;
 };
 
@@ -90,6 +91,7 @@ struct ReduceArgs {
   int max_partitions;
   void* out;
   int out_dtype;
+  const float* sinks;  // [num_heads] sink logits, nullable
   const int32_t* status;
 };
 

@@ -63,6 +63,7 @@ struct PrefillArgs {
   float scale_log2;
   int causal;
   int window;
+  const float* sinks;  // [num_heads] sink logits, nullable
   const int32_t* status;
 };
 
@@ -637,9 +638,18 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
   // --- finish: normalise, write ---------------------------------------------------
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    const float l = l_acc[rb][0];
     if (!row_ok[rb]) continue;
-    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    // An attention sink ("ManagedPagedAttention.cs", ForwardWithSinks) is one more
+    // position with score z and a zero value: in raw score units z / scale, it joins
+    // the reference max and the exp-sum here (without one, mx = m_run, fo = 1, fz =
+    // 0 and nothing changes).
+    const float zr = a.sinks != nullptr ? a.sinks[row_head[rb]] * (kLog2e / a.scale_log2) : -INFINITY;
+    const float mx = fmaxf(m_run[rb], zr);
+    const float fo = __builtin_amdgcn_exp2f((m_run[rb] - mx) * a.scale_log2);
+    const float fz = __builtin_amdgcn_exp2f((zr - mx) * a.scale_log2);
+    const float l = fmaf(l_acc[rb][0], fo, fz);
+    m_run[rb] = mx;
+    const float inv = l > 0.f ? fo / l : 0.f;
     const int64_t obase = (row_tok[rb] * a.num_heads + row_head[rb]) * (int64_t)DV;
 #pragma unroll
     for (int nd = 0; nd < ND; ++nd) {

@@ -238,11 +238,17 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const RowsArgs a) {
   const int G = a.group;
   for (int idx = threadIdx.x; idx < G * DV; idx += blockDim.x) {
     const int h = idx / DV, d = idx - h * DV;
+    const int hq = g * G + h;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) M = fmaxf(M, red_m[w][h]);
+    // an attention sink (unsplit calls): one more position with score z (z log2(e)
+    // in these log2 units) and a zero value; split calls leave it to the reduction
+    const float zl = (a.sinks != nullptr && a.partition_size == 0) ? a.sinks[hq] * kLog2e : -INFINITY;
+    M = fmaxf(M, zl);
     float L = 0.f, O = 0.f;
     if (M != -INFINITY) {
+      L = exp2f(zl - M);
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         const float f = exp2f(red_m[w][h] - M);
@@ -251,7 +257,6 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const RowsArgs a) {
       }
     }
     const float o = L > 0.f ? O * (1.0f / L) : 0.f;
-    const int hq = g * G + h;
     if (a.partition_size == 0) {
       store_as(a.out, a.out_dtype, (q_row * a.num_heads + hq) * (int64_t)DV + d, o);
       if (a.lse != nullptr && d == 0)
