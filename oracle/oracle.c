@@ -24,6 +24,8 @@
  *   - "cpu_mla_prefill.cpp", MlaPrefillAttention: the two-pass softmax (max, then
  *     exp-sum and weighted sum), zero output and lse = -inf for an empty row, lse
  *     in natural log.  MergeAttnStates: the merge and its two edge cases.
+ *     GatherMlaCache: the gather of a paged latent cache into contiguous rows.
+ *   - "ManagedPagedAttention.cs", ForwardWithSinks: attention sinks.
  *
  * Arithmetic: every stored element is decoded exactly to binary32 and then widened
  * to binary64; every sum, exp and log is binary64.  Work is split over (sequence,
@@ -576,6 +578,98 @@ int orc_merge_states(const void* prefix_out, const float* prefix_lse, const void
         o[d] = load_elem(prefix_out, dtype, row + d) * (pw / sum) +
                load_elem(suffix_out, dtype, row + d) * (sw / sum);
       if (out_lse) out_lse[li] = log(sum) + M;
+    }
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Element encoding (round to nearest, ties to even)                          */
+/* ------------------------------------------------------------------------- */
+
+/* binary64 -> binary16.  Magnitudes from 65520 (half an ulp above 65504) round to
+ * infinity; below 2^-14 the result is a multiple of 2^-24 (subnormal or zero). */
+static uint16_t double_to_half(double x) {
+  uint16_t sign = signbit(x) ? 0x8000 : 0;
+  double a = fabs(x);
+  if (isnan(x)) return (uint16_t)(sign | 0x7e00);
+  if (a >= 65520.0) return (uint16_t)(sign | 0x7c00);
+  if (a < ldexp(1.0, -14)) return (uint16_t)(sign | (uint16_t)nearbyint(ldexp(a, 24)));
+  int e;
+  double m = frexp(a, &e);         /* a = m * 2^e, m in [0.5, 1) */
+  double r = nearbyint(ldexp(m, 11)); /* the 11 significant bits, in [1024, 2048] */
+  int biased = e + 14;             /* a = (r / 1024) * 2^(biased - 15) */
+  if (r == 2048.0) {
+    r = 1024.0;
+    biased += 1;
+  }
+  if (biased >= 31) return (uint16_t)(sign | 0x7c00);
+  return (uint16_t)(sign | (biased << 10) | ((int)r - 1024));
+}
+
+/* binary64 holding a binary32 value exactly -> bfloat16 (the high half of the
+ * binary32 word, rounded on the low half).  NaN stays a quiet NaN. */
+static uint16_t double_to_bf16(double x) {
+  float f = (float)x;
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  if (isnan(f)) return (uint16_t)((u >> 16) | 0x0040);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+static void store_elem(void* base, int dtype, int64_t i, double x) {
+  if (dtype == ORC_F32)
+    ((float*)base)[i] = (float)x;
+  else if (dtype == ORC_F16)
+    ((uint16_t*)base)[i] = double_to_half(x);
+  else
+    ((uint16_t*)base)[i] = double_to_bf16(x);
+}
+
+/* Encode n binary64 values (each a binary32 value) to storage (exposed so the
+ * encoders can be pinned). */
+int orc_encode_elems(const double* src, int dtype, int64_t n, void* out) {
+  if (elem_bytes(dtype) == 0) return ORC_EUNSUPPORTED;
+  for (int64_t i = 0; i < n; ++i) store_elem(out, dtype, i, src[i]);
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Gather of a paged latent cache into contiguous rows                         */
+/* ------------------------------------------------------------------------- */
+
+/* "cpu_mla_prefill.cpp", GatherMlaCache.  Output row t belongs to sequence
+ * b = token_to_seq[t]; it is skipped (left untouched) when t >= cu_seq_lens[b + 1].
+ * Otherwise its position in the sequence is t - cu_seq_lens[b], plus seq_starts[b]
+ * when seq_starts is given, and it receives the cache row at slot position % b of
+ * block block_table[b][position / block_size], converted to the output dtype.  The
+ * cache row of (block, slot) starts at element block * src_block_stride + slot *
+ * src_slot_stride; output row t at element t * dst_row_stride.  Every row that is
+ * copied is checked before anything is written: b in [0, num_seqs), a position >= 0,
+ * its block index below max_blocks and the block id in [0, num_blocks). */
+int orc_gather_cache(const void* src, int src_dtype, int64_t num_blocks, int block_size, int head_dim,
+                     int64_t src_block_stride, int64_t src_slot_stride, void* dst, int dst_dtype,
+                     int64_t dst_row_stride, const int32_t* block_table, int max_blocks,
+                     const int32_t* cu_seq_lens, const int32_t* token_to_seq, const int32_t* seq_starts,
+                     int num_seqs, int64_t num_tokens) {
+  if (elem_bytes(src_dtype) == 0 || elem_bytes(dst_dtype) == 0) return ORC_EUNSUPPORTED;
+  if (num_blocks < 1 || block_size < 1 || head_dim < 1 || num_seqs < 0 || num_tokens < 0 || max_blocks < 1)
+    return ORC_EINVAL;
+  for (int pass = 0; pass < 2; ++pass) { /* pass 0 checks, pass 1 copies */
+    for (int64_t t = 0; t < num_tokens; ++t) {
+      int64_t b = token_to_seq[t];
+      if (b < 0 || b >= num_seqs) return ORC_EINVAL;
+      if (t >= cu_seq_lens[b + 1]) continue;
+      int64_t pos = t - cu_seq_lens[b] + (seq_starts ? seq_starts[b] : 0);
+      if (pos < 0) return ORC_EINVAL;
+      int64_t idx = pos / block_size, slot = pos % block_size;
+      if (idx >= max_blocks) return ORC_EINVAL;
+      int64_t block = block_table[b * max_blocks + idx];
+      if (block < 0 || block >= num_blocks) return ORC_EINVAL;
+      if (pass == 0) continue;
+      int64_t from = block * src_block_stride + slot * src_slot_stride, to = t * dst_row_stride;
+      for (int d = 0; d < head_dim; ++d) store_elem(dst, dst_dtype, to + d, load_elem(src, src_dtype, from + d));
     }
   }
   return ORC_OK;

@@ -75,7 +75,8 @@ class Oracle:
         self.path = path
         self.lib = ctypes.CDLL(path)
         for name in ("orc_decode_elems", "orc_gather", "orc_attend_gathered", "orc_varlen",
-                     "orc_decode", "orc_reduce_partitions", "orc_merge_states", "orc_write_kv"):
+                     "orc_decode", "orc_reduce_partitions", "orc_merge_states", "orc_write_kv",
+                     "orc_encode_elems", "orc_gather_cache"):
             getattr(self.lib, name).restype = ctypes.c_int
 
     # -- element decoding ------------------------------------------------------------
@@ -214,6 +215,36 @@ class Oracle:
         if st:
             raise OracleError(st, "merge_states")
         return out, out_lse
+
+    # -- latent-cache gather -----------------------------------------------------------
+    def encode_elems(self, values, dtype):
+        """float64 values (each a binary32 value) -> storage array of `dtype`."""
+        v = np.ascontiguousarray(values, dtype=np.float64)
+        out = np.empty(v.shape, dtype=NUMPY_STORAGE[dtype])
+        st = self.lib.orc_encode_elems(_ptr(v), DTYPE_CODE[dtype], ctypes.c_int64(v.size), _ptr(out))
+        if st:
+            raise OracleError(st, "encode_elems")
+        return out
+
+    def gather_cache(self, cache, src_dtype, block_table, cu_seq_lens, token_to_seq, seq_starts, dst_dtype,
+                     num_tokens, dst=None):
+        """Gather rows of a paged cache [num_blocks, block_size, head_dim] into dst
+        [num_tokens, head_dim] of dst_dtype (rows that are skipped keep dst's
+        contents; a NaN-filled dst by default).  Returns (status, dst)."""
+        c = _storage(cache, src_dtype)
+        nb, b, D = c.shape
+        bt = _i32(block_table)
+        cu = _i32(cu_seq_lens)
+        t2s = _i32(token_to_seq)
+        starts = None if seq_starts is None else _i32(seq_starts)
+        if dst is None:
+            nan = {"f32": np.float32(np.nan), "f16": np.float16(np.nan), "bf16": np.uint16(0x7FC0)}[dst_dtype]
+            dst = np.full((num_tokens, D), nan, dtype=NUMPY_STORAGE[dst_dtype])
+        st = self.lib.orc_gather_cache(_ptr(c), DTYPE_CODE[src_dtype], ctypes.c_int64(nb), b, D,
+                                       ctypes.c_int64(b * D), ctypes.c_int64(D), _ptr(dst), DTYPE_CODE[dst_dtype],
+                                       ctypes.c_int64(D), _ptr(bt), bt.shape[1], _ptr(cu), _ptr(t2s),
+                                       _ptr(starts), cu.size - 1, ctypes.c_int64(num_tokens))
+        return st, dst
 
     # -- KV write --------------------------------------------------------------------
     def write_kv(self, k_pool, v_pool, dtype, k_new, v_new, slot_mapping):

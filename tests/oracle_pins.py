@@ -17,7 +17,10 @@ oracle disagrees with what the pages or the mathematics fix:
   the "cpu_mla_prefill.cpp" page (MergeAttnStates);
 * attention sinks as defined by ForwardWithSinks ("ManagedPagedAttention.cs"): a
   sink equals one more visible position with a zero value (checked against the
-  sink-free path on a pool that holds such a position), plus closed forms.
+  sink-free path on a pool that holds such a position), plus closed forms;
+* the latent-cache gather (GatherMlaCache) returns the logical rows a cache was
+  scattered from, and its rounding to binary16 / bfloat16 gives numpy's and torch's
+  bits.
 
 The same functions run against deliberately broken builds of the oracle in
 test_oracle_mutants.py, which checks that each planted mistake fails at least one.
@@ -616,11 +619,111 @@ def pin_sink_closed_forms(orc):
         assert a[0] == b[0] == 0 and np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2])
 
 
+def _same_bits(a, b):
+    """Bitwise equality of two storage arrays of one type (float32, float16, or bf16
+    as uint16), any NaN equal to any NaN."""
+    a, b = np.asarray(a), np.asarray(b)
+    if a.dtype != b.dtype or a.shape != b.shape:
+        return False
+    if a.dtype == np.uint16:  # bf16 bits
+        an = ((a & 0x7F80) == 0x7F80) & ((a & 0x007F) != 0)
+        bn = ((b & 0x7F80) == 0x7F80) & ((b & 0x007F) != 0)
+        ua, ub = a, b
+    else:
+        an, bn = np.isnan(a), np.isnan(b)
+        ua = a.view(np.uint32 if a.dtype == np.float32 else np.uint16)
+        ub = b.view(ua.dtype)
+    return np.array_equal(an, bn) and np.array_equal(ua[~an], ub[~bn])
+
+
+def pin_encoders(orc):
+    """Rounding to binary16 and bfloat16 (nearest, ties to even) gives the bits
+    numpy's float16 and torch's bfloat16 conversions give: every bf16 and f16 value,
+    binary32 edge values and a million random binary32 bit patterns."""
+    rng = np.random.default_rng(31)
+    pats = [np.arange(1 << 16, dtype=np.uint32) << 16,  # every bf16 value as binary32
+            np.arange(1 << 16, dtype=np.uint16).view(np.float16).astype(np.float32).view(np.uint32),
+            rng.integers(0, 1 << 32, size=1 << 20, dtype=np.uint64).astype(np.uint32),
+            np.array([0x477FEFFF, 0x477FF000, 0x477FF001, 0x387FC000, 0x33000000, 0x33000001, 0x7F7FFFFF,
+                      0x7F7F8000, 0x7F7F7FFF, 0x80000000, 0x00000001], dtype=np.uint32)]
+    f32 = np.concatenate(pats).view(np.float32)
+    with np.errstate(invalid="ignore", over="ignore"):
+        vals = f32.astype(np.float64)
+        f16 = f32.astype(np.float16)
+    assert _same_bits(orc.encode_elems(vals, "f16"), f16)
+    ref = torch.from_numpy(f32.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert _same_bits(orc.encode_elems(vals, "bf16"), ref)
+    assert _same_bits(orc.encode_elems(vals, "f32"), f32)
+
+
+def _gather_case(rng, lengths, D, dtype, b):
+    """A Case with one kv head (its pool is a [blocks, b, D] latent cache)."""
+    case = Case(rng, lengths, H=1, Hkv=1, dk=D, dv=D, dtype=dtype, b=b)
+    return case, case.k_pool.reshape(case.num_blocks, b, D)
+
+
+def pin_gather_returns_logical_rows(orc):
+    """GatherMlaCache ("cpu_mla_prefill.cpp") on a cache scattered from logical
+    per-sequence rows returns those rows: whole sequences, windows starting at
+    seq_starts, rows past a sequence's end left untouched, and a conversion to
+    another dtype equal to the library conversion of the logical rows."""
+    rng = np.random.default_rng(33)
+    for dtype, b in (("bf16", 16), ("f32", 4), ("f16", 8)):
+        case, cache = _gather_case(rng, [37, 5, 60, 16], 24, dtype, b)
+        logical = [k.reshape(len(k), 24) for k in case.K]
+        # whole sequences, packed
+        lens = np.array(case.lengths)
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        t2s = np.repeat(np.arange(len(lens)), lens).astype(np.int32)
+        st, out = orc.gather_cache(cache, dtype, case.tables, cu, t2s, None, dtype, int(cu[-1]))
+        assert st == 0 and _same_bits(out, np.concatenate(logical))
+        # windows: sequence s contributes take[s] rows from starts[s]; two spare rows
+        # past the last sequence's end must stay untouched
+        starts = np.array([3, 0, 41, 15], dtype=np.int32)
+        take = np.array([20, 5, 19, 1], dtype=np.int32)
+        cu = np.concatenate([[0], np.cumsum(take)]).astype(np.int32)
+        T = int(cu[-1]) + 2
+        t2s = np.concatenate([np.repeat(np.arange(4), take), [3, 3]]).astype(np.int32)
+        sentinel = stored(np.full((T, 24), 7.0), dtype)
+        st, out = orc.gather_cache(cache, dtype, case.tables, cu, t2s, starts, dtype, T, dst=sentinel.copy())
+        want = np.concatenate([logical[s][starts[s]:starts[s] + take[s]] for s in range(4)])
+        assert st == 0 and _same_bits(out[:-2], want)
+        assert _same_bits(out[-2:], sentinel[-2:])
+        # to another dtype
+        other = {"bf16": "f32", "f32": "bf16", "f16": "bf16"}[dtype]
+        st, out = orc.gather_cache(cache, dtype, case.tables, cu, t2s, starts, other, T)
+        w64 = widen(want, dtype)
+        assert st == 0 and _same_bits(out[:-2], stored(w64, other))
+
+
+def pin_gather_rejections(orc):
+    """A sequence index outside [0, num_seqs), a negative position, a block index past
+    the table row or a block id outside the cache is refused before any write."""
+    rng = np.random.default_rng(34)
+    case, cache = _gather_case(rng, [10, 7], 8, "f32", 4)
+    cu = np.array([0, 10, 17], np.int32)
+    t2s = np.repeat(np.arange(2), [10, 7]).astype(np.int32)
+    st, _ = orc.gather_cache(cache, "f32", case.tables, cu, t2s, None, "f32", 17)
+    assert st == 0
+    bad_t2s = t2s.copy()
+    bad_t2s[4] = 2
+    bad_tab = case.tables.copy()
+    bad_tab[1, 0] = case.num_blocks
+    cases = [dict(t2s=bad_t2s), dict(starts=np.array([0, -1], np.int32)),
+             dict(starts=np.array([0, 4 * case.max_blocks], np.int32)), dict(tables=bad_tab)]
+    for kw in cases:
+        dst = np.full((17, 8), 5.0, np.float32)
+        st, out = orc.gather_cache(cache, "f32", kw.get("tables", case.tables), cu, kw.get("t2s", t2s),
+                                   kw.get("starts"), "f32", 17, dst=dst)
+        assert st == EINVAL and np.all(out == 5.0), kw
+
+
 PINS = [pin_hand_example, pin_hand_example_per_block, pin_hand_example_written_through_slots,
         pin_decode_matches_dense, pin_varlen_matches_dense, pin_empty_rows, pin_decoders,
         pin_permutation_invariance, pin_closed_forms, pin_partitions_reduce_to_unsplit,
         pin_merge_halves_equal_whole, pin_merge_edge_rules, pin_invariance, pin_write_kv_round_trip,
-        pin_rejections, pin_sink_is_a_zero_value_position, pin_sink_closed_forms]
+        pin_rejections, pin_sink_is_a_zero_value_position, pin_sink_closed_forms, pin_encoders,
+        pin_gather_returns_logical_rows, pin_gather_rejections]
 
 
 def run_all(path):

@@ -63,6 +63,17 @@ MUTANTS = {
         "attend(qrow, K, V, P->dk, P->dv, lo, hi, job->scale, -INFINITY, sc, orow, &m, &l);",
         "attend(qrow, K, V, P->dk, P->dv, lo, hi, job->scale, job->sinks ? job->sinks[h] : -INFINITY, sc, orow, &m, &l);"),
     "reduce_without_sink": ("double total = sink == -INFINITY ? 0.0 : exp(sink - M);", "double total = 0.0;"),
+    # encoders and the latent-cache gather (GatherMlaCache)
+    "half_rounds_toward_zero": ("double r = nearbyint(ldexp(m, 11));", "double r = trunc(ldexp(m, 11));"),
+    "half_subnormal_truncates": ("(uint16_t)nearbyint(ldexp(a, 24))", "(uint16_t)trunc(ldexp(a, 24))"),
+    "bf16_truncates": ("u += 0x7fffu + ((u >> 16) & 1u);", ""),
+    "bf16_ties_away": ("u += 0x7fffu + ((u >> 16) & 1u);", "u += 0x8000u;"),
+    "gather_ignores_seq_starts": ("int64_t pos = t - cu_seq_lens[b] + (seq_starts ? seq_starts[b] : 0);",
+                                  "int64_t pos = t - cu_seq_lens[b];"),
+    "gather_slot_is_block_index": ("int64_t idx = pos / block_size, slot = pos % block_size;",
+                                   "int64_t idx = pos / block_size, slot = idx % block_size;"),
+    "gather_copies_rows_past_end": ("if (t >= cu_seq_lens[b + 1]) continue;", ""),
+    "gather_trusts_block_ids": ("if (block < 0 || block >= num_blocks) return ORC_EINVAL;", ""),
 }
 
 
