@@ -7,7 +7,7 @@ sharing a 256-token prefix).  One step = pa_write_kv of the 64 new tokens + pa_d
 sum over sequences and kv heads of the visible positions times
 (head_dim_k + head_dim_v) * 2 bytes, divided by the wall time of a step.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|long|varlen|mla]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|long|varlen|mla|gather]
                     [--partition-size P] [--no-cpu-baseline] [--copy-calibration] [--sweep]
 
 Prints one JSON line.  The roofline object divides the same algorithmic bytes (or
@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=["decode", "long", "varlen", "mla"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "long", "varlen", "mla", "gather"])
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
@@ -299,6 +299,41 @@ def run_prefill(args):
     print(json.dumps(line), flush=True)
 
 
+def run_gather(args):
+    """Secondary workload: the latent-cache gather (pa_gather_cache) of every context
+    row of the MLA-style requests, 576-wide bf16 rows from a permuted block pool.
+    One step = one gather call; GB/s counts the rows read and written once."""
+    import torch
+
+    from paged_kv_attention_table_amd import pa_gather_cache
+    from paged_kv_attention_table_amd import workloads as W
+
+    g = W.latent_gather()
+    cache = dev(g.cache, g.dtype)
+    tables, cu, t2s = dev(g.block_tables), dev(g.cu_seq_lens), dev(g.token_to_seq)
+    T, D = int(g.cu_seq_lens[-1]), g.cache.shape[2]
+    dst = torch.empty((T, D), dtype=torch.bfloat16, device="cuda")
+
+    def call():
+        pa_gather_cache(cache, dst, tables, cu, t2s)
+
+    for _ in range(args.warmup):
+        call()
+    ms, avg_ms, med_ms = timed_loop(args.steps, lambda: None, call)
+    nbytes = T * D * 2 * 2
+    value = nbytes / (ms * 1e-3) / 1e9
+    achieved = nbytes / (avg_ms * 1e-3) / 1e9
+    line = {"metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": g.dtype, "data": "synthetic",
+            "config": {"workload": g.name, "requests": int(g.ctx_lens.size), "rows": T, "head_dim": D,
+                       "block_size": int(g.cache.shape[1]), "step": "pa_gather_cache"},
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                         "kernel": "gather_cache_kernel", "avg_ms": round(avg_ms, 5), "median_ms": round(med_ms, 5)}}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -311,6 +346,8 @@ def main():
 
     if args.workload in ("varlen", "mla"):
         return run_prefill(args)
+    if args.workload == "gather":
+        return run_gather(args)
     w = W.config2() if args.workload == "decode" else W.config3()
     if args.partition_size is not None:
         P = args.partition_size

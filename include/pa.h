@@ -159,6 +159,28 @@ int pa_merge_states(void* out, float* out_lse, const void* prefix_out, const flo
                     int32_t num_heads, int32_t head_dim, int64_t prefill_tokens_with_context,
                     int32_t dtype, void* stream);
 
+/* Gather of a paged latent cache into contiguous rows ("cpu_mla_prefill.cpp",
+ * GatherMlaCache): the step that lays out a context chunk of an MLA latent cache
+ * before chunked prefill.  cache: num_blocks x block_size rows of head_dim elements
+ * in cache_dtype, row (block, slot) at element block * cache_block_stride + slot *
+ * cache_slot_stride.  dst: num_tokens rows of head_dim elements in dst_dtype, row t
+ * at element t * dst_row_stride (>= head_dim).  Row t belongs to sequence
+ * b = token_to_seq[t]; it is left untouched when t >= cu_seq_lens[b + 1]; otherwise
+ * its position is t - cu_seq_lens[b], plus seq_starts[b] when seq_starts is
+ * non-NULL, and it receives the cache row at slot position % block_size of block
+ * block_table[b][position / block_size], rounded to nearest even when the dtypes
+ * differ.  block_table [num_seqs, max_blocks], cu_seq_lens [num_seqs + 1],
+ * token_to_seq [num_tokens], seq_starts [num_seqs] (nullable): device int32.
+ * Device checks (with status): b in [0, num_seqs), position >= 0, position /
+ * block_size < max_blocks, block id in [0, num_blocks); without a status word such
+ * rows are skipped.  Supported: F32 / F16 / BF16 on either side. */
+int pa_gather_cache(const void* cache, int32_t cache_dtype, int64_t num_blocks, int32_t block_size,
+                    int32_t head_dim, int64_t cache_block_stride, int64_t cache_slot_stride, void* dst,
+                    int32_t dst_dtype, int64_t dst_row_stride, const int32_t* block_table,
+                    int32_t max_blocks, const int32_t* cu_seq_lens, const int32_t* token_to_seq,
+                    const int32_t* seq_starts, int32_t num_seqs, int64_t num_tokens, int32_t* status,
+                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,4 +1,4 @@
-"""ctypes binding of libpa.so: the four entry points of include/pa.h under the same
+"""ctypes binding of libpa.so: the entry points of include/pa.h under the same
 names, taking torch tensors that live on the GPU.
 
 The binding only marshals arguments (device pointers, sizes, dtype codes, the
@@ -21,7 +21,7 @@ PA_OK, PA_EINVAL, PA_ESHAPE, PA_EUNSUPPORTED, PA_EDEVICE = 0, 1, 2, 3, 4
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 DTYPE_CODE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 
-EXPORTS = ("pa_strerror", "pa_write_kv", "pa_decode", "pa_varlen", "pa_merge_states")
+EXPORTS = ("pa_strerror", "pa_write_kv", "pa_decode", "pa_varlen", "pa_merge_states", "pa_gather_cache")
 
 
 class PaKvPool(ctypes.Structure):
@@ -61,6 +61,9 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
                               vp, vp, vp]
     lib.pa_merge_states.restype = ctypes.c_int
     lib.pa_merge_states.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i64, i32, vp]
+    lib.pa_gather_cache.restype = ctypes.c_int
+    lib.pa_gather_cache.argtypes = [vp, i32, i64, i32, i32, i64, i64, vp, i32, i64, vp, i32, vp, vp, vp, i32, i64,
+                                    vp, vp]
     _lib = lib
     return lib
 
@@ -222,3 +225,29 @@ def pa_merge_states(out, out_lse, prefix_out, prefix_lse, suffix_out, suffix_lse
                                 _ptr(suffix_lse), T, H, D, int(prefill_tokens_with_context), DTYPE_CODE[out.dtype],
                                 _stream(stream))
     _check(st, "pa_merge_states")
+
+
+def pa_gather_cache(cache, dst, block_table, cu_seq_lens, token_to_seq, seq_starts=None, status=None, stream=None):
+    """Gather rows of a paged cache [num_blocks, block_size, head_dim] (or any view
+    whose last dim is contiguous) into dst [num_tokens, head_dim] (rows may be
+    strided; dtype may differ)."""
+    _dev(cache, "cache", ndim=3)
+    _dev(block_table, "block_table", dtype=torch.int32, ndim=2)
+    _dev(cu_seq_lens, "cu_seq_lens", dtype=torch.int32, ndim=1)
+    _dev(token_to_seq, "token_to_seq", dtype=torch.int32, ndim=1)
+    _dev(seq_starts, "seq_starts", dtype=torch.int32, ndim=1)
+    _dev(status, "status", dtype=torch.int32)
+    if not isinstance(dst, torch.Tensor) or dst.device.type != "cuda" or dst.dim() != 2 or dst.stride(1) != 1:
+        raise ValueError("dst must be a 2-d GPU tensor with contiguous rows")
+    nb, b, D = cache.shape
+    T = token_to_seq.numel()
+    S = cu_seq_lens.numel() - 1
+    _shape(dst, (T, D), "dst")
+    if block_table.shape[0] != S:
+        raise ValueError("block_table must have one row per sequence")
+    _shape(seq_starts, (S,), "seq_starts")
+    st = load().pa_gather_cache(_ptr(cache), DTYPE_CODE[cache.dtype], nb, b, D, b * D, D, dst.data_ptr(),
+                                DTYPE_CODE[dst.dtype], dst.stride(0), _ptr(block_table), block_table.shape[1],
+                                _ptr(cu_seq_lens), _ptr(token_to_seq), _ptr(seq_starts), S, T, _ptr(status),
+                                _stream(stream))
+    _check(st, "pa_gather_cache")

@@ -386,4 +386,46 @@ int pa_merge_states(void* out, float* out_lse, const void* prefix_out, const flo
   return from_hip(launch_merge(a, static_cast<hipStream_t>(stream)));
 }
 
+int pa_gather_cache(const void* cache, int32_t cache_dtype, int64_t num_blocks, int32_t block_size, int32_t head_dim,
+                    int64_t cache_block_stride, int64_t cache_slot_stride, void* dst, int32_t dst_dtype,
+                    int64_t dst_row_stride, const int32_t* block_table, int32_t max_blocks, const int32_t* cu_seq_lens,
+                    const int32_t* token_to_seq, const int32_t* seq_starts, int32_t num_seqs, int64_t num_tokens,
+                    int32_t* status, void* stream) {
+  const int cb = element_bytes(cache_dtype), db = element_bytes(dst_dtype);
+  if (cb == 0 || db == 0) return PA_EUNSUPPORTED;
+  if (num_tokens < 0 || num_blocks < 1 || block_size < 1 || head_dim < 1 || max_blocks < 1 || num_seqs < 0)
+    return PA_EINVAL;
+  if (cache_slot_stride < head_dim || cache_block_stride < 1 || dst_row_stride < head_dim) return PA_EINVAL;
+  if (num_tokens > 0 && (cache == nullptr || dst == nullptr || block_table == nullptr || cu_seq_lens == nullptr ||
+                         token_to_seq == nullptr || num_seqs < 1))
+    return PA_EINVAL;
+  if (num_tokens > 0x7fffffffLL) return PA_EUNSUPPORTED;
+  GatherArgs g = {};
+  g.cache = cache;
+  g.cache_dtype = cache_dtype;
+  g.num_blocks = num_blocks;
+  g.block_size = block_size;
+  g.head_dim = head_dim;
+  g.block_stride = cache_block_stride;
+  g.slot_stride = cache_slot_stride;
+  g.dst = dst;
+  g.dst_dtype = dst_dtype;
+  g.dst_stride = dst_row_stride;
+  g.block_table = block_table;
+  g.max_blocks = max_blocks;
+  g.cu_seq_lens = cu_seq_lens;
+  g.token_to_seq = token_to_seq;
+  g.seq_starts = seq_starts;
+  g.num_seqs = num_seqs;
+  g.num_tokens = num_tokens;
+  g.status = status;
+  // 16-byte copies when nothing is converted and every row starts 16-byte aligned
+  const bool aligned = ((uintptr_t)cache % 16 == 0) && ((uintptr_t)dst % 16 == 0) &&
+                       ((int64_t)head_dim * cb) % 16 == 0 && (cache_block_stride * cb) % 16 == 0 &&
+                       (cache_slot_stride * cb) % 16 == 0 && (dst_row_stride * db) % 16 == 0;
+  g.vec16 = cache_dtype == dst_dtype && aligned;
+  g.units_per_row = g.vec16 ? head_dim * cb / 16 : head_dim;
+  return from_hip(launch_gather(g, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -60,6 +60,31 @@ struct ValidateArgs {
   int causal;
   int32_t* status;
 };
+// Latent-cache gather ("cpu_mla_prefill.cpp", GatherMlaCache).
+struct GatherArgs {
+  const void* cache;
+  int cache_dtype;
+  int64_t num_blocks;
+  int block_size;
+  int head_dim;
+  int64_t block_stride;  // elements
+  int64_t slot_stride;   // elements
+  void* dst;
+  int dst_dtype;
+  int64_t dst_stride;  // elements per output row
+  const int32_t* block_table;
+  int max_blocks;
+  const int32_t* cu_seq_lens;
+  const int32_t* token_to_seq;
+  const int32_t* seq_starts;  // nullable
+  int num_seqs;
+  int64_t num_tokens;
+  int vec16;           // same dtype, rows and bases 16-byte aligned: 16-byte copies
+  int units_per_row;   // 16-byte chunks (vec16) or elements per row
+  int32_t* status;     // nullable
+};
+hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
+
 constexpr int kValidateWrite = 0;
 constexpr int kValidateDecode = 1;
 constexpr int kValidateVarlen = 2;

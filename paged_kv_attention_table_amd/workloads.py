@@ -374,6 +374,48 @@ def config5(small=False, permuted=False):
                                 num_heads=H, dk=192, dv=128, chunk=chunk, permuted=permuted)
 
 
+@dataclass
+class LatentGather:
+    """A paged latent cache and the index arrays of one gather of every context row."""
+    name: str
+    dtype: str
+    cache: np.ndarray         # [num_blocks, block_size, head_dim] storage
+    block_tables: np.ndarray  # [R, max_blocks] int32, seeded permutation of block ids
+    ctx_lens: np.ndarray      # [R]
+    cu_seq_lens: np.ndarray   # [R + 1]
+    token_to_seq: np.ndarray  # [T]
+    seed: int
+
+
+def latent_gather(small=False):
+    """The context of the MLA-style chunked-prefill requests (the same seeded lengths,
+    uniform in [0, 16384]) as a paged latent cache of 576-wide bf16 rows (a 512-wide
+    compressed KV row plus a 64-wide rotary key), block size 16, block ids a seeded
+    permutation; the gather reads every context row of every request once."""
+    seed = 1005
+    rng = np.random.default_rng(seed + 10_000)
+    R, clo, chi = (3, 0, 700) if small else (8, 0, 16384)
+    rng.integers(20 if small else 256, 150 if small else 1024, size=R, endpoint=True)  # new tokens (unused)
+    ctx = rng.integers(clo, chi, size=R, endpoint=True).astype(np.int64)
+    if small:
+        ctx[0] = 0
+    b, D = 16, 576
+    need = [(int(n) + b - 1) // b for n in ctx]
+    nb = max(1, sum(need)) + 1
+    grng = np.random.default_rng(seed + 20_000)
+    ids = grng.permutation(nb).astype(np.int32)
+    tables = np.full((R, max(1, max(need))), ids[-1], dtype=np.int32)
+    cur = 0
+    for r, k in enumerate(need):
+        tables[r, :k] = ids[cur:cur + k]
+        cur += k
+    cache = normal(seed, 50, (nb, b, D), "bf16")
+    cu = np.concatenate([[0], np.cumsum(ctx)]).astype(np.int32)
+    t2s = np.repeat(np.arange(R), ctx).astype(np.int32)
+    return LatentGather("mla-latent-gather" + ("-small" if small else ""), "bf16", cache, tables,
+                        ctx.astype(np.int32), cu, t2s, seed)
+
+
 def chunk_tables(cp: ChunkedPrefill, c: int):
     """Per-request (seq_lens, block table slice) of context chunk c."""
     per = cp.chunk // cp.block_size

@@ -17,9 +17,9 @@ def declared_functions():
     return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(pa_\w+)\s*\(", text, flags=re.M)))
 
 
-def test_header_declares_the_four_calls():
+def test_header_declares_the_calls():
     names = declared_functions()
-    for n in ("pa_write_kv", "pa_decode", "pa_varlen", "pa_merge_states", "pa_strerror"):
+    for n in ("pa_write_kv", "pa_decode", "pa_varlen", "pa_merge_states", "pa_gather_cache", "pa_strerror"):
         assert n in names, names
 
 
@@ -117,6 +117,28 @@ def test_write_and_merge_host_checks():
     assert lib.pa_merge_states(FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 0, 8, -1, 0, None) == binding.PA_EINVAL
     assert lib.pa_merge_states(FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 2, 8, -1, 9, None) == binding.PA_EUNSUPPORTED
     assert lib.pa_merge_states(FAKE, None, None, FAKE, FAKE, FAKE, 4, 2, 8, -1, 0, None) == binding.PA_EINVAL
+
+
+def test_gather_host_checks():
+    lib = binding.load()
+    ok = (FAKE, binding.PA_BF16, 8, 16, 64, 16 * 64, 64, FAKE, binding.PA_BF16, 64, FAKE, 4, FAKE, FAKE, None, 2, 10,
+          None, None)
+
+    def call(change):
+        a = list(ok)
+        for k, v in change.items():
+            a[k] = v
+        return lib.pa_gather_cache(*a)
+
+    assert call({1: 7}) == binding.PA_EUNSUPPORTED      # cache dtype
+    assert call({8: 9}) == binding.PA_EUNSUPPORTED      # dst dtype
+    assert call({16: -1}) == binding.PA_EINVAL          # negative token count
+    assert call({2: 0}) == binding.PA_EINVAL            # no blocks
+    assert call({6: 63}) == binding.PA_EINVAL           # slot stride below the row
+    assert call({9: 32}) == binding.PA_EINVAL           # output rows overlap
+    assert call({0: None}) == binding.PA_EINVAL         # no cache
+    assert call({13: None}) == binding.PA_EINVAL        # no token_to_seq
+    assert call({15: 0}) == binding.PA_EINVAL           # tokens but no sequences
 
 
 def test_binding_refuses_host_tensors():
