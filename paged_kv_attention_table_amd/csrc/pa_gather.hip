@@ -5,12 +5,12 @@
 // slot position % block_size of block block_table[b][position / block_size],
 // converted to the output dtype.
 //
-// Mapping onto gfx950: the copy is a stream of (row, unit) pairs, one per thread,
-// so consecutive lanes read and write consecutive 16-byte chunks of a row (same
-// dtype, aligned rows) or consecutive elements (conversions, other layouts).  The
-// row's source offset comes from four dependent index loads that all lanes of the
-// row share (broadcast from the caches).  With a status word, one workgroup checks
-// every row first and the copy kernel exits before writing when it fails.
+// Mapping onto gfx950: same dtype and 16-byte aligned rows -- a wave looks up the
+// sources of 8 rows at once (one lane each) and its 64 lanes stream the rows'
+// 16-byte chunks, consecutive lanes on consecutive chunks.  Conversions and other
+// layouts: one thread per (row, element), consecutive lanes on consecutive elements.
+// With a status word, one workgroup checks every row first and the copy kernels
+// exit before writing when it fails.
 #include "pa_common.h"
 #include "pa_internal.h"
 
@@ -70,13 +70,36 @@ __global__ __launch_bounds__(256) void gather_cache_kernel(const GatherArgs a) {
   if (row >= a.num_tokens) return;
   int64_t src;
   if (gather_row(a, row, &src) != kGatherCopy) return;  // skipped, or refused without a status word
-  if (a.vec16) {
-    constexpr int EB = S::bytes;
-    const u32x4* from = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.cache) + src * EB) + u;
-    u32x4* to = reinterpret_cast<u32x4*>(static_cast<char*>(a.dst) + row * a.dst_stride * EB) + u;
-    *to = *from;
-  } else {
-    copy_elem<S, D>(a, src + u, row * a.dst_stride + u);
+  copy_elem<S, D>(a, src + u, row * a.dst_stride + u);
+}
+
+// Same dtype, 16-byte aligned rows: a wave copies kGatherRows rows.  Lanes 0 ..
+// kGatherRows - 1 look up one row's source each; every lane then takes the wave's
+// 16-byte chunks lane, lane + 64, ... (consecutive lanes, consecutive chunks) with
+// its row's source offset fetched from the lane that looked it up.
+constexpr int kGatherRows = 8;
+
+__global__ __launch_bounds__(256) void gather_rows16_kernel(const GatherArgs a) {
+  if (status_failed(a.status)) return;
+  const int lane = lane_id();
+  const int64_t row0 = ((int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave) * kGatherRows;
+  if (row0 >= a.num_tokens) return;
+  int64_t src = -1;
+  if (lane < kGatherRows && row0 + lane < a.num_tokens) {
+    int64_t s;
+    if (gather_row(a, row0 + lane, &s) == kGatherCopy) src = s;
+  }
+  const int cpr = a.units_per_row;
+  const int total = kGatherRows * cpr;
+  const char* cache = static_cast<const char*>(a.cache);
+  char* dst = static_cast<char*>(a.dst);
+  const int64_t eb = a.cache_dtype == PA_F32 ? 4 : 2;
+  for (int k = lane; k < total; k += kWave) {
+    const int r = k / cpr, c = k - r * cpr;
+    const int64_t s = __shfl(src, r);
+    if (s < 0) continue;  // past the last row, skipped, or refused
+    const u32x4 x = *reinterpret_cast<const u32x4*>(cache + s * eb + 16 * c);
+    *reinterpret_cast<u32x4*>(dst + (row0 + r) * a.dst_stride * eb + 16 * c) = x;
   }
 }
 
@@ -97,8 +120,15 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t stream) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (a.num_tokens == 0) return hipSuccess;
+  if (a.vec16) {
+    const int64_t rows_per_wg = 4 * kGatherRows;
+    const int64_t wgs = (a.num_tokens + rows_per_wg - 1) / rows_per_wg;
+    if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(gather_rows16_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
   const int64_t threads = a.num_tokens * a.units_per_row;
-  if (threads == 0) return hipSuccess;
   const int64_t wgs = (threads + 255) / 256;
   if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid((unsigned)wgs);
