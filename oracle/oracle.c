@@ -26,6 +26,11 @@
  *     in natural log.  MergeAttnStates: the merge and its two edge cases.
  *     GatherMlaCache: the gather of a paged latent cache into contiguous rows.
  *   - "ManagedPagedAttention.cs", ForwardWithSinks: attention sinks.
+ *   - "paged_attention_v2_pytorch.py", phase 1 (the batched KV gather): the cache's
+ *     k_scale / v_scale multiply every gathered K / V element.  "Paged attention for
+ *     decode in C", the table of extensions: fp8 KV caches, read here as the OCP
+ *     8-bit E4M3 format (4 exponent bits with bias 7, 3 fraction bits, no
+ *     infinities, one NaN pattern per sign).
  *
  * Arithmetic: every stored element is decoded exactly to binary32 and then widened
  * to binary64; every sum, exp and log is binary64.  Work is split over (sequence,
@@ -46,6 +51,7 @@
 #define ORC_F32 0
 #define ORC_F16 1
 #define ORC_BF16 2
+#define ORC_FP8_E4M3 3
 
 /* ------------------------------------------------------------------------- */
 /* Element decoding                                                           */
@@ -54,6 +60,7 @@
 static int elem_bytes(int dtype) {
   if (dtype == ORC_F32) return 4;
   if (dtype == ORC_F16 || dtype == ORC_BF16) return 2;
+  if (dtype == ORC_FP8_E4M3) return 1;
   return 0;
 }
 
@@ -80,9 +87,27 @@ static double bf16_to_double(uint16_t h) {
   return (double)f;
 }
 
+/* OCP 8-bit E4M3: sign bit, 4 exponent bits with bias 7, 3 fraction bits.  Exponent
+ * field 0 is zero or subnormal (f * 2^-9); exponent 15 with fraction 7 is NaN, every
+ * other pattern is finite (largest 448); there is no infinity.                     */
+static double e4m3_to_double(uint8_t b) {
+  int sign = b >> 7;
+  int e = (b >> 3) & 0xf;
+  int f = b & 0x7;
+  double mag;
+  if (e == 0)
+    mag = ldexp((double)f, -9);
+  else if (e == 15 && f == 7)
+    mag = NAN;
+  else
+    mag = ldexp((double)(8 + f), e - 10); /* (1 + f / 8) * 2^(e - 7) */
+  return sign ? -mag : mag;
+}
+
 static double load_elem(const void* base, int dtype, int64_t i) {
   if (dtype == ORC_F32) return (double)((const float*)base)[i];
   if (dtype == ORC_F16) return half_to_double(((const uint16_t*)base)[i]);
+  if (dtype == ORC_FP8_E4M3) return e4m3_to_double(((const uint8_t*)base)[i]);
   return bf16_to_double(((const uint16_t*)base)[i]);
 }
 
@@ -140,15 +165,16 @@ static void parallel_for(int64_t ntasks, int nthreads, task_fn fn, void* ctx) {
 /* ------------------------------------------------------------------------- */
 
 /* Copy positions 0..n-1 of one sequence, kv head g, out of a pool laid out as
- * [num_blocks, block_size, num_kv_heads, head_dim] into dst[j * head_dim + d].
+ * [num_blocks, block_size, num_kv_heads, head_dim] into dst[j * head_dim + d], each
+ * element multiplied by the pool's scale (k_scale or v_scale).
  * Position j is in block table[j / block_size] at offset j % block_size.        */
-static void gather_head(const void* pool, int dtype, int block_size, int num_kv_heads,
+static void gather_head(const void* pool, int dtype, double scale, int block_size, int num_kv_heads,
                         int head_dim, const int32_t* table, int64_t n, int g, double* dst) {
   for (int64_t j = 0; j < n; ++j) {
     int64_t block_id = table[j / block_size];
     int64_t slot = block_id * block_size + j % block_size;
     int64_t base = (slot * num_kv_heads + g) * head_dim;
-    for (int d = 0; d < head_dim; ++d) dst[j * head_dim + d] = load_elem(pool, dtype, base + d);
+    for (int d = 0; d < head_dim; ++d) dst[j * head_dim + d] = load_elem(pool, dtype, base + d) * scale;
   }
 }
 
@@ -245,6 +271,8 @@ struct pool_desc {
   const void* k;
   const void* v;
   int dtype;
+  double k_scale; /* multiplies every stored K element */
+  double v_scale; /* multiplies every stored V element */
   int64_t num_blocks;
   int block_size;
   int num_kv_heads;
@@ -320,8 +348,8 @@ static void attn_task(void* ctx, int64_t task) {
   double* sc = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
   double* qrow = (double*)malloc(sizeof(double) * (size_t)P->dk);
   double* orow = (double*)malloc(sizeof(double) * (size_t)P->dv);
-  gather_head(P->k, P->dtype, P->block_size, P->num_kv_heads, P->dk, table, n, g, K);
-  gather_head(P->v, P->dtype, P->block_size, P->num_kv_heads, P->dv, table, n, g, V);
+  gather_head(P->k, P->dtype, P->k_scale, P->block_size, P->num_kv_heads, P->dk, table, n, g, K);
+  gather_head(P->v, P->dtype, P->v_scale, P->block_size, P->num_kv_heads, P->dv, table, n, g, V);
 
   for (int64_t t = t0; t < t1; ++t) {
     int64_t start, end;
@@ -366,6 +394,8 @@ static void attn_task(void* ctx, int64_t task) {
 static int check_job(const struct attn_job* job) {
   const struct pool_desc* P = &job->pool;
   if (elem_bytes(P->dtype) == 0 || elem_bytes(job->q_dtype) == 0) return ORC_EUNSUPPORTED;
+  if (!isfinite(P->k_scale) || !(P->k_scale > 0.0) || !isfinite(P->v_scale) || !(P->v_scale > 0.0))
+    return ORC_EINVAL;
   if (P->num_kv_heads < 1 || job->num_heads < 1 || P->dk < 1 || P->dv < 1) return ORC_ESHAPE;
   if (job->num_heads % P->num_kv_heads != 0) return ORC_ESHAPE;
   if (P->block_size < 1 || P->num_blocks < 1 || job->num_seqs < 0 || job->max_blocks < 0)
@@ -399,12 +429,14 @@ int orc_varlen(const void* k_pool, const void* v_pool, int kv_dtype, int64_t num
                const int32_t* seq_lens, const int32_t* positions, const int32_t* block_tables,
                int max_blocks, double scale, int causal, int sliding_window,
                const uint8_t* row_mask, double* out, double* lse, const double* sinks,
-               int num_threads) {
+               double k_scale, double v_scale, int num_threads) {
   struct attn_job job;
   memset(&job, 0, sizeof job);
   job.pool.k = k_pool;
   job.pool.v = v_pool;
   job.pool.dtype = kv_dtype;
+  job.pool.k_scale = k_scale;
+  job.pool.v_scale = v_scale;
   job.pool.num_blocks = num_blocks;
   job.pool.block_size = block_size;
   job.pool.num_kv_heads = num_kv_heads;
@@ -446,7 +478,8 @@ int orc_decode(const void* k_pool, const void* v_pool, int kv_dtype, int64_t num
                int num_heads, const int32_t* block_tables, int max_blocks, const int32_t* seq_lens,
                int num_seqs, double scale, int sliding_window, int partition_size,
                int max_partitions, double* out, double* lse, double* max_logits,
-               double* exp_sums, double* tmp_out, const double* sinks, int num_threads) {
+               double* exp_sums, double* tmp_out, const double* sinks, double k_scale,
+               double v_scale, int num_threads) {
   if (num_seqs < 0) return ORC_EINVAL;
   for (int s = 0; s < num_seqs; ++s)
     if (seq_lens[s] < 1) return ORC_EINVAL;
@@ -468,6 +501,8 @@ int orc_decode(const void* k_pool, const void* v_pool, int kv_dtype, int64_t num
   job.pool.k = k_pool;
   job.pool.v = v_pool;
   job.pool.dtype = kv_dtype;
+  job.pool.k_scale = k_scale;
+  job.pool.v_scale = v_scale;
   job.pool.num_blocks = num_blocks;
   job.pool.block_size = block_size;
   job.pool.num_kv_heads = num_kv_heads;
@@ -549,7 +584,7 @@ int orc_merge_states(const void* prefix_out, const float* prefix_lse, const void
                      const float* suffix_lse, int dtype, int64_t num_tokens, int num_heads,
                      int head_dim, int64_t prefill_tokens_with_context, double* out,
                      double* out_lse) {
-  if (elem_bytes(dtype) == 0) return ORC_EUNSUPPORTED;
+  if (elem_bytes(dtype) == 0 || dtype == ORC_FP8_E4M3) return ORC_EUNSUPPORTED;
   if (num_tokens < 0 || num_heads < 1 || head_dim < 1) return ORC_EINVAL;
   int64_t with_prefix = prefill_tokens_with_context < 0 ? num_tokens : prefill_tokens_with_context;
   for (int64_t t = 0; t < num_tokens; ++t) {
@@ -618,6 +653,9 @@ static uint16_t double_to_bf16(double x) {
   return (uint16_t)(u >> 16);
 }
 
+/* The types results are stored in (an fp8 cache is only ever read here). */
+static int encodable(int dtype) { return dtype == ORC_F32 || dtype == ORC_F16 || dtype == ORC_BF16; }
+
 static void store_elem(void* base, int dtype, int64_t i, double x) {
   if (dtype == ORC_F32)
     ((float*)base)[i] = (float)x;
@@ -630,7 +668,7 @@ static void store_elem(void* base, int dtype, int64_t i, double x) {
 /* Encode n binary64 values (each a binary32 value) to storage (exposed so the
  * encoders can be pinned). */
 int orc_encode_elems(const double* src, int dtype, int64_t n, void* out) {
-  if (elem_bytes(dtype) == 0) return ORC_EUNSUPPORTED;
+  if (!encodable(dtype)) return ORC_EUNSUPPORTED;
   for (int64_t i = 0; i < n; ++i) store_elem(out, dtype, i, src[i]);
   return ORC_OK;
 }
@@ -653,7 +691,7 @@ int orc_gather_cache(const void* src, int src_dtype, int64_t num_blocks, int blo
                      int64_t dst_row_stride, const int32_t* block_table, int max_blocks,
                      const int32_t* cu_seq_lens, const int32_t* token_to_seq, const int32_t* seq_starts,
                      int num_seqs, int64_t num_tokens) {
-  if (elem_bytes(src_dtype) == 0 || elem_bytes(dst_dtype) == 0) return ORC_EUNSUPPORTED;
+  if (!encodable(src_dtype) || !encodable(dst_dtype)) return ORC_EUNSUPPORTED;
   if (num_blocks < 1 || block_size < 1 || head_dim < 1 || num_seqs < 0 || num_tokens < 0 || max_blocks < 1)
     return ORC_EINVAL;
   for (int pass = 0; pass < 2; ++pass) { /* pass 0 checks, pass 1 copies */

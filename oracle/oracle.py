@@ -4,8 +4,9 @@ TEST INFRASTRUCTURE.  Only the test suite, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this module.  The GPU library and its
 binding never import it; the two implementations share no code.
 
-Arrays are numpy.  Stored element types are named ``"f32"``, ``"f16"`` or ``"bf16"``;
-bf16 arrays are carried as ``uint16`` bit patterns.  Every result is float64.
+Arrays are numpy.  Stored element types are named ``"f32"``, ``"f16"``, ``"bf16"`` or
+``"fp8_e4m3"``; bf16 arrays are carried as ``uint16`` and fp8 arrays as ``uint8`` bit
+patterns.  Every result is float64.
 """
 from __future__ import annotations
 
@@ -20,8 +21,8 @@ SOURCE = os.path.join(HERE, "oracle.c")
 LIBRARY = os.path.join(HERE, "liboracle.so")
 
 OK, EINVAL, ESHAPE, EUNSUPPORTED = 0, 1, 2, 3
-DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
-NUMPY_STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
+DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2, "fp8_e4m3": 3}
+NUMPY_STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "fp8_e4m3": np.uint8}
 
 _c_int_p = ctypes.POINTER(ctypes.c_int32)
 _c_dbl_p = ctypes.POINTER(ctypes.c_double)
@@ -123,9 +124,10 @@ class Oracle:
     # -- varlen ----------------------------------------------------------------------
     def varlen(self, k_pool, v_pool, kv_dtype, q, q_dtype, query_start_loc, seq_lens, positions,
                block_tables, scale, causal, sliding_window, row_mask=None, threads=None,
-               out=None, lse=None, sinks=None):
+               out=None, lse=None, sinks=None, k_scale=1.0, v_scale=1.0):
         """Returns (status, out [T, H, dv], lse [H, T]).  Rows outside row_mask stay NaN.
-        sinks: [H] sink logits (float64) or None."""
+        sinks: [H] sink logits (float64) or None.  k_scale / v_scale multiply every
+        stored K / V element."""
         k_pool = _storage(k_pool, kv_dtype)
         v_pool = _storage(v_pool, kv_dtype)
         nb, b, hkv, dk = k_pool.shape
@@ -147,12 +149,14 @@ class Oracle:
                                  dk, dv, _ptr(q), DTYPE_CODE[q_dtype], H, ctypes.c_int64(T), _ptr(qsl), S,
                                  _ptr(sl), _ptr(pos), _ptr(bt), max_blocks, ctypes.c_double(scale),
                                  int(bool(causal)), int(sliding_window), _ptr(mask), _ptr(out), _ptr(lse),
-                                 _ptr(_sinks(sinks, H)), threads or default_threads())
+                                 _ptr(_sinks(sinks, H)), ctypes.c_double(k_scale), ctypes.c_double(v_scale),
+                                 threads or default_threads())
         return st, out, lse
 
     # -- decode ----------------------------------------------------------------------
     def decode(self, k_pool, v_pool, kv_dtype, q, q_dtype, block_tables, seq_lens, scale,
-               sliding_window=0, partition_size=0, max_partitions=0, threads=None, out=None, sinks=None):
+               sliding_window=0, partition_size=0, max_partitions=0, threads=None, out=None, sinks=None,
+               k_scale=1.0, v_scale=1.0):
         """Unsplit: (status, out [S, H, dv], lse [H, S]).
         Split (partition_size > 0): (status, max_logits, exp_sums, tmp_out), entries
         past each sequence's partition count NaN."""
@@ -174,7 +178,8 @@ class Oracle:
                                      hkv, dk, dv, _ptr(q), DTYPE_CODE[q_dtype], H, _ptr(bt), max_blocks,
                                      _ptr(sl), S, ctypes.c_double(scale), int(sliding_window),
                                      int(partition_size), int(max_partitions), _ptr(out), _ptr(lse),
-                                     None, None, None, _ptr(_sinks(sinks, H)), thr)
+                                     None, None, None, _ptr(_sinks(sinks, H)), ctypes.c_double(k_scale),
+                                     ctypes.c_double(v_scale), thr)
             return st, out, lse
         ml = np.full((S, H, max_partitions), np.nan, dtype=np.float64)
         es = np.full((S, H, max_partitions), np.nan, dtype=np.float64)
@@ -183,7 +188,7 @@ class Oracle:
                                  dk, dv, _ptr(q), DTYPE_CODE[q_dtype], H, _ptr(bt), max_blocks, _ptr(sl), S,
                                  ctypes.c_double(scale), int(sliding_window), int(partition_size),
                                  int(max_partitions), None, None, _ptr(ml), _ptr(es), _ptr(to),
-                                 _ptr(_sinks(sinks, H)), thr)
+                                 _ptr(_sinks(sinks, H)), ctypes.c_double(k_scale), ctypes.c_double(v_scale), thr)
         return st, ml, es, to
 
     def reduce_partitions(self, max_logits, exp_sums, tmp_out, seq_lens, partition_size, sinks=None):

@@ -20,7 +20,11 @@ oracle disagrees with what the pages or the mathematics fix:
   sink-free path on a pool that holds such a position), plus closed forms;
 * the latent-cache gather (GatherMlaCache) returns the logical rows a cache was
   scattered from, and its rounding to binary16 / bfloat16 gives numpy's and torch's
-  bits.
+  bits;
+* fp8 (E4M3) caches: every pattern decodes as torch's float8_e4m3fn, with the
+  format's landmarks; a pool with k_scale / v_scale attends like SDPA over the cache
+  torch dequantizes ("paged_attention_v2_pytorch.py", phase 1), and the scales obey
+  their closed forms.
 
 The same functions run against deliberately broken builds of the oracle in
 test_oracle_mutants.py, which checks that each planted mistake fails at least one.
@@ -45,12 +49,15 @@ EINVAL, ESHAPE = 1, 2
 # --------------------------------------------------------------------------------
 
 def stored(values_f64, dtype):
-    """Round float values to storage (f32 / f16 / bf16 bits) with library routines."""
+    """Round float values to storage (f32 / f16 / bf16 / fp8 e4m3 bits) with library
+    routines."""
     a = np.asarray(values_f64, dtype=np.float32)
     if dtype == "f32":
         return a.copy()
     if dtype == "f16":
         return a.astype(np.float16)
+    if dtype == "fp8_e4m3":
+        return torch.from_numpy(a.copy()).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     return torch.from_numpy(a.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
@@ -58,11 +65,14 @@ def widen(a, dtype):
     """Storage -> float64 with numpy / torch (independent of the oracle's decoders)."""
     if dtype == "bf16":
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).double().numpy()
+    if dtype == "fp8_e4m3":
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).view(torch.float8_e4m3fn).double().numpy()
     return np.asarray(a).astype(np.float64)
 
 
 def nan_storage(dtype):
-    return {"f32": np.float32(np.nan), "f16": np.float16(np.nan), "bf16": np.uint16(0x7FC0)}[dtype]
+    return {"f32": np.float32(np.nan), "f16": np.float16(np.nan), "bf16": np.uint16(0x7FC0),
+            "fp8_e4m3": np.uint8(0x7F)}[dtype]
 
 
 class Case:
@@ -718,12 +728,116 @@ def pin_gather_rejections(orc):
         assert st == EINVAL and np.all(out == 5.0), kw
 
 
+# --------------------------------------------------------------------------------
+# fp8 caches and the per-tensor K / V scales
+# --------------------------------------------------------------------------------
+
+def pin_e4m3_decoder(orc):
+    """Every fp8 pattern decodes as torch's float8_e4m3fn decodes it, and the format's
+    landmarks hold: 448 is the largest finite value, 2^-9 the smallest subnormal,
+    2^-6 the smallest normal, 0x38 is 1, the sign bit negates, 0x7F / 0xFF are NaN
+    and nothing is infinite; the positive patterns 0x00..0x7E increase."""
+    bits = np.arange(256, dtype=np.uint8)
+    got = orc.decode_elems(bits, "fp8_e4m3")
+    ref = torch.from_numpy(bits.copy()).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(got, ref, equal_nan=True)
+    assert got[0x7E] == 448.0 and got[0xFE] == -448.0
+    assert got[0x01] == 2.0 ** -9 and got[0x07] == 7 * 2.0 ** -9 and got[0x08] == 2.0 ** -6
+    assert got[0x38] == 1.0 and got[0xB8] == -1.0 and got[0x39] == 1.125
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF]) and not np.isinf(got).any()
+    assert np.count_nonzero(np.isnan(got)) == 2
+    assert np.all(np.diff(got[:0x7F]) > 0)
+    assert np.array_equal(got[0x80:0xFF], -got[:0x7F]) and math.copysign(1.0, got[0x80]) == -1.0
+
+
+def _fp8_case(rng, lengths, H, Hkv, D, b):
+    """An fp8 case whose stored values span the subnormals up to about 40 (the logical
+    values are those times the scales)."""
+    case = Case(rng, lengths, H=H, Hkv=Hkv, dk=D, dv=D, dtype="f32", b=b)
+    k8 = [stored(8.0 * widen(k, "f32"), "fp8_e4m3") for k in case.K]
+    v8 = [stored(8.0 * widen(v, "f32"), "fp8_e4m3") for v in case.V]
+    kp = np.full(case.k_pool.shape, 0x7F, np.uint8)
+    vp = np.full(case.v_pool.shape, 0x7F, np.uint8)
+    for s, n in enumerate(lengths):
+        for j in range(n):
+            kp[case.tables[s, j // b], j % b] = k8[s][j]
+            vp[case.tables[s, j // b], j % b] = v8[s][j]
+    return case, k8, v8, kp, vp
+
+
+def pin_fp8_pool_is_the_dequantized_cache(orc):
+    """"paged_attention_v2_pytorch.py", phase 1: an fp8 pool with k_scale / v_scale
+    attends like SDPA over the cache torch dequantizes (stored value times scale),
+    for decode (unsplit and through partitions), windows and varlen chunks."""
+    rng = np.random.default_rng(41)
+    ks, vs = 0.1171875, 0.0732421875
+    case, k8, v8, kp, vp = _fp8_case(rng, [1, 29, 70], H=8, Hkv=2, D=32, b=8)
+    assert np.any((k8[2] & 0x78) == 0) and np.any((k8[2] & 0x7F) >= 0x50)  # subnormals and large codes
+    q = stored(rng.standard_normal((3, 8, 32)), "bf16")
+    for window in (0, 13):
+        st, out, lse = orc.decode(kp, vp, "fp8_e4m3", q, "bf16", case.tables, case.lengths, 0.2,
+                                  sliding_window=window, k_scale=ks, v_scale=vs)
+        assert st == 0, st
+        st, ml, es, to = orc.decode(kp, vp, "fp8_e4m3", q, "bf16", case.tables, case.lengths, 0.2,
+                                    sliding_window=window, partition_size=16, max_partitions=5,
+                                    k_scale=ks, v_scale=vs)
+        assert st == 0, st
+        red = orc.reduce_partitions(ml, es, to, case.lengths, 16)
+        for s, n in enumerate(case.lengths):
+            lo, hi = _ranges(np.array([n - 1]), n, True, window)
+            ref, rlse = dense_reference(widen(q[s:s + 1], "bf16"), widen(k8[s], "fp8_e4m3") * ks,
+                                        widen(v8[s], "fp8_e4m3") * vs, lo, hi, 0.2, 4)
+            np.testing.assert_allclose(out[s], ref[0], atol=1e-12, rtol=1e-12)
+            np.testing.assert_allclose(lse[:, s], rlse[:, 0], atol=1e-12, rtol=1e-12)
+            np.testing.assert_allclose(red[s], ref[0], atol=1e-12, rtol=1e-12)
+    segments = [(0, 1), (20, 9), (69, 1)]
+    qv = stored(rng.standard_normal((11, 8, 32)), "f16")
+    qsl = np.array([0, 1, 10, 11], np.int32)
+    positions = np.concatenate([np.arange(c, c + k) for c, k in segments]).astype(np.int32)
+    st, out, lse = orc.varlen(kp, vp, "fp8_e4m3", qv, "f16", qsl, case.lengths, positions, case.tables, 0.3,
+                              True, 0, k_scale=ks, v_scale=vs)
+    assert st == 0, st
+    for s, n in enumerate(case.lengths):
+        t0, t1 = qsl[s], qsl[s + 1]
+        lo, hi = _ranges(positions[t0:t1], n, True, 0)
+        ref, rlse = dense_reference(widen(qv[t0:t1], "f16"), widen(k8[s], "fp8_e4m3") * ks,
+                                    widen(v8[s], "fp8_e4m3") * vs, lo, hi, 0.3, 4)
+        np.testing.assert_allclose(out[t0:t1], ref, atol=1e-12, rtol=1e-12)
+        np.testing.assert_allclose(lse[:, t0:t1], rlse, atol=1e-12, rtol=1e-12)
+
+
+def pin_scale_closed_forms(orc):
+    """On any pool, k_scale = c scores like a softmax scale multiplied by c, and
+    v_scale = c multiplies every output by c and leaves the lse alone; scales that are
+    zero, negative or not finite are rejected."""
+    rng = np.random.default_rng(43)
+    case = Case(rng, [9, 33], H=4, Hkv=2, dk=16, dv=16, dtype="f32", b=4)
+    q = stored(rng.standard_normal((2, 4, 16)), "f32")
+    st, base, blse = orc.decode(case.k_pool, case.v_pool, "f32", q, "f32", case.tables, case.lengths, 0.25)
+    assert st == 0
+    st, out, lse = orc.decode(case.k_pool, case.v_pool, "f32", q, "f32", case.tables, case.lengths, 0.125,
+                              k_scale=2.0)
+    assert st == 0 and np.array_equal(out, base) and np.array_equal(lse, blse)
+    st, out, lse = orc.decode(case.k_pool, case.v_pool, "f32", q, "f32", case.tables, case.lengths, 0.25,
+                              v_scale=0.375)
+    assert st == 0 and np.array_equal(lse, blse)
+    np.testing.assert_allclose(out, 0.375 * base, rtol=1e-13, atol=1e-15)
+    for bad in (0.0, -1.0, math.inf, math.nan):
+        for kw in ({"k_scale": bad}, {"v_scale": bad}):
+            st, *_ = orc.decode(case.k_pool, case.v_pool, "f32", q, "f32", case.tables, case.lengths, 0.25, **kw)
+            assert st == EINVAL, (kw, st)
+            st, *_ = orc.varlen(case.k_pool, case.v_pool, "f32", q, "f32", [0, 1, 2], case.lengths, [8, 32],
+                                case.tables, 0.25, True, 0, **kw)
+            assert st == EINVAL, (kw, st)
+
+
 PINS = [pin_hand_example, pin_hand_example_per_block, pin_hand_example_written_through_slots,
         pin_decode_matches_dense, pin_varlen_matches_dense, pin_empty_rows, pin_decoders,
         pin_permutation_invariance, pin_closed_forms, pin_partitions_reduce_to_unsplit,
         pin_merge_halves_equal_whole, pin_merge_edge_rules, pin_invariance, pin_write_kv_round_trip,
         pin_rejections, pin_sink_is_a_zero_value_position, pin_sink_closed_forms, pin_encoders,
-        pin_gather_returns_logical_rows, pin_gather_rejections]
+        pin_gather_returns_logical_rows, pin_gather_rejections, pin_e4m3_decoder,
+        pin_fp8_pool_is_the_dequantized_cache, pin_scale_closed_forms]
 
 
 def run_all(path):

@@ -74,6 +74,17 @@ MUTANTS = {
                                    "int64_t idx = pos / block_size, slot = idx % block_size;"),
     "gather_copies_rows_past_end": ("if (t >= cu_seq_lens[b + 1]) continue;", ""),
     "gather_trusts_block_ids": ("if (block < 0 || block >= num_blocks) return ORC_EINVAL;", ""),
+    # fp8 (E4M3) caches and the per-tensor K / V scales
+    "e4m3_bias_8": ("mag = ldexp((double)(8 + f), e - 10);", "mag = ldexp((double)(8 + f), e - 11);"),
+    "e4m3_subnormal_as_normal": ("mag = ldexp((double)f, -9);", "mag = ldexp((double)(8 + f), -10);"),
+    "e4m3_nan_as_largest": ("else if (e == 15 && f == 7)\n    mag = NAN;", "else if (e == 16)\n    mag = NAN;"),
+    "e4m3_exponent_15_is_nan": ("else if (e == 15 && f == 7)", "else if (e == 15)"),
+    "e4m3_sign_ignored": ("  return sign ? -mag : mag;\n}\n\nstatic double load_elem",
+                          "  return mag;\n}\n\nstatic double load_elem"),
+    "k_scale_on_v": ("gather_head(P->v, P->dtype, P->v_scale", "gather_head(P->v, P->dtype, P->k_scale"),
+    "v_scale_dropped": ("gather_head(P->v, P->dtype, P->v_scale", "gather_head(P->v, P->dtype, 1.0"),
+    "scale_divides": ("load_elem(pool, dtype, base + d) * scale;", "load_elem(pool, dtype, base + d) / scale;"),
+    "scales_unchecked": ("  if (!isfinite(P->k_scale) || !(P->k_scale > 0.0) || !isfinite(P->v_scale) || !(P->v_scale > 0.0))\n    return ORC_EINVAL;\n", ""),
 }
 
 
