@@ -7,8 +7,13 @@ sharing a 256-token prefix).  One step = pa_write_kv of the 64 new tokens + pa_d
 sum over sequences and kv heads of the visible positions times
 (head_dim_k + head_dim_v) * 2 bytes, divided by the wall time of a step.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|long|varlen|mla|gather]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload decode|long|decode-fp8|long-fp8|varlen|mla|gather]
                     [--partition-size P] [--no-cpu-baseline] [--copy-calibration] [--sweep]
+
+decode-fp8 / long-fp8 are the same decode workloads over an fp8 (E4M3) cache with
+per-tensor k_scale / v_scale (queries stay f16 / bf16); their bytes count one byte
+per K / V element.
 
 Prints one JSON line.  The roofline object divides the same algorithmic bytes (or
 flops) by the attention call's average duration, taken from HIP events recorded on
@@ -50,7 +55,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=["decode", "long", "varlen", "mla", "gather"])
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "long", "decode-fp8", "long-fp8", "varlen", "mla", "gather"])
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
@@ -137,13 +143,18 @@ def dev(a, dtype=None):
     a = np.ascontiguousarray(a)
     if dtype == "bf16":
         return torch.from_numpy(a.view(np.int16)).to("cuda").view(torch.bfloat16)
+    if dtype == "fp8_e4m3":
+        return torch.from_numpy(a.view(np.uint8)).to("cuda").view(torch.float8_e4m3fn)
     return torch.from_numpy(a).to("cuda")
+
+
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}
 
 
 def decode_bytes(w):
     """Algorithmic KV bytes of one decode call: every visible position of every
     (sequence, kv head) read once, K and V."""
-    eb = 4 if w.dtype == "f32" else 2
+    eb = ELEM_BYTES[w.dtype]
     n = w.seq_lens.astype(np.int64)
     if w.sliding_window > 0:
         n = np.minimum(n, w.sliding_window)
@@ -182,8 +193,8 @@ def cpu_baseline_decode(w, budget_s):
     S = w.num_seqs
 
     def call(n):
-        orc.decode(kp, vp, w.dtype, w.q[:n], w.dtype, w.block_tables[:n], w.seq_lens[:n], w.scale,
-                   threads=threads)
+        orc.decode(kp, vp, w.dtype, w.q[:n], w.query_dtype, w.block_tables[:n], w.seq_lens[:n], w.scale,
+                   threads=threads, k_scale=w.k_scale, v_scale=w.v_scale)
 
     t0 = time.perf_counter()
     call(min(S, 4))
@@ -197,7 +208,7 @@ def cpu_baseline_decode(w, budget_s):
         dt = time.perf_counter() - t0
         if dt >= budget_s or dt + dt / reps > 1.5 * budget_s:
             break
-    eb = 4 if w.dtype == "f32" else 2
+    eb = ELEM_BYTES[w.dtype]
     nbytes = int(w.seq_lens[:take].astype(np.int64).sum()) * w.num_kv_heads * (w.dk + w.dv) * eb * reps
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"first {take} of {S} sequences, whole oracle decode call (gather + two-pass fp64) "
@@ -348,13 +359,16 @@ def main():
         return run_prefill(args)
     if args.workload == "gather":
         return run_gather(args)
-    w = W.config2() if args.workload == "decode" else W.config3()
+    base = args.workload.removesuffix("-fp8")
+    w = W.config2() if base == "decode" else W.config3()
+    if args.workload.endswith("-fp8"):
+        w = W.to_fp8(w)
     if args.partition_size is not None:
         P = args.partition_size
     else:
-        P = 0 if args.workload == "decode" else 512
+        P = 0 if base == "decode" else 512
     kp, vp = dev(w.k_pool, w.dtype), dev(w.v_pool, w.dtype)
-    q = dev(w.q, w.dtype)
+    q = dev(w.q, w.query_dtype)
     tables, lens = dev(w.block_tables), dev(w.seq_lens)
     k_new, v_new, slots = dev(w.k_new, w.dtype), dev(w.v_new, w.dtype), dev(w.slot_mapping)
     S, H = w.num_seqs, w.num_heads
@@ -372,7 +386,8 @@ def main():
 
     def decode(p=P, buf=ws, status=None, sinks=None):
         pa_decode(kp, vp, q, out, tables, lens, w.scale, sliding_window=w.sliding_window, partition_size=p,
-                  max_logits=buf[0], exp_sums=buf[1], tmp_out=buf[2], status=status, sinks=sinks)
+                  max_logits=buf[0], exp_sums=buf[1], tmp_out=buf[2], status=status, sinks=sinks,
+                  k_scale=w.k_scale, v_scale=w.v_scale)
 
     def write():
         pa_write_kv(kp, vp, k_new, v_new, slots)
@@ -397,8 +412,9 @@ def main():
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": w.name, "num_seqs": S, "seq_lens": [int(w.seq_lens.min()), max_len],
+        "vs_baseline": None, "dtype": w.query_dtype, "data": "synthetic",
+        "config": {"workload": w.name, "kv_dtype": w.dtype, "num_seqs": S,
+                   "seq_lens": [int(w.seq_lens.min()), max_len],
                    "num_heads": H, "num_kv_heads": w.num_kv_heads, "head_dim": w.dk, "block_size": w.block_size,
                    "partition_size": P, "kv_bytes_per_step": nbytes, "step": "pa_write_kv + pa_decode"},
         "roofline": roof,

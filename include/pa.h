@@ -21,6 +21,12 @@
  *     must be finite and > 0 (else PA_EINVAL).
  *   - lse arrays are float32 [num_heads, tokens] in natural log; a row that sees no
  *     position has output 0 and lse -inf ("cpu_mla_prefill.cpp", MlaPrefillAttention).
+ *   - Every stored K element counts as its value times the pool's k_scale, every V
+ *     element as its value times v_scale ("paged_attention_v2_pytorch.py", phase 1,
+ *     the KV gather); 1.0 leaves a cache as stored.  A pool of PA_FP8_E4M3 holds
+ *     the OCP 8-bit E4M3 format (4 exponent bits, bias 7, 3 fraction bits, largest
+ *     finite 448, no infinities) -- the fp8 KV caches of "Paged attention for decode
+ *     in C" (table of extensions); its queries and outputs are f16 or bf16.
  *
  * Ownership and streams: the caller owns every buffer.  The library allocates no
  * memory, keeps no state between calls, and enqueues all work on `stream` (a
@@ -58,7 +64,7 @@ typedef enum pa_status {
   PA_EDEVICE = 4       /* a HIP launch failed */
 } pa_status;
 
-typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 } pa_dtype;
 
 typedef struct pa_kv_pool {
   void* k;              /* device, [num_blocks, block_size, num_kv_heads, head_dim_k] */
@@ -69,6 +75,8 @@ typedef struct pa_kv_pool {
   int32_t head_dim_k;   /* QK head dim */
   int32_t head_dim_v;   /* V head dim */
   int32_t dtype;        /* pa_dtype of both pools */
+  float k_scale;        /* finite, > 0: K element = stored value * k_scale (1.0: none) */
+  float v_scale;        /* finite, > 0: V element = stored value * v_scale (1.0: none) */
 } pa_kv_pool;
 
 /* Static text for a status code. */
@@ -76,8 +84,9 @@ const char* pa_strerror(int status);
 
 /* Write new tokens' K and V into their pool slots (TensorSharp page,
  * WriteKvToPagedPool).  k_new [num_tokens, num_kv_heads, head_dim_k] and v_new
- * [num_tokens, num_kv_heads, head_dim_v] are device arrays in the pool dtype;
- * token t goes to slot slot_mapping[t] (device int32).  Bytes are copied unchanged.
+ * [num_tokens, num_kv_heads, head_dim_v] are device arrays in the pool dtype (already
+ * quantized, for an fp8 pool); token t goes to slot slot_mapping[t] (device int32).
+ * Bytes are copied unchanged; a row must be a multiple of 4 bytes.
  * Device check (with status): every slot in [0, num_blocks * block_size).  A slot
  * repeated within one call is written by one of its tokens, unspecified which.
  * num_tokens == 0 enqueues nothing. */
@@ -87,7 +96,8 @@ int pa_write_kv(const pa_kv_pool* pool, const void* k_new, const void* v_new,
 /* One decode step ("Paged attention for decode in C", sections 2.2-2.6): for each
  * sequence s and head h, the query q[s, h, :] sits at position seq_lens[s] - 1
  * (causal) and attends over its visible positions.
- *   q [num_seqs, num_heads, head_dim_k] in q_dtype (must equal the pool dtype);
+ *   q [num_seqs, num_heads, head_dim_k] in q_dtype (the pool dtype; F16 or BF16 for
+ *     an fp8 pool);
  *   out [num_seqs, num_heads, head_dim_v] in out_dtype (PA_F32 or q_dtype);
  *   block_tables [num_seqs, max_blocks]; seq_lens [num_seqs] (device int32).
  * partition_size == 0: one pass per (sequence, kv head).
@@ -112,7 +122,8 @@ int pa_write_kv(const pa_kv_pool* pool, const void* k_new, const void* v_new,
  * the output; -inf means no sink.  With partitions the workspaces stay sink-free and
  * the sink joins in the combining step.
  * Supported: head_dim_k == head_dim_v in {32, 64, 128, 256}; num_heads /
- * num_kv_heads <= 16; any block_size. */
+ * num_kv_heads <= 16; any block_size.  PA_FP8_E4M3 pools: q_dtype PA_F16 or PA_BF16,
+ * head dims 128, block_size a power of two >= 16. */
 int pa_decode(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out, int32_t out_dtype,
               const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
               int32_t num_seqs, int32_t num_heads, float scale, int32_t sliding_window,
@@ -138,7 +149,9 @@ int pa_decode(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
  * sink's mass (a row that sees nothing gets out = 0 and lse = sinks[h]); when
  * states of several calls are merged, give the sinks to one of them only.
  * Supported: (head_dim_k, head_dim_v) in {(32,32), (64,64), (128,128), (256,256),
- * (192,128)}; num_heads / num_kv_heads <= 16; any block_size. */
+ * (192,128)}; num_heads / num_kv_heads <= 16; any block_size.  PA_FP8_E4M3 pools: as
+ * for pa_decode, and only calls whose sequences hold at most one query token each
+ * (max_query_len <= 1). */
 int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out, int32_t out_dtype,
               float* lse, const int32_t* query_start_loc, const int32_t* seq_lens,
               const int32_t* positions, const int32_t* block_tables, int32_t max_blocks,

@@ -18,8 +18,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libpa.so")
 
 PA_OK, PA_EINVAL, PA_ESHAPE, PA_EUNSUPPORTED, PA_EDEVICE = 0, 1, 2, 3, 4
-PA_F32, PA_F16, PA_BF16 = 0, 1, 2
-DTYPE_CODE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
+DTYPE_CODE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
+              torch.float8_e4m3fn: PA_FP8_E4M3}
 
 EXPORTS = ("pa_strerror", "pa_write_kv", "pa_decode", "pa_varlen", "pa_merge_states", "pa_gather_cache")
 
@@ -27,7 +28,8 @@ EXPORTS = ("pa_strerror", "pa_write_kv", "pa_decode", "pa_varlen", "pa_merge_sta
 class PaKvPool(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("num_blocks", ctypes.c_int64),
                 ("block_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
-                ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
 
 
 class PaError(RuntimeError):
@@ -110,15 +112,23 @@ def _check(status, what):
         raise PaError(status, what)
 
 
-def make_pool(k_pool: torch.Tensor, v_pool: torch.Tensor) -> PaKvPool:
-    """Descriptor for pools [num_blocks, block_size, num_kv_heads, head_dim]."""
+def _code(t, name):
+    if t.dtype not in DTYPE_CODE:
+        raise TypeError(f"{name}: no element type code for {t.dtype}")
+    return DTYPE_CODE[t.dtype]
+
+
+def make_pool(k_pool: torch.Tensor, v_pool: torch.Tensor, k_scale: float = 1.0, v_scale: float = 1.0) -> PaKvPool:
+    """Descriptor for pools [num_blocks, block_size, num_kv_heads, head_dim] (f32, f16,
+    bf16 or float8_e4m3fn); K / V elements count as stored value times k_scale /
+    v_scale."""
     _dev(k_pool, "k_pool", ndim=4)
     _dev(v_pool, "v_pool", dtype=k_pool.dtype, ndim=4)
     nb, b, hkv, dk = k_pool.shape
     if tuple(v_pool.shape[:3]) != (nb, b, hkv):
         raise ValueError("k_pool and v_pool disagree on blocks / block size / kv heads")
     return PaKvPool(k_pool.data_ptr(), v_pool.data_ptr(), nb, b, hkv, dk, v_pool.shape[3],
-                    DTYPE_CODE[k_pool.dtype])
+                    _code(k_pool, "k_pool"), float(k_scale), float(v_scale))
 
 
 # ------------------------------------------------------------------------------------
@@ -141,11 +151,13 @@ def pa_write_kv(k_pool, v_pool, k_new, v_new, slot_mapping, status=None, stream=
 
 
 def pa_decode(k_pool, v_pool, q, out, block_tables, seq_lens, scale, sliding_window=0, partition_size=0,
-              max_logits=None, exp_sums=None, tmp_out=None, status=None, stream=None, sinks=None):
-    """One decode step; q [S, H, D], out [S, H, D] (float32 or q's dtype); sinks [H]
-    float32 attention-sink logits or None."""
-    pool = make_pool(k_pool, v_pool)
-    _dev(q, "q", dtype=k_pool.dtype, ndim=3)
+              max_logits=None, exp_sums=None, tmp_out=None, status=None, stream=None, sinks=None, k_scale=1.0,
+              v_scale=1.0):
+    """One decode step; q [S, H, D] (the pools' dtype; f16 / bf16 over fp8 pools), out
+    [S, H, D] (float32 or q's dtype); sinks [H] float32 attention-sink logits or None;
+    k_scale / v_scale: the pools' per-tensor scales."""
+    pool = make_pool(k_pool, v_pool, k_scale, v_scale)
+    _dev(q, "q", ndim=3)
     _dev(out, "out", ndim=3)
     _dev(block_tables, "block_tables", dtype=torch.int32, ndim=2)
     _dev(seq_lens, "seq_lens", dtype=torch.int32, ndim=1)
@@ -169,7 +181,7 @@ def pa_decode(k_pool, v_pool, q, out, block_tables, seq_lens, scale, sliding_win
         _shape(max_logits, (S, H, max_partitions), "max_logits")
         _shape(exp_sums, (S, H, max_partitions), "exp_sums")
         _shape(tmp_out, (S, H, max_partitions, pool.head_dim_v), "tmp_out")
-    st = load().pa_decode(ctypes.byref(pool), _ptr(q), DTYPE_CODE[q.dtype], _ptr(out), DTYPE_CODE[out.dtype],
+    st = load().pa_decode(ctypes.byref(pool), _ptr(q), _code(q, "q"), _ptr(out), _code(out, "out"),
                           _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), S, H, float(scale),
                           int(sliding_window), int(partition_size), int(max_partitions), _ptr(max_logits),
                           _ptr(exp_sums), _ptr(tmp_out), _ptr(sinks), _ptr(status), _stream(stream))
@@ -177,11 +189,13 @@ def pa_decode(k_pool, v_pool, q, out, block_tables, seq_lens, scale, sliding_win
 
 
 def pa_varlen(k_pool, v_pool, q, out, query_start_loc, seq_lens, positions, block_tables, max_query_len, scale,
-              causal=True, sliding_window=0, lse=None, status=None, stream=None, sinks=None):
+              causal=True, sliding_window=0, lse=None, status=None, stream=None, sinks=None, k_scale=1.0,
+              v_scale=1.0):
     """Varlen attention; q [T, H, Dk], out [T, H, Dv], lse [H, T] (optional); sinks
-    [H] float32 attention-sink logits or None."""
-    pool = make_pool(k_pool, v_pool)
-    _dev(q, "q", dtype=k_pool.dtype, ndim=3)
+    [H] float32 attention-sink logits or None; k_scale / v_scale: the pools'
+    per-tensor scales."""
+    pool = make_pool(k_pool, v_pool, k_scale, v_scale)
+    _dev(q, "q", ndim=3)
     _dev(out, "out", ndim=3)
     _dev(lse, "lse", dtype=torch.float32, ndim=2)
     _dev(query_start_loc, "query_start_loc", dtype=torch.int32, ndim=1)
@@ -200,7 +214,7 @@ def pa_varlen(k_pool, v_pool, q, out, query_start_loc, seq_lens, positions, bloc
     _shape(positions, (T,), "positions")
     if block_tables.shape[0] != S:
         raise ValueError("block_tables must have one row per sequence")
-    st = load().pa_varlen(ctypes.byref(pool), _ptr(q), DTYPE_CODE[q.dtype], _ptr(out), DTYPE_CODE[out.dtype],
+    st = load().pa_varlen(ctypes.byref(pool), _ptr(q), _code(q, "q"), _ptr(out), _code(out, "out"),
                           _ptr(lse), _ptr(query_start_loc), _ptr(seq_lens), _ptr(positions), _ptr(block_tables),
                           block_tables.shape[1], seq_lens.numel(), T, int(max_query_len), H, float(scale),
                           int(bool(causal)), int(sliding_window), _ptr(sinks), _ptr(status), _stream(stream))

@@ -40,6 +40,8 @@ bool prefill_supported(int dtype, int dk, int dv, int group, int block_size, int
 
 hipError_t launch_decode_bf16(const RowsArgs& a, int block_shift, int dk, int dv, dim3 grid, hipStream_t stream);
 hipError_t launch_decode_f16(const RowsArgs& a, int block_shift, int dk, int dv, dim3 grid, hipStream_t stream);
+hipError_t launch_decode_fp8_bf16(const RowsArgs& a, int block_shift, int dk, int dv, dim3 grid, hipStream_t stream);
+hipError_t launch_decode_fp8_f16(const RowsArgs& a, int block_shift, int dk, int dv, dim3 grid, hipStream_t stream);
 
 // The MFMA decode kernel: f16 / bf16, a power-of-two block size that is a multiple
 // of 16, up to 16 q heads per kv head.
@@ -51,14 +53,19 @@ bool decode_mfma_supported(int dtype, int dk, int dv, int group, int block_size)
 }
 
 // Row kernel launch: the MFMA decode kernel when it supports the shape, else the
-// general per-row kernel.
-hipError_t launch_row_kernel(const RowsArgs& a, int dtype, int dk, int dv, dim3 grid, hipStream_t stream) {
-  if (decode_mfma_supported(dtype, dk, dv, a.group, a.block_size)) {
-    int shift = 0;
-    while ((1 << shift) < a.block_size) ++shift;
+// general per-row kernel.  `dtype` is the queries' (f16 / bf16 for an fp8 pool).
+hipError_t launch_row_kernel(const RowsArgs& a, int kv_dtype, int dtype, int dk, int dv, dim3 grid,
+                             hipStream_t stream) {
+  int shift = 0;
+  while ((1 << shift) < a.block_size) ++shift;
+  if (kv_dtype == PA_FP8_E4M3) {
+    if (!decode_mfma_supported(dtype, dk, dv, a.group, a.block_size)) return hipErrorInvalidValue;
+    return dtype == PA_BF16 ? launch_decode_fp8_bf16(a, shift, dk, dv, grid, stream)
+                            : launch_decode_fp8_f16(a, shift, dk, dv, grid, stream);
+  }
+  if (decode_mfma_supported(dtype, dk, dv, a.group, a.block_size))
     return dtype == PA_BF16 ? launch_decode_bf16(a, shift, dk, dv, grid, stream)
                             : launch_decode_f16(a, shift, dk, dv, grid, stream);
-  }
   return launch_rows(a, dtype, dk, dv, grid, stream);
 }
 
@@ -75,6 +82,7 @@ using namespace pa;
 
 namespace {
 
+// Bytes of a value type (queries, outputs, merged states, latent rows).
 int element_bytes(int dtype) {
   switch (dtype) {
     case PA_F32: return 4;
@@ -84,13 +92,34 @@ int element_bytes(int dtype) {
   }
 }
 
+// Bytes of a pool element: the value types, or one byte of fp8.
+int pool_element_bytes(int dtype) { return dtype == PA_FP8_E4M3 ? 1 : element_bytes(dtype); }
+
 int check_pool(const pa_kv_pool* pool) {
   if (pool == nullptr || pool->k == nullptr || pool->v == nullptr) return PA_EINVAL;
   if (pool->num_blocks < 1 || pool->block_size < 1 || pool->num_kv_heads < 1 || pool->head_dim_k < 1 ||
       pool->head_dim_v < 1)
     return PA_EINVAL;
-  if (element_bytes(pool->dtype) == 0) return PA_EUNSUPPORTED;
+  if (pool_element_bytes(pool->dtype) == 0) return PA_EUNSUPPORTED;
+  if (!isfinite(pool->k_scale) || !(pool->k_scale > 0.f) || !isfinite(pool->v_scale) || !(pool->v_scale > 0.f))
+    return PA_EINVAL;
   return PA_OK;
+}
+
+// The queries' type must be the pool's, or f16 / bf16 over an fp8 pool.
+bool query_type_ok(const pa_kv_pool* pool, int q_dtype) {
+  if (pool->dtype == PA_FP8_E4M3) return q_dtype == PA_F16 || q_dtype == PA_BF16;
+  return q_dtype == pool->dtype;
+}
+
+// The softmax scale with k_scale folded in (a score is scale * k_scale * <q, stored
+// k>); false when the product is not a finite positive binary32.
+bool folded_scale(const pa_kv_pool* pool, float scale, float& scale_log2) {
+  if (!isfinite(scale) || !(scale > 0.f)) return false;
+  const float s = scale * pool->k_scale;
+  if (!isfinite(s) || !(s > 0.f) || !isfinite(s * kLog2e) || !(s * kLog2e > 0.f)) return false;
+  scale_log2 = s * kLog2e;
+  return true;
 }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_EDEVICE; }
@@ -124,7 +153,7 @@ int pa_write_kv(const pa_kv_pool* pool, const void* k_new, const void* v_new, co
   if (st != PA_OK) return st;
   if (num_tokens < 0) return PA_EINVAL;
   if (num_tokens > 0 && (k_new == nullptr || v_new == nullptr || slot_mapping == nullptr)) return PA_EINVAL;
-  const int eb = element_bytes(pool->dtype);
+  const int eb = pool_element_bytes(pool->dtype);
   WriteArgs a;
   a.k_pool = pool->k;
   a.v_pool = pool->v;
@@ -165,11 +194,15 @@ int pa_decode(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
     return PA_EINVAL;
   if (num_heads % pool->num_kv_heads != 0) return PA_ESHAPE;
   if (pool->head_dim_k != pool->head_dim_v) return PA_EUNSUPPORTED;
-  if (q_dtype != pool->dtype) return PA_EUNSUPPORTED;
+  if (!query_type_ok(pool, q_dtype)) return PA_EUNSUPPORTED;
   if (out_dtype != PA_F32 && out_dtype != q_dtype) return PA_EUNSUPPORTED;
   const int group = num_heads / pool->num_kv_heads;
-  if (!rows_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group)) return PA_EUNSUPPORTED;
-  if (!isfinite(scale) || !(scale > 0.f)) return PA_EINVAL;
+  const bool fp8 = pool->dtype == PA_FP8_E4M3;
+  if (fp8 ? !decode_mfma_supported(q_dtype, pool->head_dim_k, pool->head_dim_v, group, pool->block_size)
+          : !rows_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group))
+    return PA_EUNSUPPORTED;
+  float scale_log2;
+  if (!folded_scale(pool, scale, scale_log2)) return PA_EINVAL;
   if (partition_size > 0) {
     if (partition_size % pool->block_size != 0) return PA_EINVAL;
     if (max_partitions < 1 || max_logits == nullptr || exp_sums == nullptr || tmp_out == nullptr)
@@ -214,7 +247,8 @@ int pa_decode(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
   a.num_rows = num_seqs;
   a.num_heads = num_heads;
   a.group = group;
-  a.scale_log2 = scale * kLog2e;
+  a.scale_log2 = scale_log2;
+  a.v_scale = pool->v_scale;
   a.causal = 1;
   a.window = sliding_window;
   a.partition_size = partition_size;
@@ -225,7 +259,7 @@ int pa_decode(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
   a.sinks = sinks;
   a.status = status;
   const dim3 grid((unsigned)num_seqs, (unsigned)pool->num_kv_heads, (unsigned)(partition_size > 0 ? max_partitions : 1));
-  st = from_hip(launch_row_kernel(a, pool->dtype, pool->head_dim_k, pool->head_dim_v, grid, s));
+  st = from_hip(launch_row_kernel(a, pool->dtype, q_dtype, pool->head_dim_k, pool->head_dim_v, grid, s));
   if (st != PA_OK || partition_size == 0) return st;
 
   ReduceArgs r = {};
@@ -260,13 +294,21 @@ int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
   if (num_tokens > 0 && (q == nullptr || out == nullptr || num_seqs == 0)) return PA_EINVAL;
   if (causal && num_tokens > 0 && positions == nullptr) return PA_EINVAL;
   if (num_heads % pool->num_kv_heads != 0) return PA_ESHAPE;
-  if (q_dtype != pool->dtype) return PA_EUNSUPPORTED;
+  if (!query_type_ok(pool, q_dtype)) return PA_EUNSUPPORTED;
   if (out_dtype != PA_F32 && out_dtype != q_dtype) return PA_EUNSUPPORTED;
   const int group = num_heads / pool->num_kv_heads;
-  if (!rows_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group) &&
-      !prefill_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group, pool->block_size, pool->num_blocks))
+  if (pool->dtype == PA_FP8_E4M3) {
+    // fp8 pools: one query token per sequence, through the MFMA decode kernel
+    if (max_query_len > 1 ||
+        !decode_mfma_supported(q_dtype, pool->head_dim_k, pool->head_dim_v, group, pool->block_size))
+      return PA_EUNSUPPORTED;
+  } else if (!rows_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group) &&
+             !prefill_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group, pool->block_size,
+                                pool->num_blocks)) {
     return PA_EUNSUPPORTED;
-  if (!isfinite(scale) || !(scale > 0.f)) return PA_EINVAL;
+  }
+  float scale_log2;
+  if (!folded_scale(pool, scale, scale_log2)) return PA_EINVAL;
   if (num_tokens > 0x7fffffffLL || num_seqs > 65535) return PA_EUNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (status != nullptr) {
@@ -308,7 +350,8 @@ int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
   a.num_rows = num_tokens;
   a.num_heads = num_heads;
   a.group = group;
-  a.scale_log2 = scale * kLog2e;
+  a.scale_log2 = scale_log2;
+  a.v_scale = pool->v_scale;
   a.causal = causal ? 1 : 0;
   a.window = sliding_window;
   a.partition_size = 0;
@@ -320,7 +363,7 @@ int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
     // every token through the per-row kernel
     a.single_token_seqs = 0;
     const dim3 grid((unsigned)num_tokens, (unsigned)pool->num_kv_heads, 1);
-    return from_hip(launch_row_kernel(a, pool->dtype, pool->head_dim_k, pool->head_dim_v, grid, s));
+    return from_hip(launch_row_kernel(a, pool->dtype, q_dtype, pool->head_dim_k, pool->head_dim_v, grid, s));
   }
   // sequences with several tokens: tiled MFMA kernel; single tokens: per-row kernel
   PrefillArgs p = {};
@@ -346,7 +389,8 @@ int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
   p.tokens_per_tile = kPrefillRows / group;
   const bool rows_take_singles = rows_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group);
   p.min_q_len = rows_take_singles ? 2 : 1;
-  p.scale_log2 = scale * kLog2e;
+  p.scale_log2 = scale_log2;
+  p.v_scale = pool->v_scale;
   p.causal = causal ? 1 : 0;
   p.window = sliding_window;
   p.sinks = sinks;
@@ -359,7 +403,7 @@ int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
   if (st != PA_OK || !rows_take_singles) return st;
   a.single_token_seqs = 1;
   const dim3 grid((unsigned)num_seqs, (unsigned)pool->num_kv_heads, 1);
-  return from_hip(launch_row_kernel(a, pool->dtype, pool->head_dim_k, pool->head_dim_v, grid, s));
+  return from_hip(launch_row_kernel(a, pool->dtype, q_dtype, pool->head_dim_k, pool->head_dim_v, grid, s));
 }
 
 int pa_merge_states(void* out, float* out_lse, const void* prefix_out, const float* prefix_lse,

@@ -26,6 +26,17 @@
 // are fetched up to 64 at a time with one vector load and broadcast per tile, so
 // no K/V load waits on a table lookup.  Requires a power-of-two block size that is
 // a multiple of 16 (a tile then lies inside one block) and head dims of 128.
+//
+// fp8 (E4M3) pools (F8): a tile's K and V are 2 KB each, brought in by two direct
+// loads of 8 positions x 128 bytes apiece, the 16-byte chunk k of position r stored
+// at chunk slot k ^ ((r >> 1) & 7).  K comes back as two 16-byte reads per lane
+// (position l%16, bytes 32 (l/16) .. +32: the QK reduction runs over head-dim
+// elements in that order, and q is read in the same order); V comes back through
+// 8-bit transpose reads (ds_read_b64_tr_b8), each giving a lane one head-dim element
+// at 4 positions for two d blocks.  Every element is widened exactly to f16 / bf16
+// (the queries' type) by the packed hardware conversion and enters the same MFMAs;
+// the cache's k_scale is folded into the softmax scale and v_scale into the final
+// normalisation, so no per-element scaling is done.
 #pragma once
 
 #include "pa_common.h"
@@ -51,6 +62,27 @@ template <>
 __device__ __forceinline__ f32x4 mfma_16x16x16<F16>(u32x2 a, u32x2 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0, 0,
                                                0);
+}
+
+// Two fp8 (E4M3) values -- bytes 0, 1 of w (HI: bytes 2, 3) -- widened exactly to the
+// queries' 16-bit type, packed low element first.
+template <typename T, bool HI>
+__device__ __forceinline__ uint32_t widen_fp8x2(uint32_t w);
+template <>
+__device__ __forceinline__ uint32_t widen_fp8x2<BF16, false>(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+}
+template <>
+__device__ __forceinline__ uint32_t widen_fp8x2<BF16, true>(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+}
+template <>
+__device__ __forceinline__ uint32_t widen_fp8x2<F16, false>(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+}
+template <>
+__device__ __forceinline__ uint32_t widen_fp8x2<F16, true>(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
 }
 
 // Which sequence and which visible range a row workgroup covers (partition `part`
@@ -104,13 +136,15 @@ __device__ __forceinline__ bool decode_row_range(const RowsArgs& a, int row, int
 // partition]); its waves take the range's tiles round-robin and merge their states
 // through LDS at the end.  WP = true (split, one wave): the wave answers one (row,
 // kv head, partition) alone and writes the partition's state from registers.
-template <typename T, int DK, int NW, bool WP, int NB>
+template <typename T, int DK, int NW, bool WP, int NB, bool F8>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, int block_shift, uint32_t grid_rows) {
   static_assert(!WP || NW == 1, "split mode runs one wave per workgroup");
   static_assert(NB >= 2 && NB <= 4, "2 to 4 tile buffers per wave");
-  constexpr int DV = 128;        // V rows of 256 bytes: 16 lanes x 16 bytes
-  constexpr int KCH = DK / 32;   // 16-byte K chunks per lane
-  constexpr int ND = DV / 16;    // 16-wide d blocks of O^T
+  static_assert(!F8 || DK == 128, "fp8 tiles of 128-byte rows");
+  constexpr int EB = F8 ? 1 : 2;  // bytes per cache element
+  constexpr int DV = 128;         // V rows of 256 bytes (16 lanes x 16 bytes), 128 for fp8
+  constexpr int KCH = DK / 32;    // K operands (8 elements) per lane
+  constexpr int ND = DV / 16;     // 16-wide d blocks of O^T
   // A tile's V arrives by direct global->LDS loads: load ii (0..3) writes
   // positions ii + 4c (c = 0..3) as four contiguous 256-byte rows (1 KB, one
   // 16-byte piece per lane); the loads' blocks are 1 KB + 32 bytes apart, so the
@@ -122,10 +156,11 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
   // (16 positions x one chunk per 16 lanes) touch 16 distinct bank groups.
   constexpr int KROWB = DK * 2;             // bytes of one K row
   constexpr int KPIECES = KROWB / 256;      // 256-byte pieces per row
-  constexpr int KBLK = 1024;                // one load: 4 rows x 256 bytes
-  constexpr int KBUF = 4 * KPIECES * KBLK;  // a tile's K
+  constexpr int KBLK = 1024;                // one load: 4 rows x 256 bytes (fp8: 8 x 128)
   static_assert(KROWB % 256 == 0, "K rows of whole 256-byte pieces");
-  constexpr int kTileLoads = 4 * KPIECES + 4;  // load instructions per tile and wave
+  constexpr int KBUF = F8 ? 2 * KBLK : 4 * KPIECES * KBLK;  // a tile's K
+  constexpr int VBUF8 = 2 * KBLK;                           // a tile's fp8 V
+  constexpr int kTileLoads = F8 ? 4 : 4 * KPIECES + 4;      // load instructions per tile and wave
   struct Merge {
     float m[NW][16];
     float l[NW][16];
@@ -134,7 +169,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
   __shared__ float true_max[NW][16];
   struct Tiles {
     char k[NW][NB][KBUF];
-    char v[NW][NB][VBUF];
+    char v[NW][NB][F8 ? VBUF8 : VBUF];
   };
   __shared__ __align__(16) union {
     Tiles t;
@@ -177,18 +212,22 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
   const int c = lane >> 4, r16 = lane & 15;
   const int G = a.group, hkv = a.num_kv_heads, b = a.block_size;
   const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks;
-  const char* kbase = static_cast<const char*>(a.k_pool) + (int64_t)g * DK * 2;
-  const char* vbase = static_cast<const char*>(a.v_pool) + (int64_t)g * DV * 2;
-  const int64_t krow = (int64_t)hkv * DK * 2, vrow = (int64_t)hkv * DV * 2;
+  const char* kbase = static_cast<const char*>(a.k_pool) + (int64_t)g * DK * EB;
+  const char* vbase = static_cast<const char*>(a.v_pool) + (int64_t)g * DV * EB;
+  const int64_t krow = (int64_t)hkv * DK * EB, vrow = (int64_t)hkv * DV * EB;
   const int tr_r = r16 >> 2, tr_q = r16 & 3;
 
-  // q heads of the group as the B operand of S^T = K Q^T
+  // q heads of the group as the B operand of S^T = K Q^T: operand u of lane group c
+  // holds head-dim elements 8 (4u + c) .. +8 (fp8: 32c + 8u .. +8, the order in
+  // which the K reads below deliver them)
   u32x4 qb[KCH];
   {
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (q_row * a.num_heads + g * G + r16) * DK;
 #pragma unroll
-    for (int u = 0; u < KCH; ++u)
-      qb[u] = r16 < G ? *reinterpret_cast<const u32x4*>(qrow + (4 * u + c) * 8) : u32x4{0u, 0u, 0u, 0u};
+    for (int u = 0; u < KCH; ++u) {
+      const int e0 = F8 ? 32 * c + 8 * u : (4 * u + c) * 8;
+      qb[u] = r16 < G ? *reinterpret_cast<const u32x4*>(qrow + e0) : u32x4{0u, 0u, 0u, 0u};
+    }
     // take the q loads' wait here, before any K/V load is in flight; otherwise the
     // compiler guards the loop's first use of qb with a full vmcnt(0) every tile
 #pragma unroll
@@ -210,7 +249,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
     l = sum_over_groups(l);
     if (r16 < G) {
       const int64_t pi = ((int64_t)s * a.num_heads + g * G + r16) * a.max_partitions + p;
-      const float inv = l > 0.f ? 1.0f / l : 0.f;
+      const float inv = l > 0.f ? a.v_scale / l : 0.f;
       float* dst = a.tmp_out + pi * DV + 4 * c;
 #pragma unroll
       for (int nd = 0; nd < ND; ++nd) *reinterpret_cast<f32x4*>(dst + 16 * nd) = o[nd] * inv;
@@ -224,6 +263,23 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
   const int my_first = (lo >> 4) + wave;  // this wave's tiles: my_first + NW * i, i < my_tiles
   const int last = (hi - 1) >> 4;
   const int my_tiles = (lo < hi && last >= my_first) ? (last - my_first) / NW + 1 : 0;
+
+  // fp8 tiles, lane constants: the LDS offsets of this lane's two K chunks (2c and
+  // 2c + 1 of position r16) and of the rows it names for the four V transpose reads
+  // (position 4c + (r16 / 2) % 4, d bytes 16 nd + 64 (r16 / 8) + 8 (r16 % 2) .. +8;
+  // a transpose read then hands lane r16 the elements d = 16 nd + r16 (bytes 0..3)
+  // and d = 16 (nd + 4) + r16 (bytes 4..7) of positions 4c .. 4c + 3).
+  uint32_t k8_off[2] = {0u, 0u}, v8_off[4] = {0u, 0u, 0u, 0u};
+  if constexpr (F8) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      k8_off[h] = (uint32_t)((r16 >> 3) * KBLK + (r16 & 7) * 128 + 16 * ((2 * c + h) ^ ((r16 >> 1) & 7)));
+    const int pos = 4 * c + ((r16 >> 1) & 3);
+#pragma unroll
+    for (int nd = 0; nd < 4; ++nd)
+      v8_off[nd] = (uint32_t)((pos >> 3) * KBLK + (pos & 7) * 128 + 16 * ((nd | 4 * (r16 >> 3)) ^ ((pos >> 1) & 7)) +
+                              8 * (r16 & 1));
+  }
 
   int ids = 0;  // block ids of up to 64 upcoming tiles, one per lane
   auto load_ids = [&](int i0) {
@@ -250,6 +306,22 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
     char* kl = sh.t.k[wave][i % NB];
     char* vl = sh.t.v[wave][i % NB];
     const int lim = n - 1 - t0;  // >= 0: every tile starts inside the sequence
+    if constexpr (F8) {
+      // load ld writes positions 8 ld + lane / 8, 16 bytes per lane: chunk slot
+      // lane % 8 of position r receives the row's chunk (lane % 8) ^ ((r >> 1) & 7)
+      const char* vt8 = vbase + slot0 * vrow;
+#pragma unroll
+      for (int ld = 0; ld < 2; ++ld) {
+        const int r = 8 * ld + (lane >> 3);
+        const int rr = r < lim ? r : lim;
+        const int ch = (lane & 7) ^ ((r >> 1) & 7);
+        __builtin_amdgcn_global_load_lds(kt + rr * krow + ch * 16,
+                                         (__attribute__((address_space(3))) void*)(kl + ld * KBLK), 16, 0, kLoadNT);
+        __builtin_amdgcn_global_load_lds(vt8 + rr * vrow + ch * 16,
+                                         (__attribute__((address_space(3))) void*)(vl + ld * KBLK), 16, 0, kLoadNT);
+      }
+      return;
+    }
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int rr = ii + 4 * c < lim ? ii + 4 * c : lim;
@@ -290,37 +362,68 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
     // direct loads write with a full vmcnt(0) wait, draining tile i + 1's loads.
     const uint32_t kl_a = lds_addr(kl), lb_a = lds_addr(lb);
     u32x4 kc[KCH];
-#pragma unroll
-    for (int u = 0; u < KCH; ++u) {
-      // logical chunk 4u + c of position r16 = 4 * row + block
-      const int kk = 4 * u + c, piece = kk >> 4, chunk = (kk & 15) ^ (4 * tr_r) ^ tr_q;
-      asm volatile("ds_read_b128 %0, %1" : "=v"(kc[u]) : "v"(kl_a + (piece * 4 + tr_q) * KBLK + tr_r * 256 + chunk * 16));
-    }
     u32x2 va[ND];
-    const uint32_t va_a = lb_a + tr_r * VBLK + c * 256 + 4 * tr_q * 2;
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %8\n\t"
-        "ds_read_b64_tr_b16 %1, %8 offset:32\n\t"
-        "ds_read_b64_tr_b16 %2, %8 offset:64\n\t"
-        "ds_read_b64_tr_b16 %3, %8 offset:96\n\t"
-        "ds_read_b64_tr_b16 %4, %8 offset:128\n\t"
-        "ds_read_b64_tr_b16 %5, %8 offset:160\n\t"
-        "ds_read_b64_tr_b16 %6, %8 offset:192\n\t"
-        "ds_read_b64_tr_b16 %7, %8 offset:224"
-        : "=&v"(va[0]), "=&v"(va[1]), "=&v"(va[2]), "=&v"(va[3]), "=&v"(va[4]), "=&v"(va[5]), "=&v"(va[6]),
-          "=&v"(va[7])
-        : "v"(va_a));
-    // the reads of buffer i % NB complete (and their registers are valid) before
-    // tile i + NB's loads may overwrite it
-    static_assert(KCH == 4 && ND == 8, "operand wait below lists 4 K and 8 V registers");
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(kc[0]), "+v"(kc[1]), "+v"(kc[2]), "+v"(kc[3]), "+v"(va[0]), "+v"(va[1]), "+v"(va[2]),
-                   "+v"(va[3]), "+v"(va[4]), "+v"(va[5]), "+v"(va[6]), "+v"(va[7])
-                 :
-                 : "memory");
-    if (i + NB < my_tiles) {
-      if (((i + NB) & 63) == 0) load_ids(i + NB);
-      fetch(i + NB);
+    if constexpr (F8) {
+      u32x4 k8[2];
+      u32x2 v8[4];
+      asm volatile("ds_read_b128 %0, %1" : "=v"(k8[0]) : "v"(kl_a + k8_off[0]));
+      asm volatile("ds_read_b128 %0, %1" : "=v"(k8[1]) : "v"(kl_a + k8_off[1]));
+#pragma unroll
+      for (int nd = 0; nd < 4; ++nd) asm volatile("ds_read_b64_tr_b8 %0, %1" : "=v"(v8[nd]) : "v"(lb_a + v8_off[nd]));
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(k8[0]), "+v"(k8[1]), "+v"(v8[0]), "+v"(v8[1]), "+v"(v8[2]), "+v"(v8[3])
+                   :
+                   : "memory");
+      if (i + NB < my_tiles) {
+        if (((i + NB) & 63) == 0) load_ids(i + NB);
+        fetch(i + NB);
+      }
+      // K operand u = 2h + w: bytes 8w .. 8w + 7 of read h
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int w = 0; w < 2; ++w)
+          kc[2 * h + w] = u32x4{widen_fp8x2<T, false>(k8[h][2 * w]), widen_fp8x2<T, true>(k8[h][2 * w]),
+                                widen_fp8x2<T, false>(k8[h][2 * w + 1]), widen_fp8x2<T, true>(k8[h][2 * w + 1])};
+#pragma unroll
+      for (int nd = 0; nd < 4; ++nd) {
+        va[nd] = u32x2{widen_fp8x2<T, false>(v8[nd][0]), widen_fp8x2<T, true>(v8[nd][0])};
+        va[nd + 4] = u32x2{widen_fp8x2<T, false>(v8[nd][1]), widen_fp8x2<T, true>(v8[nd][1])};
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < KCH; ++u) {
+        // logical chunk 4u + c of position r16 = 4 * row + block
+        const int kk = 4 * u + c, piece = kk >> 4, chunk = (kk & 15) ^ (4 * tr_r) ^ tr_q;
+        asm volatile("ds_read_b128 %0, %1"
+                     : "=v"(kc[u])
+                     : "v"(kl_a + (piece * 4 + tr_q) * KBLK + tr_r * 256 + chunk * 16));
+      }
+      const uint32_t va_a = lb_a + tr_r * VBLK + c * 256 + 4 * tr_q * 2;
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %8\n\t"
+          "ds_read_b64_tr_b16 %1, %8 offset:32\n\t"
+          "ds_read_b64_tr_b16 %2, %8 offset:64\n\t"
+          "ds_read_b64_tr_b16 %3, %8 offset:96\n\t"
+          "ds_read_b64_tr_b16 %4, %8 offset:128\n\t"
+          "ds_read_b64_tr_b16 %5, %8 offset:160\n\t"
+          "ds_read_b64_tr_b16 %6, %8 offset:192\n\t"
+          "ds_read_b64_tr_b16 %7, %8 offset:224"
+          : "=&v"(va[0]), "=&v"(va[1]), "=&v"(va[2]), "=&v"(va[3]), "=&v"(va[4]), "=&v"(va[5]), "=&v"(va[6]),
+            "=&v"(va[7])
+          : "v"(va_a));
+      // the reads of buffer i % NB complete (and their registers are valid) before
+      // tile i + NB's loads may overwrite it
+      static_assert(KCH == 4 && ND == 8, "operand wait below lists 4 K and 8 V registers");
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(kc[0]), "+v"(kc[1]), "+v"(kc[2]), "+v"(kc[3]), "+v"(va[0]), "+v"(va[1]), "+v"(va[2]),
+                     "+v"(va[3]), "+v"(va[4]), "+v"(va[5]), "+v"(va[6]), "+v"(va[7])
+                   :
+                   : "memory");
+      if (i + NB < my_tiles) {
+        if (((i + NB) & 63) == 0) load_ids(i + NB);
+        fetch(i + NB);
+      }
     }
 
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
@@ -417,7 +520,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
         O = fmaf(sh.r.o[w][h][d], f, O);
       }
     }
-    const float out_v = L > 0.f ? O * (1.0f / L) : 0.f;
+    const float out_v = L > 0.f ? O * (a.v_scale / L) : 0.f;
     if (a.partition_size == 0) {
       store_as(a.out, a.out_dtype, (q_row * a.num_heads + hq) * (int64_t)DV + d, out_v);
       if (a.lse != nullptr && d == 0)
@@ -446,22 +549,28 @@ constexpr int kOneWaveBufs = 2;
 // that every CU still gets enough waves.
 constexpr int64_t kOneWaveItems = 8192;
 
+// fp8 tiles are half the bytes: four buffers per wave keep as many bytes in flight
+// (unsplit: 8 waves x 4 x 4 KB = 128 KB of LDS).
+constexpr int kFp8Bufs = 4;
+
 // `grid` is (rows, kv heads, partitions); the kernel takes it flattened.
-template <typename T>
+template <typename T, bool F8>
 hipError_t launch_decode_typed(const RowsArgs& a, int block_shift, int dk, int dv, dim3 grid, hipStream_t stream) {
   if ((int)grid.y != a.num_kv_heads || dk != 128 || dv != 128) return hipErrorInvalidValue;
   const uint32_t rows = grid.x;
   const uint64_t n = (uint64_t)grid.x * grid.y * grid.z;
   if (n > 0xffffffffull) return hipErrorInvalidValue;
+  constexpr int one_bufs = F8 ? kFp8Bufs : kOneWaveBufs, part_bufs = F8 ? kFp8Bufs : kPartBufs,
+                whole_bufs = F8 ? kFp8Bufs : kWholeBufs;
   if (a.partition_size > 0 && (int64_t)n >= kOneWaveItems)
-    hipLaunchKernelGGL((decode_mfma_kernel<T, 128, 1, true, kOneWaveBufs>), dim3((uint32_t)n), dim3(64), 0, stream, a, block_shift,
-                       rows);
+    hipLaunchKernelGGL((decode_mfma_kernel<T, 128, 1, true, one_bufs, F8>), dim3((uint32_t)n), dim3(64), 0, stream, a,
+                       block_shift, rows);
   else if (a.partition_size > 0)
-    hipLaunchKernelGGL((decode_mfma_kernel<T, 128, kPartWaves, false, kPartBufs>), dim3((uint32_t)n), dim3(kPartWaves * 64), 0,
-                       stream, a, block_shift, rows);
+    hipLaunchKernelGGL((decode_mfma_kernel<T, 128, kPartWaves, false, part_bufs, F8>), dim3((uint32_t)n),
+                       dim3(kPartWaves * 64), 0, stream, a, block_shift, rows);
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<T, 128, kWholeWaves, false, kWholeBufs>), dim3((uint32_t)n), dim3(kWholeWaves * 64), 0,
-                       stream, a, block_shift, rows);
+    hipLaunchKernelGGL((decode_mfma_kernel<T, 128, kWholeWaves, false, whole_bufs, F8>), dim3((uint32_t)n),
+                       dim3(kWholeWaves * 64), 0, stream, a, block_shift, rows);
   return hipGetLastError();
 }
 

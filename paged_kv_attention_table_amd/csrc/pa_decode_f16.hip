@@ -4,7 +4,7 @@
 namespace pa {
 
 hipError_t launch_decode_f16(const RowsArgs& a, int block_shift, int dk, int dv, dim3 grid, hipStream_t stream) {
-  return launch_decode_typed<F16>(a, block_shift, dk, dv, grid, stream);
+  return launch_decode_typed<F16, false>(a, block_shift, dk, dv, grid, stream);
 }
 
 }  // namespace pa

@@ -29,7 +29,8 @@ struct RowsArgs {
   int64_t num_rows;  // decode: sequences; varlen: tokens
   int num_heads;
   int group;  // q heads per kv head
-  float scale_log2;
+  float scale_log2;  // softmax scale (with the pool's k_scale folded in) times log2(e)
+  float v_scale;     // the pool's v_scale: multiplies every output (and partition output)
   int causal;
   int window;
   int partition_size;  // 0: whole visible range

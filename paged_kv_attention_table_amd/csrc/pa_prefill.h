@@ -60,7 +60,8 @@ struct PrefillArgs {
   int tokens_per_tile;  // kPrefillRows / group (rounded down)
   int tiles_per_seq;    // ceil(max_query_len / tokens_per_tile)
   int min_q_len;        // sequences with fewer tokens are left to the per-row kernel
-  float scale_log2;
+  float scale_log2;     // softmax scale (with the pool's k_scale folded in) times log2(e)
+  float v_scale;        // the pool's v_scale: multiplies every output
   int causal;
   int window;
   const float* sinks;  // [num_heads] sink logits, nullable
@@ -649,7 +650,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
     const float fz = __builtin_amdgcn_exp2f((zr - mx) * a.scale_log2);
     const float l = fmaf(l_acc[rb][0], fo, fz);
     m_run[rb] = mx;
-    const float inv = l > 0.f ? fo / l : 0.f;
+    const float inv = l > 0.f ? fo * a.v_scale / l : 0.f;
     const int64_t obase = (row_tok[rb] * a.num_heads + row_head[rb]) * (int64_t)DV;
 #pragma unroll
     for (int nd = 0; nd < ND; ++nd) {

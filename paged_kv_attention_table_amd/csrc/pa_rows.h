@@ -256,7 +256,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const RowsArgs a) {
         O = fmaf(red_acc[w][h][d], f, O);
       }
     }
-    const float o = L > 0.f ? O * (1.0f / L) : 0.f;
+    const float o = L > 0.f ? O * (a.v_scale / L) : 0.f;
     if (a.partition_size == 0) {
       store_as(a.out, a.out_dtype, (q_row * a.num_heads + hq) * (int64_t)DV + d, o);
       if (a.lse != nullptr && d == 0)

@@ -11,7 +11,8 @@ query_start_loc, seq_lens, block tables, positions and a slot mapping where
 slot = block_id * block_size + offset.  The "Paged attention for decode in C" page
 (section 2.1) fixes where a position lives: block table[j // b], offset j % b.
 
-Every array is numpy.  bf16 values are carried as uint16 bit patterns.  Slots that
+Every array is numpy.  bf16 values are carried as uint16 bit patterns and fp8
+(E4M3) values as uint8 bit patterns.  Slots that
 no sequence may read (unused blocks, the tail of each last block, the padding block
 that pads short table rows, and the slots of tokens that are still to be written)
 hold NaN, so a stray read shows up in the output.
@@ -25,8 +26,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
-NAN_BITS = {"f16": np.uint16(0x7E00), "bf16": np.uint16(0x7FC0)}
+STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "fp8_e4m3": np.uint8}
+NAN_BITS = {"f16": np.uint16(0x7E00), "bf16": np.uint16(0x7FC0), "fp8_e4m3": np.uint8(0x7F)}
 
 _CHUNK = 1 << 22
 
@@ -98,6 +99,13 @@ class Paged:
     max_partitions: int = 0
     seed: int = 0
     meta: dict = field(default_factory=dict)
+    q_dtype: str = ""     # the queries' storage type when it differs from the pools' (fp8 pools)
+    k_scale: float = 1.0  # the pools' per-tensor scales: element = stored value * scale
+    v_scale: float = 1.0
+
+    @property
+    def query_dtype(self):
+        return self.q_dtype or self.dtype
 
     @property
     def num_seqs(self):
@@ -452,3 +460,47 @@ def merge_case(seed, num_tokens, num_heads, head_dim, special_fraction=0.05):
     pl[special & (kinds == 4)] = inf
     sl[special & (kinds == 4)] = inf
     return po, pl, so, sl, special
+
+
+# ---------------------------------------------------------------------------------
+# fp8 (E4M3) caches
+# ---------------------------------------------------------------------------------
+
+def widen_storage(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Storage bits -> float32 values (numpy / torch conversions)."""
+    if dtype == "f32":
+        return np.asarray(a, dtype=np.float32)
+    if dtype == "f16":
+        return np.asarray(a).astype(np.float32)
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).float().numpy()
+
+
+def quantize_e4m3(values_f32: np.ndarray, scale: float) -> np.ndarray:
+    """values / scale rounded to E4M3 bits by torch's float8_e4m3fn conversion (NaN
+    stays NaN)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(values_f32, dtype=np.float32) / np.float32(scale))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def to_fp8(w: Paged, k_scale: float = 1.0 / 16, v_scale: float = 1.0 / 32, q_dtype: str | None = None) -> Paged:
+    """The same workload over an fp8 (E4M3) cache with per-tensor scales: every K / V
+    value (pools and new tokens, NaN poison included) is divided by its scale and
+    rounded to E4M3, so a stored element times the scale approximates the original
+    N(0, 1) value; the queries keep their values in q_dtype (the workload's f16 or
+    bf16 by default)."""
+    q_dtype = q_dtype or w.dtype
+    assert q_dtype in ("f16", "bf16")
+    q = w.q if q_dtype == w.dtype else _round_to(widen_storage(w.q, w.dtype), q_dtype)
+    fp8 = lambda a, sc: quantize_e4m3(widen_storage(a, w.dtype), sc)  # noqa: E731
+    return Paged(name=w.name + "-fp8", kind=w.kind, dtype="fp8_e4m3", block_size=w.block_size,
+                 num_heads=w.num_heads, num_kv_heads=w.num_kv_heads, dk=w.dk, dv=w.dv,
+                 k_pool=fp8(w.k_pool, k_scale), v_pool=fp8(w.v_pool, v_scale), q=q,
+                 query_start_loc=w.query_start_loc, seq_lens=w.seq_lens, positions=w.positions,
+                 block_tables=w.block_tables, k_new=fp8(w.k_new, k_scale), v_new=fp8(w.v_new, v_scale),
+                 slot_mapping=w.slot_mapping, scale=w.scale, causal=w.causal, sliding_window=w.sliding_window,
+                 partition_size=w.partition_size, max_partitions=w.max_partitions, seed=w.seed, meta=dict(w.meta),
+                 q_dtype=q_dtype, k_scale=float(k_scale), v_scale=float(v_scale))

@@ -12,8 +12,8 @@ import torch
 
 from paged_kv_attention_table_amd import workloads as W
 
-TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3}
-TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3, "fp8_e4m3": 2e-3}
+TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "fp8_e4m3": torch.float8_e4m3fn}
 
 
 def threads():
@@ -21,18 +21,22 @@ def threads():
 
 
 def dev(a, dtype=None):
-    """numpy -> cuda tensor; bf16 arrays are uint16 bit patterns."""
+    """numpy -> cuda tensor; bf16 arrays are uint16 and fp8 arrays uint8 bit patterns."""
     a = np.ascontiguousarray(a)
     if dtype == "bf16":
         return torch.from_numpy(a.view(np.int16)).to("cuda").view(torch.bfloat16)
+    if dtype == "fp8_e4m3":
+        return torch.from_numpy(a.view(np.uint8)).to("cuda").view(torch.float8_e4m3fn)
     return torch.from_numpy(a).to("cuda")
 
 
 def host(t, dtype=None):
-    """cuda tensor -> numpy (bf16 as uint16 bits)."""
+    """cuda tensor -> numpy (bf16 as uint16 bits, fp8 as uint8 bits)."""
     t = t.detach().cpu()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
     return t.numpy()
 
 
@@ -83,7 +87,7 @@ class OnDevice:
         self.w = w
         self.k_pool = dev(w.k_pool, w.dtype)
         self.v_pool = dev(w.v_pool, w.dtype)
-        self.q = dev(w.q, w.dtype)
+        self.q = dev(w.q, w.query_dtype)
         self.qsl = dev(w.query_start_loc)
         self.seq_lens = dev(w.seq_lens)
         self.positions = dev(w.positions)

@@ -38,10 +38,10 @@ def test_strerror_texts():
 
 def _pool(**kw):
     d = dict(k=0x1000, v=0x2000, num_blocks=4, block_size=16, num_kv_heads=2, head_dim_k=64, head_dim_v=64,
-             dtype=binding.PA_F16)
+             dtype=binding.PA_F16, k_scale=1.0, v_scale=1.0)
     d.update(kw)
     return binding.PaKvPool(d["k"], d["v"], d["num_blocks"], d["block_size"], d["num_kv_heads"], d["head_dim_k"],
-                            d["head_dim_v"], d["dtype"])
+                            d["head_dim_v"], d["dtype"], d["k_scale"], d["v_scale"])
 
 
 FAKE = ctypes.c_void_p(0x3000)  # never dereferenced: every case below fails before any launch
@@ -147,3 +147,64 @@ def test_binding_refuses_host_tensors():
     t = torch.zeros(2, 2, 2, 2)
     with pytest.raises(TypeError):
         binding.make_pool(t, t)
+
+
+def _decode(pool, q_dtype=binding.PA_BF16, out_dtype=binding.PA_F32, H=4, scale=0.1):
+    return binding.load().pa_decode(ctypes.byref(pool), FAKE, q_dtype, FAKE, out_dtype, FAKE, 4, FAKE, 2, H, scale,
+                                    0, 0, 0, None, None, None, None, None, None)
+
+
+def _varlen(pool, q_dtype=binding.PA_BF16, max_query_len=1, scale=0.1):
+    return binding.load().pa_varlen(ctypes.byref(pool), FAKE, q_dtype, FAKE, binding.PA_F32, None, FAKE, FAKE, FAKE,
+                                    FAKE, 4, 2, 10, max_query_len, 4, scale, 1, 0, None, None, None)
+
+
+FP8 = dict(dtype=binding.PA_FP8_E4M3, head_dim_k=128, head_dim_v=128)
+
+
+@pytest.mark.parametrize("change,q_dtype,out_dtype,H", [
+    ({}, binding.PA_F32, binding.PA_F32, 4),                       # fp8 pools take f16 / bf16 queries
+    ({}, binding.PA_FP8_E4M3, binding.PA_F32, 4),                  # ... never fp8 ones
+    ({}, binding.PA_BF16, binding.PA_F16, 4),                      # out: f32 or the queries' type
+    (dict(head_dim_k=64, head_dim_v=64), binding.PA_BF16, binding.PA_F32, 4),   # head dims 128 only
+    (dict(block_size=8), binding.PA_BF16, binding.PA_F32, 4),      # power-of-two blocks of >= 16
+    (dict(block_size=48), binding.PA_F16, binding.PA_F32, 4),
+    ({}, binding.PA_BF16, binding.PA_F32, 2 * 17),                 # at most 16 q heads per kv head
+])
+def test_fp8_decode_unsupported(change, q_dtype, out_dtype, H):
+    assert _decode(_pool(**{**FP8, **change}), q_dtype, out_dtype, H) == binding.PA_EUNSUPPORTED
+
+
+def test_fp8_varlen_and_value_types():
+    # varlen over an fp8 pool: one query token per sequence only
+    assert _varlen(_pool(**FP8), max_query_len=2) == binding.PA_EUNSUPPORTED
+    assert _varlen(_pool(**FP8), q_dtype=binding.PA_F32) == binding.PA_EUNSUPPORTED
+    # a non-fp8 pool still wants queries of its own type
+    assert _decode(_pool(dtype=binding.PA_BF16), q_dtype=binding.PA_F16) == binding.PA_EUNSUPPORTED
+    lib = binding.load()
+    # merged states and gathered latent rows are value types, never fp8
+    assert lib.pa_merge_states(FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 2, 8, -1, binding.PA_FP8_E4M3,
+                               None) == binding.PA_EUNSUPPORTED
+    ok = [FAKE, binding.PA_BF16, 8, 16, 64, 16 * 64, 64, FAKE, binding.PA_BF16, 64, FAKE, 4, FAKE, FAKE, None, 2, 10,
+          None, None]
+    for idx in (1, 8):
+        a = list(ok)
+        a[idx] = binding.PA_FP8_E4M3
+        assert lib.pa_gather_cache(*a) == binding.PA_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("bad", [0.0, -2.0, float("inf"), float("nan")])
+@pytest.mark.parametrize("which", ["k_scale", "v_scale"])
+def test_pool_scales_must_be_positive_and_finite(bad, which):
+    for pool in (_pool(**{which: bad}), _pool(**FP8, **{which: bad})):
+        q = binding.PA_F16 if pool.dtype == binding.PA_F16 else binding.PA_BF16
+        assert _decode(pool, q_dtype=q) == binding.PA_EINVAL
+        assert _varlen(pool, q_dtype=q) == binding.PA_EINVAL
+        assert binding.load().pa_write_kv(ctypes.byref(pool), FAKE, FAKE, FAKE, 3, None, None) == binding.PA_EINVAL
+
+
+def test_folded_scale_must_stay_finite():
+    # scale * k_scale overflows / underflows binary32
+    assert _decode(_pool(**FP8, k_scale=1e30), scale=1e30) == binding.PA_EINVAL
+    assert _decode(_pool(**FP8, k_scale=1e-30), scale=1e-30) == binding.PA_EINVAL
+    assert _varlen(_pool(**FP8, k_scale=1e30), scale=1e30) == binding.PA_EINVAL
