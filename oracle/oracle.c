@@ -26,6 +26,12 @@
  *     in natural log.  MergeAttnStates: the merge and its two edge cases.
  *     GatherMlaCache: the gather of a paged latent cache into contiguous rows.
  *   - "ManagedPagedAttention.cs", ForwardWithSinks: attention sinks.
+ *   - "paged_attention_v2_pytorch.py", phase 1 (Alibi): a per-head slope times the
+ *     key's position is added to each score.  Here the position is counted from the
+ *     row's last visible position, end - 1 (slope * (j - (end - 1))): per row this
+ *     differs from the page's slope * j by a constant, so every softmax weight and
+ *     output is the page's, while lse and partition maxima are the page's minus
+ *     slope * (end - 1).
  *   - "paged_attention_v2_pytorch.py", phase 1 (the batched KV gather): the cache's
  *     k_scale / v_scale multiply every gathered K / V element.  "Paged attention for
  *     decode in C", the table of extensions: fp8 KV caches, read here as the OCP
@@ -205,22 +211,23 @@ int orc_gather(const void* pool, int dtype, int64_t num_blocks, int block_size, 
 /* ------------------------------------------------------------------------- */
 
 /* One query q[dk] against keys K[j * dk + d] and values V[j * dv + d] for the
- * visible positions lo <= j < hi.  Pass 1 forms each score scale * <q, k_j> and the
- * maximum m; pass 2 forms e_j = exp(s_j - m), l = sum e_j and a = sum e_j v_j.  The
+ * visible positions lo <= j < hi.  Pass 1 forms each score scale * <q, k_j> plus the
+ * ALiBi term slope * (j - ref) (slope 0: none) and the maximum m; pass 2 forms
+ * e_j = exp(s_j - m), l = sum e_j and a = sum e_j v_j.  The
  * output is a * (1 / l).  An attention sink ("ManagedPagedAttention.cs",
  * ForwardWithSinks) is one more position with score `sink` and a zero value: it
  * enters the maximum and the exp-sum, not the numerator (sink = -inf: none).  An
  * empty range without a sink gives a zero output, m = -inf, l = 0; with a sink, a
  * zero output, m = sink, l = 1.  s is scratch of at least hi - lo doubles.        */
 static void attend(const double* q, const double* K, const double* V, int dk, int dv, int64_t lo,
-                   int64_t hi, double scale, double sink, double* s, double* out, double* m_out,
-                   double* l_out) {
+                   int64_t hi, double scale, double sink, double slope, int64_t ref, double* s,
+                   double* out, double* m_out, double* l_out) {
   for (int d = 0; d < dv; ++d) out[d] = 0.0;
   double m = sink;
   for (int64_t j = lo; j < hi; ++j) {
     double dot = 0.0;
     for (int d = 0; d < dk; ++d) dot += q[d] * K[j * dk + d];
-    s[j - lo] = scale * dot;
+    s[j - lo] = scale * dot + slope * (double)(j - ref);
     if (s[j - lo] > m) m = s[j - lo];
   }
   if (m == -INFINITY) { /* nothing visible and no sink */
@@ -256,7 +263,7 @@ int orc_attend_gathered(const double* q, const double* K, const double* V, int64
   double* s = (double*)malloc(sizeof(double) * (size_t)widest);
   for (int64_t r = 0; r < num_rows; ++r) {
     double m, l;
-    attend(q + r * dk, K, V, dk, dv, lo[r], hi[r], scale, -INFINITY, s, out + r * dv, &m, &l);
+    attend(q + r * dk, K, V, dk, dv, lo[r], hi[r], scale, -INFINITY, 0.0, 0, s, out + r * dv, &m, &l);
     lse[r] = lse_of(m, l);
   }
   free(s);
@@ -297,6 +304,7 @@ struct attn_job {
   int sliding_window;
   const uint8_t* row_mask; /* [T * H], nullable: compute every row */
   const double* sinks;     /* [H] sink logits, nullable: none */
+  const double* alibi;     /* [H] ALiBi slopes, nullable: none */
   double* out;             /* [T, H, dv] */
   double* lse;             /* [H, T], nullable */
   /* split-KV outputs (partition_size > 0) */
@@ -358,10 +366,13 @@ static void attn_task(void* ctx, int64_t task) {
       if (!row_wanted(job, t, h)) continue;
       for (int d = 0; d < P->dk; ++d)
         qrow[d] = load_elem(job->q, job->q_dtype, (t * job->num_heads + h) * P->dk + d);
+      /* ALiBi: slope of head h, positions counted from the row's last visible one */
+      const double slope = job->alibi ? job->alibi[h] : 0.0;
+      const int64_t ref = end - 1;
       if (job->partition_size <= 0) {
         double m, l;
         const double sink = job->sinks ? job->sinks[h] : -INFINITY;
-        attend(qrow, K, V, P->dk, P->dv, start, end, job->scale, sink, sc, orow, &m, &l);
+        attend(qrow, K, V, P->dk, P->dv, start, end, job->scale, sink, slope, ref, sc, orow, &m, &l);
         memcpy(job->out + (t * job->num_heads + h) * P->dv, orow, sizeof(double) * (size_t)P->dv);
         if (job->lse) job->lse[(int64_t)h * job->num_tokens + t] = lse_of(m, l);
       } else {
@@ -373,7 +384,7 @@ static void attn_task(void* ctx, int64_t task) {
           if (lo < start) lo = start;
           if (hi > end) hi = end;
           double m, l; /* partition states leave the sink to the reduction */
-          attend(qrow, K, V, P->dk, P->dv, lo, hi, job->scale, -INFINITY, sc, orow, &m, &l);
+          attend(qrow, K, V, P->dk, P->dv, lo, hi, job->scale, -INFINITY, slope, ref, sc, orow, &m, &l);
           int64_t idx = ((int64_t)s * job->num_heads + h) * job->max_partitions + p;
           job->max_logits[idx] = m;
           job->exp_sums[idx] = l;
@@ -429,7 +440,7 @@ int orc_varlen(const void* k_pool, const void* v_pool, int kv_dtype, int64_t num
                const int32_t* seq_lens, const int32_t* positions, const int32_t* block_tables,
                int max_blocks, double scale, int causal, int sliding_window,
                const uint8_t* row_mask, double* out, double* lse, const double* sinks,
-               double k_scale, double v_scale, int num_threads) {
+               const double* alibi_slopes, double k_scale, double v_scale, int num_threads) {
   struct attn_job job;
   memset(&job, 0, sizeof job);
   job.pool.k = k_pool;
@@ -457,6 +468,7 @@ int orc_varlen(const void* k_pool, const void* v_pool, int kv_dtype, int64_t num
   job.sliding_window = sliding_window;
   job.row_mask = row_mask;
   job.sinks = sinks;
+  job.alibi = alibi_slopes;
   job.out = out;
   job.lse = lse;
   int st = check_job(&job);
@@ -478,8 +490,8 @@ int orc_decode(const void* k_pool, const void* v_pool, int kv_dtype, int64_t num
                int num_heads, const int32_t* block_tables, int max_blocks, const int32_t* seq_lens,
                int num_seqs, double scale, int sliding_window, int partition_size,
                int max_partitions, double* out, double* lse, double* max_logits,
-               double* exp_sums, double* tmp_out, const double* sinks, double k_scale,
-               double v_scale, int num_threads) {
+               double* exp_sums, double* tmp_out, const double* sinks, const double* alibi_slopes,
+               double k_scale, double v_scale, int num_threads) {
   if (num_seqs < 0) return ORC_EINVAL;
   for (int s = 0; s < num_seqs; ++s)
     if (seq_lens[s] < 1) return ORC_EINVAL;
@@ -529,6 +541,7 @@ int orc_decode(const void* k_pool, const void* v_pool, int kv_dtype, int64_t num
   job.exp_sums = exp_sums;
   job.tmp_out = tmp_out;
   job.sinks = sinks;
+  job.alibi = alibi_slopes;
   int st = check_job(&job);
   if (st == ORC_OK) parallel_for((int64_t)num_seqs * num_kv_heads, num_threads, attn_task, &job);
   free(pos);

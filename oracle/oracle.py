@@ -49,7 +49,8 @@ def _storage(a, dtype):
 
 
 def _sinks(sinks, num_heads):
-    """Sink logits as a contiguous float64 [H] array, or None."""
+    """Per-head values (sink logits, ALiBi slopes) as a contiguous float64 [H] array,
+    or None."""
     if sinks is None:
         return None
     a = np.ascontiguousarray(sinks, dtype=np.float64)
@@ -124,10 +125,10 @@ class Oracle:
     # -- varlen ----------------------------------------------------------------------
     def varlen(self, k_pool, v_pool, kv_dtype, q, q_dtype, query_start_loc, seq_lens, positions,
                block_tables, scale, causal, sliding_window, row_mask=None, threads=None,
-               out=None, lse=None, sinks=None, k_scale=1.0, v_scale=1.0):
+               out=None, lse=None, sinks=None, k_scale=1.0, v_scale=1.0, alibi_slopes=None):
         """Returns (status, out [T, H, dv], lse [H, T]).  Rows outside row_mask stay NaN.
         sinks: [H] sink logits (float64) or None.  k_scale / v_scale multiply every
-        stored K / V element."""
+        stored K / V element.  alibi_slopes: [H] ALiBi slopes or None."""
         k_pool = _storage(k_pool, kv_dtype)
         v_pool = _storage(v_pool, kv_dtype)
         nb, b, hkv, dk = k_pool.shape
@@ -149,14 +150,14 @@ class Oracle:
                                  dk, dv, _ptr(q), DTYPE_CODE[q_dtype], H, ctypes.c_int64(T), _ptr(qsl), S,
                                  _ptr(sl), _ptr(pos), _ptr(bt), max_blocks, ctypes.c_double(scale),
                                  int(bool(causal)), int(sliding_window), _ptr(mask), _ptr(out), _ptr(lse),
-                                 _ptr(_sinks(sinks, H)), ctypes.c_double(k_scale), ctypes.c_double(v_scale),
-                                 threads or default_threads())
+                                 _ptr(_sinks(sinks, H)), _ptr(_sinks(alibi_slopes, H)), ctypes.c_double(k_scale),
+                                 ctypes.c_double(v_scale), threads or default_threads())
         return st, out, lse
 
     # -- decode ----------------------------------------------------------------------
     def decode(self, k_pool, v_pool, kv_dtype, q, q_dtype, block_tables, seq_lens, scale,
                sliding_window=0, partition_size=0, max_partitions=0, threads=None, out=None, sinks=None,
-               k_scale=1.0, v_scale=1.0):
+               k_scale=1.0, v_scale=1.0, alibi_slopes=None):
         """Unsplit: (status, out [S, H, dv], lse [H, S]).
         Split (partition_size > 0): (status, max_logits, exp_sums, tmp_out), entries
         past each sequence's partition count NaN."""
@@ -178,8 +179,8 @@ class Oracle:
                                      hkv, dk, dv, _ptr(q), DTYPE_CODE[q_dtype], H, _ptr(bt), max_blocks,
                                      _ptr(sl), S, ctypes.c_double(scale), int(sliding_window),
                                      int(partition_size), int(max_partitions), _ptr(out), _ptr(lse),
-                                     None, None, None, _ptr(_sinks(sinks, H)), ctypes.c_double(k_scale),
-                                     ctypes.c_double(v_scale), thr)
+                                     None, None, None, _ptr(_sinks(sinks, H)), _ptr(_sinks(alibi_slopes, H)),
+                                     ctypes.c_double(k_scale), ctypes.c_double(v_scale), thr)
             return st, out, lse
         ml = np.full((S, H, max_partitions), np.nan, dtype=np.float64)
         es = np.full((S, H, max_partitions), np.nan, dtype=np.float64)
@@ -188,7 +189,8 @@ class Oracle:
                                  dk, dv, _ptr(q), DTYPE_CODE[q_dtype], H, _ptr(bt), max_blocks, _ptr(sl), S,
                                  ctypes.c_double(scale), int(sliding_window), int(partition_size),
                                  int(max_partitions), None, None, _ptr(ml), _ptr(es), _ptr(to),
-                                 _ptr(_sinks(sinks, H)), ctypes.c_double(k_scale), ctypes.c_double(v_scale), thr)
+                                 _ptr(_sinks(sinks, H)), _ptr(_sinks(alibi_slopes, H)), ctypes.c_double(k_scale),
+                                 ctypes.c_double(v_scale), thr)
         return st, ml, es, to
 
     def reduce_partitions(self, max_logits, exp_sums, tmp_out, seq_lens, partition_size, sinks=None):

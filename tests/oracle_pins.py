@@ -24,7 +24,10 @@ oracle disagrees with what the pages or the mathematics fix:
 * fp8 (E4M3) caches: every pattern decodes as torch's float8_e4m3fn, with the
   format's landmarks; a pool with k_scale / v_scale attends like SDPA over the cache
   torch dequantizes ("paged_attention_v2_pytorch.py", phase 1), and the scales obey
-  their closed forms.
+  their closed forms;
+* ALiBi: outputs equal the v2 page's slope * position form computed by torch; the
+  lse is the page's minus slope * (end - 1), the position the bias is counted from
+  here; a one-position window returns the value and score exactly.
 
 The same functions run against deliberately broken builds of the oracle in
 test_oracle_mutants.py, which checks that each planted mistake fails at least one.
@@ -831,13 +834,104 @@ def pin_scale_closed_forms(orc):
             assert st == EINVAL, (kw, st)
 
 
+# --------------------------------------------------------------------------------
+# ALiBi ("paged_attention_v2_pytorch.py", phase 1)
+# --------------------------------------------------------------------------------
+
+def alibi_slopes(H):
+    """The geometric slopes 2^(-8 (h + 1) / H) (the page takes slopes as given)."""
+    return np.array([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)])
+
+
+def page_alibi_reference(q_rows, K, V, lo, hi, scale, group, slopes):
+    """The page's form with torch in float64: scores scale * q.k + slope_h * j (j the
+    key's absolute position), masked to [lo, hi), softmax over keys; lse by
+    torch.logsumexp.  Returns out [R, H, dv], lse [H, R]."""
+    q = torch.from_numpy(np.ascontiguousarray(q_rows, dtype=np.float64))  # [R, H, dk]
+    k = torch.from_numpy(np.ascontiguousarray(K, dtype=np.float64)).repeat_interleave(group, dim=1)
+    v = torch.from_numpy(np.ascontiguousarray(V, dtype=np.float64)).repeat_interleave(group, dim=1)
+    n = K.shape[0]
+    j = torch.arange(n, dtype=torch.float64)
+    scores = torch.einsum("rhd,nhd->rhn", q, k) * scale + torch.from_numpy(slopes)[None, :, None] * j[None, None, :]
+    vis = (j[None, :] >= torch.as_tensor(lo)[:, None]) & (j[None, :] < torch.as_tensor(hi)[:, None])
+    scores = scores.masked_fill(~vis[:, None, :], float("-inf"))
+    out = torch.einsum("rhn,nhd->rhd", torch.softmax(scores, dim=-1), v)
+    return out.numpy(), torch.logsumexp(scores, dim=-1).numpy().T
+
+
+def pin_alibi_matches_the_pages_bias(orc):
+    """Decode (unsplit and split), varlen causal and not, windows, GQA 4:1: every
+    output equals the page's form; lse equals the page's minus slope * (end - 1)."""
+    rng = np.random.default_rng(47)
+    H, Hkv = 8, 2
+    slopes = alibi_slopes(H)
+    case = Case(rng, [1, 40, 150], H=H, Hkv=Hkv, dk=16, dv=24, dtype="f32", b=8)
+    q = stored(rng.standard_normal((3, H, 16)), "f32")
+    for window in (0, 30):
+        st, out, lse = orc.decode(case.k_pool, case.v_pool, "f32", q, "f32", case.tables, case.lengths, 0.3,
+                                  sliding_window=window, alibi_slopes=slopes)
+        assert st == 0
+        st, ml, es, to = orc.decode(case.k_pool, case.v_pool, "f32", q, "f32", case.tables, case.lengths, 0.3,
+                                    sliding_window=window, partition_size=16, max_partitions=10,
+                                    alibi_slopes=slopes)
+        assert st == 0
+        red = orc.reduce_partitions(ml, es, to, case.lengths, 16)
+        for s_, n in enumerate(case.lengths):
+            lo, hi = _ranges(np.array([n - 1]), n, True, window)
+            ref, rlse = page_alibi_reference(widen(q[s_:s_ + 1], "f32"), widen(case.K[s_], "f32"),
+                                             widen(case.V[s_], "f32"), lo, hi, 0.3, H // Hkv, slopes)
+            np.testing.assert_allclose(out[s_], ref[0], atol=1e-12, rtol=1e-12)
+            np.testing.assert_allclose(red[s_], ref[0], atol=1e-12, rtol=1e-12)
+            np.testing.assert_allclose(lse[:, s_], rlse[:, 0] - slopes * (n - 1), atol=1e-11, rtol=1e-12)
+    segments = [(0, 7), (30, 1), (100, 12)]
+    lengths = [c + k for c, k in segments]
+    case = Case(rng, lengths, H=H, Hkv=Hkv, dk=16, dv=16, dtype="f32", b=4)
+    for causal, window in ((True, 0), (True, 9), (False, 0), (False, 20)):
+        qv, qsl, positions = _varlen_segments(rng, case, segments, causal, window)
+        st, out, lse = orc.varlen(case.k_pool, case.v_pool, "f32", qv, "f32", qsl, lengths,
+                                  positions if causal else None, case.tables, 0.25, causal, window,
+                                  alibi_slopes=slopes)
+        assert st == 0
+        for s_, n in enumerate(lengths):
+            t0, t1 = qsl[s_], qsl[s_ + 1]
+            lo, hi = _ranges(positions[t0:t1], n, causal, window)
+            ref, rlse = page_alibi_reference(widen(qv[t0:t1], "f32"), widen(case.K[s_], "f32"),
+                                             widen(case.V[s_], "f32"), lo, hi, 0.25, H // Hkv, slopes)
+            np.testing.assert_allclose(out[t0:t1], ref, atol=1e-12, rtol=1e-12)
+            np.testing.assert_allclose(lse[:, t0:t1], rlse - slopes[:, None] * (hi - 1)[None, :], atol=1e-11,
+                                       rtol=1e-12)
+
+
+def pin_alibi_closed_forms(orc):
+    """A window of one position sees only the row's last position, whose ALiBi term
+    is zero: out = v exactly and lse = scale * q.k exactly, whatever the slopes.
+    Zero slopes change no bit."""
+    rng = np.random.default_rng(53)
+    case = Case(rng, [23, 40], H=4, Hkv=2, dk=16, dv=16, dtype="f32", b=4)
+    q = stored(rng.standard_normal((2, 4, 16)), "f32")
+    slopes = np.array([0.5, 1.5, 0.03125, 3.0])
+    st, out, lse = orc.decode(case.k_pool, case.v_pool, "f32", q, "f32", case.tables, case.lengths, 0.25,
+                              sliding_window=1, alibi_slopes=slopes)
+    assert st == 0
+    for s_, n in enumerate(case.lengths):
+        for h in range(4):
+            assert np.array_equal(out[s_, h], case.V[s_][n - 1, h // 2].astype(np.float64))
+            score = 0.25 * float(np.dot(q[s_, h].astype(np.float64), case.K[s_][n - 1, h // 2].astype(np.float64)))
+            assert abs(lse[h, s_] - score) <= 1e-14 * max(1.0, abs(score)), (lse[h, s_], score)
+    st, base, blse = orc.decode(case.k_pool, case.v_pool, "f32", q, "f32", case.tables, case.lengths, 0.25)
+    st, out, lse = orc.decode(case.k_pool, case.v_pool, "f32", q, "f32", case.tables, case.lengths, 0.25,
+                              alibi_slopes=np.zeros(4))
+    assert np.array_equal(out, base) and np.array_equal(lse, blse)
+
+
 PINS = [pin_hand_example, pin_hand_example_per_block, pin_hand_example_written_through_slots,
         pin_decode_matches_dense, pin_varlen_matches_dense, pin_empty_rows, pin_decoders,
         pin_permutation_invariance, pin_closed_forms, pin_partitions_reduce_to_unsplit,
         pin_merge_halves_equal_whole, pin_merge_edge_rules, pin_invariance, pin_write_kv_round_trip,
         pin_rejections, pin_sink_is_a_zero_value_position, pin_sink_closed_forms, pin_encoders,
         pin_gather_returns_logical_rows, pin_gather_rejections, pin_e4m3_decoder,
-        pin_fp8_pool_is_the_dequantized_cache, pin_scale_closed_forms]
+        pin_fp8_pool_is_the_dequantized_cache, pin_scale_closed_forms, pin_alibi_matches_the_pages_bias,
+        pin_alibi_closed_forms]
 
 
 def run_all(path):

@@ -84,6 +84,17 @@ MUTANTS = {
     "k_scale_on_v": ("gather_head(P->v, P->dtype, P->v_scale", "gather_head(P->v, P->dtype, P->k_scale"),
     "v_scale_dropped": ("gather_head(P->v, P->dtype, P->v_scale", "gather_head(P->v, P->dtype, 1.0"),
     "scale_divides": ("load_elem(pool, dtype, base + d) * scale;", "load_elem(pool, dtype, base + d) / scale;"),
+    # ALiBi (v2 page, phase 1), counted from the row's last visible position
+    "alibi_sign": ("s[j - lo] = scale * dot + slope * (double)(j - ref);",
+                   "s[j - lo] = scale * dot - slope * (double)(j - ref);"),
+    "alibi_absolute_position": ("s[j - lo] = scale * dot + slope * (double)(j - ref);",
+                                "s[j - lo] = scale * dot + slope * (double)j;"),
+    "alibi_ref_is_end": ("const int64_t ref = end - 1;", "const int64_t ref = end;"),
+    "alibi_slope_of_kv_head": ("const double slope = job->alibi ? job->alibi[h] : 0.0;",
+                               "const double slope = job->alibi ? job->alibi[g] : 0.0;"),
+    "alibi_partition_relative": (
+        "attend(qrow, K, V, P->dk, P->dv, lo, hi, job->scale, -INFINITY, slope, ref, sc, orow, &m, &l);",
+        "attend(qrow, K, V, P->dk, P->dv, lo, hi, job->scale, -INFINITY, slope, hi - 1, sc, orow, &m, &l);"),
     "scales_unchecked": ("  if (!isfinite(P->k_scale) || !(P->k_scale > 0.0) || !isfinite(P->v_scale) || !(P->v_scale > 0.0))\n    return ORC_EINVAL;\n", ""),
 }
 
