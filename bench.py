@@ -26,8 +26,8 @@ sample of the same workload on the host cores.  --copy-calibration appends, afte
 the timed region, three launches of a 1 GiB elementwise copy (torch.neg) that the
 counter runs use as the known-size reference.  --sweep (decode workloads) adds, after
 the timed region, each partition size in {0, 512, 1024}, the cost of device
-validation and that of per-head attention sinks, each as the median of 20 calls with
-the caches flushed between calls.
+validation, that of per-head attention sinks and that of ALiBi slopes, each as the
+median of 20 calls with the caches flushed between calls.
 """
 from __future__ import annotations
 
@@ -384,10 +384,10 @@ def main():
 
     ws = workspace(P)
 
-    def decode(p=P, buf=ws, status=None, sinks=None):
+    def decode(p=P, buf=ws, status=None, sinks=None, alibi=None):
         pa_decode(kp, vp, q, out, tables, lens, w.scale, sliding_window=w.sliding_window, partition_size=p,
                   max_logits=buf[0], exp_sums=buf[1], tmp_out=buf[2], status=status, sinks=sinks,
-                  k_scale=w.k_scale, v_scale=w.v_scale)
+                  k_scale=w.k_scale, v_scale=w.v_scale, alibi_slopes=alibi)
 
     def write():
         pa_write_kv(kp, vp, k_new, v_new, slots)
@@ -438,8 +438,11 @@ def main():
         # attention sinks (one logit per q head) on the bench's own partition size
         sinks = torch.linspace(-2.0, 2.0, w.num_heads, device="cuda")
         _, med_sinks = time_calls(lambda: decode(sinks=sinks), 20, flush=flush)
+        # ALiBi with the geometric slopes 2^(-8 (h + 1) / H)
+        slopes = torch.tensor([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=torch.float32, device="cuda")
+        _, med_alibi = time_calls(lambda: decode(alibi=slopes), 20, flush=flush)
         line["sweep"] = {"cold_gbs_by_partition_size": sweep, "validation_ms": round(med_status - med_plain, 5),
-                         "sinks_ms": round(med_sinks - med_plain, 5)}
+                         "sinks_ms": round(med_sinks - med_plain, 5), "alibi_ms": round(med_alibi - med_plain, 5)}
     if args.copy_calibration:
         copy_calibration()
     if not args.no_cpu_baseline:

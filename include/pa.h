@@ -121,6 +121,12 @@ int pa_write_kv(const pa_kv_pool* pool, const void* k_new, const void* v_new,
  * score sinks[h] and value zero, which takes probability mass and adds nothing to
  * the output; -inf means no sink.  With partitions the workspaces stay sink-free and
  * the sink joins in the combining step.
+ * alibi_slopes [num_heads] float32 (device, nullable): ALiBi ("paged_attention_v2_pytorch.py",
+ * phase 1): head h's score for position j gains slopes[h] * (j - (end - 1)), end - 1
+ * being the query's position.  Per row this differs from the page's slopes[h] * j by
+ * a constant, so outputs are the page's; max_logits (and lse, in pa_varlen) are the
+ * page's minus slopes[h] * (end - 1), which keeps them exact at long contexts.
+ * Slopes must be finite.  A sink logit competes with these biased scores.
  * Supported: head_dim_k == head_dim_v in {32, 64, 128, 256}; num_heads /
  * num_kv_heads <= 16; any block_size.  PA_FP8_E4M3 pools: q_dtype PA_F16 or PA_BF16,
  * head dims 128, block_size a power of two >= 16. */
@@ -128,7 +134,8 @@ int pa_decode(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
               const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
               int32_t num_seqs, int32_t num_heads, float scale, int32_t sliding_window,
               int32_t partition_size, int32_t max_partitions, float* max_logits, float* exp_sums,
-              float* tmp_out, const float* sinks, int32_t* status, void* stream);
+              float* tmp_out, const float* sinks, const float* alibi_slopes, int32_t* status,
+              void* stream);
 
 /* Variable-length attention over many sequences in one call (TensorSharp page,
  * Forward; "cpu_mla_prefill.cpp", MlaPrefillAttention): prefill chunks and single
@@ -148,6 +155,9 @@ int pa_decode(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
  * for pa_decode (TensorSharp page, ForwardWithSinks).  The lse then includes the
  * sink's mass (a row that sees nothing gets out = 0 and lse = sinks[h]); when
  * states of several calls are merged, give the sinks to one of them only.
+ * alibi_slopes [num_heads] float32 (device, nullable): ALiBi as for pa_decode, the
+ * bias counted from each row's last visible position end - 1 (the token's position
+ * when causal, seq_len - 1 otherwise).
  * Supported: (head_dim_k, head_dim_v) in {(32,32), (64,64), (128,128), (256,256),
  * (192,128)}; num_heads / num_kv_heads <= 16; any block_size.  PA_FP8_E4M3 pools: as
  * for pa_decode, and only calls whose sequences hold at most one query token each
@@ -156,8 +166,8 @@ int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
               float* lse, const int32_t* query_start_loc, const int32_t* seq_lens,
               const int32_t* positions, const int32_t* block_tables, int32_t max_blocks,
               int32_t num_seqs, int64_t num_tokens, int32_t max_query_len, int32_t num_heads,
-              float scale, int32_t causal, int32_t sliding_window, const float* sinks, int32_t* status,
-              void* stream);
+              float scale, int32_t causal, int32_t sliding_window, const float* sinks,
+              const float* alibi_slopes, int32_t* status, void* stream);
 
 /* Merge two attention states over disjoint key sets ("cpu_mla_prefill.cpp",
  * MergeAttnStates).  prefix_out, suffix_out, out: [num_tokens, num_heads, head_dim] in

@@ -57,10 +57,10 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.pa_write_kv.argtypes = [pool_p, vp, vp, vp, i64, vp, vp]
     lib.pa_decode.restype = ctypes.c_int
     lib.pa_decode.argtypes = [pool_p, vp, i32, vp, i32, vp, i32, vp, i32, i32, f32, i32, i32, i32, vp, vp, vp,
-                              vp, vp, vp]
+                              vp, vp, vp, vp]
     lib.pa_varlen.restype = ctypes.c_int
     lib.pa_varlen.argtypes = [pool_p, vp, i32, vp, i32, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, f32, i32, i32,
-                              vp, vp, vp]
+                              vp, vp, vp, vp]
     lib.pa_merge_states.restype = ctypes.c_int
     lib.pa_merge_states.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i64, i32, vp]
     lib.pa_gather_cache.restype = ctypes.c_int
@@ -152,10 +152,10 @@ def pa_write_kv(k_pool, v_pool, k_new, v_new, slot_mapping, status=None, stream=
 
 def pa_decode(k_pool, v_pool, q, out, block_tables, seq_lens, scale, sliding_window=0, partition_size=0,
               max_logits=None, exp_sums=None, tmp_out=None, status=None, stream=None, sinks=None, k_scale=1.0,
-              v_scale=1.0):
+              v_scale=1.0, alibi_slopes=None):
     """One decode step; q [S, H, D] (the pools' dtype; f16 / bf16 over fp8 pools), out
     [S, H, D] (float32 or q's dtype); sinks [H] float32 attention-sink logits or None;
-    k_scale / v_scale: the pools' per-tensor scales."""
+    k_scale / v_scale: the pools' per-tensor scales; alibi_slopes [H] float32 or None."""
     pool = make_pool(k_pool, v_pool, k_scale, v_scale)
     _dev(q, "q", ndim=3)
     _dev(out, "out", ndim=3)
@@ -166,8 +166,10 @@ def pa_decode(k_pool, v_pool, q, out, block_tables, seq_lens, scale, sliding_win
     _dev(tmp_out, "tmp_out", dtype=torch.float32)
     _dev(status, "status", dtype=torch.int32)
     _dev(sinks, "sinks", dtype=torch.float32, ndim=1)
+    _dev(alibi_slopes, "alibi_slopes", dtype=torch.float32, ndim=1)
     S, H, _ = q.shape
     _shape(sinks, (H,), "sinks")
+    _shape(alibi_slopes, (H,), "alibi_slopes")
     _shape(q, (S, H, pool.head_dim_k), "q")
     _shape(out, (S, H, pool.head_dim_v), "out")
     _shape(seq_lens, (S,), "seq_lens")
@@ -184,16 +186,17 @@ def pa_decode(k_pool, v_pool, q, out, block_tables, seq_lens, scale, sliding_win
     st = load().pa_decode(ctypes.byref(pool), _ptr(q), _code(q, "q"), _ptr(out), _code(out, "out"),
                           _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), S, H, float(scale),
                           int(sliding_window), int(partition_size), int(max_partitions), _ptr(max_logits),
-                          _ptr(exp_sums), _ptr(tmp_out), _ptr(sinks), _ptr(status), _stream(stream))
+                          _ptr(exp_sums), _ptr(tmp_out), _ptr(sinks), _ptr(alibi_slopes), _ptr(status),
+                          _stream(stream))
     _check(st, "pa_decode")
 
 
 def pa_varlen(k_pool, v_pool, q, out, query_start_loc, seq_lens, positions, block_tables, max_query_len, scale,
               causal=True, sliding_window=0, lse=None, status=None, stream=None, sinks=None, k_scale=1.0,
-              v_scale=1.0):
+              v_scale=1.0, alibi_slopes=None):
     """Varlen attention; q [T, H, Dk], out [T, H, Dv], lse [H, T] (optional); sinks
     [H] float32 attention-sink logits or None; k_scale / v_scale: the pools'
-    per-tensor scales."""
+    per-tensor scales; alibi_slopes [H] float32 or None."""
     pool = make_pool(k_pool, v_pool, k_scale, v_scale)
     _dev(q, "q", ndim=3)
     _dev(out, "out", ndim=3)
@@ -204,8 +207,10 @@ def pa_varlen(k_pool, v_pool, q, out, query_start_loc, seq_lens, positions, bloc
     _dev(block_tables, "block_tables", dtype=torch.int32, ndim=2)
     _dev(status, "status", dtype=torch.int32)
     _dev(sinks, "sinks", dtype=torch.float32, ndim=1)
+    _dev(alibi_slopes, "alibi_slopes", dtype=torch.float32, ndim=1)
     T, H, _ = q.shape
     _shape(sinks, (H,), "sinks")
+    _shape(alibi_slopes, (H,), "alibi_slopes")
     S = seq_lens.numel()
     _shape(q, (T, H, pool.head_dim_k), "q")
     _shape(out, (T, H, pool.head_dim_v), "out")
@@ -217,7 +222,8 @@ def pa_varlen(k_pool, v_pool, q, out, query_start_loc, seq_lens, positions, bloc
     st = load().pa_varlen(ctypes.byref(pool), _ptr(q), _code(q, "q"), _ptr(out), _code(out, "out"),
                           _ptr(lse), _ptr(query_start_loc), _ptr(seq_lens), _ptr(positions), _ptr(block_tables),
                           block_tables.shape[1], seq_lens.numel(), T, int(max_query_len), H, float(scale),
-                          int(bool(causal)), int(sliding_window), _ptr(sinks), _ptr(status), _stream(stream))
+                          int(bool(causal)), int(sliding_window), _ptr(sinks), _ptr(alibi_slopes), _ptr(status),
+                          _stream(stream))
     _check(st, "pa_varlen")
 
 

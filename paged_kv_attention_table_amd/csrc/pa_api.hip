@@ -186,7 +186,7 @@ int pa_decode(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
               const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens, int32_t num_seqs,
               int32_t num_heads, float scale, int32_t sliding_window, int32_t partition_size,
               int32_t max_partitions, float* max_logits, float* exp_sums, float* tmp_out, const float* sinks,
-              int32_t* status, void* stream) {
+              const float* alibi_slopes, int32_t* status, void* stream) {
   int st = check_pool(pool);
   if (st != PA_OK) return st;
   if (num_seqs < 0 || num_heads < 1 || max_blocks < 1 || partition_size < 0) return PA_EINVAL;
@@ -257,6 +257,7 @@ int pa_decode(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
   a.exp_sums = exp_sums;
   a.tmp_out = tmp_out;
   a.sinks = sinks;
+  a.alibi = alibi_slopes;
   a.status = status;
   const dim3 grid((unsigned)num_seqs, (unsigned)pool->num_kv_heads, (unsigned)(partition_size > 0 ? max_partitions : 1));
   st = from_hip(launch_row_kernel(a, pool->dtype, q_dtype, pool->head_dim_k, pool->head_dim_v, grid, s));
@@ -285,7 +286,7 @@ int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
               const int32_t* query_start_loc, const int32_t* seq_lens, const int32_t* positions,
               const int32_t* block_tables, int32_t max_blocks, int32_t num_seqs, int64_t num_tokens,
               int32_t max_query_len, int32_t num_heads, float scale, int32_t causal, int32_t sliding_window,
-              const float* sinks, int32_t* status, void* stream) {
+              const float* sinks, const float* alibi_slopes, int32_t* status, void* stream) {
   int st = check_pool(pool);
   if (st != PA_OK) return st;
   if (num_seqs < 0 || num_tokens < 0 || num_heads < 1 || max_blocks < 1 || max_query_len < 0) return PA_EINVAL;
@@ -357,6 +358,7 @@ int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
   a.partition_size = 0;
   a.max_partitions = 1;
   a.sinks = sinks;
+  a.alibi = alibi_slopes;
   a.status = status;
 
   if (!prefill_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group, pool->block_size, pool->num_blocks) || max_query_len <= 1) {
@@ -394,6 +396,7 @@ int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
   p.causal = causal ? 1 : 0;
   p.window = sliding_window;
   p.sinks = sinks;
+  p.alibi = alibi_slopes;
   p.status = status;
   p.tiles_per_seq = (max_query_len + p.tokens_per_tile - 1) / p.tokens_per_tile;
   const int64_t groups8 = ((int64_t)num_seqs * pool->num_kv_heads + 7) / 8 * 8;

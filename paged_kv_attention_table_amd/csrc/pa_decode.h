@@ -86,9 +86,10 @@ __device__ __forceinline__ uint32_t widen_fp8x2<F16, true>(uint32_t w) {
 }
 
 // Which sequence and which visible range a row workgroup covers (partition `part`
-// of it in split mode); false: nothing to do.
+// of it in split mode), and the row's last visible position `ref` (whole range, the
+// origin of ALiBi positions); false: nothing to do.
 __device__ __forceinline__ bool decode_row_range(const RowsArgs& a, int row, int part, int& s, int64_t& q_row, int& n,
-                                                 int& lo, int& hi) {
+                                                 int& lo, int& hi, int& ref) {
   q_row = row;
   if (a.query_start_loc == nullptr) {
     s = row;
@@ -123,6 +124,7 @@ __device__ __forceinline__ bool decode_row_range(const RowsArgs& a, int row, int
   if (a.window > 0) start = end - a.window > 0 ? end - a.window : 0;
   lo = start;
   hi = end;
+  ref = end - 1;
   if (a.partition_size > 0) {
     const int p0 = part * a.partition_size;
     if (p0 >= n) return false;
@@ -204,9 +206,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
     const uint64_t hit = __ballot(lane < S && rank == row);
     row = hit ? __builtin_ctzll(hit) : row;
   }
-  int s, n, lo, hi;
+  int s, n, lo, hi, ref;
   int64_t q_row;
-  if (!decode_row_range(a, row, pz, s, q_row, n, lo, hi)) return;  // uniform per workgroup
+  if (!decode_row_range(a, row, pz, s, q_row, n, lo, hi, ref)) return;  // uniform per workgroup
 
 
   const int c = lane >> 4, r16 = lane & 15;
@@ -233,6 +235,14 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
 #pragma unroll
     for (int u = 0; u < KCH; ++u) asm volatile("" ::"v"(qb[u]));
   }
+  // ALiBi ("paged_attention_v2_pytorch.py", phase 1): head r16's slope in raw score
+  // units; position j's score gains slope * (j - ref).  The loop counts positions from
+  // pref, the last one this workgroup covers (ref itself unless split), so that scores
+  // and exp-sums stay exact however far the partition lies from the query; a
+  // partition's maximum then gets slope * (pref - ref) added when it is stored.
+  const bool alibi = a.alibi != nullptr;
+  const float slope_r = (alibi && r16 < G) ? a.alibi[g * G + r16] * (kLog2e / a.scale_log2) : 0.f;
+  const int pref = hi - 1;
   f32x4 o[ND];
   float m_run, m_true, l_run;  // reference max, true max (raw score units), exp-sum share
 #pragma unroll
@@ -254,7 +264,8 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
 #pragma unroll
       for (int nd = 0; nd < ND; ++nd) *reinterpret_cast<f32x4*>(dst + 16 * nd) = o[nd] * inv;
       if (c == 0) {
-        a.max_logits[pi] = l > 0.f ? m_true * a.scale_log2 * kLn2 : -INFINITY;
+        const float m_abs = m_true + slope_r * (float)(pref - ref);  // ALiBi origin back at ref
+        a.max_logits[pi] = l > 0.f ? m_abs * a.scale_log2 * kLn2 : -INFINITY;
         a.exp_sums[pi] = l > 0.f ? l * __builtin_amdgcn_exp2f((m_run - m_true) * a.scale_log2) : 0.f;
       }
     }
@@ -430,6 +441,11 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
 #pragma unroll
     for (int u = 0; u < KCH; ++u) sc = mfma_16x16x32<T>(kc[u], qb[u], sc);
     float sv[4] = {sc[0], sc[1], sc[2], sc[3]};
+    if (alibi) {
+      const float jb = (float)(t0 + 4 * c - pref);  // exact: |j - pref| < 2^24
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) sv[ii] = fmaf(slope_r, jb + (float)ii, sv[ii]);
+    }
     if (t0 < lo || t0 + 16 > hi) {
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
@@ -529,7 +545,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
       const int64_t pi = ((int64_t)s * a.num_heads + hq) * a.max_partitions + pz;
       a.tmp_out[pi * DV + d] = out_v;
       if (d == 0) {
-        a.max_logits[pi] = L > 0.f ? M * a.scale_log2 * kLn2 : -INFINITY;
+        // ALiBi origin back at ref (see the loop)
+        const float off = alibi ? a.alibi[hq] * (kLog2e / a.scale_log2) * (float)(pref - ref) : 0.f;
+        a.max_logits[pi] = L > 0.f ? (M + off) * a.scale_log2 * kLn2 : -INFINITY;
         a.exp_sums[pi] = L;
       }
     }

@@ -39,6 +39,7 @@ struct RowsArgs {
   float* exp_sums;
   float* tmp_out;
   const float* sinks;  // [num_heads] sink logits, nullable; unsplit outputs only
+  const float* alibi;  // [num_heads] ALiBi slopes, nullable
   const int32_t* status;
 };
 

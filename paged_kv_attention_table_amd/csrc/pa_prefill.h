@@ -65,6 +65,7 @@ struct PrefillArgs {
   int causal;
   int window;
   const float* sinks;  // [num_heads] sink logits, nullable
+  const float* alibi;  // [num_heads] ALiBi slopes, nullable
   const int32_t* status;
 };
 
@@ -129,7 +130,9 @@ struct TileRegs {
   u32x4 v[VN];
 };
 
-template <typename T, int DK, int DV>
+// ALIBI: a.alibi is non-null (a separate instantiation, so the loop without it keeps
+// its registers).
+template <typename T, int DK, int DV, bool ALIBI>
 __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const PrefillArgs a) {
   constexpr int KT = kPrefillKeys;
   constexpr int NTH = kPrefillThreads;
@@ -203,6 +206,14 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
     if (a.window > 0) start = end - a.window > 0 ? end - a.window : 0;
     vis_lo[rb] = row_ok[rb] ? start : 0;
     vis_hi[rb] = row_ok[rb] ? end : 0;
+  }
+  // ALiBi ("paged_attention_v2_pytorch.py", phase 1): each row's slope in raw score
+  // units; key j's score gains slope * (j - (end - 1)), end = vis_hi
+  float slope_r[2] = {0.f, 0.f};
+  if constexpr (ALIBI) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+      slope_r[rb] = row_ok[rb] ? a.alibi[row_head[rb]] * (kLog2e / a.scale_log2) : 0.f;
   }
   __syncthreads();
 #pragma unroll
@@ -439,6 +450,17 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
       const int t0 = t_first + i * KT;
       // Tiles inside every row's visible range skip the masking.
       const bool masked = !(w_lo_max <= t0 && w_hi_min >= t0 + KT);  // some row sees only part of it
+      if constexpr (ALIBI) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const float jb = (float)(t0 + 4 * c - (vis_hi[rb] - 1));  // exact: |j - ref| < 2^24
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+              sc[kb][rb][ii] = fmaf(slope_r[rb], jb + (float)(kb * 16 + ii), sc[kb][rb][ii]);
+        }
+      }
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         if (masked) {
@@ -669,18 +691,24 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
   }
 }
 
-template <typename T>
-hipError_t launch_prefill_typed(const PrefillArgs& a, int dk, int dv, dim3 grid, hipStream_t stream) {
+template <typename T, bool ALIBI>
+hipError_t launch_prefill_dims(const PrefillArgs& a, int dk, int dv, dim3 grid, hipStream_t stream) {
   const dim3 block(kPrefillThreads);
   if (dk == 128 && dv == 128)
-    hipLaunchKernelGGL((prefill_kernel<T, 128, 128>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<T, 128, 128, ALIBI>), grid, block, 0, stream, a);
   else if (dk == 192 && dv == 128)
-    hipLaunchKernelGGL((prefill_kernel<T, 192, 128>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<T, 192, 128, ALIBI>), grid, block, 0, stream, a);
   else if (dk == 64 && dv == 64)
-    hipLaunchKernelGGL((prefill_kernel<T, 64, 64>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<T, 64, 64, ALIBI>), grid, block, 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_prefill_typed(const PrefillArgs& a, int dk, int dv, dim3 grid, hipStream_t stream) {
+  return a.alibi != nullptr ? launch_prefill_dims<T, true>(a, dk, dv, grid, stream)
+                            : launch_prefill_dims<T, false>(a, dk, dv, grid, stream);
 }
 
 }  // namespace pa

@@ -123,6 +123,12 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const RowsArgs a) {
     zero_words<KW * 4>(qw);
   }
 
+  // ALiBi ("paged_attention_v2_pytorch.py", phase 1): head r16's slope in log2 units;
+  // position j's score gains slope * (j - (end - 1)).  Positions are counted from
+  // pref = hi - 1 (end - 1 unless split), so that a partition far from the query keeps
+  // exact scores and exp-sums; its stored maximum gets slope * (pref - end + 1) back.
+  const float slope_l = (a.alibi != nullptr && r16 < a.group) ? a.alibi[g * a.group + r16] * kLog2e : 0.f;
+  const int pref = hi - 1;
   float m_run = -INFINITY;  // log2 units, for head r16
   float l_run = 0.f;        // this lane group's share of the exp-sum, head r16
   float acc[GMAX][VE];
@@ -175,7 +181,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const RowsArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = t0 + 4 * c + i;
-        sv[i] = (j >= lo && j < hi) ? sc[i] * a.scale_log2 : -INFINITY;
+        sv[i] = (j >= lo && j < hi) ? fmaf(slope_l, (float)(j - pref), sc[i] * a.scale_log2) : -INFINITY;
         mx = fmaxf(mx, sv[i]);
       }
       mx = max_over_groups(mx);
@@ -265,7 +271,8 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const RowsArgs a) {
       const int64_t pi = ((int64_t)s * a.num_heads + hq) * a.max_partitions + part;
       a.tmp_out[pi * DV + d] = o;
       if (d == 0) {
-        a.max_logits[pi] = L > 0.f ? M * kLn2 : -INFINITY;
+        const float off = a.alibi != nullptr ? a.alibi[hq] * kLog2e * (float)(pref - (end - 1)) : 0.f;
+        a.max_logits[pi] = L > 0.f ? (M + off) * kLn2 : -INFINITY;
         a.exp_sums[pi] = L;
       }
     }

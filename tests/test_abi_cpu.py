@@ -61,7 +61,7 @@ def test_decode_host_checks(pool, H, expect):
     lib = binding.load()
     p = None if pool is None else ctypes.byref(_pool(**pool))
     st = lib.pa_decode(p, FAKE, binding.PA_F16, FAKE, binding.PA_F32, FAKE, 4, FAKE, 2, H, 0.1, 0, 0, 0, None,
-                       None, None, None, None, None)
+                       None, None, None, None, None, None)
     assert st == expect
 
 
@@ -69,16 +69,16 @@ def test_decode_partition_checks():
     lib = binding.load()
     p = ctypes.byref(_pool())
     args = lambda P, pmax, ws: (p, FAKE, binding.PA_F16, FAKE, binding.PA_F32, FAKE, 4, FAKE, 2, 4, 0.1, 0, P, pmax,
-                                ws, ws, ws, None, None, None)
+                                ws, ws, ws, None, None, None, None)
     assert lib.pa_decode(*args(24, 4, FAKE)) == binding.PA_EINVAL      # not a multiple of the block size
     assert lib.pa_decode(*args(32, 0, FAKE)) == binding.PA_EINVAL      # no partitions
     assert lib.pa_decode(*args(32, 4, None)) == binding.PA_EINVAL      # missing workspace
     assert lib.pa_decode(*args(-16, 4, FAKE)) == binding.PA_EINVAL
     # q dtype must match the pool, out must be f32 or q's dtype
     assert lib.pa_decode(p, FAKE, binding.PA_BF16, FAKE, binding.PA_F32, FAKE, 4, FAKE, 2, 4, 0.1, 0, 0, 0, None,
-                         None, None, None, None, None) == binding.PA_EUNSUPPORTED
+                         None, None, None, None, None, None) == binding.PA_EUNSUPPORTED
     assert lib.pa_decode(p, FAKE, binding.PA_F16, FAKE, binding.PA_BF16, FAKE, 4, FAKE, 2, 4, 0.1, 0, 0, 0, None,
-                         None, None, None, None, None) == binding.PA_EUNSUPPORTED
+                         None, None, None, None, None, None) == binding.PA_EUNSUPPORTED
 
 
 def test_varlen_host_checks():
@@ -86,15 +86,15 @@ def test_varlen_host_checks():
     p = ctypes.byref(_pool())
     # causal without positions
     assert lib.pa_varlen(p, FAKE, binding.PA_F16, FAKE, binding.PA_F32, None, FAKE, FAKE, None, FAKE, 4, 2, 10, 8,
-                         4, 0.1, 1, 0, None, None, None) == binding.PA_EINVAL
+                         4, 0.1, 1, 0, None, None, None, None) == binding.PA_EINVAL
     # no query_start_loc
     assert lib.pa_varlen(p, FAKE, binding.PA_F16, FAKE, binding.PA_F32, None, None, FAKE, FAKE, FAKE, 4, 2, 10, 8,
-                         4, 0.1, 1, 0, None, None, None) == binding.PA_EINVAL
+                         4, 0.1, 1, 0, None, None, None, None) == binding.PA_EINVAL
     # tokens but no sequences
     assert lib.pa_varlen(p, FAKE, binding.PA_F16, FAKE, binding.PA_F32, None, FAKE, FAKE, FAKE, FAKE, 4, 0, 10, 8,
-                         4, 0.1, 1, 0, None, None, None) == binding.PA_EINVAL
+                         4, 0.1, 1, 0, None, None, None, None) == binding.PA_EINVAL
     assert lib.pa_varlen(p, FAKE, binding.PA_F16, FAKE, binding.PA_F32, None, FAKE, FAKE, FAKE, FAKE, 4, 2, 10, 8,
-                         5, 0.1, 1, 0, None, None, None) == binding.PA_ESHAPE
+                         5, 0.1, 1, 0, None, None, None, None) == binding.PA_ESHAPE
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.125, float("inf"), float("nan")])
@@ -102,9 +102,9 @@ def test_scale_must_be_positive_and_finite(scale):
     lib = binding.load()
     p = ctypes.byref(_pool())
     assert lib.pa_decode(p, FAKE, binding.PA_F16, FAKE, binding.PA_F32, FAKE, 4, FAKE, 2, 4, scale, 0, 0, 0, None,
-                         None, None, None, None, None) == binding.PA_EINVAL
+                         None, None, None, None, None, None) == binding.PA_EINVAL
     assert lib.pa_varlen(p, FAKE, binding.PA_F16, FAKE, binding.PA_F32, None, FAKE, FAKE, FAKE, FAKE, 4, 2, 10, 8,
-                         4, scale, 1, 0, None, None, None) == binding.PA_EINVAL
+                         4, scale, 1, 0, None, None, None, None) == binding.PA_EINVAL
 
 
 def test_write_and_merge_host_checks():
@@ -151,12 +151,12 @@ def test_binding_refuses_host_tensors():
 
 def _decode(pool, q_dtype=binding.PA_BF16, out_dtype=binding.PA_F32, H=4, scale=0.1):
     return binding.load().pa_decode(ctypes.byref(pool), FAKE, q_dtype, FAKE, out_dtype, FAKE, 4, FAKE, 2, H, scale,
-                                    0, 0, 0, None, None, None, None, None, None)
+                                    0, 0, 0, None, None, None, None, None, None, None)
 
 
 def _varlen(pool, q_dtype=binding.PA_BF16, max_query_len=1, scale=0.1):
     return binding.load().pa_varlen(ctypes.byref(pool), FAKE, q_dtype, FAKE, binding.PA_F32, None, FAKE, FAKE, FAKE,
-                                    FAKE, 4, 2, 10, max_query_len, 4, scale, 1, 0, None, None, None)
+                                    FAKE, 4, 2, 10, max_query_len, 4, scale, 1, 0, None, None, None, None)
 
 
 FP8 = dict(dtype=binding.PA_FP8_E4M3, head_dim_k=128, head_dim_v=128)

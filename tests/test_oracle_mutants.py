@@ -41,7 +41,7 @@ MUTANTS = {
     "reduce_without_rescale": ("double w = exp_sums[base + p] * exp(max_logits[base + p] - M);",
                                "double w = exp_sums[base + p];"),
     # arithmetic slips
-    "scale_dropped": ("s[j - lo] = scale * dot;", "s[j - lo] = dot;"),
+    "scale_dropped": ("s[j - lo] = scale * dot + slope", "s[j - lo] = dot + slope"),
     "causal_excludes_self": ("int64_t e = job->causal ? (int64_t)job->positions[t] + 1 : n;",
                              "int64_t e = job->causal ? (int64_t)job->positions[t] : n;"),
     "lse_without_max": ("return l > 0.0 ? m + log(l) : -INFINITY;", "return l > 0.0 ? log(l) : -INFINITY;"),
@@ -60,8 +60,9 @@ MUTANTS = {
     "sink_left_out_of_max": ("  double m = sink;\n", "  double m = -INFINITY;\n"),
     "sink_left_out_of_sum": ("double l = sink == -INFINITY ? 0.0 : exp(sink - m);", "double l = 0.0;"),
     "sink_counted_per_partition": (
-        "attend(qrow, K, V, P->dk, P->dv, lo, hi, job->scale, -INFINITY, sc, orow, &m, &l);",
-        "attend(qrow, K, V, P->dk, P->dv, lo, hi, job->scale, job->sinks ? job->sinks[h] : -INFINITY, sc, orow, &m, &l);"),
+        "attend(qrow, K, V, P->dk, P->dv, lo, hi, job->scale, -INFINITY, slope, ref, sc, orow, &m, &l);",
+        "attend(qrow, K, V, P->dk, P->dv, lo, hi, job->scale, job->sinks ? job->sinks[h] : -INFINITY, slope, ref, sc, "
+        "orow, &m, &l);"),
     "reduce_without_sink": ("double total = sink == -INFINITY ? 0.0 : exp(sink - M);", "double total = 0.0;"),
     # encoders and the latent-cache gather (GatherMlaCache)
     "half_rounds_toward_zero": ("double r = nearbyint(ldexp(m, 11));", "double r = trunc(ldexp(m, 11));"),
