@@ -160,9 +160,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
   constexpr int KPIECES = KROWB / 256;      // 256-byte pieces per row
   constexpr int KBLK = 1024;                // one load: 4 rows x 256 bytes (fp8: 8 x 128)
   static_assert(KROWB % 256 == 0, "K rows of whole 256-byte pieces");
-  constexpr int KBUF = F8 ? 2 * KBLK : 4 * KPIECES * KBLK;  // a tile's K
-  constexpr int VBUF8 = 2 * KBLK;                           // a tile's fp8 V
-  constexpr int kTileLoads = F8 ? 4 : 4 * KPIECES + 4;      // load instructions per tile and wave
+  constexpr int KBUF = F8 ? 4 * KBLK : 4 * KPIECES * KBLK;  // a tile's K (fp8: 32 rows of 128 bytes)
+  constexpr int VBUF8 = 4 * KBLK;                           // a tile's fp8 V
+  constexpr int kTileLoads = F8 ? 8 : 4 * KPIECES + 4;      // load instructions per tile and wave
   struct Merge {
     float m[NW][16];
     float l[NW][16];
@@ -271,68 +271,94 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
     }
   };
 
-  const int my_first = (lo >> 4) + wave;  // this wave's tiles: my_first + NW * i, i < my_tiles
-  const int last = (hi - 1) >> 4;
+  // Tiles of TP positions aligned to absolute positions: 16 for 16-bit caches, 32 for
+  // fp8 (the same 8 KB of K and V per tile).
+  constexpr int TSH = F8 ? 5 : 4;
+  constexpr int TP = 1 << TSH;
+  const int my_first = (lo >> TSH) + wave;  // this wave's tiles: my_first + NW * i, i < my_tiles
+  const int last = (hi - 1) >> TSH;
   const int my_tiles = (lo < hi && last >= my_first) ? (last - my_first) / NW + 1 : 0;
 
-  // fp8 tiles, lane constants: the LDS offsets of this lane's two K chunks (2c and
-  // 2c + 1 of position r16) and of the rows it names for the four V transpose reads
-  // (position 4c + (r16 / 2) % 4, d bytes 16 nd + 64 (r16 / 8) + 8 (r16 % 2) .. +8;
-  // a transpose read then hands lane r16 the elements d = 16 nd + r16 (bytes 0..3)
-  // and d = 16 (nd + 4) + r16 (bytes 4..7) of positions 4c .. 4c + 3).
-  uint32_t k8_off[2] = {0u, 0u}, v8_off[4] = {0u, 0u, 0u, 0u};
+  // fp8 tiles: tile row r (0..31) holds its 16-byte chunk k in slot k ^ kswz(r) of
+  // its 128-byte LDS row, which keeps both read kinds below free of bank conflicts.
+  auto kswz = [](int r) { return ((r >> 1) & 3) | ((((r >> 3) ^ (r >> 4)) & 1) << 2); };
+  // Lane constants: the LDS offsets of this lane's K chunks 2c and 2c + 1 of rows r16
+  // (chain 0) and 16 + r16 (chain 1), and of the row piece it names for each V
+  // transpose read nd: position pos(c, r16 / 2) -- 4c + k for k < 4, 16 + 4c + k - 4
+  // otherwise -- bytes 16 nd + 8 (r16 % 2) .. +8.  The read then hands lane r16 the
+  // element d = 16 nd + r16 of positions pos(c, 0..7): the A operand (V^T) of a
+  // 16x16x32 MFMA whose reduction index 8c + k is position pos(c, k).
+  uint32_t k8_off[2][2] = {{0u, 0u}, {0u, 0u}}, v8_off[ND] = {};
   if constexpr (F8) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-      k8_off[h] = (uint32_t)((r16 >> 3) * KBLK + (r16 & 7) * 128 + 16 * ((2 * c + h) ^ ((r16 >> 1) & 7)));
-    const int pos = 4 * c + ((r16 >> 1) & 3);
+    for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
-    for (int nd = 0; nd < 4; ++nd)
-      v8_off[nd] = (uint32_t)((pos >> 3) * KBLK + (pos & 7) * 128 + 16 * ((nd | 4 * (r16 >> 3)) ^ ((pos >> 1) & 7)) +
-                              8 * (r16 & 1));
+      for (int h = 0; h < 2; ++h) {
+        const int r = 16 * ch + r16;
+        k8_off[ch][h] = (uint32_t)((r >> 3) * KBLK + (r & 7) * 128 + 16 * ((2 * c + h) ^ kswz(r)));
+      }
+    const int k = r16 >> 1, pos = k < 4 ? 4 * c + k : 16 + 4 * c + (k - 4);
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd)
+      v8_off[nd] = (uint32_t)((pos >> 3) * KBLK + (pos & 7) * 128 + 16 * (nd ^ kswz(pos)) + 8 * (r16 & 1));
   }
 
-  int ids = 0;  // block ids of up to 64 upcoming tiles, one per lane
+  // Block ids of upcoming tiles, one per lane: of tile i0 + lane (16-bit), or of the
+  // 16-position half lane % 2 of tile i0 + lane / 2 (fp8: with 16-token blocks a tile
+  // spans two).  Halves past the sequence read some in-bounds entry of the row; their
+  // loads are redirected into the first half below.
+  constexpr int IDS_PER_TILE = F8 ? 2 : 1;
+  constexpr int TILES_PER_IDS = 64 / IDS_PER_TILE;
+  int ids = 0;
   auto load_ids = [&](int i0) {
-    const int i = i0 + lane;
-    int idx = ((my_first + NW * (i < my_tiles ? i : 0)) << 4) >> block_shift;
+    const int i = i0 + lane / IDS_PER_TILE;
+    const int half = F8 ? (lane & 1) : 0;
+    int idx = (((my_first + NW * (i < my_tiles ? i : 0)) << TSH) + 16 * half) >> block_shift;
     idx = idx < a.max_blocks ? idx : a.max_blocks - 1;
     const int id = table[idx];
     ids = id < 0 ? 0 : (id >= a.num_blocks ? (int)(a.num_blocks - 1) : id);
   };
   // K and V of tile i into LDS buffer i % NB by direct loads (non-temporal: the
-  // data is streamed once).  Load ii writes positions ii + 4c'' (c'' = lane / 16)
-  // as contiguous 256-byte rows, one 16-byte piece per lane; for K the piece a lane
-  // fetches is swizzled: LDS chunk slot of logical chunk k in row c'' of load ii is
-  // k ^ 4c'' ^ ii (within the 256-byte piece).  Positions past the sequence read
-  // the sequence's last position instead (finite data, in the same block; their
-  // scores are masked), so every tile issues exactly kTileLoads loads and a
-  // counted wait can tell tiles apart.
+  // data is streamed once).  16-bit: load ii writes positions ii + 4c'' (c'' = lane /
+  // 16) as contiguous 256-byte rows, one 16-byte piece per lane; for K the piece a
+  // lane fetches is swizzled: LDS chunk slot of logical chunk k in row c'' of load ii
+  // is k ^ 4c'' ^ ii (within the 256-byte piece).  fp8: load ld writes tile rows
+  // 8 ld + lane / 8, chunk slot lane % 8 receiving the row's chunk (lane % 8) ^
+  // kswz(row).  Positions past the sequence read the sequence's last position instead
+  // (finite data, in the same block; their scores are masked), so every tile issues
+  // exactly kTileLoads loads and a counted wait can tell tiles apart.
   auto fetch = [&](int i) {
-    const int t0 = (my_first + NW * i) << 4;
-    const int blk = __builtin_amdgcn_readlane(ids, i & 63);
-    const int64_t slot0 = (int64_t)blk * b + (t0 & (b - 1));
-    const char* kt = kbase + slot0 * krow;
-    const char* vt = vbase + slot0 * vrow + r16 * 16;
+    const int t0 = (my_first + NW * i) << TSH;
     char* kl = sh.t.k[wave][i % NB];
     char* vl = sh.t.v[wave][i % NB];
     const int lim = n - 1 - t0;  // >= 0: every tile starts inside the sequence
     if constexpr (F8) {
-      // load ld writes positions 8 ld + lane / 8, 16 bytes per lane: chunk slot
-      // lane % 8 of position r receives the row's chunk (lane % 8) ^ ((r >> 1) & 7)
-      const char* vt8 = vbase + slot0 * vrow;
+      const int blk0 = __builtin_amdgcn_readlane(ids, (2 * i) & 63);
+      const int blk1 = __builtin_amdgcn_readlane(ids, (2 * i + 1) & 63);
+      const int64_t s0 = (int64_t)blk0 * b + (t0 & (b - 1));
+      const int64_t s1 = (int64_t)blk1 * b + ((t0 + 16) & (b - 1));
+      const char* k0 = kbase + s0 * krow;
+      const char* k1 = kbase + s1 * krow;
+      const char* v0 = vbase + s0 * vrow;
+      const char* v1 = vbase + s1 * vrow;
 #pragma unroll
-      for (int ld = 0; ld < 2; ++ld) {
+      for (int ld = 0; ld < 4; ++ld) {
         const int r = 8 * ld + (lane >> 3);
         const int rr = r < lim ? r : lim;
-        const int ch = (lane & 7) ^ ((r >> 1) & 7);
-        __builtin_amdgcn_global_load_lds(kt + rr * krow + ch * 16,
+        const int ch = (lane & 7) ^ kswz(r);
+        const bool first = ld < 2 || rr < 16;  // row rr lies in the tile's first half
+        const int64_t ro = (int64_t)(rr & 15);
+        __builtin_amdgcn_global_load_lds((first ? k0 : k1) + ro * krow + ch * 16,
                                          (__attribute__((address_space(3))) void*)(kl + ld * KBLK), 16, 0, kLoadNT);
-        __builtin_amdgcn_global_load_lds(vt8 + rr * vrow + ch * 16,
+        __builtin_amdgcn_global_load_lds((first ? v0 : v1) + ro * vrow + ch * 16,
                                          (__attribute__((address_space(3))) void*)(vl + ld * KBLK), 16, 0, kLoadNT);
       }
       return;
     }
+    const int blk = __builtin_amdgcn_readlane(ids, i & 63);
+    const int64_t slot0 = (int64_t)blk * b + (t0 & (b - 1));
+    const char* kt = kbase + slot0 * krow;
+    const char* vt = vbase + slot0 * vrow + r16 * 16;
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int rr = ii + 4 * c < lim ? ii + 4 * c : lim;
@@ -346,19 +372,12 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
                                        0, kLoadNT);
     }
   };
-  // one tile: wait for its loads (the later tiles' may stay in flight), copy its K
-  // operands and transposed V from LDS into registers, refill the freed buffer with
-  // tile i + NB, then S, softmax and PV from registers.  NB tiles per wave are in
-  // flight while one is computed.
-  auto step = [&](int i) {
-    const int t0 = (my_first + NW * i) << 4;
-    const char* kl = sh.t.k[wave][i % NB];
-    const char* lb = sh.t.v[wave][i % NB];
-    // The waits are explicit because the direct-to-LDS loads are not otherwise
-    // ordered with the LDS reads below; the clobbers keep later loads from being
-    // hoisted above them.  Vector-memory counts retire in order, so with the
-    // kTileLoads loads of each of `ahead` later tiles issued after tile i's, "at most
-    // ahead * kTileLoads outstanding" means tile i has landed.
+  // The waits are explicit because the direct-to-LDS loads are not otherwise
+  // ordered with the LDS reads; the clobbers keep later loads from being hoisted
+  // above them.  Vector-memory counts retire in order, so with the kTileLoads loads
+  // of each of `ahead` later tiles issued after tile i's, "at most ahead *
+  // kTileLoads outstanding" means tile i has landed.
+  auto wait_tile = [&](int i) {
     const int ahead = my_tiles - 1 - i;  // tiles issued after tile i, up to NB - 1
     if (NB >= 4 && ahead >= 3)
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * kTileLoads) : "memory");
@@ -368,74 +387,71 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kTileLoads) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+  auto refill = [&](int i) {
+    if (i + NB < my_tiles) {
+      if (((i + NB) & (TILES_PER_IDS - 1)) == 0) load_ids(i + NB);
+      fetch(i + NB);
+    }
+  };
+  // The reference-max update shared by both tile kinds: mx is the tile's max over
+  // the group's lanes (raw units).
+  auto rescale = [&](float mx) {
+    m_true = fmaxf(m_true, mx);
+    if (__any((mx - m_run) * a.scale_log2 > kRescaleLog2)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * a.scale_log2);
+      l_run *= alpha;
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd) o[nd] *= alpha;
+      m_run = m_new;
+    }
+  };
+  // one 16-bit tile: wait for its loads (the later tiles' may stay in flight), copy
+  // its K operands and transposed V from LDS into registers, refill the freed buffer
+  // with tile i + NB, then S, softmax and PV from registers.  NB tiles per wave are
+  // in flight while one is computed.
+  auto step = [&](int i) {
+    const int t0 = (my_first + NW * i) << 4;
+    const char* kl = sh.t.k[wave][i % NB];
+    const char* lb = sh.t.v[wave][i % NB];
+    wait_tile(i);
     // The LDS reads are issued as inline asm and their results are tied to the
     // lgkmcnt wait below: the compiler would otherwise guard reads of memory that
     // direct loads write with a full vmcnt(0) wait, draining tile i + 1's loads.
     const uint32_t kl_a = lds_addr(kl), lb_a = lds_addr(lb);
     u32x4 kc[KCH];
     u32x2 va[ND];
-    if constexpr (F8) {
-      u32x4 k8[2];
-      u32x2 v8[4];
-      asm volatile("ds_read_b128 %0, %1" : "=v"(k8[0]) : "v"(kl_a + k8_off[0]));
-      asm volatile("ds_read_b128 %0, %1" : "=v"(k8[1]) : "v"(kl_a + k8_off[1]));
 #pragma unroll
-      for (int nd = 0; nd < 4; ++nd) asm volatile("ds_read_b64_tr_b8 %0, %1" : "=v"(v8[nd]) : "v"(lb_a + v8_off[nd]));
-      asm volatile("s_waitcnt lgkmcnt(0)"
-                   : "+v"(k8[0]), "+v"(k8[1]), "+v"(v8[0]), "+v"(v8[1]), "+v"(v8[2]), "+v"(v8[3])
-                   :
-                   : "memory");
-      if (i + NB < my_tiles) {
-        if (((i + NB) & 63) == 0) load_ids(i + NB);
-        fetch(i + NB);
-      }
-      // K operand u = 2h + w: bytes 8w .. 8w + 7 of read h
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int w = 0; w < 2; ++w)
-          kc[2 * h + w] = u32x4{widen_fp8x2<T, false>(k8[h][2 * w]), widen_fp8x2<T, true>(k8[h][2 * w]),
-                                widen_fp8x2<T, false>(k8[h][2 * w + 1]), widen_fp8x2<T, true>(k8[h][2 * w + 1])};
-#pragma unroll
-      for (int nd = 0; nd < 4; ++nd) {
-        va[nd] = u32x2{widen_fp8x2<T, false>(v8[nd][0]), widen_fp8x2<T, true>(v8[nd][0])};
-        va[nd + 4] = u32x2{widen_fp8x2<T, false>(v8[nd][1]), widen_fp8x2<T, true>(v8[nd][1])};
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < KCH; ++u) {
-        // logical chunk 4u + c of position r16 = 4 * row + block
-        const int kk = 4 * u + c, piece = kk >> 4, chunk = (kk & 15) ^ (4 * tr_r) ^ tr_q;
-        asm volatile("ds_read_b128 %0, %1"
-                     : "=v"(kc[u])
-                     : "v"(kl_a + (piece * 4 + tr_q) * KBLK + tr_r * 256 + chunk * 16));
-      }
-      const uint32_t va_a = lb_a + tr_r * VBLK + c * 256 + 4 * tr_q * 2;
-      asm volatile(
-          "ds_read_b64_tr_b16 %0, %8\n\t"
-          "ds_read_b64_tr_b16 %1, %8 offset:32\n\t"
-          "ds_read_b64_tr_b16 %2, %8 offset:64\n\t"
-          "ds_read_b64_tr_b16 %3, %8 offset:96\n\t"
-          "ds_read_b64_tr_b16 %4, %8 offset:128\n\t"
-          "ds_read_b64_tr_b16 %5, %8 offset:160\n\t"
-          "ds_read_b64_tr_b16 %6, %8 offset:192\n\t"
-          "ds_read_b64_tr_b16 %7, %8 offset:224"
-          : "=&v"(va[0]), "=&v"(va[1]), "=&v"(va[2]), "=&v"(va[3]), "=&v"(va[4]), "=&v"(va[5]), "=&v"(va[6]),
-            "=&v"(va[7])
-          : "v"(va_a));
-      // the reads of buffer i % NB complete (and their registers are valid) before
-      // tile i + NB's loads may overwrite it
-      static_assert(KCH == 4 && ND == 8, "operand wait below lists 4 K and 8 V registers");
-      asm volatile("s_waitcnt lgkmcnt(0)"
-                   : "+v"(kc[0]), "+v"(kc[1]), "+v"(kc[2]), "+v"(kc[3]), "+v"(va[0]), "+v"(va[1]), "+v"(va[2]),
-                     "+v"(va[3]), "+v"(va[4]), "+v"(va[5]), "+v"(va[6]), "+v"(va[7])
-                   :
-                   : "memory");
-      if (i + NB < my_tiles) {
-        if (((i + NB) & 63) == 0) load_ids(i + NB);
-        fetch(i + NB);
-      }
+    for (int u = 0; u < KCH; ++u) {
+      // logical chunk 4u + c of position r16 = 4 * row + block
+      const int kk = 4 * u + c, piece = kk >> 4, chunk = (kk & 15) ^ (4 * tr_r) ^ tr_q;
+      asm volatile("ds_read_b128 %0, %1"
+                   : "=v"(kc[u])
+                   : "v"(kl_a + (piece * 4 + tr_q) * KBLK + tr_r * 256 + chunk * 16));
     }
+    const uint32_t va_a = lb_a + tr_r * VBLK + c * 256 + 4 * tr_q * 2;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:32\n\t"
+        "ds_read_b64_tr_b16 %2, %8 offset:64\n\t"
+        "ds_read_b64_tr_b16 %3, %8 offset:96\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:128\n\t"
+        "ds_read_b64_tr_b16 %5, %8 offset:160\n\t"
+        "ds_read_b64_tr_b16 %6, %8 offset:192\n\t"
+        "ds_read_b64_tr_b16 %7, %8 offset:224"
+        : "=&v"(va[0]), "=&v"(va[1]), "=&v"(va[2]), "=&v"(va[3]), "=&v"(va[4]), "=&v"(va[5]), "=&v"(va[6]),
+          "=&v"(va[7])
+        : "v"(va_a));
+    // the reads of buffer i % NB complete (and their registers are valid) before
+    // tile i + NB's loads may overwrite it
+    static_assert(KCH == 4 && ND == 8, "operand wait below lists 4 K and 8 V registers");
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(kc[0]), "+v"(kc[1]), "+v"(kc[2]), "+v"(kc[3]), "+v"(va[0]), "+v"(va[1]), "+v"(va[2]),
+                   "+v"(va[3]), "+v"(va[4]), "+v"(va[5]), "+v"(va[6]), "+v"(va[7])
+                 :
+                 : "memory");
+    refill(i);
 
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -454,16 +470,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
       }
     }
     float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    mx = max_over_groups(mx);
-    m_true = fmaxf(m_true, mx);
-    if (__any((mx - m_run) * a.scale_log2 > kRescaleLog2)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * a.scale_log2);
-      l_run *= alpha;
-#pragma unroll
-      for (int nd = 0; nd < ND; ++nd) o[nd] *= alpha;
-      m_run = m_new;
-    }
+    rescale(max_over_groups(mx));
     const float mc = m_run * a.scale_log2;
     float p[4];
 #pragma unroll
@@ -486,6 +493,93 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
       }
     }
   };
+  // one fp8 tile of 32 positions: S^T of positions 0..15 and 16..31 as two 16-row
+  // chains, one softmax step over both, and O^T += V^T P^T on 16x16x32 MFMAs whose
+  // reduction index 8c + k is position pos(c, k) -- P^T's rows are already there:
+  // lane (head, c) holds the two chains' positions 4c .. 4c + 3.
+  auto step8 = [&](int i) {
+    const int t0 = (my_first + NW * i) << 5;
+    const uint32_t kl_a = lds_addr(sh.t.k[wave][i % NB]), lb_a = lds_addr(sh.t.v[wave][i % NB]);
+    wait_tile(i);
+    u32x4 k8[2][2];
+    u32x2 v8[ND];
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) asm volatile("ds_read_b128 %0, %1" : "=v"(k8[ch][h]) : "v"(kl_a + k8_off[ch][h]));
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd) asm volatile("ds_read_b64_tr_b8 %0, %1" : "=v"(v8[nd]) : "v"(lb_a + v8_off[nd]));
+    static_assert(ND == 8, "operand wait below lists 4 K and 8 V registers");
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(k8[0][0]), "+v"(k8[0][1]), "+v"(k8[1][0]), "+v"(k8[1][1]), "+v"(v8[0]), "+v"(v8[1]),
+                   "+v"(v8[2]), "+v"(v8[3]), "+v"(v8[4]), "+v"(v8[5]), "+v"(v8[6]), "+v"(v8[7])
+                 :
+                 : "memory");
+    refill(i);
+
+    // S^T, chain ch: K operand u = 2h + w is bytes 8w .. 8w + 7 of read (ch, h)
+    f32x4 sc[2];
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+      sc[ch] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          const u32x4 kop = u32x4{widen_fp8x2<T, false>(k8[ch][h][2 * w]), widen_fp8x2<T, true>(k8[ch][h][2 * w]),
+                                  widen_fp8x2<T, false>(k8[ch][h][2 * w + 1]),
+                                  widen_fp8x2<T, true>(k8[ch][h][2 * w + 1])};
+          sc[ch] = mfma_16x16x32<T>(kop, qb[2 * h + w], sc[ch]);
+        }
+    }
+    float sv[8];  // position 16 (k / 4) + 4c + k % 4 for k = 0..7
+#pragma unroll
+    for (int k = 0; k < 8; ++k) sv[k] = sc[k >> 2][k & 3];
+    if (alibi) {
+      const float jb = (float)(t0 + 4 * c - pref);  // exact: |j - pref| < 2^24
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sv[k] = fmaf(slope_r, jb + (float)(16 * (k >> 2) + (k & 3)), sv[k]);
+    }
+    if (t0 < lo || t0 + 32 > hi) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int j = t0 + 16 * (k >> 2) + 4 * c + (k & 3);
+        if (j < lo || j >= hi) sv[k] = -INFINITY;
+      }
+    }
+    const float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+    rescale(max_over_groups(mx));
+    const float mc = m_run * a.scale_log2;
+    float p[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) p[k] = __builtin_amdgcn_exp2f(fmaf(sv[k], a.scale_log2, -mc));
+    l_run += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    // O^T[d][head] += V^T[d][position] P^T[position][head]
+    u32x4 va[ND];
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd)
+      va[nd] = u32x4{widen_fp8x2<T, false>(v8[nd][0]), widen_fp8x2<T, true>(v8[nd][0]),
+                     widen_fp8x2<T, false>(v8[nd][1]), widen_fp8x2<T, true>(v8[nd][1])};
+    if constexpr (T::code == PA_F16) {
+      const u32x4 pb = u32x4{pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3]), pack_f16x2(p[4], p[5]),
+                             pack_f16x2(p[6], p[7])};
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd) o[nd] = mfma_16x16x32<F16>(va[nd], pb, o[nd]);
+    } else {
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hw[e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
+        lw[e] = pack_bf16x2(p[2 * e] - __uint_as_float(hw[e] << 16), p[2 * e + 1] - __uint_as_float(hw[e] & 0xffff0000u));
+      }
+      const u32x4 pb = u32x4{hw[0], hw[1], hw[2], hw[3]}, pl = u32x4{lw[0], lw[1], lw[2], lw[3]};
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd) {
+        o[nd] = mfma_16x16x32<BF16>(va[nd], pb, o[nd]);
+        o[nd] = mfma_16x16x32<BF16>(va[nd], pl, o[nd]);
+      }
+    }
+  };
 
   if (my_tiles > 0) {
     load_ids(0);
@@ -493,7 +587,12 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
     for (int j = 0; j < NB; ++j)
       if (j < my_tiles) fetch(j);
   }
-  for (int i = 0; i < my_tiles; ++i) step(i);
+  for (int i = 0; i < my_tiles; ++i) {
+    if constexpr (F8)
+      step8(i);
+    else
+      step(i);
+  }
   if constexpr (WP) {
     write_state(pz);  // (-inf, 0, 0) when the window leaves the partition empty
     return;
@@ -567,9 +666,10 @@ constexpr int kOneWaveBufs = 2;
 // that every CU still gets enough waves.
 constexpr int64_t kOneWaveItems = 8192;
 
-// fp8 tiles are half the bytes: four buffers per wave keep as many bytes in flight
-// (unsplit: 8 waves x 4 x 4 KB = 128 KB of LDS).
-constexpr int kFp8Bufs = 4;
+// fp8 tiles of 32 positions hold as many bytes as 16-bit tiles of 16: the same two
+// buffers per wave (unsplit: 8 waves x 2 x 8 KB = 128 KB of LDS).
+constexpr int kFp8Bufs = 2;
+constexpr int kFp8WholeWaves = 8;
 
 // `grid` is (rows, kv heads, partitions); the kernel takes it flattened.
 template <typename T, bool F8>
@@ -587,8 +687,9 @@ hipError_t launch_decode_typed(const RowsArgs& a, int block_shift, int dk, int d
     hipLaunchKernelGGL((decode_mfma_kernel<T, 128, kPartWaves, false, part_bufs, F8>), dim3((uint32_t)n),
                        dim3(kPartWaves * 64), 0, stream, a, block_shift, rows);
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<T, 128, kWholeWaves, false, whole_bufs, F8>), dim3((uint32_t)n),
-                       dim3(kWholeWaves * 64), 0, stream, a, block_shift, rows);
+    hipLaunchKernelGGL((decode_mfma_kernel<T, 128, F8 ? kFp8WholeWaves : kWholeWaves, false, whole_bufs, F8>),
+                       dim3((uint32_t)n), dim3((F8 ? kFp8WholeWaves : kWholeWaves) * 64), 0, stream, a, block_shift,
+                       rows);
   return hipGetLastError();
 }
 
