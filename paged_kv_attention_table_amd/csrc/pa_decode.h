@@ -230,18 +230,16 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
       const int e0 = F8 ? 32 * c + 8 * u : (4 * u + c) * 8;
       qb[u] = r16 < G ? *reinterpret_cast<const u32x4*>(qrow + e0) : u32x4{0u, 0u, 0u, 0u};
     }
-    // take the q loads' wait here, before any K/V load is in flight; otherwise the
-    // compiler guards the loop's first use of qb with a full vmcnt(0) every tile
-#pragma unroll
-    for (int u = 0; u < KCH; ++u) asm volatile("" ::"v"(qb[u]));
   }
   // ALiBi ("paged_attention_v2_pytorch.py", phase 1): head r16's slope in raw score
   // units; position j's score gains slope * (j - ref).  The loop counts positions from
   // pref, the last one this workgroup covers (ref itself unless split), so that scores
   // and exp-sums stay exact however far the partition lies from the query; a
   // partition's maximum then gets slope * (pref - ref) added when it is stored.
+  // (slope_r is loaded after the first table load, below: a load issued earlier and
+  // used here would make the compiler wait for the q loads before that table load.)
   const bool alibi = a.alibi != nullptr;
-  const float slope_r = (alibi && r16 < G) ? a.alibi[g * G + r16] * (kLog2e / a.scale_log2) : 0.f;
+  float slope_r = 0.f;
   const int pref = hi - 1;
   f32x4 o[ND];
   float m_run, m_true, l_run;  // reference max, true max (raw score units), exp-sum share
@@ -581,8 +579,15 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
     }
   };
 
+  // The first block ids are loaded while the q loads are still in flight (two round
+  // trips overlap); the q loads' wait is taken here, before any K/V load is in
+  // flight -- otherwise the compiler guards the loop's first use of qb with a full
+  // vmcnt(0) every tile.
+  if (my_tiles > 0) load_ids(0);
+  if (alibi && r16 < G) slope_r = a.alibi[g * G + r16] * (kLog2e / a.scale_log2);
+#pragma unroll
+  for (int u = 0; u < KCH; ++u) asm volatile("" ::"v"(qb[u]));
   if (my_tiles > 0) {
-    load_ids(0);
 #pragma unroll
     for (int j = 0; j < NB; ++j)
       if (j < my_tiles) fetch(j);
