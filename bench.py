@@ -47,6 +47,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+VARLEN_PARTITION = 0  # split-KV partition size for the varlen workload's single-token rows
 METRIC = "paged-decode KV GB/s (% HBM peak); varlen prefill TFLOP/s (% MFMA peak)"
 
 
@@ -254,19 +255,29 @@ def run_prefill(args):
         lse = torch.empty((w.num_heads, w.num_tokens), device="cuda")
         max_q = int(np.diff(w.query_start_loc).max())
         flops = varlen_flops(w)
+        # single-token rows split over partitions (a caller workspace) unless
+        # --partition-size 0
+        P = VARLEN_PARTITION if args.partition_size is None else args.partition_size
+        pmax = -(-int(w.seq_lens.max()) // P) if P else 0
+        ws = [torch.empty(sh, device="cuda") for sh in ((w.num_seqs, w.num_heads, pmax),
+                                                         (w.num_seqs, w.num_heads, pmax),
+                                                         (w.num_seqs, w.num_heads, pmax, w.dv))] if P else [None] * 3
 
         def attn():
             pa_varlen(kp, vp, q, out, qsl, lens, pos, tables, max_q, w.scale, causal=True,
-                      sliding_window=w.sliding_window, lse=lse)
+                      sliding_window=w.sliding_window, lse=lse, partition_size=P, max_logits=ws[0],
+                      exp_sums=ws[1], tmp_out=ws[2])
 
         def write():
             pa_write_kv(kp, vp, k_new, v_new, slots)
 
-        kernel_label = "pa_varlen call (prefill tile kernel + single-token row kernel)"
+        kernel_label = ("pa_varlen call (prefill tile kernel + single-token row kernel"
+                        + (" split, + partition reduce)" if P else ")"))
         name, dtype = w.name, w.dtype
         cfg = {"workload": name, "prefill_seqs": 4, "decode_seqs": 12, "num_tokens": w.num_tokens,
                "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.dk,
-               "sliding_window": w.sliding_window, "step": "pa_write_kv + pa_varlen"}
+               "sliding_window": w.sliding_window, "single_token_partition_size": P,
+               "step": "pa_write_kv + pa_varlen"}
     else:
         cp = W.config5()
         kp, vp = dev(cp.k_pool, cp.dtype), dev(cp.v_pool, cp.dtype)

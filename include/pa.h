@@ -158,6 +158,15 @@ int pa_decode(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
  * alibi_slopes [num_heads] float32 (device, nullable): ALiBi as for pa_decode, the
  * bias counted from each row's last visible position end - 1 (the token's position
  * when causal, seq_len - 1 otherwise).
+ * partition_size > 0 (a multiple of block_size): sequences holding exactly one query
+ * token are computed split-KV, as pa_decode does ("paged_attention_v2_pytorch.py",
+ * phases 1 and 2), so that a few long single-token rows spread over the whole GPU.
+ * max_logits / exp_sums [num_seqs, num_heads, max_partitions] and tmp_out [num_seqs,
+ * num_heads, max_partitions, head_dim_v] are caller-owned float32 scratch, indexed by
+ * sequence; their contents after the call are unspecified.  Device check (with
+ * status): ceil(seq_len / partition_size) <= max_partitions for those sequences.
+ * partition_size == 0: no split, workspaces may be NULL.  Ignored for shapes whose
+ * single-token rows run on the tiled kernel (the row kernels do not take them).
  * Supported: (head_dim_k, head_dim_v) in {(32,32), (64,64), (128,128), (256,256),
  * (192,128)}; num_heads / num_kv_heads <= 16; any block_size.  PA_FP8_E4M3 pools: as
  * for pa_decode, and only calls whose sequences hold at most one query token each
@@ -166,8 +175,9 @@ int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
               float* lse, const int32_t* query_start_loc, const int32_t* seq_lens,
               const int32_t* positions, const int32_t* block_tables, int32_t max_blocks,
               int32_t num_seqs, int64_t num_tokens, int32_t max_query_len, int32_t num_heads,
-              float scale, int32_t causal, int32_t sliding_window, const float* sinks,
-              const float* alibi_slopes, int32_t* status, void* stream);
+              float scale, int32_t causal, int32_t sliding_window, int32_t partition_size,
+              int32_t max_partitions, float* max_logits, float* exp_sums, float* tmp_out,
+              const float* sinks, const float* alibi_slopes, int32_t* status, void* stream);
 
 /* Merge two attention states over disjoint key sets ("cpu_mla_prefill.cpp",
  * MergeAttnStates).  prefix_out, suffix_out, out: [num_tokens, num_heads, head_dim] in

@@ -60,7 +60,7 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
                               vp, vp, vp, vp]
     lib.pa_varlen.restype = ctypes.c_int
     lib.pa_varlen.argtypes = [pool_p, vp, i32, vp, i32, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, f32, i32, i32,
-                              vp, vp, vp, vp]
+                              i32, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.pa_merge_states.restype = ctypes.c_int
     lib.pa_merge_states.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i64, i32, vp]
     lib.pa_gather_cache.restype = ctypes.c_int
@@ -193,10 +193,12 @@ def pa_decode(k_pool, v_pool, q, out, block_tables, seq_lens, scale, sliding_win
 
 def pa_varlen(k_pool, v_pool, q, out, query_start_loc, seq_lens, positions, block_tables, max_query_len, scale,
               causal=True, sliding_window=0, lse=None, status=None, stream=None, sinks=None, k_scale=1.0,
-              v_scale=1.0, alibi_slopes=None):
+              v_scale=1.0, alibi_slopes=None, partition_size=0, max_logits=None, exp_sums=None, tmp_out=None):
     """Varlen attention; q [T, H, Dk], out [T, H, Dv], lse [H, T] (optional); sinks
     [H] float32 attention-sink logits or None; k_scale / v_scale: the pools'
-    per-tensor scales; alibi_slopes [H] float32 or None."""
+    per-tensor scales; alibi_slopes [H] float32 or None.  partition_size > 0 splits
+    sequences of one query token over partitions, with float32 scratch max_logits /
+    exp_sums [S, H, P] and tmp_out [S, H, P, Dv]."""
     pool = make_pool(k_pool, v_pool, k_scale, v_scale)
     _dev(q, "q", ndim=3)
     _dev(out, "out", ndim=3)
@@ -208,9 +210,21 @@ def pa_varlen(k_pool, v_pool, q, out, query_start_loc, seq_lens, positions, bloc
     _dev(status, "status", dtype=torch.int32)
     _dev(sinks, "sinks", dtype=torch.float32, ndim=1)
     _dev(alibi_slopes, "alibi_slopes", dtype=torch.float32, ndim=1)
+    _dev(max_logits, "max_logits", dtype=torch.float32)
+    _dev(exp_sums, "exp_sums", dtype=torch.float32)
+    _dev(tmp_out, "tmp_out", dtype=torch.float32)
     T, H, _ = q.shape
     _shape(sinks, (H,), "sinks")
     _shape(alibi_slopes, (H,), "alibi_slopes")
+    max_partitions = 0
+    if partition_size:
+        if max_logits is None or exp_sums is None or tmp_out is None:
+            raise ValueError("split single-token rows need max_logits, exp_sums and tmp_out")
+        max_partitions = max_logits.shape[-1]
+        S_ = seq_lens.numel()
+        _shape(max_logits, (S_, H, max_partitions), "max_logits")
+        _shape(exp_sums, (S_, H, max_partitions), "exp_sums")
+        _shape(tmp_out, (S_, H, max_partitions, pool.head_dim_v), "tmp_out")
     S = seq_lens.numel()
     _shape(q, (T, H, pool.head_dim_k), "q")
     _shape(out, (T, H, pool.head_dim_v), "out")
@@ -222,8 +236,9 @@ def pa_varlen(k_pool, v_pool, q, out, query_start_loc, seq_lens, positions, bloc
     st = load().pa_varlen(ctypes.byref(pool), _ptr(q), _code(q, "q"), _ptr(out), _code(out, "out"),
                           _ptr(lse), _ptr(query_start_loc), _ptr(seq_lens), _ptr(positions), _ptr(block_tables),
                           block_tables.shape[1], seq_lens.numel(), T, int(max_query_len), H, float(scale),
-                          int(bool(causal)), int(sliding_window), _ptr(sinks), _ptr(alibi_slopes), _ptr(status),
-                          _stream(stream))
+                          int(bool(causal)), int(sliding_window), int(partition_size), int(max_partitions),
+                          _ptr(max_logits), _ptr(exp_sums), _ptr(tmp_out), _ptr(sinks), _ptr(alibi_slopes),
+                          _ptr(status), _stream(stream))
     _check(st, "pa_varlen")
 
 

@@ -286,6 +286,7 @@ int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
               const int32_t* query_start_loc, const int32_t* seq_lens, const int32_t* positions,
               const int32_t* block_tables, int32_t max_blocks, int32_t num_seqs, int64_t num_tokens,
               int32_t max_query_len, int32_t num_heads, float scale, int32_t causal, int32_t sliding_window,
+              int32_t partition_size, int32_t max_partitions, float* max_logits, float* exp_sums, float* tmp_out,
               const float* sinks, const float* alibi_slopes, int32_t* status, void* stream) {
   int st = check_pool(pool);
   if (st != PA_OK) return st;
@@ -311,10 +312,19 @@ int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
   float scale_log2;
   if (!folded_scale(pool, scale, scale_log2)) return PA_EINVAL;
   if (num_tokens > 0x7fffffffLL || num_seqs > 65535) return PA_EUNSUPPORTED;
+  if (partition_size < 0) return PA_EINVAL;
+  if (partition_size > 0) {
+    if (partition_size % pool->block_size != 0) return PA_EINVAL;
+    if (max_partitions < 1 || max_logits == nullptr || exp_sums == nullptr || tmp_out == nullptr)
+      return PA_EINVAL;
+    if (max_partitions > 8192) return PA_EUNSUPPORTED;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (status != nullptr) {
     ValidateArgs v = {};
     v.mode = kValidateVarlen;
+    v.partition_size = partition_size;
+    v.max_partitions = max_partitions;
     v.num_blocks = pool->num_blocks;
     v.block_size = pool->block_size;
     v.block_tables = block_tables;
@@ -361,11 +371,55 @@ int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
   a.alibi = alibi_slopes;
   a.status = status;
 
+  // Sequences of exactly one query token can run split-KV: partitions on the row
+  // kernels (one row per sequence), then the log-sum-exp reduce, which writes their
+  // outputs and lse.
+  const bool fp8 = pool->dtype == PA_FP8_E4M3;
+  const bool rows_take_singles = fp8 || rows_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group);
+  const bool split = partition_size > 0 && rows_take_singles;
+  auto split_singles = [&]() -> int {
+    RowsArgs b = a;
+    b.single_token_seqs = 1;
+    b.skip_single_token_seqs = 0;
+    b.partition_size = partition_size;
+    b.max_partitions = max_partitions;
+    b.max_logits = max_logits;
+    b.exp_sums = exp_sums;
+    b.tmp_out = tmp_out;
+    const dim3 grid((unsigned)num_seqs, (unsigned)pool->num_kv_heads, (unsigned)max_partitions);
+    int rc = from_hip(launch_row_kernel(b, pool->dtype, q_dtype, pool->head_dim_k, pool->head_dim_v, grid, s));
+    if (rc != PA_OK) return rc;
+    ReduceArgs r = {};
+    r.max_logits = max_logits;
+    r.exp_sums = exp_sums;
+    r.tmp_out = tmp_out;
+    r.seq_lens = seq_lens;
+    r.max_blocks = max_blocks;
+    r.block_size = pool->block_size;
+    r.num_seqs = num_seqs;
+    r.num_heads = num_heads;
+    r.head_dim = pool->head_dim_v;
+    r.partition_size = partition_size;
+    r.max_partitions = max_partitions;
+    r.out = out;
+    r.out_dtype = out_dtype;
+    r.sinks = sinks;
+    r.query_start_loc = query_start_loc;
+    r.lse = lse;
+    r.num_rows = num_tokens;
+    r.status = status;
+    return from_hip(launch_reduce(r, s));
+  };
+
   if (!prefill_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group, pool->block_size, pool->num_blocks) || max_query_len <= 1) {
-    // every token through the per-row kernel
+    // every token through the per-row kernel (single-token sequences split, if asked)
+    if (split && max_query_len <= 1) return split_singles();
     a.single_token_seqs = 0;
+    a.skip_single_token_seqs = split ? 1 : 0;
     const dim3 grid((unsigned)num_tokens, (unsigned)pool->num_kv_heads, 1);
-    return from_hip(launch_row_kernel(a, pool->dtype, q_dtype, pool->head_dim_k, pool->head_dim_v, grid, s));
+    st = from_hip(launch_row_kernel(a, pool->dtype, q_dtype, pool->head_dim_k, pool->head_dim_v, grid, s));
+    if (st != PA_OK || !split) return st;
+    return split_singles();
   }
   // sequences with several tokens: tiled MFMA kernel; single tokens: per-row kernel
   PrefillArgs p = {};
@@ -389,7 +443,6 @@ int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
   p.group = group;
   p.block_shift = pow2_shift(pool->block_size);
   p.tokens_per_tile = kPrefillRows / group;
-  const bool rows_take_singles = rows_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group);
   p.min_q_len = rows_take_singles ? 2 : 1;
   p.scale_log2 = scale_log2;
   p.v_scale = pool->v_scale;
@@ -404,6 +457,7 @@ int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
   if (wgs > 0x7fffffffLL) return PA_EUNSUPPORTED;
   st = from_hip(launch_prefill(p, pool->dtype, pool->head_dim_k, pool->head_dim_v, dim3((unsigned)wgs), s));
   if (st != PA_OK || !rows_take_singles) return st;
+  if (split) return split_singles();
   a.single_token_seqs = 1;
   const dim3 grid((unsigned)num_seqs, (unsigned)pool->num_kv_heads, 1);
   return from_hip(launch_row_kernel(a, pool->dtype, q_dtype, pool->head_dim_k, pool->head_dim_v, grid, s));

@@ -105,6 +105,8 @@ __device__ __forceinline__ bool decode_row_range(const RowsArgs& a, int row, int
       if (a.query_start_loc[mid] <= row) lo_s = mid; else hi_s = mid - 1;
     }
     s = lo_s;
+    // sequences of one token run split, in a launch of their own
+    if (a.skip_single_token_seqs && a.query_start_loc[s + 1] - a.query_start_loc[s] == 1) return false;
   }
   n = a.seq_lens[s];
   const int cap = a.max_blocks * a.block_size;

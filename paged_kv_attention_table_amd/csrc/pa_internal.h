@@ -25,6 +25,7 @@ struct RowsArgs {
   const int32_t* query_start_loc;  // nullptr: decode (row = sequence, query at n - 1)
   const int32_t* positions;        // varlen causal positions, nullable
   int single_token_seqs;           // varlen: row = sequence, only sequences of one token
+  int skip_single_token_seqs;      // varlen, row = token: leave sequences of one token out
   int num_seqs;
   int64_t num_rows;  // decode: sequences; varlen: tokens
   int num_heads;
@@ -119,6 +120,12 @@ struct ReduceArgs {
   void* out;
   int out_dtype;
   const float* sinks;  // [num_heads] sink logits, nullable
+  // varlen (nullable for decode): only sequences of exactly one query token were
+  // split; their output row is query_start_loc[s], and lse [num_heads, num_rows]
+  // (nullable) receives M + ln(sum of weights)
+  const int32_t* query_start_loc;
+  float* lse;
+  int64_t num_rows;
   const int32_t* status;
 };
 

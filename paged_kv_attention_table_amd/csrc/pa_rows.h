@@ -81,6 +81,8 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const RowsArgs a) {
       if (a.query_start_loc[mid] <= row) lo_s = mid; else hi_s = mid - 1;
     }
     s = lo_s;
+    // sequences of one token run split, in a launch of their own
+    if (a.skip_single_token_seqs && a.query_start_loc[s + 1] - a.query_start_loc[s] == 1) return;
   }
   int n = a.seq_lens[s];
   const int cap = a.max_blocks * b;

@@ -86,15 +86,15 @@ def test_varlen_host_checks():
     p = ctypes.byref(_pool())
     # causal without positions
     assert lib.pa_varlen(p, FAKE, binding.PA_F16, FAKE, binding.PA_F32, None, FAKE, FAKE, None, FAKE, 4, 2, 10, 8,
-                         4, 0.1, 1, 0, None, None, None, None) == binding.PA_EINVAL
+                         4, 0.1, 1, 0, 0, 0, None, None, None, None, None, None, None) == binding.PA_EINVAL
     # no query_start_loc
     assert lib.pa_varlen(p, FAKE, binding.PA_F16, FAKE, binding.PA_F32, None, None, FAKE, FAKE, FAKE, 4, 2, 10, 8,
-                         4, 0.1, 1, 0, None, None, None, None) == binding.PA_EINVAL
+                         4, 0.1, 1, 0, 0, 0, None, None, None, None, None, None, None) == binding.PA_EINVAL
     # tokens but no sequences
     assert lib.pa_varlen(p, FAKE, binding.PA_F16, FAKE, binding.PA_F32, None, FAKE, FAKE, FAKE, FAKE, 4, 0, 10, 8,
-                         4, 0.1, 1, 0, None, None, None, None) == binding.PA_EINVAL
+                         4, 0.1, 1, 0, 0, 0, None, None, None, None, None, None, None) == binding.PA_EINVAL
     assert lib.pa_varlen(p, FAKE, binding.PA_F16, FAKE, binding.PA_F32, None, FAKE, FAKE, FAKE, FAKE, 4, 2, 10, 8,
-                         5, 0.1, 1, 0, None, None, None, None) == binding.PA_ESHAPE
+                         5, 0.1, 1, 0, 0, 0, None, None, None, None, None, None, None) == binding.PA_ESHAPE
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.125, float("inf"), float("nan")])
@@ -104,7 +104,7 @@ def test_scale_must_be_positive_and_finite(scale):
     assert lib.pa_decode(p, FAKE, binding.PA_F16, FAKE, binding.PA_F32, FAKE, 4, FAKE, 2, 4, scale, 0, 0, 0, None,
                          None, None, None, None, None, None) == binding.PA_EINVAL
     assert lib.pa_varlen(p, FAKE, binding.PA_F16, FAKE, binding.PA_F32, None, FAKE, FAKE, FAKE, FAKE, 4, 2, 10, 8,
-                         4, scale, 1, 0, None, None, None, None) == binding.PA_EINVAL
+                         4, scale, 1, 0, 0, 0, None, None, None, None, None, None, None) == binding.PA_EINVAL
 
 
 def test_write_and_merge_host_checks():
@@ -156,7 +156,7 @@ def _decode(pool, q_dtype=binding.PA_BF16, out_dtype=binding.PA_F32, H=4, scale=
 
 def _varlen(pool, q_dtype=binding.PA_BF16, max_query_len=1, scale=0.1):
     return binding.load().pa_varlen(ctypes.byref(pool), FAKE, q_dtype, FAKE, binding.PA_F32, None, FAKE, FAKE, FAKE,
-                                    FAKE, 4, 2, 10, max_query_len, 4, scale, 1, 0, None, None, None, None)
+                                    FAKE, 4, 2, 10, max_query_len, 4, scale, 1, 0, 0, 0, None, None, None, None, None, None, None)
 
 
 FP8 = dict(dtype=binding.PA_FP8_E4M3, head_dim_k=128, head_dim_v=128)
@@ -208,3 +208,18 @@ def test_folded_scale_must_stay_finite():
     assert _decode(_pool(**FP8, k_scale=1e30), scale=1e30) == binding.PA_EINVAL
     assert _decode(_pool(**FP8, k_scale=1e-30), scale=1e-30) == binding.PA_EINVAL
     assert _varlen(_pool(**FP8, k_scale=1e30), scale=1e30) == binding.PA_EINVAL
+
+
+def test_varlen_split_host_checks():
+    lib = binding.load()
+    p = ctypes.byref(_pool())
+
+    def call(P, pmax, ws):
+        return lib.pa_varlen(p, FAKE, binding.PA_F16, FAKE, binding.PA_F32, None, FAKE, FAKE, FAKE, FAKE, 4, 2, 10, 8,
+                             4, 0.1, 1, 0, P, pmax, ws, ws, ws, None, None, None, None)
+
+    assert call(-16, 4, FAKE) == binding.PA_EINVAL      # negative partition size
+    assert call(24, 4, FAKE) == binding.PA_EINVAL       # not a multiple of the block size
+    assert call(32, 0, FAKE) == binding.PA_EINVAL       # no partitions
+    assert call(32, 4, None) == binding.PA_EINVAL       # missing workspace
+    assert call(32, 8193, FAKE) == binding.PA_EUNSUPPORTED
