@@ -179,6 +179,22 @@ int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
               int32_t max_partitions, float* max_logits, float* exp_sums, float* tmp_out,
               const float* sinks, const float* alibi_slopes, int32_t* status, void* stream);
 
+/* Varlen attention merged into an existing state ("cpu_mla_prefill.cpp",
+ * MlaPrefillAttention then MergeAttnStates, fused): out [num_tokens, num_heads,
+ * head_dim_v] float32 and lse [num_heads, num_tokens] float32 hold a state over some
+ * keys; this call computes the attention of q over its visible positions, as
+ * pa_varlen does, and merges it in as the suffix by pa_merge_states' rules (an lse of
+ * +inf counts as -inf; when both lse are -inf the row is left as it is and its lse
+ * becomes -inf).  The other arguments are pa_varlen's, without split-KV.  lse must be
+ * non-NULL (else PA_EINVAL).  It saves writing this call's state and reading both
+ * back, as a separate pa_merge_states would.  Supported: as pa_varlen. */
+int pa_varlen_merge(const pa_kv_pool* pool, const void* q, int32_t q_dtype, float* out, float* lse,
+                    const int32_t* query_start_loc, const int32_t* seq_lens, const int32_t* positions,
+                    const int32_t* block_tables, int32_t max_blocks, int32_t num_seqs, int64_t num_tokens,
+                    int32_t max_query_len, int32_t num_heads, float scale, int32_t causal,
+                    int32_t sliding_window, const float* sinks, const float* alibi_slopes, int32_t* status,
+                    void* stream);
+
 /* Merge two attention states over disjoint key sets ("cpu_mla_prefill.cpp",
  * MergeAttnStates).  prefix_out, suffix_out, out: [num_tokens, num_heads, head_dim] in
  * dtype; prefix_lse, suffix_lse, out_lse (nullable): float32 [num_heads, num_tokens].

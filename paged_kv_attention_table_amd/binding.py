@@ -22,7 +22,8 @@ PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 DTYPE_CODE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
               torch.float8_e4m3fn: PA_FP8_E4M3}
 
-EXPORTS = ("pa_strerror", "pa_write_kv", "pa_decode", "pa_varlen", "pa_merge_states", "pa_gather_cache")
+EXPORTS = ("pa_strerror", "pa_write_kv", "pa_decode", "pa_varlen", "pa_varlen_merge", "pa_merge_states",
+           "pa_gather_cache")
 
 
 class PaKvPool(ctypes.Structure):
@@ -61,6 +62,9 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.pa_varlen.restype = ctypes.c_int
     lib.pa_varlen.argtypes = [pool_p, vp, i32, vp, i32, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, f32, i32, i32,
                               i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.pa_varlen_merge.restype = ctypes.c_int
+    lib.pa_varlen_merge.argtypes = [pool_p, vp, i32, vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, f32, i32, i32,
+                                    vp, vp, vp, vp]
     lib.pa_merge_states.restype = ctypes.c_int
     lib.pa_merge_states.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i64, i32, vp]
     lib.pa_gather_cache.restype = ctypes.c_int
@@ -240,6 +244,41 @@ def pa_varlen(k_pool, v_pool, q, out, query_start_loc, seq_lens, positions, bloc
                           _ptr(max_logits), _ptr(exp_sums), _ptr(tmp_out), _ptr(sinks), _ptr(alibi_slopes),
                           _ptr(status), _stream(stream))
     _check(st, "pa_varlen")
+
+
+def pa_varlen_merge(k_pool, v_pool, q, out, query_start_loc, seq_lens, positions, block_tables, max_query_len, scale,
+                    causal=True, sliding_window=0, lse=None, status=None, stream=None, sinks=None, k_scale=1.0,
+                    v_scale=1.0, alibi_slopes=None):
+    """pa_varlen's arguments; the attention is merged into the state held by out
+    [T, H, Dv] float32 and lse [H, T] float32 (required), both updated in place."""
+    if lse is None:
+        raise ValueError("pa_varlen_merge needs the state's lse")
+    pool = make_pool(k_pool, v_pool, k_scale, v_scale)
+    _dev(q, "q", ndim=3)
+    _dev(out, "out", dtype=torch.float32, ndim=3)
+    _dev(lse, "lse", dtype=torch.float32, ndim=2)
+    _dev(query_start_loc, "query_start_loc", dtype=torch.int32, ndim=1)
+    _dev(seq_lens, "seq_lens", dtype=torch.int32, ndim=1)
+    _dev(positions, "positions", dtype=torch.int32, ndim=1)
+    _dev(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _dev(status, "status", dtype=torch.int32)
+    _dev(sinks, "sinks", dtype=torch.float32, ndim=1)
+    _dev(alibi_slopes, "alibi_slopes", dtype=torch.float32, ndim=1)
+    T, H, _ = q.shape
+    S = seq_lens.numel()
+    _shape(sinks, (H,), "sinks")
+    _shape(alibi_slopes, (H,), "alibi_slopes")
+    _shape(out, (T, H, pool.head_dim_v), "out")
+    _shape(lse, (H, T), "lse")
+    _shape(query_start_loc, (S + 1,), "query_start_loc")
+    _shape(positions, (T,), "positions")
+    if block_tables.shape[0] != S:
+        raise ValueError("block_tables must have one row per sequence")
+    st = load().pa_varlen_merge(ctypes.byref(pool), _ptr(q), _code(q, "q"), _ptr(out), _ptr(lse),
+                                _ptr(query_start_loc), _ptr(seq_lens), _ptr(positions), _ptr(block_tables),
+                                block_tables.shape[1], S, T, int(max_query_len), H, float(scale), int(bool(causal)),
+                                int(sliding_window), _ptr(sinks), _ptr(alibi_slopes), _ptr(status), _stream(stream))
+    _check(st, "pa_varlen_merge")
 
 
 def pa_merge_states(out, out_lse, prefix_out, prefix_lse, suffix_out, suffix_lse, prefill_tokens_with_context=-1,

@@ -8,17 +8,19 @@ and merge kernels) without printing it; the order used here is
     state <- chunk 0;  state <- merge(state, chunk c) for c = 1 .. C-1;
     out   <- merge(state, new tokens causal).
 A request whose context ends before chunk c contributes an empty (-inf) state for
-it, which the merge rules absorb.
+it, which the merge rules absorb.  Every merge is fused into the attention call that
+produces its suffix (pa_varlen_merge), so the state lives in the caller's out / lse
+and no piece is written out and read back.
 
-The plan holds only device metadata and workspaces; ``run`` issues pa_varlen and
-pa_merge_states calls on the current stream.  No arithmetic happens here.
+The plan holds only device metadata; ``run`` issues pa_varlen / pa_varlen_merge
+calls on the current stream.  No arithmetic happens here.
 """
 from __future__ import annotations
 
 import numpy as np
 import torch
 
-from .binding import pa_merge_states, pa_varlen
+from .binding import pa_varlen, pa_varlen_merge
 
 
 class ChunkedPrefillPlan:
@@ -50,26 +52,19 @@ class ChunkedPrefillPlan:
         self.positions = torch.from_numpy(
             np.concatenate([np.arange(n, dtype=np.int32) for n in new_lens]) if self.T else np.zeros(0, np.int32)
         ).to(device)
-        H, Dv = num_heads, head_dim_v
-        f32 = dict(dtype=torch.float32, device=device)
-        self.state_out = torch.empty((self.T, H, Dv), **f32)
-        self.state_lse = torch.empty((H, self.T), **f32)
-        self.piece_out = torch.empty((self.T, H, Dv), **f32)
-        self.piece_lse = torch.empty((H, self.T), **f32)
+        self.state_lse = torch.empty((num_heads, self.T), dtype=torch.float32, device=device)
 
     def run(self, k_pool, v_pool, q, out, out_lse=None, stream=None):
-        """out [T, H, Dv] (float32) <- attention of q over context chunks + new tokens."""
+        """out [T, H, Dv] (float32) <- attention of q over context chunks + new tokens;
+        out_lse [H, T] (optional) <- its lse."""
+        lse = self.state_lse if out_lse is None else out_lse
         for c, (lens, tab) in enumerate(self.chunks):
-            dst_out, dst_lse = (self.state_out, self.state_lse) if c == 0 else (self.piece_out, self.piece_lse)
-            pa_varlen(k_pool, v_pool, q, dst_out, self.qsl, lens, None, tab, self.max_q, self.scale, causal=False,
-                      lse=dst_lse, stream=stream)
-            if c > 0:
-                pa_merge_states(self.state_out, self.state_lse, self.state_out, self.state_lse, self.piece_out,
-                                self.piece_lse, stream=stream)
+            call = pa_varlen if c == 0 else pa_varlen_merge
+            call(k_pool, v_pool, q, out, self.qsl, lens, None, tab, self.max_q, self.scale, causal=False, lse=lse,
+                 stream=stream)
         if not self.chunks:
             pa_varlen(k_pool, v_pool, q, out, self.qsl, self.new_lens, self.positions, self.new_tables, self.max_q,
-                      self.scale, causal=True, lse=out_lse, stream=stream)
+                      self.scale, causal=True, lse=lse, stream=stream)
             return
-        pa_varlen(k_pool, v_pool, q, self.piece_out, self.qsl, self.new_lens, self.positions, self.new_tables,
-                  self.max_q, self.scale, causal=True, lse=self.piece_lse, stream=stream)
-        pa_merge_states(out, out_lse, self.state_out, self.state_lse, self.piece_out, self.piece_lse, stream=stream)
+        pa_varlen_merge(k_pool, v_pool, q, out, self.qsl, self.new_lens, self.positions, self.new_tables, self.max_q,
+                        self.scale, causal=True, lse=lse, stream=stream)

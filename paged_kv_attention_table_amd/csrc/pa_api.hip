@@ -282,14 +282,21 @@ int pa_decode(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
   return from_hip(launch_reduce(r, s));
 }
 
-int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out, int32_t out_dtype, float* lse,
-              const int32_t* query_start_loc, const int32_t* seq_lens, const int32_t* positions,
-              const int32_t* block_tables, int32_t max_blocks, int32_t num_seqs, int64_t num_tokens,
-              int32_t max_query_len, int32_t num_heads, float scale, int32_t causal, int32_t sliding_window,
-              int32_t partition_size, int32_t max_partitions, float* max_logits, float* exp_sums, float* tmp_out,
-              const float* sinks, const float* alibi_slopes, int32_t* status, void* stream) {
+// pa_varlen and pa_varlen_merge (merge != 0: out, float32, and lse hold a state that
+// this call's attention is merged into).
+static int varlen_impl(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out, int32_t out_dtype,
+                       float* lse, const int32_t* query_start_loc, const int32_t* seq_lens, const int32_t* positions,
+                       const int32_t* block_tables, int32_t max_blocks, int32_t num_seqs, int64_t num_tokens,
+                       int32_t max_query_len, int32_t num_heads, float scale, int32_t causal, int32_t sliding_window,
+                       int32_t partition_size, int32_t max_partitions, float* max_logits, float* exp_sums,
+                       float* tmp_out, const float* sinks, const float* alibi_slopes, int32_t* status, void* stream,
+                       int merge) {
   int st = check_pool(pool);
   if (st != PA_OK) return st;
+  if (merge) {
+    if (lse == nullptr) return PA_EINVAL;
+    if (out_dtype != PA_F32 || partition_size != 0) return PA_EUNSUPPORTED;
+  }
   if (num_seqs < 0 || num_tokens < 0 || num_heads < 1 || max_blocks < 1 || max_query_len < 0) return PA_EINVAL;
   if (query_start_loc == nullptr) return PA_EINVAL;
   if (num_seqs > 0 && (seq_lens == nullptr || block_tables == nullptr)) return PA_EINVAL;
@@ -369,6 +376,7 @@ int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
   a.max_partitions = 1;
   a.sinks = sinks;
   a.alibi = alibi_slopes;
+  a.merge = merge;
   a.status = status;
 
   // Sequences of exactly one query token can run split-KV: partitions on the row
@@ -450,6 +458,7 @@ int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
   p.window = sliding_window;
   p.sinks = sinks;
   p.alibi = alibi_slopes;
+  p.merge = merge;
   p.status = status;
   p.tiles_per_seq = (max_query_len + p.tokens_per_tile - 1) / p.tokens_per_tile;
   const int64_t groups8 = ((int64_t)num_seqs * pool->num_kv_heads + 7) / 8 * 8;
@@ -461,6 +470,28 @@ int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
   a.single_token_seqs = 1;
   const dim3 grid((unsigned)num_seqs, (unsigned)pool->num_kv_heads, 1);
   return from_hip(launch_row_kernel(a, pool->dtype, q_dtype, pool->head_dim_k, pool->head_dim_v, grid, s));
+}
+
+int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out, int32_t out_dtype, float* lse,
+              const int32_t* query_start_loc, const int32_t* seq_lens, const int32_t* positions,
+              const int32_t* block_tables, int32_t max_blocks, int32_t num_seqs, int64_t num_tokens,
+              int32_t max_query_len, int32_t num_heads, float scale, int32_t causal, int32_t sliding_window,
+              int32_t partition_size, int32_t max_partitions, float* max_logits, float* exp_sums, float* tmp_out,
+              const float* sinks, const float* alibi_slopes, int32_t* status, void* stream) {
+  return varlen_impl(pool, q, q_dtype, out, out_dtype, lse, query_start_loc, seq_lens, positions, block_tables,
+                     max_blocks, num_seqs, num_tokens, max_query_len, num_heads, scale, causal, sliding_window,
+                     partition_size, max_partitions, max_logits, exp_sums, tmp_out, sinks, alibi_slopes, status, stream,
+                     0);
+}
+
+int pa_varlen_merge(const pa_kv_pool* pool, const void* q, int32_t q_dtype, float* out, float* lse,
+                    const int32_t* query_start_loc, const int32_t* seq_lens, const int32_t* positions,
+                    const int32_t* block_tables, int32_t max_blocks, int32_t num_seqs, int64_t num_tokens,
+                    int32_t max_query_len, int32_t num_heads, float scale, int32_t causal, int32_t sliding_window,
+                    const float* sinks, const float* alibi_slopes, int32_t* status, void* stream) {
+  return varlen_impl(pool, q, q_dtype, out, PA_F32, lse, query_start_loc, seq_lens, positions, block_tables,
+                     max_blocks, num_seqs, num_tokens, max_query_len, num_heads, scale, causal, sliding_window, 0, 0,
+                     nullptr, nullptr, nullptr, sinks, alibi_slopes, status, stream, 1);
 }
 
 int pa_merge_states(void* out, float* out_lse, const void* prefix_out, const float* prefix_lse,

@@ -41,6 +41,7 @@ struct RowsArgs {
   float* tmp_out;
   const float* sinks;  // [num_heads] sink logits, nullable; unsplit outputs only
   const float* alibi;  // [num_heads] ALiBi slopes, nullable
+  int merge;           // out (float32) and lse hold a state: merge this call's into it
   const int32_t* status;
 };
 

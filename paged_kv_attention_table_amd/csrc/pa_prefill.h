@@ -66,6 +66,7 @@ struct PrefillArgs {
   int window;
   const float* sinks;  // [num_heads] sink logits, nullable
   const float* alibi;  // [num_heads] ALiBi slopes, nullable
+  int merge;           // out (float32) and lse hold a state: merge this call's into it
   const int32_t* status;
 };
 
@@ -130,9 +131,9 @@ struct TileRegs {
   u32x4 v[VN];
 };
 
-// ALIBI: a.alibi is non-null (a separate instantiation, so the loop without it keeps
-// its registers).
-template <typename T, int DK, int DV, bool ALIBI>
+// ALIBI: a.alibi is non-null; MERGE: a.merge is set (separate instantiations, so the
+// loop without them keeps its registers).
+template <typename T, int DK, int DV, bool ALIBI, bool MERGE>
 __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const PrefillArgs a) {
   constexpr int KT = kPrefillKeys;
   constexpr int NTH = kPrefillThreads;
@@ -674,6 +675,25 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
     m_run[rb] = mx;
     const float inv = l > 0.f ? fo * a.v_scale / l : 0.f;
     const int64_t obase = (row_tok[rb] * a.num_heads + row_head[rb]) * (int64_t)DV;
+    const int64_t li = (int64_t)row_head[rb] * a.num_tokens + row_tok[rb];
+    const float lse_new = l > 0.f ? (m_run[rb] * a.scale_log2 + log2f(l)) * kLn2 : -INFINITY;
+    if constexpr (MERGE) {
+      // merge into the state held by out (float32) and lse: this call is the suffix.
+      // The row's four lanes read its lse before one of them writes it (one wave).
+      float wp, ws, lse_m;
+      bool keep;
+      merge_state_weights(a.lse[li], lse_new, wp, ws, lse_m, keep);
+      if (!keep) {
+#pragma unroll
+        for (int nd = 0; nd < ND; ++nd) {
+          float* dst = static_cast<float*>(a.out) + obase + 16 * nd + 4 * c;
+          const f32x4 prev = *reinterpret_cast<const f32x4*>(dst);
+          *reinterpret_cast<f32x4*>(dst) = prev * wp + (o[nd][rb] * inv) * ws;
+        }
+      }
+      if (c == 0) a.lse[li] = lse_m;
+      continue;
+    }
 #pragma unroll
     for (int nd = 0; nd < ND; ++nd) {
       const int d0 = 16 * nd + 4 * c;
@@ -685,21 +705,19 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
         for (int ii = 0; ii < 4; ++ii) store_as(a.out, a.out_dtype, obase + d0 + ii, v[ii]);
       }
     }
-    if (a.lse != nullptr && c == 0)
-      a.lse[(int64_t)row_head[rb] * a.num_tokens + row_tok[rb]] =
-          l > 0.f ? (m_run[rb] * a.scale_log2 + log2f(l)) * kLn2 : -INFINITY;
+    if (a.lse != nullptr && c == 0) a.lse[li] = lse_new;
   }
 }
 
-template <typename T, bool ALIBI>
+template <typename T, bool ALIBI, bool MERGE>
 hipError_t launch_prefill_dims(const PrefillArgs& a, int dk, int dv, dim3 grid, hipStream_t stream) {
   const dim3 block(kPrefillThreads);
   if (dk == 128 && dv == 128)
-    hipLaunchKernelGGL((prefill_kernel<T, 128, 128, ALIBI>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<T, 128, 128, ALIBI, MERGE>), grid, block, 0, stream, a);
   else if (dk == 192 && dv == 128)
-    hipLaunchKernelGGL((prefill_kernel<T, 192, 128, ALIBI>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<T, 192, 128, ALIBI, MERGE>), grid, block, 0, stream, a);
   else if (dk == 64 && dv == 64)
-    hipLaunchKernelGGL((prefill_kernel<T, 64, 64, ALIBI>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<T, 64, 64, ALIBI, MERGE>), grid, block, 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -707,8 +725,11 @@ hipError_t launch_prefill_dims(const PrefillArgs& a, int dk, int dv, dim3 grid, 
 
 template <typename T>
 hipError_t launch_prefill_typed(const PrefillArgs& a, int dk, int dv, dim3 grid, hipStream_t stream) {
-  return a.alibi != nullptr ? launch_prefill_dims<T, true>(a, dk, dv, grid, stream)
-                            : launch_prefill_dims<T, false>(a, dk, dv, grid, stream);
+  if (a.merge)
+    return a.alibi != nullptr ? launch_prefill_dims<T, true, true>(a, dk, dv, grid, stream)
+                              : launch_prefill_dims<T, false, true>(a, dk, dv, grid, stream);
+  return a.alibi != nullptr ? launch_prefill_dims<T, true, false>(a, dk, dv, grid, stream)
+                            : launch_prefill_dims<T, false, false>(a, dk, dv, grid, stream);
 }
 
 }  // namespace pa

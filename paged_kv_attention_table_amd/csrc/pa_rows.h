@@ -244,6 +244,13 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const RowsArgs a) {
 
   // --- merge the waves and write ---------------------------------------------------
   const int G = a.group;
+  // merging into a state held by out (float32) and lse: every head's previous lse is
+  // read before any is written
+  __shared__ float prev_lse[GMAX];
+  if (a.merge) {
+    if ((int)threadIdx.x < G) prev_lse[threadIdx.x] = a.lse[(int64_t)(g * G + threadIdx.x) * a.num_rows + q_row];
+    __syncthreads();
+  }
   for (int idx = threadIdx.x; idx < G * DV; idx += blockDim.x) {
     const int h = idx / DV, d = idx - h * DV;
     const int hq = g * G + h;
@@ -266,9 +273,19 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const RowsArgs a) {
     }
     const float o = L > 0.f ? O * (a.v_scale / L) : 0.f;
     if (a.partition_size == 0) {
-      store_as(a.out, a.out_dtype, (q_row * a.num_heads + hq) * (int64_t)DV + d, o);
-      if (a.lse != nullptr && d == 0)
-        a.lse[(int64_t)hq * a.num_rows + q_row] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+      const int64_t oi = (q_row * a.num_heads + hq) * (int64_t)DV + d;
+      const float lse_new = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+      if (a.merge) {  // this call is the suffix of the merge
+        float wp, ws, lse_m;
+        bool keep;
+        merge_state_weights(prev_lse[h], lse_new, wp, ws, lse_m, keep);
+        float* dst = static_cast<float*>(a.out) + oi;
+        if (!keep) *dst = *dst * wp + o * ws;
+        if (d == 0) a.lse[(int64_t)hq * a.num_rows + q_row] = lse_m;
+      } else {
+        store_as(a.out, a.out_dtype, oi, o);
+        if (a.lse != nullptr && d == 0) a.lse[(int64_t)hq * a.num_rows + q_row] = lse_new;
+      }
     } else {
       const int64_t pi = ((int64_t)s * a.num_heads + hq) * a.max_partitions + part;
       a.tmp_out[pi * DV + d] = o;

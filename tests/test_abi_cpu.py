@@ -19,7 +19,8 @@ def declared_functions():
 
 def test_header_declares_the_calls():
     names = declared_functions()
-    for n in ("pa_write_kv", "pa_decode", "pa_varlen", "pa_merge_states", "pa_gather_cache", "pa_strerror"):
+    for n in ("pa_write_kv", "pa_decode", "pa_varlen", "pa_varlen_merge", "pa_merge_states", "pa_gather_cache",
+              "pa_strerror"):
         assert n in names, names
 
 
@@ -223,3 +224,18 @@ def test_varlen_split_host_checks():
     assert call(32, 0, FAKE) == binding.PA_EINVAL       # no partitions
     assert call(32, 4, None) == binding.PA_EINVAL       # missing workspace
     assert call(32, 8193, FAKE) == binding.PA_EUNSUPPORTED
+
+
+def test_varlen_merge_host_checks():
+    lib = binding.load()
+    p = ctypes.byref(_pool())
+    # the state's lse is required
+    assert lib.pa_varlen_merge(p, FAKE, binding.PA_F16, FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 2, 10, 8, 4, 0.1, 1, 0,
+                               None, None, None, None) == binding.PA_EINVAL
+    # the usual pa_varlen checks apply: q dtype, shape, scale
+    assert lib.pa_varlen_merge(p, FAKE, binding.PA_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 10, 8, 4, 0.1, 1,
+                               0, None, None, None, None) == binding.PA_EUNSUPPORTED
+    assert lib.pa_varlen_merge(p, FAKE, binding.PA_F16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 10, 8, 5, 0.1, 1, 0,
+                               None, None, None, None) == binding.PA_ESHAPE
+    assert lib.pa_varlen_merge(p, FAKE, binding.PA_F16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 10, 8, 4, 0.0, 1, 0,
+                               None, None, None, None) == binding.PA_EINVAL
