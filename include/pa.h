@@ -17,8 +17,9 @@
  *   - A query at position pos of a sequence of seq_len tokens sees positions
  *     [start, end): end = pos + 1 when causal, else seq_len; start = max(0, end -
  *     sliding_window) when sliding_window > 0, else 0.  Scores are
- *     scale * <q, k_j>, normalised by softmax over the visible positions; scale
- *     must be finite and > 0 (else PA_EINVAL).
+ *     scale * <q, k_j> (plus an ALiBi term when slopes are given, see pa_decode),
+ *     normalised by softmax over the visible positions; scale must be finite and
+ *     > 0 (else PA_EINVAL).
  *   - lse arrays are float32 [num_heads, tokens] in natural log; a row that sees no
  *     position has output 0 and lse -inf ("cpu_mla_prefill.cpp", MlaPrefillAttention).
  *   - Every stored K element counts as its value times the pool's k_scale, every V
@@ -26,7 +27,8 @@
  *     the KV gather); 1.0 leaves a cache as stored.  A pool of PA_FP8_E4M3 holds
  *     the OCP 8-bit E4M3 format (4 exponent bits, bias 7, 3 fraction bits, largest
  *     finite 448, no infinities) -- the fp8 KV caches of "Paged attention for decode
- *     in C" (table of extensions); its queries and outputs are f16 or bf16.
+ *     in C" (table of extensions); its queries are f16 or bf16 (outputs float32 or
+ *     the queries' type).
  *
  * Ownership and streams: the caller owns every buffer.  The library allocates no
  * memory, keeps no state between calls, and enqueues all work on `stream` (a
