@@ -10,6 +10,7 @@ sum over sequences and kv heads of the visible positions times
     python bench.py [--gpus 1] [--steps K] [--warmup W]
                     [--workload decode|long|decode-fp8|long-fp8|varlen|mla|gather]
                     [--partition-size P] [--no-cpu-baseline] [--copy-calibration] [--sweep]
+                    [--ceilings]
 
 decode-fp8 / long-fp8 are the same decode workloads over an fp8 (E4M3) cache with
 per-tensor k_scale / v_scale (queries stay f16 / bf16); their bytes count one byte
@@ -27,7 +28,10 @@ the timed region, three launches of a 1 GiB elementwise copy (torch.neg) that th
 counter runs use as the known-size reference.  --sweep (decode workloads) adds, after
 the timed region, each partition size in {0, 512, 1024}, the cost of device
 validation, that of per-head attention sinks and that of ALiBi slopes, each as the
-median of 20 calls with the caches flushed between calls.
+median of 20 calls with the caches flushed between calls.  --ceilings adds, after
+the timed region, what plain library work reaches on the same GPU as context for the
+roofline fractions: a 1 GiB device copy (GB/s read + written) and an 8192^3 bf16
+matrix product (TFLOP/s), each the median of 10 event-timed runs.
 """
 from __future__ import annotations
 
@@ -63,6 +67,7 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--ceilings", action="store_true")
     return ap.parse_args()
 
 
@@ -110,6 +115,32 @@ def copy_calibration():
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
     del src, dst
+
+
+def ceilings():
+    """Measured context for the peaks: a 1 GiB copy and an 8192^3 bf16 matrix
+    product (contiguous operands), median of 10 runs each."""
+    import torch
+
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    nb = src.numel() * 4
+    for _ in range(2):
+        torch.neg(src, out=dst)
+    _, copy_ms = time_calls(lambda: torch.neg(src, out=dst), 10)
+    del src, dst
+    n = 8192
+    a = torch.randn((n, n), device="cuda").to(torch.bfloat16)
+    b = torch.randn((n, n), device="cuda").to(torch.bfloat16)
+    c = torch.empty((n, n), dtype=torch.bfloat16, device="cuda")
+    for _ in range(2):
+        torch.matmul(a, b, out=c)
+    _, mm_ms = time_calls(lambda: torch.matmul(a, b, out=c), 10)
+    torch.cuda.synchronize()
+    del a, b, c
+    return {"copy_gbs": round(2 * nb / (copy_ms * 1e-3) / 1e9, 1),
+            "gemm_bf16_tflops": round(2 * n ** 3 / (mm_ms * 1e-3) / 1e12, 1),
+            "what": "torch.neg 1 GiB copy (read + written), torch.matmul 8192^3 bf16; median of 10"}
 
 
 def host_cores():
@@ -316,6 +347,8 @@ def run_prefill(args):
             "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
                          "kernel": kernel_label, "avg_ms": round(avg_ms, 5), "median_ms": round(med_ms, 5)}}
+    if args.ceilings:
+        line["ceilings"] = ceilings()
     if args.copy_calibration:
         copy_calibration()
     print(json.dumps(line), flush=True)
@@ -353,6 +386,8 @@ def run_gather(args):
             "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                          "kernel": "gather_cache_kernel", "avg_ms": round(avg_ms, 5), "median_ms": round(med_ms, 5)}}
+    if args.ceilings:
+        line["ceilings"] = ceilings()
     print(json.dumps(line), flush=True)
 
 
@@ -454,6 +489,8 @@ def main():
         _, med_alibi = time_calls(lambda: decode(alibi=slopes), 20, flush=flush)
         line["sweep"] = {"cold_gbs_by_partition_size": sweep, "validation_ms": round(med_status - med_plain, 5),
                          "sinks_ms": round(med_sinks - med_plain, 5), "alibi_ms": round(med_alibi - med_plain, 5)}
+    if args.ceilings:
+        line["ceilings"] = ceilings()
     if args.copy_calibration:
         copy_calibration()
     if not args.no_cpu_baseline:
