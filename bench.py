@@ -267,6 +267,96 @@ def chunked_flops(cp):
     return int(total) * cp.num_heads * 2 * (cp.dk + cp.dv)
 
 
+def _timed_rows(run, per_row_flops, total_rows, budget_s, what):
+    """Times run(m) (the oracle on the first m rows) on a bounded sample: a short
+    calibration call, then m sized to the budget and the call repeated until about
+    budget_s seconds of host time have passed.  Reports GFLOP/s of visible pairs."""
+    m0 = min(total_rows, 16)
+    t0 = time.perf_counter()
+    run(m0)
+    per = (time.perf_counter() - t0) / max(float(per_row_flops[:m0].sum()), 1.0)
+    cum = np.cumsum(per_row_flops)
+    m = int(np.searchsorted(cum, budget_s / max(per, 1e-18))) + 1
+    m = max(m0, min(total_rows, m))
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        run(m)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= budget_s or dt + dt / reps > 1.5 * budget_s:
+            break
+    fl = float(cum[m - 1]) * reps
+    return {"value": round(fl / dt / 1e9, 4), "unit": "GFLOP/s", "cores": host_cores(), "kind": "oracle",
+            "sample": f"{what}: first {m} of {total_rows} query tokens (all heads), repeated {reps} times, {dt:.1f} s"}
+
+
+def cpu_baseline_varlen(w, budget_s):
+    """The oracle's varlen (fp64) on the first rows of the packed mixed call."""
+    from oracle import oracle as orc_mod
+
+    orc = orc_mod.get()
+    kp, vp = w.k_pool.copy(), w.v_pool.copy()
+    orc.write_kv(kp, vp, w.dtype, w.k_new, w.v_new, w.slot_mapping)
+    T, H = w.num_tokens, w.num_heads
+    per_row = np.zeros(T, dtype=np.float64)
+    for s in range(w.num_seqs):
+        t0, t1 = int(w.query_start_loc[s]), int(w.query_start_loc[s + 1])
+        end = w.positions[t0:t1].astype(np.int64) + 1
+        start = np.maximum(0, end - w.sliding_window) if w.sliding_window > 0 else np.zeros_like(end)
+        per_row[t0:t1] = (end - start) * H * 2 * (w.dk + w.dv)
+
+    def run(m):
+        mask = np.zeros((T, H), dtype=np.uint8)
+        mask[:m] = 1
+        st, _, _ = orc.varlen(kp, vp, w.dtype, w.q, w.dtype, w.query_start_loc, w.seq_lens, w.positions,
+                              w.block_tables, w.scale, True, w.sliding_window, row_mask=mask, threads=host_cores())
+        assert st == 0
+
+    return _timed_rows(run, per_row, T, budget_s, "oracle varlen call, causal, window")
+
+
+def cpu_baseline_chunked(cp, budget_s):
+    """The oracle on the chunked composition for the first request's first rows: its
+    varlen (fp64) per context chunk and for the causal new tokens, the states folded
+    with its merge_states in the driver's order."""
+    from oracle import oracle as orc_mod
+
+    orc = orc_mod.get()
+    kp, vp = cp.k_pool.copy(), cp.v_pool.copy()
+    orc.write_kv(kp, vp, cp.dtype, cp.k_new, cp.v_new, cp.slot_mapping)
+    T, H = cp.num_tokens, cp.num_heads
+    ctx0, n0 = int(cp.ctx_lens[0]), int(cp.new_lens[0])
+    per_row = (ctx0 + np.arange(1, n0 + 1, dtype=np.float64)) * H * 2 * (cp.dk + cp.dv)
+    per = cp.chunk // cp.block_size
+    qsl = np.zeros(cp.ctx_lens.size + 1, dtype=np.int32)
+    qsl[1:] = np.cumsum(cp.new_lens)
+    positions = np.concatenate([np.arange(n, dtype=np.int32) for n in cp.new_lens])
+    nchunks = -(-int(cp.ctx_lens.max()) // cp.chunk)
+
+    def run(m):
+        mask = np.zeros((T, H), dtype=np.uint8)
+        mask[:m] = 1
+        state = None
+        for c in range(nchunks + 1):
+            if c < nchunks:
+                lens = np.clip(cp.ctx_lens - c * cp.chunk, 0, cp.chunk).astype(np.int32)
+                tab = np.ascontiguousarray(cp.ctx_tables[:, c * per:(c + 1) * per])
+                if tab.shape[1] == 0:
+                    continue
+                st, o, l = orc.varlen(kp, vp, cp.dtype, cp.q, cp.dtype, qsl, lens, None, tab, cp.scale, False, 0,
+                                      row_mask=mask, threads=host_cores())
+            else:
+                st, o, l = orc.varlen(kp, vp, cp.dtype, cp.q, cp.dtype, qsl, cp.new_lens.astype(np.int32), positions,
+                                      cp.new_tables, cp.scale, True, 0, row_mask=mask, threads=host_cores())
+            assert st == 0
+            o, l = o[:m].astype(np.float32), np.ascontiguousarray(l[:, :m]).astype(np.float32)
+            state = (o, l) if state is None else orc.merge_states(state[0], state[1], o, l, "f32")[:2]
+            state = (np.asarray(state[0], dtype=np.float32), np.asarray(state[1], dtype=np.float32))
+
+    return _timed_rows(run, per_row, n0, budget_s, "oracle chunked composition of request 0 (context chunks "
+                       "+ causal new tokens, merged)")
+
+
 def run_prefill(args):
     """Secondary workloads: mixed varlen (config of 4 prefill chunks + 12 decode
     tokens) or the MLA-style chunked prefill.  Prints one JSON line in TFLOP/s."""
@@ -327,11 +417,12 @@ def run_prefill(args):
         def write():
             pa_write_kv(kp, vp, k_new, v_new, slots)
 
-        kernel_label = "chunked prefill (pa_varlen per context chunk + causal new tokens + pa_merge_states)"
+        kernel_label = ("chunked prefill (pa_varlen on the first context chunk, pa_varlen_merge on the others "
+                        "and on the causal new tokens)")
         name, dtype = cp.name, cp.dtype
         cfg = {"workload": name, "requests": int(cp.ctx_lens.size), "num_tokens": cp.num_tokens,
                "num_heads": cp.num_heads, "head_dim_k": cp.dk, "head_dim_v": cp.dv, "chunk": cp.chunk,
-               "step": "pa_write_kv + chunked pa_varlen + pa_merge_states"}
+               "step": "pa_write_kv + chunked prefill (pa_varlen, then pa_varlen_merge)"}
     def step():
         write()
         attn()
@@ -351,6 +442,9 @@ def run_prefill(args):
         line["ceilings"] = ceilings()
     if args.copy_calibration:
         copy_calibration()
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = (cpu_baseline_varlen(w, args.cpu_budget_s) if args.workload == "varlen"
+                                else cpu_baseline_chunked(cp, args.cpu_budget_s))
     print(json.dumps(line), flush=True)
 
 
