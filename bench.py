@@ -357,6 +357,24 @@ def cpu_baseline_chunked(cp, budget_s):
                        "+ causal new tokens, merged)")
 
 
+def cpu_baseline_gather(g, budget_s):
+    """The oracle's latent-cache gather on the whole workload, repeated to the budget."""
+    from oracle import oracle as orc_mod
+
+    orc = orc_mod.get()
+    T, D = int(g.cu_seq_lens[-1]), g.cache.shape[2]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        st, _ = orc.gather_cache(g.cache, g.dtype, g.block_tables, g.cu_seq_lens, g.token_to_seq, None, g.dtype, T)
+        assert st == 0
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= budget_s or dt + dt / reps > 1.5 * budget_s:
+            break
+    return {"value": round(T * D * 2 * 2 * reps / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"the whole gather ({T} rows of {D}), one thread, repeated {reps} times, {dt:.1f} s"}
+
+
 def run_prefill(args):
     """Secondary workloads: mixed varlen (config of 4 prefill chunks + 12 decode
     tokens) or the MLA-style chunked prefill.  Prints one JSON line in TFLOP/s."""
@@ -482,6 +500,8 @@ def run_gather(args):
                          "kernel": "gather_cache_kernel", "avg_ms": round(avg_ms, 5), "median_ms": round(med_ms, 5)}}
     if args.ceilings:
         line["ceilings"] = ceilings()
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_gather(g, args.cpu_budget_s)
     print(json.dumps(line), flush=True)
 
 
