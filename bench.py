@@ -73,7 +73,10 @@ def parse():
 
 CSRC = os.path.join(ROOT, "paged_kv_attention_table_amd", "csrc")
 KERNEL_SOURCES = {"decode_mfma_kernel": ("pa_decode.h", "pa_common.h", "pa_misc.hip"),
-                  "prefill_kernel": ("pa_prefill.h", "pa_common.h")}
+                  "prefill_kernel": ("pa_prefill.h", "pa_common.h"),
+                  "pa_varlen_call": ("pa_prefill.h", "pa_decode.h", "pa_rows.h", "pa_common.h", "pa_misc.hip",
+                                     "pa_api.hip")}
+TRAFFIC_TABLES = ("traffic.md", "traffic_prefill.md")
 
 
 def kernel_source_hash(kernel):
@@ -85,22 +88,23 @@ def kernel_source_hash(kernel):
 
 
 def traffic_lookup(kernel, workload, partition_size):
-    """HBM bytes per launch (read, write) recorded in profiles/traffic.md for this
-    kernel, workload and partition size, or None when absent or when the kernel's
-    sources changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "traffic.md")
-    if not os.path.exists(path):
-        return None
+    """HBM bytes per launch (read, write) recorded in the traffic tables under
+    profiles/ for this kernel (or call), workload and partition size, or None when
+    absent or when the sources changed since the counters were taken."""
     want = kernel_source_hash(kernel)
-    for line in open(path):
-        cells = [c.strip() for c in line.strip().strip("|").split("|")]
-        if len(cells) < 6 or cells[0] != kernel:
+    for table in TRAFFIC_TABLES:
+        path = os.path.join(ROOT, "profiles", table)
+        if not os.path.exists(path):
             continue
-        if cells[1] == workload and cells[2] == str(partition_size) and cells[3] == want:
-            try:
-                return int(cells[4]), int(cells[5])
-            except ValueError:
-                return None
+        for line in open(path):
+            cells = [c.strip() for c in line.strip().strip("|").split("|")]
+            if len(cells) < 6 or cells[0] != kernel:
+                continue
+            if cells[1] == workload and cells[2] == str(partition_size) and cells[3] == want:
+                try:
+                    return int(cells[4]), int(cells[5])
+                except ValueError:
+                    return None
     return None
 
 
@@ -456,6 +460,10 @@ def run_prefill(args):
             "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
                          "kernel": kernel_label, "avg_ms": round(avg_ms, 5), "median_ms": round(med_ms, 5)}}
+    t = traffic_lookup("pa_varlen_call", name, P if args.workload == "varlen" else 0)
+    if t is not None:
+        line["roofline"]["traffic"] = t[0] + t[1]
+        line["roofline"]["traffic_read"], line["roofline"]["traffic_write"] = t
     if args.ceilings:
         line["ceilings"] = ceilings()
     if args.copy_calibration:
