@@ -25,10 +25,11 @@ profiles/traffic.md and reported only while the kernel's source hash still match
 the one recorded there.  The cpu_baseline object times the CPU oracle on a bounded
 sample of the same workload on the host cores.  --copy-calibration appends, after
 the timed region, three launches of a 1 GiB elementwise copy (torch.neg) that the
-counter runs use as the known-size reference.  --sweep (decode workloads) adds, after
-the timed region, each partition size in {0, 512, 1024}, the cost of device
-validation, that of per-head attention sinks and that of ALiBi slopes, each as the
-median of 20 calls with the caches flushed between calls.  --ceilings adds, after
+counter runs use as the known-size reference.  --sweep adds, after the timed region,
+for the decode workloads each partition size in {0, 512, 1024}, the cost of device
+validation, that of per-head attention sinks and that of ALiBi slopes, and for the
+prefill workloads the call's cold rate (and, for the varlen call, the cost of device
+validation), each as the median of 20 calls with the caches flushed between calls.  --ceilings adds, after
 the timed region, what plain library work reaches on the same GPU as context for the
 roofline fractions: a 1 GiB device copy (GB/s read + written) and an 8192^3 bf16
 matrix product (TFLOP/s), each the median of 10 event-timed runs.
@@ -406,10 +407,10 @@ def run_prefill(args):
                                                          (w.num_seqs, w.num_heads, pmax),
                                                          (w.num_seqs, w.num_heads, pmax, w.dv))] if P else [None] * 3
 
-        def attn():
+        def attn(status=None):
             pa_varlen(kp, vp, q, out, qsl, lens, pos, tables, max_q, w.scale, causal=True,
                       sliding_window=w.sliding_window, lse=lse, partition_size=P, max_logits=ws[0],
-                      exp_sums=ws[1], tmp_out=ws[2])
+                      exp_sums=ws[1], tmp_out=ws[2], status=status)
 
         def write():
             pa_write_kv(kp, vp, k_new, v_new, slots)
@@ -460,6 +461,21 @@ def run_prefill(args):
             "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
                          "kernel": kernel_label, "avg_ms": round(avg_ms, 5), "median_ms": round(med_ms, 5)}}
+    if args.sweep:
+        # context, after the timed region: the call with the caches flushed between
+        # calls (median of 20), and for the varlen call the cost of device validation
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        flush = lambda: scratch.fill_(1)  # noqa: E731
+        _, med_cold = time_calls(attn, 20, flush=flush)
+        sw = {"cold_tflops": round(flops / (med_cold * 1e-3) / 1e12, 1), "cold_ms": round(med_cold, 5)}
+        if args.workload == "varlen":
+            status = torch.zeros(1, dtype=torch.int32, device="cuda")
+            _, med_status = time_calls(lambda: attn(status), 20, flush=flush)
+            if int(status.item()) != 0:
+                raise RuntimeError(f"device validation reported status {int(status.item())}")
+            sw["validation_ms"] = round(med_status - med_cold, 5)
+        del scratch
+        line["sweep"] = sw
     t = traffic_lookup("pa_varlen_call", name, P if args.workload == "varlen" else 0)
     if t is not None:
         line["roofline"]["traffic"] = t[0] + t[1]
