@@ -521,6 +521,9 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
       // (pipelined: V reads stay below the P products; hoisted among them they push
       // the loop past 256 VGPRs)
       if constexpr (PIPE) __builtin_amdgcn_sched_barrier(0);
+      // (pipelined: the PV products issue at raised wave priority, so that with two
+      // waves on a SIMD the one holding MFMA work is served first; +1 %)
+      if constexpr (PIPE) __builtin_amdgcn_s_setprio(1);
       const int tr_r = r16 >> 2, tr_q = r16 & 3;
 #pragma unroll
       for (int nd = 0; nd < ND; ++nd) {
@@ -554,6 +557,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
           l_acc[rb] = mfma_16x16x32<BF16>(u32x4{one2, one2, one2, one2}, pl[rb], l_acc[rb]);
         }
       }
+      if constexpr (PIPE) __builtin_amdgcn_s_setprio(0);
     };
 
     // Software pipeline over key tiles, in rings of NBUF LDS buffers (tile j in
@@ -588,11 +592,15 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
     auto step = [&](int i, auto slot_tag, auto more, auto live_tag) {
       constexpr bool LIVE = decltype(live_tag)::value;
       constexpr int B = decltype(slot_tag)::value, B1 = (B + 1) % NBUF, BK = (B + KA) % NBUF;
+      // the next tiles' loads also issue at raised priority (pipelined), so that they
+      // leave early and their latency hides under this step
+      if constexpr (PIPE) __builtin_amdgcn_s_setprio(1);
       if (more) {
         fetch_v(rq[B1], RV);
         rq[BK] = tile_rows(min(i + KA, last));
         dma_k(rq[BK], BK);
       }
+      if constexpr (PIPE) __builtin_amdgcn_s_setprio(0);
       if constexpr (!LIVE) {
         // no real row in this wave: nothing to compute
       } else if constexpr (PIPE) {
