@@ -390,7 +390,7 @@ def run_prefill(args):
     from paged_kv_attention_table_amd.chunked import ChunkedPrefillPlan
 
     if args.workload == "varlen":
-        w = W.config4()
+        w = W.mixed_varlen()
         kp, vp = dev(w.k_pool, w.dtype), dev(w.v_pool, w.dtype)
         q = dev(w.q, w.dtype)
         qsl, lens, pos, tables = dev(w.query_start_loc), dev(w.seq_lens), dev(w.positions), dev(w.block_tables)
@@ -423,7 +423,7 @@ def run_prefill(args):
                "sliding_window": w.sliding_window, "single_token_partition_size": P,
                "step": "pa_write_kv + pa_varlen"}
     else:
-        cp = W.config5()
+        cp = W.mla_chunked()
         kp, vp = dev(cp.k_pool, cp.dtype), dev(cp.v_pool, cp.dtype)
         q = dev(cp.q, cp.dtype)
         k_new, v_new, slots = dev(cp.k_new, cp.dtype), dev(cp.v_new, cp.dtype), dev(cp.slot_mapping)
@@ -544,7 +544,7 @@ def main():
     if args.workload == "gather":
         return run_gather(args)
     base = args.workload.removesuffix("-fp8")
-    w = W.config2() if base == "decode" else W.config3()
+    w = W.batched_decode() if base == "decode" else W.long_decode()
     if args.workload.endswith("-fp8"):
         w = W.to_fp8(w)
     if args.partition_size is not None:

@@ -229,14 +229,14 @@ def make_decode(name, seed, *, seq_lens, dtype, num_heads, num_kv_heads, head_di
 # The five workloads, at full size and scaled down (same structure, fewer tokens).
 # ---------------------------------------------------------------------------------
 
-def config1():
+def tiny_decode():
     """Tiny decode: seqLens {1, 17, 33, 100}, H=4, Hkv=2, D=64, b=16, fp32, pool of 64
     blocks whose ids come from one seeded permutation, scale 1/8, causal, no window."""
     return make_decode("tiny-decode", 1001, seq_lens=[1, 17, 33, 100], dtype="f32", num_heads=4,
                        num_kv_heads=2, head_dim=64, scale=1.0 / 8.0, pool_blocks=64)
 
 
-def config2(small=False, partition_size=512):
+def batched_decode(small=False, partition_size=512):
     """Batched decode, Llama-8B-like: 64 sequences, lengths uniform in [512, 4096],
     H=32, Hkv=8, D=128, f16, scale 1/sqrt(128); 8 forks share their first 256 tokens."""
     seed = 1002
@@ -249,7 +249,7 @@ def config2(small=False, partition_size=512):
                        shared=(fork_ids, prefix // 16))
 
 
-def config3(small=False):
+def long_decode(small=False):
     """Long-context split-KV decode: 8 sequences, lengths uniform in [32768, 131072],
     H=64, Hkv=8, D=128, bf16, partitions of 512 (up to 256 of them)."""
     seed = 1003
@@ -261,7 +261,7 @@ def config3(small=False):
                        max_partitions=pmax)
 
 
-def config4(small=False, shuffle=False):
+def mixed_varlen(small=False, shuffle=False):
     """Mixed continuous batching: 4 prefill chunks of 512 new tokens on contexts uniform
     in [0, 2048], then 12 decode tokens on contexts uniform in [256, 8192], packed in
     one query_start_loc; H=32, Hkv=8, D=128, bf16, causal, window 1024."""
@@ -363,7 +363,7 @@ def make_chunked_prefill(name, seed, *, ctx_lens, new_lens, num_heads, dk, dv, d
                           seed=seed)
 
 
-def config5(small=False, permuted=False):
+def mla_chunked(small=False, permuted=False):
     """MLA-style chunked prefill: 8 requests, new tokens uniform in [256, 1024]
     (causal), context uniform in [0, 16384] read in non-causal chunks of 4096;
     H=128 (no GQA), QK dim 192, V dim 128, bf16."""

@@ -63,17 +63,17 @@ def assert_close(got, want, tol, what, mask=None):
 def workload(name):
     """Cached seeded workloads by name."""
     table = {
-        "config1": W.config1,
-        "config2": lambda: W.config2(),
-        "config2-small": lambda: W.config2(small=True),
-        "config3": lambda: W.config3(),
-        "config3-small": lambda: W.config3(small=True),
-        "config4": lambda: W.config4(),
-        "config4-small": lambda: W.config4(small=True),
-        "config4-shuffled": lambda: W.config4(shuffle=True),
-        "config5": lambda: W.config5(),
-        "config5-small": lambda: W.config5(small=True),
-        "config5-small-permuted": lambda: W.config5(small=True, permuted=True),
+        "tiny-decode": W.tiny_decode,
+        "batched-decode": lambda: W.batched_decode(),
+        "batched-decode-small": lambda: W.batched_decode(small=True),
+        "long-decode": lambda: W.long_decode(),
+        "long-decode-small": lambda: W.long_decode(small=True),
+        "mixed-varlen": lambda: W.mixed_varlen(),
+        "mixed-varlen-small": lambda: W.mixed_varlen(small=True),
+        "mixed-varlen-shuffled": lambda: W.mixed_varlen(shuffle=True),
+        "mla-chunked": lambda: W.mla_chunked(),
+        "mla-chunked-small": lambda: W.mla_chunked(small=True),
+        "mla-chunked-small-permuted": lambda: W.mla_chunked(small=True, permuted=True),
     }
     return table[name]()
 

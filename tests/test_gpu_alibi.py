@@ -69,8 +69,8 @@ def check_decode(orc, w, P, sinks=None, window=None, pmax=None):
         assert_close(to, rto, tol, "tmp_out", mask=used)
 
 
-DECODE = [("config1", 0), ("config1", 16), ("config2-small", 0), ("config2-small", 512), ("config3-small", 512),
-          ("config2", 0), ("config3", 512)]
+DECODE = [("tiny-decode", 0), ("tiny-decode", 16), ("batched-decode-small", 0), ("batched-decode-small", 512), ("long-decode-small", 512),
+          ("batched-decode", 0), ("long-decode", 512)]
 
 
 @pytest.mark.parametrize("name,P", DECODE, ids=[f"{n}-P{p}" for n, p in DECODE])
@@ -79,11 +79,11 @@ def test_alibi_decode(orc, name, P):
 
 
 def test_alibi_decode_one_wave_partitions_and_window(orc):
-    check_decode(orc, workload("config2-small"), 16, window=100, pmax=4096)
+    check_decode(orc, workload("batched-decode-small"), 16, window=100, pmax=4096)
 
 
 def test_alibi_decode_with_sinks(orc):
-    w = workload("config2-small")
+    w = workload("batched-decode-small")
     rng = np.random.default_rng(61)
     z = (rng.standard_normal(w.num_heads) * 3).astype(np.float32)
     z[::4] = -np.inf
@@ -93,7 +93,7 @@ def test_alibi_decode_with_sinks(orc):
 
 @pytest.mark.parametrize("P", [0, 512])
 def test_alibi_decode_fp8(orc, P):
-    check_decode(orc, W.to_fp8(workload("config2-small"), q_dtype="bf16"), P)
+    check_decode(orc, W.to_fp8(workload("batched-decode-small"), q_dtype="bf16"), P)
 
 
 def run_varlen(orc, w, causal, window):
@@ -118,8 +118,8 @@ def run_varlen(orc, w, causal, window):
     assert_close(host(lse), rlse, TOL[w.dtype], f"{w.name} causal={causal} w={window} lse")
 
 
-VARLEN = [("config4-small", True, None), ("config4-small", True, 0), ("config4-small", False, 0),
-          ("config4-small", False, 50), ("config4-shuffled", True, None)]
+VARLEN = [("mixed-varlen-small", True, None), ("mixed-varlen-small", True, 0), ("mixed-varlen-small", False, 0),
+          ("mixed-varlen-small", False, 50), ("mixed-varlen-shuffled", True, None)]
 
 
 @pytest.mark.parametrize("name,causal,window", VARLEN, ids=[f"{n}-c{int(c)}-w{w}" for n, c, w in VARLEN])

@@ -34,7 +34,7 @@ def run_decode(d, P, pmax=None, out_dtype=torch.float32, sliding_window=None):
     return out, ws
 
 
-@pytest.mark.parametrize("name", ["config1", "config2-small", "config3-small", "config4-small"])
+@pytest.mark.parametrize("name", ["tiny-decode", "batched-decode-small", "long-decode-small", "mixed-varlen-small"])
 def test_write_kv_bit_exact(orc, name):
     w = workload(name)
     d = OnDevice(w)  # writes through pa_write_kv with a status word
@@ -42,9 +42,9 @@ def test_write_kv_bit_exact(orc, name):
     assert bits_equal(host(d.k_pool), kp) and bits_equal(host(d.v_pool), vp)
 
 
-CASES = [("config1", 0), ("config2-small", 0), ("config2-small", 512), ("config2-small", 32), ("config2-small", 16),
-         ("config3-small", 512), ("config3-small", 0), ("config2", 512), ("config2", 0), ("config2", 1024),
-         ("config3", 512)]
+CASES = [("tiny-decode", 0), ("batched-decode-small", 0), ("batched-decode-small", 512), ("batched-decode-small", 32), ("batched-decode-small", 16),
+         ("long-decode-small", 512), ("long-decode-small", 0), ("batched-decode", 512), ("batched-decode", 0), ("batched-decode", 1024),
+         ("long-decode", 512)]
 
 
 def check_decode(orc, name, P, pmax=None, window=None):
@@ -88,8 +88,8 @@ def test_decode_parity(orc, name, P):
 # items to run one wave per partition (the layout the long-context workload uses) on
 # small inputs: most partitions lie past the context and must stay untouched, and
 # the window empties some partitions wholly.
-ONE_WAVE = [("config2-small", 16, 4096, 0), ("config2-small", 16, 4096, 100), ("config3-small", 64, 2048, 0),
-           ("config3-small", 32, 1000, 700)]
+ONE_WAVE = [("batched-decode-small", 16, 4096, 0), ("batched-decode-small", 16, 4096, 100), ("long-decode-small", 64, 2048, 0),
+           ("long-decode-small", 32, 1000, 700)]
 
 
 @pytest.mark.parametrize("name,P,pmax,win", ONE_WAVE, ids=[f"{n}-P{p}-pmax{m}-w{w}" for n, p, m, w in ONE_WAVE])
@@ -99,7 +99,7 @@ def test_decode_one_wave_partitions(orc, name, P, pmax, win):
 
 def test_decode_window_and_out_dtype(orc):
     """A sliding window on a split decode, and an f16 output (oracle rounded to f16)."""
-    w = workload("config2-small")
+    w = workload("batched-decode-small")
     d = OnDevice(w)
     kp, vp = d.host_pools_after_write(orc)
     for win, P in ((100, 0), (100, 64), (1, 0), (333, 512)):
@@ -119,7 +119,7 @@ def test_decode_window_and_out_dtype(orc):
 def test_decode_batch_invariance(P):
     """A sequence decoded alone gives the same bits as in the batch (decode page,
     section 2.5): the reduction order depends only on the sequence."""
-    w = workload("config2-small")
+    w = workload("batched-decode-small")
     d = OnDevice(w)
     out, _ = run_decode(d, P)
     full = host(out)
@@ -140,7 +140,7 @@ def test_decode_batch_invariance(P):
 def test_decode_forks_read_shared_blocks():
     """Two sequences whose tables name the same blocks, with the same query, give
     the same bits."""
-    w = workload("config2-small")
+    w = workload("batched-decode-small")
     d = OnDevice(w)
     forks = [s for s in range(w.num_seqs) if np.array_equal(w.block_tables[s, :2], w.block_tables[0, :2])]
     tables = d.tables.clone()
@@ -181,7 +181,7 @@ def test_indexing_probe_bit_exact():
 
 
 def test_write_kv_status_rejects_bad_slot():
-    w = workload("config2-small")
+    w = workload("batched-decode-small")
     d = OnDevice(w, write=False)
     before_k, before_v = host(d.k_pool).copy(), host(d.v_pool).copy()
     for bad in (w.num_blocks * w.block_size, -1):

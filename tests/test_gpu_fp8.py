@@ -74,7 +74,7 @@ def check_decode(orc, w, P, pmax=None, window=None, sinks=None):
         assert np.all(np.isnan(ml[~used])) and np.all(np.isnan(to[~used])), "partitions past the context written"
 
 
-@pytest.mark.parametrize("name", ["config2-small", "config3-small"])
+@pytest.mark.parametrize("name", ["batched-decode-small", "long-decode-small"])
 def test_fp8_write_kv_bit_exact(orc, name):
     w = fp8_workload(name)
     d = OnDevice(w)
@@ -83,11 +83,11 @@ def test_fp8_write_kv_bit_exact(orc, name):
 
 
 # (workload, partition size, queries' type): unsplit (8 waves per workgroup), split
-# with 4 waves per partition, and split with one wave per partition (config3: 8 x 8 x
+# with 4 waves per partition, and split with one wave per partition (long_decode: 8 x 8 x
 # 256 items); both query types.
-CASES = [("config2-small", 0, "bf16"), ("config2-small", 0, "f16"), ("config2-small", 512, "bf16"),
-         ("config2-small", 16, "f16"), ("config3-small", 512, "bf16"), ("config3-small", 0, "f16"),
-         ("config2", 0, "f16"), ("config2", 512, "bf16"), ("config3", 512, "bf16")]
+CASES = [("batched-decode-small", 0, "bf16"), ("batched-decode-small", 0, "f16"), ("batched-decode-small", 512, "bf16"),
+         ("batched-decode-small", 16, "f16"), ("long-decode-small", 512, "bf16"), ("long-decode-small", 0, "f16"),
+         ("batched-decode", 0, "f16"), ("batched-decode", 512, "bf16"), ("long-decode", 512, "bf16")]
 
 
 @pytest.mark.parametrize("name,P,qd", CASES, ids=[f"{n}-P{p}-{q}" for n, p, q in CASES])
@@ -99,7 +99,7 @@ def test_fp8_decode_parity(orc, name, P, qd):
 def test_fp8_decode_one_wave_partitions(orc):
     """An oversized max_partitions on a small batch: one wave per partition, most
     partitions past the context (untouched), a window that empties some."""
-    w = fp8_workload("config2-small")
+    w = fp8_workload("batched-decode-small")
     check_decode(orc, w, 16, pmax=4096, window=100)
 
 
@@ -128,7 +128,7 @@ def test_fp8_decode_shapes(orc, H, Hkv, b, window, with_sinks):
 def test_fp8_decode_out_in_query_type(orc):
     """Output in the queries' 16-bit type (the oracle's result rounded to it)."""
     for qd, tt, bits in (("bf16", torch.bfloat16, 8), ("f16", torch.float16, 11)):
-        w = fp8_workload("config2-small", q_dtype=qd)
+        w = fp8_workload("batched-decode-small", q_dtype=qd)
         d = OnDevice(w)
         kp, vp = d.host_pools_after_write(orc)
         out, _ = run_decode(d, 0, out_dtype=tt)
@@ -173,10 +173,10 @@ def test_fp8_varlen_single_tokens(orc):
 
 
 # k_scale / v_scale on pools that are not fp8: (workload, entry point, partition size).
-# config1 is fp32 with head dim 64 (per-row kernel); config2-small f16 (MFMA decode and
-# the split reduce); config4-small bf16 varlen (tiled prefill plus single-token rows).
-SCALED = [("config1", "decode", 0), ("config1", "decode", 16), ("config2-small", "decode", 0),
-          ("config2-small", "decode", 512), ("config4-small", "varlen", 0)]
+# tiny_decode is fp32 with head dim 64 (per-row kernel); batched-decode-small f16 (MFMA decode and
+# the split reduce); mixed-varlen-small bf16 varlen (tiled prefill plus single-token rows).
+SCALED = [("tiny-decode", "decode", 0), ("tiny-decode", "decode", 16), ("batched-decode-small", "decode", 0),
+          ("batched-decode-small", "decode", 512), ("mixed-varlen-small", "varlen", 0)]
 
 
 @pytest.mark.parametrize("name,call,P", SCALED, ids=[f"{n}-{c}-P{p}" for n, c, p in SCALED])

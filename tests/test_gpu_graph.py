@@ -61,7 +61,7 @@ def replays_match_eager(run, outputs, reset=None, reps=3):
 @pytest.mark.parametrize("P", [0, 64])
 def test_graph_write_and_decode(P):
     """pa_write_kv then pa_decode (unsplit, and split with its reduce) in one graph."""
-    w = workload("config2-small")
+    w = workload("batched-decode-small")
     d = OnDevice(w, write=False)
     S, H = w.num_seqs, w.num_heads
     out = torch.empty((S, H, w.dv), device="cuda")
@@ -83,7 +83,7 @@ def test_graph_write_and_decode(P):
 
 def test_graph_mixed_varlen():
     """Prefill tiles and single-token rows of one pa_varlen call, with lse and status."""
-    w = workload("config4-small")
+    w = workload("mixed-varlen-small")
     d = OnDevice(w)
     T, H = w.num_tokens, w.num_heads
     out = torch.empty((T, H, w.dv), dtype=d.q.dtype, device="cuda")
@@ -102,7 +102,7 @@ def test_graph_mixed_varlen():
 def test_graph_varlen_merge_state_reset():
     """pa_varlen_merge reads the state it updates, so the state is reset eagerly before
     each replay; every replay must then give the eager merge."""
-    w = workload("config4-small")
+    w = workload("mixed-varlen-small")
     d = OnDevice(w)
     T, H = w.num_tokens, w.num_heads
     rng = np.random.default_rng(77)
@@ -126,7 +126,7 @@ def test_graph_varlen_merge_state_reset():
 def test_graph_chunked_prefill():
     """The chunked-context driver (pa_varlen, then pa_varlen_merge per further chunk and
     for the causal new tokens) captured whole."""
-    cp = workload("config5-small")
+    cp = workload("mla-chunked-small")
     k_pool, v_pool = dev(cp.k_pool, cp.dtype), dev(cp.v_pool, cp.dtype)
     st = torch.full((1,), -7, dtype=torch.int32, device="cuda")
     pa_write_kv(k_pool, v_pool, dev(cp.k_new, cp.dtype), dev(cp.v_new, cp.dtype), dev(cp.slot_mapping), status=st)

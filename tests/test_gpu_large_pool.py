@@ -70,9 +70,9 @@ def oracle_pools(orc, w):
     return kp, vp
 
 
-@pytest.mark.parametrize("name,fp8,P", [("config2-small", False, 0), ("config2-small", False, 512),
-                                        ("config2-small", True, 0), ("config3-small", True, 512),
-                                        ("config1", False, 0), ("config1", False, 16)])
+@pytest.mark.parametrize("name,fp8,P", [("batched-decode-small", False, 0), ("batched-decode-small", False, 512),
+                                        ("batched-decode-small", True, 0), ("long-decode-small", True, 512),
+                                        ("tiny-decode", False, 0), ("tiny-decode", False, 16)])
 def test_decode_past_2_31_elements(orc, name, fp8, P):
     w = workload(name)
     if fp8:
@@ -103,7 +103,7 @@ def test_decode_past_2_31_elements(orc, name, fp8, P):
 def test_varlen_past_2_31_elements(orc):
     """Prefill tiles (the kernel forms 32-bit pool rows and 64-bit byte offsets) and
     the single-token rows of the mixed workload."""
-    w = workload("config4-small")
+    w = workload("mixed-varlen-small")
     d = BigDevice(w)
     kp, vp = oracle_pools(orc, w)
     T, H = w.num_tokens, w.num_heads

@@ -32,7 +32,7 @@ def decode_status(d, tables=None, lens=None, P=0, pmax=None):
 
 
 def test_decode_rejections():
-    d = OnDevice(workload("config2-small"))
+    d = OnDevice(workload("batched-decode-small"))
     w = d.w
     assert decode_status(d)[0] == 0
     cases = []
@@ -63,7 +63,7 @@ def varlen_status(d, qsl=None, pos=None, lens=None, max_q=None):
 
 
 def test_varlen_rejections():
-    d = OnDevice(workload("config4-small"))
+    d = OnDevice(workload("mixed-varlen-small"))
     w = d.w
     assert varlen_status(d)[0] == 0
     p = d.positions.clone(); p[5] = int(w.seq_lens[0]); assert varlen_status(d, pos=p) == (1, True)

@@ -41,8 +41,8 @@ def run_decode(d, z, P):
     return out, ws
 
 
-@pytest.mark.parametrize("name,P", [("config1", 0), ("config1", 16), ("config2-small", 0), ("config2-small", 512),
-                                    ("config3-small", 0), ("config3-small", 512), ("config2", 0)])
+@pytest.mark.parametrize("name,P", [("tiny-decode", 0), ("tiny-decode", 16), ("batched-decode-small", 0), ("batched-decode-small", 512),
+                                    ("long-decode-small", 0), ("long-decode-small", 512), ("batched-decode", 0)])
 def test_decode_with_sinks(orc, name, P):
     w = workload(name)
     d = OnDevice(w)
@@ -81,7 +81,7 @@ def run_varlen(d, z):
 
 VARLEN = [
     # tiled kernel (D 128, pipelined) plus single-token rows on the decode kernel
-    ("config4-small", None),
+    ("mixed-varlen-small", None),
     # (dtype, H, Hkv, dk, dv, segments, causal, window, block_size)
     ("small", ("bf16", 6, 6, 192, 128, [(0, 70), (300, 21), (17, 0), (64, 64), (90, 1)], True, 0, 16)),
     ("small", ("bf16", 4, 1, 64, 64, [(300, 130), (0, 2), (77, 1)], False, 0, 16)),

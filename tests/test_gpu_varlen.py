@@ -40,7 +40,7 @@ def oracle_varlen(orc, d, causal=None, window=None, row_mask=None):
     return out, lse
 
 
-@pytest.mark.parametrize("name", ["config4-small", "config4", "config4-shuffled"])
+@pytest.mark.parametrize("name", ["mixed-varlen-small", "mixed-varlen", "mixed-varlen-shuffled"])
 def test_varlen_parity(orc, name):
     w = workload(name)
     d = OnDevice(w)
@@ -109,7 +109,7 @@ def test_varlen_bf16_values_beyond_f16(orc):
     bf16 V, so results stay finite and within the bound relative to their size."""
     import dataclasses
 
-    w = workload("config4-small")
+    w = workload("mixed-varlen-small")
     vals = (w.v_new.astype(np.uint32) << 16).view(np.float32).copy()
     starts = w.query_start_loc[:-1]
     vals[starts] *= np.float32(3.0e5)  # the first new token of every sequence, all heads and dims
@@ -144,7 +144,7 @@ def test_varlen_empty_context_rows(orc):
 
 def test_varlen_batch_invariance():
     """A sequence alone, at a different query offset, gives the same bits."""
-    w = workload("config4-small")
+    w = workload("mixed-varlen-small")
     d = OnDevice(w)
     out, lse = run_varlen(d)
     full, full_lse = host(out), host(lse)
@@ -249,7 +249,7 @@ def oracle_chunked(orc, cp, rows):
     return want
 
 
-@pytest.mark.parametrize("name", ["config5-small", "config5-small-permuted"])
+@pytest.mark.parametrize("name", ["mla-chunked-small", "mla-chunked-small-permuted"])
 def test_chunked_prefill_small(orc, name):
     cp = workload(name)
     out, lse = chunked_on_device(cp)
@@ -264,7 +264,7 @@ def test_chunked_prefill_small(orc, name):
 def test_chunked_prefill_full_sampled(orc):
     """Full-size MLA-style workload; the oracle answers 4 seeded heads x 24 seeded
     tokens per request (always including each request's first and last token)."""
-    cp = workload("config5")
+    cp = workload("mla-chunked")
     out, lse = chunked_on_device(cp)
     rng = np.random.default_rng(5005)
     qsl = cp.query_start_loc

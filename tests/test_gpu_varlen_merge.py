@@ -53,14 +53,14 @@ def check(orc, w, causal=True, window=None, sinks=None, alibi=None, seed=91):
     assert_close(host(lse), rlse, TOL[w.dtype], f"{w.name} lse")
 
 
-@pytest.mark.parametrize("name,causal,window", [("config4-small", True, None), ("config4-small", False, 0),
-                                                ("config4-small", True, 7), ("config4-shuffled", True, None)])
+@pytest.mark.parametrize("name,causal,window", [("mixed-varlen-small", True, None), ("mixed-varlen-small", False, 0),
+                                                ("mixed-varlen-small", True, 7), ("mixed-varlen-shuffled", True, None)])
 def test_merge_tiles_and_single_rows(orc, name, causal, window):
     check(orc, workload(name), causal=causal, window=window)
 
 
 def test_merge_with_sinks_and_alibi(orc):
-    w = workload("config4-small")
+    w = workload("mixed-varlen-small")
     rng = np.random.default_rng(93)
     z = rng.standard_normal(w.num_heads) * 2
     z[::3] = -np.inf

@@ -47,19 +47,19 @@ def run(orc, w, P, causal=None, window=None, sinks=None, alibi=None, pmax=None, 
     assert_close(host(lse), rlse, TOL[w.dtype], f"{w.name} P={P} lse")
 
 
-@pytest.mark.parametrize("name,P", [("config4-small", 16), ("config4-small", 128), ("config4-shuffled", 64),
-                                    ("config4", 256)])
+@pytest.mark.parametrize("name,P", [("mixed-varlen-small", 16), ("mixed-varlen-small", 128), ("mixed-varlen-shuffled", 64),
+                                    ("mixed-varlen", 256)])
 def test_split_singles_beside_prefill_tiles(orc, name, P):
     run(orc, workload(name), P)
 
 
 @pytest.mark.parametrize("causal,window", [(False, 0), (False, 100), (True, 0)])
 def test_split_singles_masks(orc, causal, window):
-    run(orc, workload("config4-small"), 32, causal=causal, window=window)
+    run(orc, workload("mixed-varlen-small"), 32, causal=causal, window=window)
 
 
 def test_split_singles_with_sinks_and_alibi(orc):
-    w = workload("config4-small")
+    w = workload("mixed-varlen-small")
     rng = np.random.default_rng(71)
     z = rng.standard_normal(w.num_heads) * 3
     z[::5] = -np.inf
@@ -88,5 +88,5 @@ def test_split_single_token_calls(orc):
 def test_split_partition_count_checked(orc):
     """A workspace with too few partitions for a single-token sequence is refused on
     the device, and nothing is written."""
-    w = workload("config4-small")
+    w = workload("mixed-varlen-small")
     run(orc, w, 16, pmax=2, expect_status=1)
