@@ -140,11 +140,15 @@ __device__ __forceinline__ bool decode_row_range(const RowsArgs& a, int row, int
 // partition]); its waves take the range's tiles round-robin and merge their states
 // through LDS at the end.  WP = true (split, one wave): the wave answers one (row,
 // kv head, partition) alone and writes the partition's state from registers.
-template <typename T, int DK, int NW, bool WP, int NB, bool F8>
+// PR (fp8 only): the workgroup answers a pair of kv heads (2g, 2g + 1) and their 2G q
+// heads; tile rows interleave the two heads slot by slot (row 2p + h is slot p of
+// head h), so each slot's K and V are read as one 256-byte piece.
+template <typename T, int DK, int NW, bool WP, int NB, bool F8, bool PR = false>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, int block_shift, uint32_t grid_rows) {
   static_assert(!WP || NW == 1, "split mode runs one wave per workgroup");
   static_assert(NB >= 2 && NB <= 4, "2 to 4 tile buffers per wave");
   static_assert(!F8 || DK == 128, "fp8 tiles of 128-byte rows");
+  static_assert(!PR || F8, "kv-head pairs on fp8 tiles only");
   constexpr int EB = F8 ? 1 : 2;  // bytes per cache element
   constexpr int DV = 128;         // V rows of 256 bytes (16 lanes x 16 bytes), 128 for fp8
   constexpr int KCH = DK / 32;    // K operands (8 elements) per lane
@@ -184,7 +188,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
   // 1-D grid, kv head fastest: the workgroups of one row's kv heads are dispatched
   // together and stream the same blocks (each head's rows are interleaved with the
   // others' in every slot) at about the same time.
-  const uint32_t wg = blockIdx.x, hkv_u = (uint32_t)a.num_kv_heads;
+  const uint32_t wg = blockIdx.x, hkv_u = (uint32_t)(PR ? a.num_kv_heads / 2 : a.num_kv_heads);
   const int g = (int)(wg % hkv_u);
   int row = (int)((wg / hkv_u) % grid_rows);
   const int pz = (int)(wg / (hkv_u * grid_rows));
@@ -215,9 +219,11 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
 
   const int c = lane >> 4, r16 = lane & 15;
   const int G = a.group, hkv = a.num_kv_heads, b = a.block_size;
+  const int GC = PR ? 2 * G : G, hbase = g * GC;  // q heads answered: hbase .. hbase + GC - 1
+  const int my_h = PR && r16 >= G ? 1 : 0;        // PR: the kv head of this lane's q head
   const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks;
-  const char* kbase = static_cast<const char*>(a.k_pool) + (int64_t)g * DK * EB;
-  const char* vbase = static_cast<const char*>(a.v_pool) + (int64_t)g * DV * EB;
+  const char* kbase = static_cast<const char*>(a.k_pool) + (int64_t)(PR ? 2 * g : g) * DK * EB;
+  const char* vbase = static_cast<const char*>(a.v_pool) + (int64_t)(PR ? 2 * g : g) * DV * EB;
   const int64_t krow = (int64_t)hkv * DK * EB, vrow = (int64_t)hkv * DV * EB;
   const int tr_r = r16 >> 2, tr_q = r16 & 3;
 
@@ -226,11 +232,11 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
   // which the K reads below deliver them)
   u32x4 qb[KCH];
   {
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (q_row * a.num_heads + g * G + r16) * DK;
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (q_row * a.num_heads + hbase + r16) * DK;
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
       const int e0 = F8 ? 32 * c + 8 * u : (4 * u + c) * 8;
-      qb[u] = r16 < G ? *reinterpret_cast<const u32x4*>(qrow + e0) : u32x4{0u, 0u, 0u, 0u};
+      qb[u] = r16 < GC ? *reinterpret_cast<const u32x4*>(qrow + e0) : u32x4{0u, 0u, 0u, 0u};
     }
   }
   // ALiBi ("paged_attention_v2_pytorch.py", phase 1): head r16's slope in raw score
@@ -257,8 +263,8 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
   auto write_state = [&](int p) {
     float l = l_run;
     l = sum_over_groups(l);
-    if (r16 < G) {
-      const int64_t pi = ((int64_t)s * a.num_heads + g * G + r16) * a.max_partitions + p;
+    if (r16 < GC) {
+      const int64_t pi = ((int64_t)s * a.num_heads + hbase + r16) * a.max_partitions + p;
       const float inv = l > 0.f ? a.v_scale / l : 0.f;
       float* dst = a.tmp_out + pi * DV + 4 * c;
 #pragma unroll
@@ -273,7 +279,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
 
   // Tiles of TP positions aligned to absolute positions: 16 for 16-bit caches, 32 for
   // fp8 (the same 8 KB of K and V per tile).
-  constexpr int TSH = F8 ? 5 : 4;
+  constexpr int TSH = F8 && !PR ? 5 : 4;
   constexpr int TP = 1 << TSH;
   const int my_first = (lo >> TSH) + wave;  // this wave's tiles: my_first + NW * i, i < my_tiles
   const int last = (hi - 1) >> TSH;
@@ -307,12 +313,12 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
   // 16-position half lane % 2 of tile i0 + lane / 2 (fp8: with 16-token blocks a tile
   // spans two).  Halves past the sequence read some in-bounds entry of the row; their
   // loads are redirected into the first half below.
-  constexpr int IDS_PER_TILE = F8 ? 2 : 1;
+  constexpr int IDS_PER_TILE = F8 && !PR ? 2 : 1;
   constexpr int TILES_PER_IDS = 64 / IDS_PER_TILE;
   int ids = 0;
   auto load_ids = [&](int i0) {
     const int i = i0 + lane / IDS_PER_TILE;
-    const int half = F8 ? (lane & 1) : 0;
+    const int half = F8 && !PR ? (lane & 1) : 0;
     int idx = (((my_first + NW * (i < my_tiles ? i : 0)) << TSH) + 16 * half) >> block_shift;
     idx = idx < a.max_blocks ? idx : a.max_blocks - 1;
     const int id = table[idx];
@@ -332,7 +338,25 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
     char* kl = sh.t.k[wave][i % NB];
     char* vl = sh.t.v[wave][i % NB];
     const int lim = n - 1 - t0;  // >= 0: every tile starts inside the sequence
-    if constexpr (F8) {
+    if constexpr (PR) {
+      // 16 positions of both heads, in one block: tile row r = 8 ld + lane / 8 is slot
+      // r / 2 of head r % 2; its 16-byte chunk (lane % 8) ^ kswz(r) lands in slot lane % 8
+      const int blk = __builtin_amdgcn_readlane(ids, i & 63);
+      const int64_t s0 = (int64_t)blk * b + (t0 & (b - 1));
+      const char* k0 = kbase + s0 * krow;
+      const char* v0 = vbase + s0 * vrow;
+#pragma unroll
+      for (int ld = 0; ld < 4; ++ld) {
+        const int r = 8 * ld + (lane >> 3);
+        const int pos = (r >> 1) < lim ? (r >> 1) : lim;
+        const int64_t off = (int64_t)pos * krow + (r & 1) * 128 + ((lane & 7) ^ kswz(r)) * 16;
+        __builtin_amdgcn_global_load_lds(k0 + off, (__attribute__((address_space(3))) void*)(kl + ld * KBLK), 16, 0,
+                                         kLoadNT);
+        __builtin_amdgcn_global_load_lds(v0 + off, (__attribute__((address_space(3))) void*)(vl + ld * KBLK), 16, 0,
+                                         kLoadNT);
+      }
+      return;
+    } else if constexpr (F8) {
       const int blk0 = __builtin_amdgcn_readlane(ids, (2 * i) & 63);
       const int blk1 = __builtin_amdgcn_readlane(ids, (2 * i + 1) & 63);
       const int64_t s0 = (int64_t)blk0 * b + (t0 & (b - 1));
@@ -498,7 +522,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
   // reduction index 8c + k is position pos(c, k) -- P^T's rows are already there:
   // lane (head, c) holds the two chains' positions 4c .. 4c + 3.
   auto step8 = [&](int i) {
-    const int t0 = (my_first + NW * i) << 5;
+    const int t0 = (my_first + NW * i) << TSH;
     const uint32_t kl_a = lds_addr(sh.t.k[wave][i % NB]), lb_a = lds_addr(sh.t.v[wave][i % NB]);
     wait_tile(i);
     u32x4 k8[2][2];
@@ -535,16 +559,34 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
     float sv[8];  // position 16 (k / 4) + 4c + k % 4 for k = 0..7
 #pragma unroll
     for (int k = 0; k < 8; ++k) sv[k] = sc[k >> 2][k & 3];
-    if (alibi) {
-      const float jb = (float)(t0 + 4 * c - pref);  // exact: |j - pref| < 2^24
-#pragma unroll
-      for (int k = 0; k < 8; ++k) sv[k] = fmaf(slope_r, jb + (float)(16 * (k >> 2) + (k & 3)), sv[k]);
-    }
-    if (t0 < lo || t0 + 32 > hi) {
+    if constexpr (PR) {
+      // entry k is tile row 16 (k / 4) + 4c + k % 4: position t0 + 8 (k / 4) + 2c + (k % 4) / 2
+      // of kv head k % 2; the other head's rows are not this lane's q head's keys
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int j = t0 + 16 * (k >> 2) + 4 * c + (k & 3);
-        if (j < lo || j >= hi) sv[k] = -INFINITY;
+        const int j = t0 + 8 * (k >> 2) + 2 * c + ((k & 3) >> 1);
+        if (alibi) sv[k] = fmaf(slope_r, (float)(j - pref), sv[k]);  // exact: |j - pref| < 2^24
+        if ((k & 1) != my_h) sv[k] = -INFINITY;
+      }
+      if (t0 < lo || t0 + TP > hi) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int j = t0 + 8 * (k >> 2) + 2 * c + ((k & 3) >> 1);
+          if (j < lo || j >= hi) sv[k] = -INFINITY;
+        }
+      }
+    } else {
+      if (alibi) {
+        const float jb = (float)(t0 + 4 * c - pref);  // exact: |j - pref| < 2^24
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sv[k] = fmaf(slope_r, jb + (float)(16 * (k >> 2) + (k & 3)), sv[k]);
+      }
+      if (t0 < lo || t0 + 32 > hi) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int j = t0 + 16 * (k >> 2) + 4 * c + (k & 3);
+          if (j < lo || j >= hi) sv[k] = -INFINITY;
+        }
       }
     }
     const float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
@@ -586,7 +628,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
   // flight -- otherwise the compiler guards the loop's first use of qb with a full
   // vmcnt(0) every tile.
   if (my_tiles > 0) load_ids(0);
-  if (alibi && r16 < G) slope_r = a.alibi[g * G + r16] * (kLog2e / a.scale_log2);
+  if (alibi && r16 < GC) slope_r = a.alibi[hbase + r16] * (kLog2e / a.scale_log2);
 #pragma unroll
   for (int u = 0; u < KCH; ++u) asm volatile("" ::"v"(qb[u]));
   if (my_tiles > 0) {
@@ -623,14 +665,14 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
   // read before any is written
   __shared__ float prev_lse[16];
   if (a.merge) {
-    if ((int)threadIdx.x < G) prev_lse[threadIdx.x] = a.lse[(int64_t)(g * G + threadIdx.x) * a.num_rows + q_row];
+    if ((int)threadIdx.x < GC) prev_lse[threadIdx.x] = a.lse[(int64_t)(hbase + threadIdx.x) * a.num_rows + q_row];
     __syncthreads();
   }
-  for (int idx = threadIdx.x; idx < G * DV; idx += blockDim.x) {
+  for (int idx = threadIdx.x; idx < GC * DV; idx += blockDim.x) {
     const int h = idx / DV, d = idx - h * DV;
     // Re-express every wave's (reference max, sums) against the true max M; the
     // factors are at most 1.
-    const int hq = g * G + h;
+    const int hq = hbase + h;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) M = fmaxf(M, true_max[w][h]);
@@ -704,6 +746,20 @@ hipError_t launch_decode_typed(const RowsArgs& a, int block_shift, int dk, int d
   if (n > 0xffffffffull) return hipErrorInvalidValue;
   constexpr int one_bufs = F8 ? kFp8Bufs : kOneWaveBufs, part_bufs = F8 ? kFp8Bufs : kPartBufs,
                 whole_bufs = F8 ? kFp8Bufs : kWholeBufs;
+  if constexpr (F8) {
+    // split fp8 calls with an even number of kv heads and at most 8 q heads per kv
+    // head: one workgroup per pair of kv heads (256-byte reads per slot)
+    if (a.partition_size > 0 && a.num_kv_heads % 2 == 0 && 2 * a.group <= 16) {
+      const uint64_t np = n / 2;
+      if ((int64_t)np >= kOneWaveItems)
+        hipLaunchKernelGGL((decode_mfma_kernel<T, 128, 1, true, one_bufs, true, true>), dim3((uint32_t)np), dim3(64),
+                           0, stream, a, block_shift, rows);
+      else
+        hipLaunchKernelGGL((decode_mfma_kernel<T, 128, kPartWaves, false, part_bufs, true, true>),
+                           dim3((uint32_t)np), dim3(kPartWaves * 64), 0, stream, a, block_shift, rows);
+      return hipGetLastError();
+    }
+  }
   if (a.partition_size > 0 && (int64_t)n >= kOneWaveItems)
     hipLaunchKernelGGL((decode_mfma_kernel<T, 128, 1, true, one_bufs, F8>), dim3((uint32_t)n), dim3(64), 0, stream, a,
                        block_shift, rows);

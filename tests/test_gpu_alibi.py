@@ -96,6 +96,12 @@ def test_alibi_decode_fp8(orc, P):
     check_decode(orc, W.to_fp8(workload("batched-decode-small"), q_dtype="bf16"), P)
 
 
+def test_alibi_decode_fp8_one_wave_window(orc):
+    """Split fp8 decode on one-wave workgroups (an oversized partition count gives
+    enough items), with a window that empties whole partitions."""
+    check_decode(orc, W.to_fp8(workload("long-decode-small"), q_dtype="bf16"), 64, window=200, pmax=4096)
+
+
 def run_varlen(orc, w, causal, window):
     d = OnDevice(w)
     kp, vp = d.host_pools_after_write(orc)

@@ -106,7 +106,7 @@ def test_fp8_decode_one_wave_partitions(orc):
 # Group sizes 1 / 8 / 16, block sizes 16 / 32 / 128, ragged lengths around the
 # 16-position tiles (1, 15, 16, 17, ...), windows, and sinks.
 SHAPES = [(8, 8, 16, 0, False), (16, 2, 32, 0, True), (32, 2, 128, 37, True), (16, 1, 16, 5, False),
-          (64, 8, 64, 0, True)]
+          (64, 8, 64, 0, True), (16, 4, 16, 37, True), (48, 6, 32, 300, False)]
 
 
 @pytest.mark.parametrize("H,Hkv,b,window,with_sinks", SHAPES,
