@@ -278,7 +278,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
   };
 
   // Tiles of TP positions aligned to absolute positions: 16 for 16-bit caches, 32 for
-  // fp8 (the same 8 KB of K and V per tile).
+  // fp8, 16 for fp8 kv-head pairs (the same 8 KB of K and V per tile).
   constexpr int TSH = F8 && !PR ? 5 : 4;
   constexpr int TP = 1 << TSH;
   const int my_first = (lo >> TSH) + wave;  // this wave's tiles: my_first + NW * i, i < my_tiles
@@ -310,8 +310,8 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
   }
 
   // Block ids of upcoming tiles, one per lane: of tile i0 + lane (16-bit), or of the
-  // 16-position half lane % 2 of tile i0 + lane / 2 (fp8: with 16-token blocks a tile
-  // spans two).  Halves past the sequence read some in-bounds entry of the row; their
+  // 16-position half lane % 2 of tile i0 + lane / 2 (fp8 without pairs: with 16-token
+  // blocks a tile spans two).  Halves past the sequence read some in-bounds entry of the row; their
   // loads are redirected into the first half below.
   constexpr int IDS_PER_TILE = F8 && !PR ? 2 : 1;
   constexpr int TILES_PER_IDS = 64 / IDS_PER_TILE;
