@@ -587,45 +587,50 @@ int orc_reduce_partitions(const double* max_logits, const double* exp_sums, cons
 /* Merge of two attention states                                               */
 /* ------------------------------------------------------------------------- */
 
-/* For each token t and head h: tokens at or past prefill_tokens_with_context (when it
- * is >= 0) take the suffix state as it is.  Otherwise a +-inf lse counts as -inf; if
- * both are then -inf the prefix output is copied and the merged lse is -inf; if not,
- * with M the larger lse, weights exp(p - M) and exp(s - M) are normalised and the
- * outputs blended, and the merged lse is M + ln(sum of weights).
+/* Two attention states over disjoint key sets combine into the state over their
+ * union ("cpu_mla_prefill.cpp", MergeAttnStates).  By definition a state's lse is
+ * the log of its softmax mass, so the union's lse is log(e^a + e^b) for the two lse
+ * a and b, and each state's output enters with the share of the mass it holds,
+ * e^(a - lse) and e^(b - lse).  Edge rules of that section, as read here: an lse of
+ * +inf (which attention never produces) counts as an empty state, -inf; when both
+ * states are empty the row keeps the prefix output and its lse is -inf.  Tokens at or
+ * past prefill_tokens_with_context (when it is >= 0) take the suffix state unchanged.
  * prefix/suffix outputs are [T, H, D] in `dtype`; every lse is binary32 [H, T].    */
+static double as_state_lse(float x) { return isinf(x) ? -INFINITY : (double)x; }
+
+/* log(e^a + e^b) for a, b not both -inf, without overflow: the larger term is
+ * factored out, leaving log1p of the smaller one's ratio to it. */
+static double log_add_exp(double a, double b) {
+  double big = a > b ? a : b, small = a > b ? b : a;
+  return big + log1p(exp(small - big));
+}
+
 int orc_merge_states(const void* prefix_out, const float* prefix_lse, const void* suffix_out,
                      const float* suffix_lse, int dtype, int64_t num_tokens, int num_heads,
                      int head_dim, int64_t prefill_tokens_with_context, double* out,
                      double* out_lse) {
   if (elem_bytes(dtype) == 0 || dtype == ORC_FP8_E4M3) return ORC_EUNSUPPORTED;
   if (num_tokens < 0 || num_heads < 1 || head_dim < 1) return ORC_EINVAL;
-  int64_t with_prefix = prefill_tokens_with_context < 0 ? num_tokens : prefill_tokens_with_context;
   for (int64_t t = 0; t < num_tokens; ++t) {
+    int suffix_only = prefill_tokens_with_context >= 0 && t >= prefill_tokens_with_context;
     for (int h = 0; h < num_heads; ++h) {
       int64_t row = (t * num_heads + h) * head_dim;
       int64_t li = (int64_t)h * num_tokens + t;
-      double* o = out + row;
-      if (t >= with_prefix) {
-        for (int d = 0; d < head_dim; ++d) o[d] = load_elem(suffix_out, dtype, row + d);
-        if (out_lse) out_lse[li] = (double)suffix_lse[li];
-        continue;
+      double a = as_state_lse(prefix_lse[li]), b = as_state_lse(suffix_lse[li]);
+      double merged;
+      if (suffix_only) { /* the suffix as it is, lse included */
+        for (int d = 0; d < head_dim; ++d) out[row + d] = load_elem(suffix_out, dtype, row + d);
+        merged = (double)suffix_lse[li];
+      } else if (a == -INFINITY && b == -INFINITY) { /* both empty */
+        for (int d = 0; d < head_dim; ++d) out[row + d] = load_elem(prefix_out, dtype, row + d);
+        merged = -INFINITY;
+      } else {
+        merged = log_add_exp(a, b);
+        double wa = exp(a - merged), wb = exp(b - merged);
+        for (int d = 0; d < head_dim; ++d)
+          out[row + d] = wa * load_elem(prefix_out, dtype, row + d) + wb * load_elem(suffix_out, dtype, row + d);
       }
-      double p = (double)prefix_lse[li];
-      double s = (double)suffix_lse[li];
-      if (isinf(p)) p = -INFINITY;
-      if (isinf(s)) s = -INFINITY;
-      double M = fmax(p, s);
-      if (isinf(M)) {
-        for (int d = 0; d < head_dim; ++d) o[d] = load_elem(prefix_out, dtype, row + d);
-        if (out_lse) out_lse[li] = M;
-        continue;
-      }
-      double pw = exp(p - M), sw = exp(s - M);
-      double sum = pw + sw;
-      for (int d = 0; d < head_dim; ++d)
-        o[d] = load_elem(prefix_out, dtype, row + d) * (pw / sum) +
-               load_elem(suffix_out, dtype, row + d) * (sw / sum);
-      if (out_lse) out_lse[li] = log(sum) + M;
+      if (out_lse) out_lse[li] = merged;
     }
   }
   return ORC_OK;

@@ -924,6 +924,86 @@ def pin_alibi_closed_forms(orc):
     assert np.array_equal(out, base) and np.array_equal(lse, blse)
 
 
+def pin_attend_gathered_matches_dense(orc):
+    """The two-pass core on caller-gathered arrays ("cpu_mla_prefill.cpp",
+    MlaPrefillAttention: QK head dim 192, V head dim 128, contiguous K / V) against
+    torch SDPA + logsumexp in float64, with every row on its own visible range --
+    full, prefix, suffix, interior, one key -- and an empty row (out 0, lse -inf).
+    The same rows computed by the paged varlen path over a pool holding those keys
+    give the same bits (both are the one definition)."""
+    rng = np.random.default_rng(31)
+    n, dk, dv = 53, 192, 128
+    K = rng.standard_normal((n, dk))
+    V = rng.standard_normal((n, dv))
+    lo = np.array([0, 0, 17, 5, 52, 30, 9, 12], dtype=np.int64)
+    hi = np.array([n, 20, n, 44, 53, 31, 9, 40], dtype=np.int64)
+    rows = lo.size
+    q = rng.standard_normal((rows, dk))
+    scale = 1.0 / math.sqrt(dk)
+    out, lse = orc.attend_gathered(q, K, V, lo, hi, scale)
+    ref, rlse = dense_reference(q[:, None, :], K[:, None, :], V[:, None, :], lo, hi, scale, 1)
+    live = hi > lo
+    np.testing.assert_allclose(out[live], ref[live, 0], atol=1e-12, rtol=0)
+    np.testing.assert_allclose(lse[live], rlse[0, live], atol=1e-12, rtol=0)
+    assert np.all(out[~live] == 0.0) and np.all(np.isneginf(lse[~live])), (out[~live], lse[~live])
+    # one visible key: its value exactly, lse = its score
+    one = np.flatnonzero(hi - lo == 1)
+    for r in one:
+        assert np.array_equal(out[r], V[lo[r]]), r
+        assert abs(lse[r] - scale * float(np.dot(q[r], K[lo[r]]))) <= 1e-13
+    # the same rows through the paged varlen path: one sequence per row, non-causal,
+    # each sequence's cache = keys [0, hi) of this one (window = hi - lo)
+    for r in range(rows):
+        if hi[r] == lo[r]:
+            continue
+        kp = stored(K[None, :, None, :], "f32")
+        vp = stored(V[None, :, None, :], "f32")
+        kk, vv = kp[0, :, 0].astype(np.float64), vp[0, :, 0].astype(np.float64)
+        qq = stored(q[r:r + 1, None, :], "f32")
+        o1, l1 = orc.attend_gathered(qq[:, 0].astype(np.float64), kk, vv, lo[r:r + 1], hi[r:r + 1], scale)
+        st, o2, l2 = orc.varlen(kp, vp, "f32", qq, "f32", [0, 1], [int(hi[r])], None, np.array([[0]], np.int32),
+                                scale, False, int(hi[r] - lo[r]))
+        assert st == 0
+        assert np.array_equal(o1[0], o2[0, 0]) and l1[0] == l2[0, 0], r
+    # out of range rows are refused
+    for bad_lo, bad_hi in ((-1, 5), (0, n + 1)):
+        try:
+            orc.attend_gathered(q[:1], K, V, [bad_lo], [bad_hi], scale)
+        except RuntimeError:
+            continue
+        raise AssertionError(f"range [{bad_lo}, {bad_hi}) accepted")
+
+
+def pin_row_mask_selects_rows(orc):
+    """orc_varlen's row mask: every selected (token, head) row equals the unmasked
+    call bit for bit, every other row is left as it was, and an empty mask computes
+    nothing (a mask only chooses which rows of the one definition are computed)."""
+    rng = np.random.default_rng(37)
+    segments = [(0, 6), (12, 1), (25, 5), (3, 1)]
+    lengths = [c + nq for c, nq in segments]
+    case = Case(rng, lengths, H=6, Hkv=2, dk=16, dv=8, dtype="bf16", b=4)
+    q, qsl, positions = _varlen_segments(rng, case, segments, True, 0)
+    T = int(qsl[-1])
+    st, full, full_lse = orc.varlen(case.k_pool, case.v_pool, "bf16", q, "bf16", qsl, lengths, positions,
+                                    case.tables, 0.3, True, 5)
+    assert st == 0 and np.all(np.isfinite(full)) and np.all(np.isfinite(full_lse))
+    for trial in range(3):
+        mask = rng.random((T, 6)) < 0.35
+        mask[trial, trial] = True  # never empty
+        sentinel = 123.0 + trial
+        out = np.full((T, 6, 8), sentinel)
+        lse = np.full((6, T), sentinel)
+        st, out, lse = orc.varlen(case.k_pool, case.v_pool, "bf16", q, "bf16", qsl, lengths, positions, case.tables,
+                                  0.3, True, 5, row_mask=mask, out=out, lse=lse)
+        assert st == 0
+        assert np.array_equal(out[mask], full[mask]) and np.array_equal(lse.T[mask], full_lse.T[mask])
+        assert np.all(out[~mask] == sentinel) and np.all(lse.T[~mask] == sentinel)
+    none = np.zeros((T, 6), dtype=bool)
+    st, out, lse = orc.varlen(case.k_pool, case.v_pool, "bf16", q, "bf16", qsl, lengths, positions, case.tables,
+                              0.3, True, 5, row_mask=none)
+    assert st == 0 and np.all(np.isnan(out)) and np.all(np.isnan(lse))
+
+
 PINS = [pin_hand_example, pin_hand_example_per_block, pin_hand_example_written_through_slots,
         pin_decode_matches_dense, pin_varlen_matches_dense, pin_empty_rows, pin_decoders,
         pin_permutation_invariance, pin_closed_forms, pin_partitions_reduce_to_unsplit,
@@ -931,7 +1011,7 @@ PINS = [pin_hand_example, pin_hand_example_per_block, pin_hand_example_written_t
         pin_rejections, pin_sink_is_a_zero_value_position, pin_sink_closed_forms, pin_encoders,
         pin_gather_returns_logical_rows, pin_gather_rejections, pin_e4m3_decoder,
         pin_fp8_pool_is_the_dequantized_cache, pin_scale_closed_forms, pin_alibi_matches_the_pages_bias,
-        pin_alibi_closed_forms]
+        pin_alibi_closed_forms, pin_attend_gathered_matches_dense, pin_row_mask_selects_rows]
 
 
 def run_all(path):

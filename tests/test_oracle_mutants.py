@@ -49,13 +49,27 @@ MUTANTS = {
     "f16_exponent_bias": ("mag = ldexp((double)(1024 + f), e - 25);", "mag = ldexp((double)(1024 + f), e - 24);"),
     "bf16_wrong_shift": ("uint32_t bits = (uint32_t)h << 16;", "uint32_t bits = (uint32_t)h << 15;"),
     "write_kv_row_is_token": ("int64_t row = block_id * block_size + offset;", "int64_t row = t;"),
-    # MergeAttnStates edge rules
-    "merge_keeps_plus_inf": ("if (isinf(p)) p = -INFINITY;", ""),
+    # the merge of two states (MergeAttnStates) and its edge rules
+    "merge_keeps_plus_inf": ("return isinf(x) ? -INFINITY : (double)x;", "return (double)x;"),
     "merge_both_ninf_emits_suffix": (
-        "for (int d = 0; d < head_dim; ++d) o[d] = load_elem(prefix_out, dtype, row + d);\n        if (out_lse) out_lse[li] = M;",
-        "for (int d = 0; d < head_dim; ++d) o[d] = load_elem(suffix_out, dtype, row + d);\n        if (out_lse) out_lse[li] = M;"),
-    "merge_pass_through_off_by_one": ("if (t >= with_prefix) {", "if (t > with_prefix) {"),
-    "merge_swapped_weights": ("load_elem(prefix_out, dtype, row + d) * (pw / sum)", "load_elem(prefix_out, dtype, row + d) * (sw / sum)"),
+        "out[row + d] = load_elem(prefix_out, dtype, row + d);\n        merged = -INFINITY;",
+        "out[row + d] = load_elem(suffix_out, dtype, row + d);\n        merged = -INFINITY;"),
+    "merge_pass_through_off_by_one": ("t >= prefill_tokens_with_context;", "t > prefill_tokens_with_context;"),
+    "merge_swapped_weights": ("out[row + d] = wa * load_elem(prefix_out", "out[row + d] = wb * load_elem(prefix_out"),
+    "merge_lse_is_the_larger": ("return big + log1p(exp(small - big));", "return big;"),
+    "merge_lse_log_not_log1p": ("return big + log1p(exp(small - big));", "return big + log(exp(small - big));"),
+    # the two-pass core on caller-gathered arrays (MlaPrefillAttention), and the row
+    # mask of the varlen oracle
+    "gathered_out_stride_dk": ("s, out + r * dv, &m, &l);", "s, out + r * dk, &m, &l);"),
+    "gathered_q_stride_dv": ("attend(q + r * dk, K, V, dk, dv, lo[r]", "attend(q + r * dv, K, V, dk, dv, lo[r]"),
+    "gathered_lo_ignored": ("dk, dv, lo[r], hi[r], scale", "dk, dv, 0, hi[r], scale"),
+    "gathered_hi_exclusive_off_by_one": ("dk, dv, lo[r], hi[r], scale", "dk, dv, lo[r], hi[r] - 1, scale"),
+    "gathered_range_unchecked": ("if (lo[r] < 0 || hi[r] > n_keys) return ORC_EINVAL;", "if (lo[r] < 0 || hi[r] > n_keys) {}"),
+    "row_mask_inverted": ("return job->row_mask == NULL || job->row_mask[t * job->num_heads + h];",
+                          "return job->row_mask == NULL || !job->row_mask[t * job->num_heads + h];"),
+    "row_mask_head_major": ("return job->row_mask == NULL || job->row_mask[t * job->num_heads + h];",
+                            "return job->row_mask == NULL || job->row_mask[(int64_t)h * job->num_tokens + t];"),
+    "row_mask_ignored": ("return job->row_mask == NULL || job->row_mask[t * job->num_heads + h];", "return 1;"),
     # attention sinks (ForwardWithSinks)
     "sink_left_out_of_max": ("  double m = sink;\n", "  double m = -INFINITY;\n"),
     "sink_left_out_of_sum": ("double l = sink == -INFINITY ? 0.0 : exp(sink - m);", "double l = 0.0;"),
