@@ -9,8 +9,8 @@
 // sources of 8 rows at once (one lane each) and its 64 lanes stream the rows'
 // 16-byte chunks, consecutive lanes on consecutive chunks.  Conversions and other
 // layouts: one thread per (row, element), consecutive lanes on consecutive elements.
-// With a status word, one workgroup checks every row first and the copy kernels
-// exit before writing when it fails.
+// With a status word, every row is checked first (over the whole grid) and the copy
+// kernels exit before writing when one is refused.
 #include "pa_common.h"
 #include "pa_internal.h"
 
@@ -34,18 +34,16 @@ __device__ __forceinline__ int gather_row(const GatherArgs& a, int64_t t, int64_
   return kGatherCopy;
 }
 
-__global__ __launch_bounds__(1024) void gather_validate_kernel(const GatherArgs a) {
-  __shared__ int bad;
-  if (threadIdx.x == 0) bad = 0;
-  __syncthreads();
-  int found = 0;
-  for (int64_t t = threadIdx.x; t < a.num_tokens; t += blockDim.x) {
+// Rows are checked over the whole grid; a wave that finds a refused row ORs
+// PA_EINVAL (1) into the status word, which a one-thread kernel cleared first.
+__global__ __launch_bounds__(256) void gather_validate_kernel(const GatherArgs a) {
+  bool found = false;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < a.num_tokens;
+       t += (int64_t)gridDim.x * blockDim.x) {
     int64_t src;
     found |= gather_row(a, t, &src) == kGatherBad;
   }
-  if (found) atomicOr(&bad, 1);
-  __syncthreads();
-  if (threadIdx.x == 0) *a.status = bad ? PA_EINVAL : PA_OK;
+  if (__any(found) && lane_id() == 0) atomicOr(a.status, PA_EINVAL);
 }
 
 template <typename S, typename D>
@@ -116,9 +114,15 @@ hipError_t launch_gather_from(const GatherArgs& a, dim3 grid, hipStream_t stream
 
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream) {
   if (a.status != nullptr) {
-    hipLaunchKernelGGL(gather_validate_kernel, dim3(1), dim3(1024), 0, stream, a);
-    const hipError_t e = hipGetLastError();
+    hipError_t e = launch_status_clear(a.status, stream);
     if (e != hipSuccess) return e;
+    if (a.num_tokens > 0) {
+      int64_t blocks = (a.num_tokens + 255) / 256;
+      if (blocks > 2048) blocks = 2048;
+      hipLaunchKernelGGL(gather_validate_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   if (a.num_tokens == 0) return hipSuccess;
   if (a.vec16) {

@@ -150,6 +150,8 @@ struct PrefillArgs;
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int dk, int dv, dim3 grid, hipStream_t stream);
 bool prefill_supported(int dtype, int dk, int dv, int group, int block_size, int64_t num_blocks);
 hipError_t launch_validate(const ValidateArgs& a, hipStream_t stream);
+// Stores PA_OK in *status (the first kernel of a validated call).
+hipError_t launch_status_clear(int32_t* status, hipStream_t stream);
 hipError_t launch_write(const WriteArgs& a, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);

@@ -225,7 +225,11 @@ def chunked_on_device(cp):
 
 def oracle_chunked(orc, cp, rows):
     """The whole result by definition: token i of request r sees every context
-    position and new positions 0..i, gathered explicitly through both tables."""
+    position and new positions 0..i, gathered explicitly through both tables.  The
+    oracle's gathered two-pass core answers each head's requested tokens; heads run
+    on a thread pool (the oracle releases the interpreter while it computes)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     kp, vp = cp.k_pool.copy(), cp.v_pool.copy()
     assert orc.write_kv(kp, vp, cp.dtype, cp.k_new, cp.v_new, cp.slot_mapping) == 0
     qsl = cp.query_start_loc
@@ -233,19 +237,28 @@ def oracle_chunked(orc, cp, rows):
     want = {}
     for r in range(cp.ctx_lens.size):
         ctx, n = int(cp.ctx_lens[r]), int(cp.new_lens[r])
-        sel = [(t, h) for (t, h) in rows if qsl[r] <= t < qsl[r + 1]]
-        if not sel:
+        by_head = {}
+        for (t, h) in rows:
+            if qsl[r] <= t < qsl[r + 1]:
+                by_head.setdefault(h, []).append(t)
+        if not by_head:
             continue
         K = np.concatenate([orc.gather(kp, cp.dtype, cp.block_size, cp.ctx_tables[r], ctx),
                             orc.gather(kp, cp.dtype, cp.block_size, cp.new_tables[r], n)])
         V = np.concatenate([orc.gather(vp, cp.dtype, cp.block_size, cp.ctx_tables[r], ctx),
                             orc.gather(vp, cp.dtype, cp.block_size, cp.new_tables[r], n)])
-        for h in sorted({h for _, h in sel}):
-            ts = [t for (t, hh) in sel if hh == h]
+
+        def head(h):
+            ts = sorted(by_head[h])
             i = np.array(ts) - qsl[r]
             o, l = orc.attend_gathered(q64[ts, h], K[:, h], V[:, h], np.zeros_like(i), ctx + i + 1, cp.scale)
-            for k, t in enumerate(ts):
-                want[(t, h)] = (o[k], l[k])
+            return h, ts, o, l
+
+        with ThreadPoolExecutor(max_workers=threads()) as ex:
+            for h, ts, o, l in ex.map(head, sorted(by_head)):
+                for k, t in enumerate(ts):
+                    want[(t, h)] = (o[k], l[k])
+        del K, V
     return want
 
 
@@ -262,18 +275,32 @@ def test_chunked_prefill_small(orc, name):
 
 
 def test_chunked_prefill_full_sampled(orc):
-    """Full-size MLA-style workload; the oracle answers 4 seeded heads x 24 seeded
-    tokens per request (always including each request's first and last token)."""
+    """Full-size MLA-style workload (8 requests, 128 heads, QK 192 / V 128, contexts to
+    16384 in chunks of 4096).  The oracle answers every (token, head) row of the two
+    requests with the least context + new tokens, and 4096 seeded distinct rows of
+    every other request, which always include each head's first and last token."""
     cp = workload("mla-chunked")
     out, lse = chunked_on_device(cp)
     rng = np.random.default_rng(5005)
     qsl = cp.query_start_loc
+    H = cp.num_heads
+    total = cp.ctx_lens + cp.new_lens
+    whole = set(np.argsort(total, kind="stable")[:2].tolist())
     rows = []
     for r in range(cp.ctx_lens.size):
-        toks = {int(qsl[r]), int(qsl[r + 1]) - 1} | set(rng.integers(qsl[r], qsl[r + 1], size=22).tolist())
-        heads = rng.choice(cp.num_heads, size=4, replace=False)
-        rows += [(t, int(h)) for t in sorted(toks) for h in heads]
+        t0, t1 = int(qsl[r]), int(qsl[r + 1])
+        if r in whole:
+            rows += [(t, h) for t in range(t0, t1) for h in range(H)]
+            continue
+        fixed = [(t, h) for h in range(H) for t in (t0, t1 - 1)]
+        flat = rng.choice((t1 - t0) * H, size=4096 - len(fixed), replace=False)
+        picked = {(t0 + int(k) // H, int(k) % H) for k in flat} | set(fixed)
+        while len(picked) < 4096:
+            k = int(rng.integers((t1 - t0) * H))
+            picked.add((t0 + k // H, k % H))
+        rows += sorted(picked)
     want = oracle_chunked(orc, cp, rows)
+    assert len(want) == len(rows)
     got = np.stack([out[t, h] for t, h in rows])
     ref = np.stack([want[r][0] for r in rows])
     assert_close(got, ref, TOL[cp.dtype], "sampled out")
