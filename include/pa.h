@@ -31,7 +31,8 @@
  *     the queries' type).
  *
  * Ownership and streams: the caller owns every buffer.  The library allocates no
- * memory, keeps no state between calls, and enqueues all work on `stream` (a
+ * memory and keeps no state between calls (pa_decode_noalloc's static device buffer
+ * aside, see there), and enqueues all work on `stream` (a
  * hipStream_t; NULL is the default stream) without synchronising.  Device pointers
  * must stay valid until the work completes.  The pool descriptor is host memory and
  * is read during the call only.
@@ -63,7 +64,8 @@ typedef enum pa_status {
   PA_EINVAL = 1,       /* bad argument or bad device content */
   PA_ESHAPE = 2,       /* num_heads % num_kv_heads != 0, or dims that disagree */
   PA_EUNSUPPORTED = 3, /* an element type / head-dim / group combination not built */
-  PA_EDEVICE = 4       /* a HIP launch failed */
+  PA_EDEVICE = 4,      /* a HIP launch failed */
+  PA_ESCRATCH = 5      /* pa_decode_noalloc: the call needs more than its static workspace */
 } pa_status;
 
 typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 } pa_dtype;
@@ -138,6 +140,27 @@ int pa_decode(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out,
               int32_t partition_size, int32_t max_partitions, float* max_logits, float* exp_sums,
               float* tmp_out, const float* sinks, const float* alibi_slopes, int32_t* status,
               void* stream);
+
+/* pa_decode for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments and
+ * results as pa_decode, except that split-KV (partition_size > 0) keeps its
+ * partition states in a static device buffer of the library instead of caller
+ * workspaces: 96 MiB per GPU, held from the first call on that GPU until the process
+ * ends.  The states need num_seqs * num_heads * max_partitions * (head_dim_v + 2) * 4
+ * bytes (each of the three arrays rounded up to 256), max_partitions =
+ * ceil(max_blocks * block_size / partition_size); a call that needs more returns
+ * PA_ESCRATCH and enqueues nothing.  partition_size == 0 is pa_decode unsplit.
+ * The buffer of the current device is used (the stream must belong to it); every
+ * call on one GPU shares it, so calls whose work overlaps on one GPU (other streams,
+ * other threads) race on it.  Nothing in it needs clearing: each call writes every
+ * state it reads.  The first call on each device resolves the buffer's address
+ * (hipGetSymbolAddress); make it outside graph capture.  The call itself allocates,
+ * frees and copies nothing. */
+int pa_decode_noalloc(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out, int32_t out_dtype,
+                      const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
+                      int32_t num_seqs, int32_t num_heads, float scale, int32_t sliding_window,
+                      int32_t partition_size, const float* sinks, const float* alibi_slopes, int32_t* status,
+                      void* stream);
 
 /* Variable-length attention over many sequences in one call (TensorSharp page,
  * Forward; "cpu_mla_prefill.cpp", MlaPrefillAttention): prefill chunks and single

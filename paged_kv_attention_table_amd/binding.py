@@ -17,13 +17,13 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libpa.so")
 
-PA_OK, PA_EINVAL, PA_ESHAPE, PA_EUNSUPPORTED, PA_EDEVICE = 0, 1, 2, 3, 4
+PA_OK, PA_EINVAL, PA_ESHAPE, PA_EUNSUPPORTED, PA_EDEVICE, PA_ESCRATCH = 0, 1, 2, 3, 4, 5
 PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 DTYPE_CODE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
               torch.float8_e4m3fn: PA_FP8_E4M3}
 
-EXPORTS = ("pa_strerror", "pa_write_kv", "pa_decode", "pa_varlen", "pa_varlen_merge", "pa_merge_states",
-           "pa_gather_cache")
+EXPORTS = ("pa_strerror", "pa_write_kv", "pa_decode", "pa_decode_noalloc", "pa_varlen", "pa_varlen_merge",
+           "pa_merge_states", "pa_gather_cache")
 
 
 class PaKvPool(ctypes.Structure):
@@ -59,6 +59,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.pa_decode.restype = ctypes.c_int
     lib.pa_decode.argtypes = [pool_p, vp, i32, vp, i32, vp, i32, vp, i32, i32, f32, i32, i32, i32, vp, vp, vp,
                               vp, vp, vp, vp]
+    lib.pa_decode_noalloc.restype = ctypes.c_int
+    lib.pa_decode_noalloc.argtypes = [pool_p, vp, i32, vp, i32, vp, i32, vp, i32, i32, f32, i32, i32, vp, vp, vp, vp]
     lib.pa_varlen.restype = ctypes.c_int
     lib.pa_varlen.argtypes = [pool_p, vp, i32, vp, i32, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, f32, i32, i32,
                               i32, i32, vp, vp, vp, vp, vp, vp, vp]
@@ -193,6 +195,33 @@ def pa_decode(k_pool, v_pool, q, out, block_tables, seq_lens, scale, sliding_win
                           _ptr(exp_sums), _ptr(tmp_out), _ptr(sinks), _ptr(alibi_slopes), _ptr(status),
                           _stream(stream))
     _check(st, "pa_decode")
+
+
+def pa_decode_noalloc(k_pool, v_pool, q, out, block_tables, seq_lens, scale, sliding_window=0, partition_size=0,
+                      status=None, stream=None, sinks=None, k_scale=1.0, v_scale=1.0, alibi_slopes=None):
+    """pa_decode whose split-KV partition states live in the library's static device
+    buffer (no workspace arguments, nothing allocated by the call)."""
+    pool = make_pool(k_pool, v_pool, k_scale, v_scale)
+    _dev(q, "q", ndim=3)
+    _dev(out, "out", ndim=3)
+    _dev(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _dev(seq_lens, "seq_lens", dtype=torch.int32, ndim=1)
+    _dev(status, "status", dtype=torch.int32)
+    _dev(sinks, "sinks", dtype=torch.float32, ndim=1)
+    _dev(alibi_slopes, "alibi_slopes", dtype=torch.float32, ndim=1)
+    S, H, _ = q.shape
+    _shape(sinks, (H,), "sinks")
+    _shape(alibi_slopes, (H,), "alibi_slopes")
+    _shape(q, (S, H, pool.head_dim_k), "q")
+    _shape(out, (S, H, pool.head_dim_v), "out")
+    _shape(seq_lens, (S,), "seq_lens")
+    if block_tables.shape[0] != S:
+        raise ValueError("block_tables must have one row per sequence")
+    st = load().pa_decode_noalloc(ctypes.byref(pool), _ptr(q), _code(q, "q"), _ptr(out), _code(out, "out"),
+                                  _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), S, H, float(scale),
+                                  int(sliding_window), int(partition_size), _ptr(sinks), _ptr(alibi_slopes),
+                                  _ptr(status), _stream(stream))
+    _check(st, "pa_decode_noalloc")
 
 
 def pa_varlen(k_pool, v_pool, q, out, query_start_loc, seq_lens, positions, block_tables, max_query_len, scale,

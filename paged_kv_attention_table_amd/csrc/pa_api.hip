@@ -143,6 +143,7 @@ const char* pa_strerror(int status) {
     case PA_ESHAPE: return "shape mismatch (num_heads not a multiple of num_kv_heads, or dims disagree)";
     case PA_EUNSUPPORTED: return "unsupported element type, head dim or head-group size";
     case PA_EDEVICE: return "HIP launch failure";
+    case PA_ESCRATCH: return "the call needs more split-KV workspace than the library's static buffer holds";
     default: return "unknown status";
   }
 }

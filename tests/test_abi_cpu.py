@@ -19,8 +19,8 @@ def declared_functions():
 
 def test_header_declares_the_calls():
     names = declared_functions()
-    for n in ("pa_write_kv", "pa_decode", "pa_varlen", "pa_varlen_merge", "pa_merge_states", "pa_gather_cache",
-              "pa_strerror"):
+    for n in ("pa_write_kv", "pa_decode", "pa_decode_noalloc", "pa_varlen", "pa_varlen_merge", "pa_merge_states",
+              "pa_gather_cache", "pa_strerror"):
         assert n in names, names
 
 
@@ -32,8 +32,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_strerror_texts():
-    for code in range(5):
-        assert binding.strerror(code)
+    for code in range(6):
+        assert binding.strerror(code) != "unknown status"
     assert binding.strerror(99) == "unknown status"
 
 
@@ -239,3 +239,23 @@ def test_varlen_merge_host_checks():
                                None, None, None, None) == binding.PA_ESHAPE
     assert lib.pa_varlen_merge(p, FAKE, binding.PA_F16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 10, 8, 4, 0.0, 1, 0,
                                None, None, None, None) == binding.PA_EINVAL
+
+
+def test_decode_noalloc_host_checks():
+    """The static-workspace decode refuses calls whose partition states would not fit
+    its buffer (or exceed pa_decode's partition limit) before any HIP call."""
+    lib = binding.load()
+    big = _pool(num_kv_heads=8, head_dim_k=128, head_dim_v=128)
+
+    def call(pool, S, H, max_blocks, P):
+        p = None if pool is None else ctypes.byref(pool)
+        return lib.pa_decode_noalloc(p, FAKE, binding.PA_F16, FAKE, binding.PA_F32, FAKE, max_blocks, FAKE, S, H, 0.1,
+                                     0, P, None, None, None, None)
+
+    assert call(None, 2, 4, 4, 16) == binding.PA_EINVAL
+    assert call(big, 1024, 64, 8192, 16) == binding.PA_ESCRATCH      # 2^29 partition states
+    assert call(big, 64, 64, 8192, 512) == binding.PA_ESCRATCH       # 64 * 64 * 256 * 130 * 4 B > 96 MiB
+    assert call(big, 2, 64, 8192 * 2, 16) == binding.PA_EUNSUPPORTED  # 16384 partitions (pa_decode's limit: 8192)
+    assert call(big, 2, 4, 4, 24) == binding.PA_EINVAL               # not a multiple of the block size
+    assert call(big, 2, 4, 4, -16) == binding.PA_EINVAL
+    assert binding.strerror(binding.PA_ESCRATCH) != "unknown status"
