@@ -1,38 +1,49 @@
 """Benchmark of batched paged attention on one MI355X.
 
-Default line: the batched decode workload (64 sequences, lengths uniform in
-[512, 4096], 32 q heads / 8 kv heads, head dim 128, block size 16, f16 K/V, 8 forks
-sharing a 256-token prefix).  One step = pa_write_kv of the 64 new tokens + pa_decode
-(unsplit by default: one kernel launch).  The value is decode KV bytes per second:
-sum over sequences and kv heads of the visible positions times
-(head_dim_k + head_dim_v) * 2 bytes, divided by the wall time of a step.
-
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload decode|long|decode-fp8|long-fp8|varlen|mla|gather]
+                    [--workload all|decode|long|decode-fp8|long-fp8|varlen|mla|gather]
                     [--partition-size P] [--no-cpu-baseline] [--copy-calibration] [--sweep]
                     [--ceilings]
 
-decode-fp8 / long-fp8 are the same decode workloads over an fp8 (E4M3) cache with
-per-tensor k_scale / v_scale (queries stay f16 / bf16); their bytes count one byte
-per K / V element.
+Prints one JSON line.  With the default --workload all it covers the whole metric,
+"paged-decode KV GB/s; varlen prefill TFLOP/s":
 
-Prints one JSON line.  The roofline object divides the same algorithmic bytes (or
-flops) by the attention call's average duration, taken from HIP events recorded on
-its stream around every call of the timed loop.  Its traffic field is the HBM bytes
-per launch that rocprofv3's FETCH_SIZE and WRITE_SIZE counters gave for the kernel,
-scaled by what the counters read for a copy of known size; it is read from
-profiles/traffic.md and reported only while the kernel's source hash still matches
-the one recorded there.  The cpu_baseline object times the CPU oracle on a bounded
-sample of the same workload on the host cores.  --copy-calibration appends, after
+* the headline (value, ms_per_step, roofline, cpu_baseline) is the batched decode
+  workload: 64 sequences, lengths uniform in [512, 4096], 32 q heads / 8 kv heads,
+  head dim 128, block size 16, f16 K/V, 8 forks sharing a 256-token prefix.  One
+  step = pa_write_kv of the 64 new tokens + pa_decode (unsplit: one kernel launch).
+  The value is decode KV bytes per second: over sequences and kv heads, the visible
+  positions times (head_dim_k + head_dim_v) * 2 bytes, divided by the wall time of a
+  step;
+* `secondary` holds the same fields for the mixed varlen call (4 prefill chunks of
+  512 tokens + 12 decode tokens, bf16, window 1024; TFLOP/s of visible pairs), the
+  MLA-style chunked prefill (8 requests, 128 heads, QK 192 / V 128, bf16; TFLOP/s)
+  and the long-context split decode (8 sequences up to 131072 positions, 64 q / 8 kv
+  heads, bf16, partitions of 512; GB/s), each timed over its own K steps.
+
+Every entry's roofline divides the algorithmic bytes (or flops) by the attention
+call's average duration from HIP events recorded on its stream around every call
+of the timed region (`achieved`, `frac`); beside it, `achieved_flushed` /
+`frac_flushed` take the median of 20 calls with a 512 MiB write between calls
+(outside the events), so that every K/V byte comes from HBM.  `traffic` is the HBM
+bytes per call that rocprofv3's FETCH_SIZE and WRITE_SIZE counters gave, scaled by
+what the counters read for a copy of known size; it is read from profiles/ and
+reported only while the kernels' source hash still matches the one recorded there.
+`cpu_baseline` times the CPU oracle, unchanged, on a bounded sample of the same
+workload on the host cores (thread count and CPU model given).
+
+--workload X prints X's line alone (decode-fp8 / long-fp8 are the decode workloads
+over an fp8 (E4M3) cache with per-tensor k_scale / v_scale, one byte per K / V
+element; gather is the MLA latent-cache gather).  --copy-calibration appends, after
 the timed region, three launches of a 1 GiB elementwise copy (torch.neg) that the
 counter runs use as the known-size reference.  --sweep adds, after the timed region,
 for the decode workloads each partition size in {0, 512, 1024}, the cost of device
 validation, that of per-head attention sinks and that of ALiBi slopes, and for the
-prefill workloads the call's cold rate (and, for the varlen call, the cost of device
-validation), each as the median of 20 calls with the caches flushed between calls.  --ceilings adds, after
-the timed region, what plain library work reaches on the same GPU as context for the
-roofline fractions: a 1 GiB device copy (GB/s read + written) and an 8192^3 bf16
-matrix product (TFLOP/s), each the median of 10 event-timed runs.
+prefill workloads the cost of device validation, each as the median of 20 calls
+with the caches flushed between calls.  --ceilings adds what plain library work
+reaches on the same GPU as context for the roofline fractions: a 1 GiB device copy
+(GB/s read + written) and an 8192^3 bf16 matrix product (TFLOP/s), each the median
+of 10 event-timed runs.
 """
 from __future__ import annotations
 
@@ -61,11 +72,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode",
-                    choices=["decode", "long", "decode-fp8", "long-fp8", "varlen", "mla", "gather"])
+    ap.add_argument("--workload", default="all",
+                    choices=["all", "decode", "long", "decode-fp8", "long-fp8", "varlen", "mla", "gather"])
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--secondary-cpu-budget-s", type=float, default=6.0)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--ceilings", action="store_true")
@@ -153,6 +165,27 @@ def host_cores():
         return len(os.sched_getaffinity(0))
     except AttributeError:
         return os.cpu_count() or 1
+
+
+def host_cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def flushed_median_ms(call, reps=20):
+    """Median duration of call() in ms over reps calls, each preceded (outside the
+    events) by a 512 MiB device write that evicts the L2 caches and the MALL."""
+    import torch
+
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    _, med = time_calls(call, reps, flush=lambda: scratch.fill_(1))
+    del scratch
+    return med
 
 
 def timed_loop(steps, pre, call):
@@ -247,7 +280,8 @@ def cpu_baseline_decode(w, budget_s):
             break
     eb = ELEM_BYTES[w.dtype]
     nbytes = int(w.seq_lens[:take].astype(np.int64).sum()) * w.num_kv_heads * (w.dk + w.dv) * eb * reps
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "cpu": host_cpu_model(),
+            "kind": "oracle",
             "sample": f"first {take} of {S} sequences, whole oracle decode call (gather + two-pass fp64) "
                       f"repeated {reps} times, {dt:.1f} s"}
 
@@ -291,7 +325,8 @@ def _timed_rows(run, per_row_flops, total_rows, budget_s, what):
         if dt >= budget_s or dt + dt / reps > 1.5 * budget_s:
             break
     fl = float(cum[m - 1]) * reps
-    return {"value": round(fl / dt / 1e9, 4), "unit": "GFLOP/s", "cores": host_cores(), "kind": "oracle",
+    return {"value": round(fl / dt / 1e9, 4), "unit": "GFLOP/s", "cores": host_cores(), "cpu": host_cpu_model(),
+            "kind": "oracle",
             "sample": f"{what}: first {m} of {total_rows} query tokens (all heads), repeated {reps} times, {dt:.1f} s"}
 
 
@@ -376,20 +411,21 @@ def cpu_baseline_gather(g, budget_s):
         dt = time.perf_counter() - t0
         if dt >= budget_s or dt + dt / reps > 1.5 * budget_s:
             break
-    return {"value": round(T * D * 2 * 2 * reps / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": round(T * D * 2 * 2 * reps / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "cpu": host_cpu_model(),
+            "kind": "oracle",
             "sample": f"the whole gather ({T} rows of {D}), one thread, repeated {reps} times, {dt:.1f} s"}
 
 
-def run_prefill(args):
-    """Secondary workloads: mixed varlen (config of 4 prefill chunks + 12 decode
-    tokens) or the MLA-style chunked prefill.  Prints one JSON line in TFLOP/s."""
+def prefill_entry(args, kind, cpu_budget_s):
+    """The mixed varlen call (4 prefill chunks + 12 decode tokens) or the MLA-style
+    chunked prefill: one entry in TFLOP/s of visible (query, key) pairs."""
     import torch
 
     from paged_kv_attention_table_amd import pa_varlen, pa_write_kv
     from paged_kv_attention_table_amd import workloads as W
     from paged_kv_attention_table_amd.chunked import ChunkedPrefillPlan
 
-    if args.workload == "varlen":
+    if kind == "varlen":
         w = W.mixed_varlen()
         kp, vp = dev(w.k_pool, w.dtype), dev(w.v_pool, w.dtype)
         q = dev(w.q, w.dtype)
@@ -455,39 +491,33 @@ def run_prefill(args):
     ms, avg_ms, med_ms = timed_loop(args.steps, write, attn)
     value = flops / (ms * 1e-3) / 1e12
     achieved = flops / (avg_ms * 1e-3) / 1e12
-    line = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
-            "vs_baseline": None, "dtype": dtype, "data": "synthetic", "config": dict(cfg, flops_per_step=flops),
-            "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                         "kernel": kernel_label, "avg_ms": round(avg_ms, 5), "median_ms": round(med_ms, 5)}}
-    if args.sweep:
-        # context, after the timed region: the call with the caches flushed between
-        # calls (median of 20), and for the varlen call the cost of device validation
-        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-        flush = lambda: scratch.fill_(1)  # noqa: E731
-        _, med_cold = time_calls(attn, 20, flush=flush)
-        sw = {"cold_tflops": round(flops / (med_cold * 1e-3) / 1e12, 1), "cold_ms": round(med_cold, 5)}
-        if args.workload == "varlen":
-            status = torch.zeros(1, dtype=torch.int32, device="cuda")
-            _, med_status = time_calls(lambda: attn(status), 20, flush=flush)
-            if int(status.item()) != 0:
-                raise RuntimeError(f"device validation reported status {int(status.item())}")
-            sw["validation_ms"] = round(med_status - med_cold, 5)
-        del scratch
-        line["sweep"] = sw
-    t = traffic_lookup("pa_varlen_call", name, P if args.workload == "varlen" else 0)
+    cold_ms = flushed_median_ms(attn)
+    cold = flops / (cold_ms * 1e-3) / 1e12
+    entry = {"value": round(value, 2), "unit": "TFLOP/s", "steps": args.steps, "warmup": args.warmup,
+             "ms_per_step": round(ms, 5), "dtype": dtype, "config": dict(cfg, flops_per_step=flops),
+             "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                          "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                          "kernel": kernel_label, "flops_per_call": flops, "avg_ms": round(avg_ms, 5),
+                          "median_ms": round(med_ms, 5), "achieved_flushed": round(cold, 2),
+                          "frac_flushed": round(cold / MFMA_BF16_PEAK_TFLOPS, 4),
+                          "median_ms_flushed": round(cold_ms, 5)}}
+    if args.sweep and kind == "varlen":
+        # context, after the timed region: the cost of device validation
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        med_status = flushed_median_ms(lambda: attn(status))
+        if int(status.item()) != 0:
+            raise RuntimeError(f"device validation reported status {int(status.item())}")
+        entry["sweep"] = {"validation_ms": round(med_status - cold_ms, 5)}
+    t = traffic_lookup("pa_varlen_call", name, P if kind == "varlen" else 0)
     if t is not None:
-        line["roofline"]["traffic"] = t[0] + t[1]
-        line["roofline"]["traffic_read"], line["roofline"]["traffic_write"] = t
-    if args.ceilings:
-        line["ceilings"] = ceilings()
+        entry["roofline"]["traffic"] = t[0] + t[1]
+        entry["roofline"]["traffic_read"], entry["roofline"]["traffic_write"] = t
     if args.copy_calibration:
         copy_calibration()
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = (cpu_baseline_varlen(w, args.cpu_budget_s) if args.workload == "varlen"
-                                else cpu_baseline_chunked(cp, args.cpu_budget_s))
-    print(json.dumps(line), flush=True)
+    if cpu_budget_s > 0:
+        entry["cpu_baseline"] = (cpu_baseline_varlen(w, cpu_budget_s) if kind == "varlen"
+                                 else cpu_baseline_chunked(cp, cpu_budget_s))
+    return entry
 
 
 def run_gather(args):
@@ -529,26 +559,20 @@ def run_gather(args):
     print(json.dumps(line), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1 (no multi-GPU path)"}))
-        sys.exit(2)
+def decode_entry(args, workload, cpu_budget_s, partition_size=None):
+    """A decode workload (batched, long, or their fp8 versions): one entry in GB/s of
+    visible K/V bytes.  One step = pa_write_kv of the new tokens + pa_decode."""
     import torch
 
     from paged_kv_attention_table_amd import pa_decode, pa_write_kv
     from paged_kv_attention_table_amd import workloads as W
 
-    if args.workload in ("varlen", "mla"):
-        return run_prefill(args)
-    if args.workload == "gather":
-        return run_gather(args)
-    base = args.workload.removesuffix("-fp8")
+    base = workload.removesuffix("-fp8")
     w = W.batched_decode() if base == "decode" else W.long_decode()
-    if args.workload.endswith("-fp8"):
+    if workload.endswith("-fp8"):
         w = W.to_fp8(w)
-    if args.partition_size is not None:
-        P = args.partition_size
+    if partition_size is not None:
+        P = partition_size
     else:
         P = 0 if base == "decode" else 512
     kp, vp = dev(w.k_pool, w.dtype), dev(w.v_pool, w.dtype)
@@ -583,56 +607,99 @@ def main():
     nbytes = decode_bytes(w)
     value = nbytes / (ms * 1e-3) / 1e9
     achieved = nbytes / (avg_ms * 1e-3) / 1e9
+    cold_ms = flushed_median_ms(decode)
+    cold = nbytes / (cold_ms * 1e-3) / 1e9
 
     kernel = "decode_mfma_kernel"
     roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
             "kernel": kernel + ("" if P == 0 else " + partition reduce_kernel"),
-            "bytes_per_launch": nbytes, "avg_ms": round(avg_ms, 5), "median_ms": round(med_ms, 5)}
+            "bytes_per_launch": nbytes, "avg_ms": round(avg_ms, 5), "median_ms": round(med_ms, 5),
+            "achieved_flushed": round(cold, 2), "frac_flushed": round(cold / HBM_PEAK_GBS, 4),
+            "median_ms_flushed": round(cold_ms, 5)}
     t = traffic_lookup(kernel, w.name, P)
     if t is not None:
         roof["traffic"] = t[0] + t[1]
         roof["traffic_read"], roof["traffic_write"] = t
-    line = {
-        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": w.query_dtype, "data": "synthetic",
-        "config": {"workload": w.name, "kv_dtype": w.dtype, "num_seqs": S,
-                   "seq_lens": [int(w.seq_lens.min()), max_len],
-                   "num_heads": H, "num_kv_heads": w.num_kv_heads, "head_dim": w.dk, "block_size": w.block_size,
-                   "partition_size": P, "kv_bytes_per_step": nbytes, "step": "pa_write_kv + pa_decode"},
-        "roofline": roof,
-    }
+    entry = {"value": round(value, 2), "unit": "GB/s", "steps": args.steps, "warmup": args.warmup,
+             "ms_per_step": round(ms, 5), "dtype": w.query_dtype,
+             "config": {"workload": w.name, "kv_dtype": w.dtype, "num_seqs": S,
+                        "seq_lens": [int(w.seq_lens.min()), max_len],
+                        "num_heads": H, "num_kv_heads": w.num_kv_heads, "head_dim": w.dk,
+                        "block_size": w.block_size, "partition_size": P, "kv_bytes_per_step": nbytes,
+                        "step": "pa_write_kv + pa_decode"},
+             "roofline": roof}
     if args.sweep:
         # context, after the timed region: each partition size, and the cost of device
-        # validation (status word); median of 20 calls with a 512 MiB write between
-        # calls so that the pool is read from HBM
-        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-        flush = lambda: scratch.fill_(1)
+        # validation (status word), sinks and ALiBi; median of 20 flushed calls
         sweep = {}
         for p in (0, 512, 1024):
             buf = ws if p == P else workspace(p)
-            _, med = time_calls(lambda: decode(p, buf), 20, flush=flush)
-            sweep[str(p)] = round(nbytes / (med * 1e-3) / 1e9, 1)
+            sweep[str(p)] = round(nbytes / (flushed_median_ms(lambda: decode(p, buf)) * 1e-3) / 1e9, 1)
         status = torch.zeros(1, dtype=torch.int32, device="cuda")
-        _, med_plain = time_calls(decode, 20, flush=flush)
-        _, med_status = time_calls(lambda: decode(status=status), 20, flush=flush)
+        med_plain = flushed_median_ms(decode)
+        med_status = flushed_median_ms(lambda: decode(status=status))
         if int(status.item()) != 0:
             raise RuntimeError(f"device validation reported status {int(status.item())}")
         # attention sinks (one logit per q head) on the bench's own partition size
         sinks = torch.linspace(-2.0, 2.0, w.num_heads, device="cuda")
-        _, med_sinks = time_calls(lambda: decode(sinks=sinks), 20, flush=flush)
+        med_sinks = flushed_median_ms(lambda: decode(sinks=sinks))
         # ALiBi with the geometric slopes 2^(-8 (h + 1) / H)
         slopes = torch.tensor([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=torch.float32, device="cuda")
-        _, med_alibi = time_calls(lambda: decode(alibi=slopes), 20, flush=flush)
-        line["sweep"] = {"cold_gbs_by_partition_size": sweep, "validation_ms": round(med_status - med_plain, 5),
-                         "sinks_ms": round(med_sinks - med_plain, 5), "alibi_ms": round(med_alibi - med_plain, 5)}
-    if args.ceilings:
-        line["ceilings"] = ceilings()
+        med_alibi = flushed_median_ms(lambda: decode(alibi=slopes))
+        entry["sweep"] = {"cold_gbs_by_partition_size": sweep, "validation_ms": round(med_status - med_plain, 5),
+                          "sinks_ms": round(med_sinks - med_plain, 5), "alibi_ms": round(med_alibi - med_plain, 5)}
     if args.copy_calibration:
         copy_calibration()
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline_decode(w, args.cpu_budget_s)
+    if cpu_budget_s > 0:
+        entry["cpu_baseline"] = cpu_baseline_decode(w, cpu_budget_s)
+    return entry
+
+
+def as_line(entry, args, extra=None):
+    """The contract's JSON line around one entry."""
+    line = {"metric": METRIC, "value": entry["value"], "unit": entry["unit"], "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": entry["ms_per_step"], "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": entry["dtype"], "data": "synthetic",
+            "config": entry["config"], "roofline": entry["roofline"]}
+    for k in ("sweep", "cpu_baseline"):
+        if k in entry:
+            line[k] = entry[k]
+    if extra:
+        line.update(extra)
+    return line
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1 (no multi-GPU path)"}))
+        sys.exit(2)
+    import torch
+
+    budget = 0.0 if args.no_cpu_baseline else args.cpu_budget_s
+    budget2 = 0.0 if args.no_cpu_baseline else args.secondary_cpu_budget_s
+    if args.workload == "gather":
+        return run_gather(args)
+    if args.workload in ("varlen", "mla"):
+        line = as_line(prefill_entry(args, args.workload, budget), args)
+    elif args.workload != "all":
+        line = as_line(decode_entry(args, args.workload, budget, args.partition_size), args)
+    else:
+        # the whole metric: batched decode as the headline, then the prefill half and
+        # the long-context split decode, each on its own timed steps
+        head = decode_entry(args, "decode", budget, args.partition_size)
+        torch.cuda.empty_cache()
+        secondary = []
+        for kind in ("varlen", "mla"):
+            e = prefill_entry(args, kind, budget2)
+            secondary.append(dict({"workload": e["config"]["workload"]}, **e))
+            torch.cuda.empty_cache()
+        e = decode_entry(args, "long", budget2)
+        secondary.append(dict({"workload": e["config"]["workload"]}, **e))
+        line = as_line(head, args, {"secondary": secondary})
+    if args.ceilings:
+        line["ceilings"] = ceilings()
     print(json.dumps(line), flush=True)
 
 
