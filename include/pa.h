@@ -83,7 +83,8 @@ typedef struct pa_kv_pool {
   float v_scale;        /* finite, > 0: V element = stored value * v_scale (1.0: none) */
 } pa_kv_pool;
 
-/* Static text for a status code. */
+/* Static text for a status code: the status codes of "Paged attention for decode in
+ * C" (section 4, the interface and its error returns), plus PA_ESCRATCH. */
 const char* pa_strerror(int status);
 
 /* Write new tokens' K and V into their pool slots (TensorSharp page,
@@ -195,7 +196,20 @@ int pa_decode_noalloc(const pa_kv_pool* pool, const void* q, int32_t q_dtype, vo
  * Supported: (head_dim_k, head_dim_v) in {(32,32), (64,64), (128,128), (256,256),
  * (192,128)}; num_heads / num_kv_heads <= 16; any block_size.  PA_FP8_E4M3 pools: as
  * for pa_decode, and only calls whose sequences hold at most one query token each
- * (max_query_len <= 1). */
+ * (max_query_len <= 1).
+ * Which kernel runs: sequences of two or more query tokens run on the tiled MFMA
+ * prefill kernel when the pool is F16 or BF16, (head_dim_k, head_dim_v) is (64,64),
+ * (128,128) or (192,128), block_size is a power of two >= 16 and num_blocks *
+ * block_size < 2^32; single-token sequences then run on the decode kernels.  Any
+ * other supported shape (F32 pools, head dims 32 or 256, other block sizes) runs
+ * every token on the per-row kernel, one workgroup per (token, kv head): the same
+ * results, at a small fraction of the tiled kernel's rate for long prefills.
+ * ALiBi and merging: the bias is counted from each row's own end - 1, so a row's
+ * lse carries an offset of slopes[h] * (end - 1) from the page's form.  States of
+ * calls that see a row with different ends (for example context chunks read as
+ * separate sequences) are on different origins and must not be merged with
+ * pa_merge_states or pa_varlen_merge; merge ALiBi states only when each row's end
+ * is the same in both calls. */
 int pa_varlen(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out, int32_t out_dtype,
               float* lse, const int32_t* query_start_loc, const int32_t* seq_lens,
               const int32_t* positions, const int32_t* block_tables, int32_t max_blocks,
