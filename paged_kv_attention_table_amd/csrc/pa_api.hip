@@ -38,6 +38,11 @@ bool prefill_supported(int dtype, int dk, int dv, int group, int block_size, int
   return dims && pow2 && rows32 && group >= 1 && group <= kPrefillRows;
 }
 
+hipError_t launch_varlen_fused_f16(const PrefillArgs& p, const RowsArgs& r, int block_shift, uint32_t prefill_wgs,
+                                  hipStream_t stream);
+hipError_t launch_varlen_fused_bf16(const PrefillArgs& p, const RowsArgs& r, int block_shift, uint32_t prefill_wgs,
+                                   hipStream_t stream);
+
 hipError_t launch_decode_bf16(const RowsArgs& a, int block_shift, int dk, int dv, dim3 grid, hipStream_t stream);
 hipError_t launch_decode_f16(const RowsArgs& a, int block_shift, int dk, int dv, dim3 grid, hipStream_t stream);
 hipError_t launch_decode_fp8_bf16(const RowsArgs& a, int block_shift, int dk, int dv, dim3 grid, hipStream_t stream);
@@ -465,6 +470,16 @@ static int varlen_impl(const pa_kv_pool* pool, const void* q, int32_t q_dtype, v
   const int64_t groups8 = ((int64_t)num_seqs * pool->num_kv_heads + 7) / 8 * 8;
   const int64_t wgs = groups8 * p.tiles_per_seq;
   if (wgs > 0x7fffffffLL) return PA_EUNSUPPORTED;
+  // Single-token sequences on the MFMA decode kernel's shapes share the tile launch
+  // (the fused kernel); otherwise they follow it on a launch of their own.
+  const bool fuse = rows_take_singles && !split &&
+                    decode_mfma_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group, pool->block_size);
+  if (fuse) {
+    a.single_token_seqs = 1;
+    const int shift = pow2_shift(pool->block_size);
+    return from_hip(pool->dtype == PA_BF16 ? launch_varlen_fused_bf16(p, a, shift, (uint32_t)wgs, s)
+                                           : launch_varlen_fused_f16(p, a, shift, (uint32_t)wgs, s));
+  }
   st = from_hip(launch_prefill(p, pool->dtype, pool->head_dim_k, pool->head_dim_v, dim3((unsigned)wgs), s));
   if (st != PA_OK || !rows_take_singles) return st;
   if (split) return split_singles();

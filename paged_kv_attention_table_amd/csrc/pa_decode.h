@@ -143,46 +143,66 @@ __device__ __forceinline__ bool decode_row_range(const RowsArgs& a, int row, int
 // PR (fp8 only): the workgroup answers a pair of kv heads (2g, 2g + 1) and their 2G q
 // heads; tile rows interleave the two heads slot by slot (row 2p + h is slot p of
 // head h), so each slot's K and V are read as one 256-byte piece.
-template <typename T, int DK, int NW, bool WP, int NB, bool F8, bool PR = false>
-__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, int block_shift, uint32_t grid_rows) {
+// LDS of one decode workgroup: each wave's ring of K / V tiles, reused for the
+// merge of the waves' states at the end; the waves' true maxima; the prior lse of
+// a merged call's rows.
+template <int DK, int NW, int NB, bool F8>
+struct DecodeLds {
+  static constexpr int DV = 128;
+  // V of a tile: four loads of four 256-byte rows, blocks 1 KB + 32 bytes apart (fp8:
+  // four loads of eight 128-byte rows); K: KPIECES 256-byte pieces per row
+  static constexpr int VBLK = 1024 + 32, VBUF = 4 * VBLK;
+  static constexpr int KROWB = DK * 2, KPIECES = KROWB / 256, KBLK = 1024;
+  static constexpr int KBUF = F8 ? 4 * KBLK : 4 * KPIECES * KBLK;
+  static constexpr int VBUF8 = 4 * KBLK;
+  struct Merge {
+    float m[NW][16];
+    float l[NW][16];
+    float o[NW][16][DV];
+  };
+  struct Tiles {
+    char k[NW][NB][KBUF];
+    char v[NW][NB][F8 ? VBUF8 : VBUF];
+  };
+  union Ring {
+    Tiles t;
+    Merge r;
+  };
+  __align__(16) Ring u;
+  float true_max[NW][16];
+  float prev_lse[16];
+};
+
+// One decode workgroup's work: workgroup index wg of a grid of num_wgs, with its
+// LDS in L (a kernel of its own launches it alone; the fused varlen kernel beside
+// the prefill tiles).
+template <typename T, int DK, int NW, bool WP, int NB, bool F8, bool PR>
+__device__ __forceinline__ void decode_wg(const RowsArgs& a, int block_shift, uint32_t grid_rows, uint32_t wg,
+                                          uint32_t num_wgs, DecodeLds<DK, NW, NB, F8>& L) {
   static_assert(!WP || NW == 1, "split mode runs one wave per workgroup");
   static_assert(NB >= 2 && NB <= 4, "2 to 4 tile buffers per wave");
   static_assert(!F8 || DK == 128, "fp8 tiles of 128-byte rows");
   static_assert(!PR || F8, "kv-head pairs on fp8 tiles only");
+  using Lds = DecodeLds<DK, NW, NB, F8>;
   constexpr int EB = F8 ? 1 : 2;  // bytes per cache element
-  constexpr int DV = 128;         // V rows of 256 bytes (16 lanes x 16 bytes), 128 for fp8
+  constexpr int DV = Lds::DV;     // V rows of 256 bytes (16 lanes x 16 bytes), 128 for fp8
   constexpr int KCH = DK / 32;    // K operands (8 elements) per lane
   constexpr int ND = DV / 16;     // 16-wide d blocks of O^T
   // A tile's V arrives by direct global->LDS loads: load ii (0..3) writes
   // positions ii + 4c (c = 0..3) as four contiguous 256-byte rows (1 KB, one
   // 16-byte piece per lane); the loads' blocks are 1 KB + 32 bytes apart, so the
   // transpose reads of positions 4c + r (r = 0..3) hit distinct banks.
-  constexpr int VBLK = 1024 + 32;
-  constexpr int VBUF = 4 * VBLK;
+  constexpr int VBLK = Lds::VBLK;
   // K arrives the same way, KCH/4 * 4 loads of four 256-byte row pieces each; the
   // 16-byte chunks of a row are stored XOR-swizzled so that the A-operand reads
   // (16 positions x one chunk per 16 lanes) touch 16 distinct bank groups.
-  constexpr int KROWB = DK * 2;             // bytes of one K row
-  constexpr int KPIECES = KROWB / 256;      // 256-byte pieces per row
-  constexpr int KBLK = 1024;                // one load: 4 rows x 256 bytes (fp8: 8 x 128)
-  static_assert(KROWB % 256 == 0, "K rows of whole 256-byte pieces");
-  constexpr int KBUF = F8 ? 4 * KBLK : 4 * KPIECES * KBLK;  // a tile's K (fp8: 32 rows of 128 bytes)
-  constexpr int VBUF8 = 4 * KBLK;                           // a tile's fp8 V
-  constexpr int kTileLoads = F8 ? 8 : 4 * KPIECES + 4;      // load instructions per tile and wave
-  struct Merge {
-    float m[NW][16];
-    float l[NW][16];
-    float o[NW][16][DV];
-  };
-  __shared__ float true_max[NW][16];
-  struct Tiles {
-    char k[NW][NB][KBUF];
-    char v[NW][NB][F8 ? VBUF8 : VBUF];
-  };
-  __shared__ __align__(16) union {
-    Tiles t;
-    Merge r;
-  } sh;
+  constexpr int KPIECES = Lds::KPIECES;  // 256-byte pieces per row
+  constexpr int KBLK = Lds::KBLK;        // one load: 4 rows x 256 bytes (fp8: 8 x 128)
+  static_assert(Lds::KROWB % 256 == 0, "K rows of whole 256-byte pieces");
+  constexpr int kTileLoads = F8 ? 8 : 4 * KPIECES + 4;  // load instructions per tile and wave
+  auto& sh = L.u;
+  auto& true_max = L.true_max;
+  auto& prev_lse = L.prev_lse;
 
   if (status_failed(a.status)) return;
   // 1-D grid, kv head fastest: the workgroups of one row's kv heads are dispatched
@@ -192,11 +212,11 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
   // workgroups in flight work on few rows at a time and their state stores fill
   // contiguous rows of the workspace (partition-major order measured about 10 %
   // slower on the long-context workload).
-  const uint32_t wg = blockIdx.x, hkv_u = (uint32_t)(PR ? a.num_kv_heads / 2 : a.num_kv_heads);
+  const uint32_t hkv_u = (uint32_t)(PR ? a.num_kv_heads / 2 : a.num_kv_heads);
   const int g = (int)(wg % hkv_u);
   int row, pz;
   if constexpr (WP) {
-    const uint32_t parts_u = gridDim.x / (hkv_u * grid_rows);
+    const uint32_t parts_u = num_wgs / (hkv_u * grid_rows);
     pz = (int)((wg / hkv_u) % parts_u);
     row = (int)(wg / (hkv_u * parts_u));
   } else {
@@ -674,7 +694,6 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
 
   // merging into a state held by out (float32) and lse: every head's previous lse is
   // read before any is written
-  __shared__ float prev_lse[16];
   if (a.merge) {
     if ((int)threadIdx.x < GC) prev_lse[threadIdx.x] = a.lse[(int64_t)(hbase + threadIdx.x) * a.num_rows + q_row];
     __syncthreads();
@@ -730,6 +749,12 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
   }
 }
 
+template <typename T, int DK, int NW, bool WP, int NB, bool F8, bool PR = false>
+__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, int block_shift, uint32_t grid_rows) {
+  __shared__ DecodeLds<DK, NW, NB, F8> lds;
+  decode_wg<T, DK, NW, WP, NB, F8, PR>(a, block_shift, grid_rows, blockIdx.x, gridDim.x, lds);
+}
+
 // Waves per workgroup and tile buffers per wave.  A buffer holds a tile from load
 // issue until its copy into registers, so LDS bounds the loads in flight per CU:
 // unsplit, 8 waves x 2 buffers = 130 KB, one workgroup per CU; split with few
@@ -771,10 +796,14 @@ hipError_t launch_decode_typed(const RowsArgs& a, int block_shift, int dk, int d
       return hipGetLastError();
     }
   }
+  // Unsplit varlen rows over 16-bit caches run on 4-wave workgroups, as the fused
+  // varlen kernel runs them beside prefill tiles: a row's bits then do not depend on
+  // whether its batch holds prefill sequences.
+  const bool varlen_rows = a.query_start_loc != nullptr && a.partition_size == 0 && !F8;
   if (a.partition_size > 0 && (int64_t)n >= kOneWaveItems)
     hipLaunchKernelGGL((decode_mfma_kernel<T, 128, 1, true, one_bufs, F8>), dim3((uint32_t)n), dim3(64), 0, stream, a,
                        block_shift, rows);
-  else if (a.partition_size > 0)
+  else if (a.partition_size > 0 || varlen_rows)
     hipLaunchKernelGGL((decode_mfma_kernel<T, 128, kPartWaves, false, part_bufs, F8>), dim3((uint32_t)n),
                        dim3(kPartWaves * 64), 0, stream, a, block_shift, rows);
   else

@@ -1,0 +1,11 @@
+// F16 instantiations of the fused varlen kernel (prefill tiles + decode rows).
+#include "pa_varlen_fused.h"
+
+namespace pa {
+
+hipError_t launch_varlen_fused_f16(const PrefillArgs& p, const RowsArgs& r, int block_shift, uint32_t prefill_wgs,
+                                  hipStream_t stream) {
+  return launch_varlen_fused_typed<F16>(p, r, block_shift, prefill_wgs, stream);
+}
+
+}  // namespace pa

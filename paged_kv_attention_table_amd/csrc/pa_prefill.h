@@ -67,6 +67,7 @@ struct PrefillArgs {
   const float* sinks;  // [num_heads] sink logits, nullable
   const float* alibi;  // [num_heads] ALiBi slopes, nullable
   int merge;           // out (float32) and lse hold a state: merge this call's into it
+  int rank_major;      // workgroup order: query-tile rank first (see prefill_tile)
   const int32_t* status;
 };
 
@@ -131,15 +132,28 @@ struct TileRegs {
   u32x4 v[VN];
 };
 
+// LDS of one prefill workgroup: rings of K and V tiles (V rows padded by 32 bytes),
+// the workgroup's key range and the flag of the exact bf16 pass.
+template <int DK, int DV>
+struct PrefillLds {
+  static constexpr int NBUF = 3;   // ring depth, in key tiles
+  static constexpr int VPAD = 16;  // elements of padding per V row (32 bytes)
+  static constexpr int VROW = DV + VPAD;
+  __align__(16) uint16_t k[NBUF][kPrefillKeys][DK];
+  __align__(16) uint16_t v[NBUF][kPrefillKeys][VROW];
+  int range_lo, range_hi, v_out_of_range;
+};
+
+// One prefill workgroup's work: workgroup index L of the tile grid, its LDS in sh (a
+// kernel of its own launches it alone; the fused varlen kernel beside decode rows).
 // ALIBI: a.alibi is non-null; MERGE: a.merge is set (separate instantiations, so the
 // loop without them keeps its registers).
 template <typename T, int DK, int DV, bool ALIBI, bool MERGE>
-__global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const PrefillArgs a) {
+__device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, PrefillLds<DK, DV>& sh) {
   constexpr int KT = kPrefillKeys;
   constexpr int NTH = kPrefillThreads;
-  constexpr int VPAD = 16;  // elements of padding per V row in LDS (32 bytes)
-  constexpr int VROW = DV + VPAD;
-  constexpr int NBUF = 3;  // LDS ring depth, in key tiles
+  constexpr int VROW = PrefillLds<DK, DV>::VROW;
+  constexpr int NBUF = PrefillLds<DK, DV>::NBUF;  // LDS ring depth, in key tiles
   using Regs = TileRegs<DK, DV>;
   constexpr int KCH = Regs::KCH, VCH = Regs::VCH;
   constexpr int KSTEPS = DK / 32;
@@ -152,22 +166,35 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
   // 256-byte rows the 16 rows one read touches get 16 distinct slots of the bank
   // space; with 128- or 384-byte rows consecutive rows alternate between its two
   // 128-byte halves, and (r / 2) % 8 spreads eight of them over each half.
-  __shared__ __align__(16) uint16_t k_lds[NBUF][KT][DK];
-  __shared__ __align__(16) uint16_t v_lds[NBUF][KT][VROW];
-  __shared__ int range_lo, range_hi, v_out_of_range;
+  auto& k_lds = sh.k;
+  auto& v_lds = sh.v;
+  int& range_lo = sh.range_lo;
+  int& range_hi = sh.range_hi;
+  int& v_out_of_range = sh.v_out_of_range;
 
   if (status_failed(a.status)) return;
   // XCD-aware 1-D grid.  Workgroup L runs on XCD L % 8 (the dispatcher deals
   // workgroups round-robin over the 8 XCDs); all query tiles of one (sequence, kv
   // head) group get the same L % 8, so they share that XCD's L2 for the group's
-  // K/V, and consecutive groups rotate over the XCDs.  Tiles run last-first: under
-  // a causal mask the later tiles see more keys, so the longest workgroups start
-  // first.
+  // K/V.  Tiles run last-first: under a causal mask the later tiles see more keys,
+  // so the longest workgroups start first.  Group-major order (a group's tiles 8
+  // workgroups apart, consecutive groups rotating over the XCDs) keeps a group's
+  // tiles in flight together; rank-major order (the last tile of every group, then
+  // the one before, ...; groups padded to a multiple of 8) starts the heaviest
+  // tiles of all groups first, for grids that run in about one round.
   const int TPS = a.tiles_per_seq;
-  const int L = blockIdx.x, xcd = L & 7, q8 = L >> 3;
-  const int grp = (q8 / TPS) * 8 + xcd;
+  int grp, tile;
+  if (a.rank_major) {
+    const int groups8 = (a.num_seqs * a.num_kv_heads + 7) / 8 * 8;
+    grp = L % groups8;
+    tile = TPS - 1 - L / groups8;
+  } else {
+    const int xcd = L & 7, q8 = L >> 3;
+    grp = (q8 / TPS) * 8 + xcd;
+    tile = TPS - 1 - q8 % TPS;
+  }
   if (grp >= a.num_seqs * a.num_kv_heads) return;
-  const int tile = TPS - 1 - q8 % TPS, s = grp / a.num_kv_heads, g = grp % a.num_kv_heads;
+  const int s = grp / a.num_kv_heads, g = grp % a.num_kv_heads;
   const int q0 = a.query_start_loc[s];
   const int q_len = a.query_start_loc[s + 1] - q0;
   const int TPT = a.tokens_per_tile;
@@ -715,6 +742,12 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const Prefi
     }
     if (a.lse != nullptr && c == 0) a.lse[li] = lse_new;
   }
+}
+
+template <typename T, int DK, int DV, bool ALIBI, bool MERGE>
+__global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const PrefillArgs a) {
+  __shared__ PrefillLds<DK, DV> lds;
+  prefill_tile<T, DK, DV, ALIBI, MERGE>(a, blockIdx.x, lds);
 }
 
 template <typename T, bool ALIBI, bool MERGE>

@@ -61,3 +61,18 @@ def test_no_register_reuse_under_inflight_loads(tmp_path, src, tname):
             loads, bad = untracked_load_hazards(asm, kernel)
             assert loads > 0, kernel
             assert not bad, f"{kernel}: {bad[:3]}"
+
+
+@pytest.mark.skipif(shutil.which(HIPCC) is None and not os.path.exists(HIPCC), reason="hipcc not available")
+@pytest.mark.parametrize("src,tname", [("pa_fused_bf16.hip", "4BF16"), ("pa_fused_f16.hip", "3F16")])
+def test_fused_varlen_kernel_no_register_reuse(tmp_path, src, tname):
+    """The fused varlen kernel carries the prefill tile loop (head dim 128) beside
+    the decode rows: the same check on it."""
+    out = tmp_path / (src + ".s")
+    subprocess.run([HIPCC, *FLAGS, os.path.join(CSRC, src), "-o", str(out)], check=True, capture_output=True)
+    asm = out.read_text()
+    for alibi, merge in (("0", "0"), ("1", "0"), ("0", "1"), ("1", "1")):
+        kernel = f"_ZN2pa19varlen_fused_kernelINS_{tname}ELb{alibi}ELb{merge}EEEvNS_11PrefillArgsENS_8RowsArgsEij"
+        loads, bad = untracked_load_hazards(asm, kernel)
+        assert loads > 0, kernel
+        assert not bad, f"{kernel}: {bad[:3]}"
