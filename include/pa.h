@@ -234,6 +234,32 @@ int pa_varlen_merge(const pa_kv_pool* pool, const void* q, int32_t q_dtype, floa
                     int32_t sliding_window, const float* sinks, const float* alibi_slopes, int32_t* status,
                     void* stream);
 
+/* Attention over a context segment and the sequence's new tokens in one pass
+ * ("cpu_mla_prefill.cpp": the chunked-context prefill -- MlaPrefillAttention over a
+ * context chunk and over the new tokens, MergeAttnStates to combine them -- with the
+ * two key sets in one softmax).  Token t of sequence s (query_start_loc as for
+ * pa_varlen) sees every position [0, ctx_lens[s]) of ctx_tables (non-causal) and,
+ * when new_lens[s] > 0, positions [0, new_positions[t] + 1) of new_tables (the new
+ * tokens, causal; new_positions are positions within them).  With merge == 0, out
+ * [num_tokens, num_heads, head_dim_v] and lse [num_heads, num_tokens] (float32, both
+ * required) receive the result; with merge != 0 they hold a state and the result is
+ * merged into it as the suffix, by pa_merge_states' rules.  Equal to merging the
+ * context segment's state and then the new tokens' (up to rounding), without the
+ * second pass over the state.  Pool element type = q_dtype; no window, ALiBi or
+ * split-KV; sinks as for pa_varlen.  Device checks (with status): query_start_loc
+ * as for pa_varlen; ctx_lens and new_lens >= 0 with their first ceil(len /
+ * block_size) ids in [0, num_blocks) and at most ctx_max_blocks / new_max_blocks of
+ * them; every new_position in [0, new_lens[s]) where new_lens[s] > 0.  Supported:
+ * the shapes pa_varlen runs on its tiled kernel (F16 / BF16, (head_dim_k,
+ * head_dim_v) in {(64,64), (128,128), (192,128)}, power-of-two block_size >= 16,
+ * num_blocks * block_size < 2^32); every sequence runs on the tiled kernel. */
+int pa_varlen_ctx_new(const pa_kv_pool* pool, const void* q, int32_t q_dtype, float* out, float* lse, int32_t merge,
+                      const int32_t* query_start_loc, const int32_t* ctx_lens, const int32_t* ctx_tables,
+                      int32_t ctx_max_blocks, const int32_t* new_lens, const int32_t* new_positions,
+                      const int32_t* new_tables, int32_t new_max_blocks, int32_t num_seqs, int64_t num_tokens,
+                      int32_t max_query_len, int32_t num_heads, float scale, const float* sinks, int32_t* status,
+                      void* stream);
+
 /* Merge two attention states over disjoint key sets ("cpu_mla_prefill.cpp",
  * MergeAttnStates).  prefix_out, suffix_out, out: [num_tokens, num_heads, head_dim] in
  * dtype; prefix_lse, suffix_lse, out_lse (nullable): float32 [num_heads, num_tokens].

@@ -23,7 +23,7 @@ DTYPE_CODE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_B
               torch.float8_e4m3fn: PA_FP8_E4M3}
 
 EXPORTS = ("pa_strerror", "pa_write_kv", "pa_decode", "pa_decode_noalloc", "pa_varlen", "pa_varlen_merge",
-           "pa_merge_states", "pa_gather_cache")
+           "pa_varlen_ctx_new", "pa_merge_states", "pa_gather_cache")
 
 
 class PaKvPool(ctypes.Structure):
@@ -67,6 +67,9 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.pa_varlen_merge.restype = ctypes.c_int
     lib.pa_varlen_merge.argtypes = [pool_p, vp, i32, vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, f32, i32, i32,
                                     vp, vp, vp, vp]
+    lib.pa_varlen_ctx_new.restype = ctypes.c_int
+    lib.pa_varlen_ctx_new.argtypes = [pool_p, vp, i32, vp, vp, i32, vp, vp, vp, i32, vp, vp, vp, i32, i32, i64, i32, i32,
+                                      f32, vp, vp, vp]
     lib.pa_merge_states.restype = ctypes.c_int
     lib.pa_merge_states.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i64, i32, vp]
     lib.pa_gather_cache.restype = ctypes.c_int
@@ -308,6 +311,41 @@ def pa_varlen_merge(k_pool, v_pool, q, out, query_start_loc, seq_lens, positions
                                 block_tables.shape[1], S, T, int(max_query_len), H, float(scale), int(bool(causal)),
                                 int(sliding_window), _ptr(sinks), _ptr(alibi_slopes), _ptr(status), _stream(stream))
     _check(st, "pa_varlen_merge")
+
+
+def pa_varlen_ctx_new(k_pool, v_pool, q, out, lse, query_start_loc, ctx_lens, ctx_tables, new_lens, new_positions,
+                      new_tables, max_query_len, scale, merge=False, sinks=None, status=None, stream=None, k_scale=1.0,
+                      v_scale=1.0):
+    """Attention of q [T, H, Dk] over each sequence's context segment (ctx_lens,
+    ctx_tables; non-causal) and its new tokens (new_lens, new_tables; causal by
+    new_positions [T]); out [T, H, Dv] and lse [H, T] float32 receive the result, or
+    hold a state it is merged into (merge=True)."""
+    pool = make_pool(k_pool, v_pool, k_scale, v_scale)
+    _dev(q, "q", ndim=3)
+    _dev(out, "out", dtype=torch.float32, ndim=3)
+    _dev(lse, "lse", dtype=torch.float32, ndim=2)
+    _dev(query_start_loc, "query_start_loc", dtype=torch.int32, ndim=1)
+    for t, name in ((ctx_lens, "ctx_lens"), (new_lens, "new_lens"), (new_positions, "new_positions")):
+        _dev(t, name, dtype=torch.int32, ndim=1)
+    _dev(ctx_tables, "ctx_tables", dtype=torch.int32, ndim=2)
+    _dev(new_tables, "new_tables", dtype=torch.int32, ndim=2)
+    _dev(status, "status", dtype=torch.int32)
+    _dev(sinks, "sinks", dtype=torch.float32, ndim=1)
+    T, H, _ = q.shape
+    S = ctx_lens.numel()
+    _shape(sinks, (H,), "sinks")
+    _shape(out, (T, H, pool.head_dim_v), "out")
+    _shape(lse, (H, T), "lse")
+    _shape(query_start_loc, (S + 1,), "query_start_loc")
+    _shape(new_lens, (S,), "new_lens")
+    _shape(new_positions, (T,), "new_positions")
+    if ctx_tables.shape[0] != S or new_tables.shape[0] != S:
+        raise ValueError("ctx_tables and new_tables must have one row per sequence")
+    st = load().pa_varlen_ctx_new(ctypes.byref(pool), _ptr(q), _code(q, "q"), _ptr(out), _ptr(lse), int(bool(merge)),
+                                  _ptr(query_start_loc), _ptr(ctx_lens), _ptr(ctx_tables), ctx_tables.shape[1],
+                                  _ptr(new_lens), _ptr(new_positions), _ptr(new_tables), new_tables.shape[1], S, T,
+                                  int(max_query_len), H, float(scale), _ptr(sinks), _ptr(status), _stream(stream))
+    _check(st, "pa_varlen_ctx_new")
 
 
 def pa_merge_states(out, out_lse, prefix_out, prefix_lse, suffix_out, suffix_lse, prefill_tokens_with_context=-1,

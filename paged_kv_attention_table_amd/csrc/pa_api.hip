@@ -510,6 +510,99 @@ int pa_varlen_merge(const pa_kv_pool* pool, const void* q, int32_t q_dtype, floa
                      nullptr, nullptr, nullptr, sinks, alibi_slopes, status, stream, 1);
 }
 
+int pa_varlen_ctx_new(const pa_kv_pool* pool, const void* q, int32_t q_dtype, float* out, float* lse, int32_t merge,
+                      const int32_t* query_start_loc, const int32_t* ctx_lens, const int32_t* ctx_tables,
+                      int32_t ctx_max_blocks, const int32_t* new_lens, const int32_t* new_positions,
+                      const int32_t* new_tables, int32_t new_max_blocks, int32_t num_seqs, int64_t num_tokens,
+                      int32_t max_query_len, int32_t num_heads, float scale, const float* sinks, int32_t* status,
+                      void* stream) {
+  int st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_tokens < 0 || num_heads < 1 || ctx_max_blocks < 1 || new_max_blocks < 1 ||
+      max_query_len < 0 || query_start_loc == nullptr)
+    return PA_EINVAL;
+  if (num_seqs > 0 && (ctx_lens == nullptr || ctx_tables == nullptr || new_lens == nullptr || new_tables == nullptr))
+    return PA_EINVAL;
+  if (num_tokens > 0 && (q == nullptr || out == nullptr || lse == nullptr || new_positions == nullptr || num_seqs == 0))
+    return PA_EINVAL;
+  if (num_heads % pool->num_kv_heads != 0) return PA_ESHAPE;
+  if (q_dtype != pool->dtype) return PA_EUNSUPPORTED;
+  const int group = num_heads / pool->num_kv_heads;
+  if (!prefill_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group, pool->block_size, pool->num_blocks))
+    return PA_EUNSUPPORTED;
+  float scale_log2;
+  if (!folded_scale(pool, scale, scale_log2)) return PA_EINVAL;
+  if (num_tokens > 0x7fffffffLL || num_seqs > 65535) return PA_EUNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (status != nullptr) {
+    // the context segment as a non-causal varlen call, then the new tokens' segment
+    // (positions checked where it is not empty), ORed into the same word
+    ValidateArgs v = {};
+    v.mode = kValidateVarlen;
+    v.num_blocks = pool->num_blocks;
+    v.block_size = pool->block_size;
+    v.block_tables = ctx_tables;
+    v.max_blocks = ctx_max_blocks;
+    v.seq_lens = ctx_lens;
+    v.num_seqs = num_seqs;
+    v.query_start_loc = query_start_loc;
+    v.num_tokens = num_tokens;
+    v.max_query_len = max_query_len;
+    v.status = status;
+    st = from_hip(launch_validate(v, s));
+    if (st != PA_OK) return st;
+    v.block_tables = new_tables;
+    v.max_blocks = new_max_blocks;
+    v.seq_lens = new_lens;
+    v.positions = new_positions;
+    v.causal = 1;
+    v.positions_if_nonempty = 1;
+    v.accumulate = 1;
+    st = from_hip(launch_validate(v, s));
+    if (st != PA_OK) return st;
+  }
+  if (num_tokens == 0) return PA_OK;
+  PrefillArgs p = {};
+  p.k_pool = pool->k;
+  p.v_pool = pool->v;
+  p.num_blocks = pool->num_blocks;
+  p.block_size = pool->block_size;
+  p.num_kv_heads = pool->num_kv_heads;
+  p.q = q;
+  p.out = out;
+  p.out_dtype = PA_F32;
+  p.lse = lse;
+  p.block_tables = ctx_tables;
+  p.max_blocks = ctx_max_blocks;
+  p.seq_lens = ctx_lens;
+  p.query_start_loc = query_start_loc;
+  p.positions = new_positions;
+  p.num_seqs = num_seqs;
+  p.num_tokens = num_tokens;
+  p.num_heads = num_heads;
+  p.group = group;
+  p.block_shift = pow2_shift(pool->block_size);
+  p.tokens_per_tile = kPrefillRows / group;
+  p.min_q_len = 1;
+  p.scale_log2 = scale_log2;
+  p.v_scale = pool->v_scale;
+  p.causal = 0;
+  p.window = 0;
+  p.sinks = sinks;
+  p.alibi = nullptr;
+  p.merge = merge ? 1 : 0;
+  p.new_lens = new_lens;
+  p.new_tables = new_tables;
+  p.new_max_blocks = new_max_blocks;
+  p.status = status;
+  p.tiles_per_seq = (max_query_len + p.tokens_per_tile - 1) / p.tokens_per_tile;
+  const int64_t groups8 = ((int64_t)num_seqs * pool->num_kv_heads + 7) / 8 * 8;
+  const int64_t wgs = groups8 * p.tiles_per_seq;
+  if (wgs > 0x7fffffffLL) return PA_EUNSUPPORTED;
+  if (wgs == 0) return PA_OK;
+  return from_hip(launch_prefill(p, pool->dtype, pool->head_dim_k, pool->head_dim_v, dim3((unsigned)wgs), s));
+}
+
 int pa_merge_states(void* out, float* out_lse, const void* prefix_out, const float* prefix_lse,
                     const void* suffix_out, const float* suffix_lse, int64_t num_tokens, int32_t num_heads,
                     int32_t head_dim, int64_t prefill_tokens_with_context, int32_t dtype, void* stream) {

@@ -62,6 +62,8 @@ struct ValidateArgs {
   int max_query_len;
   const int32_t* positions;
   int causal;
+  int positions_if_nonempty;  // causal positions checked only for sequences of length > 0
+  int accumulate;             // OR into the status word left by an earlier check (no clear)
   int32_t* status;
 };
 // Latent-cache gather ("cpu_mla_prefill.cpp", GatherMlaCache).

@@ -68,6 +68,15 @@ struct PrefillArgs {
   const float* alibi;  // [num_heads] ALiBi slopes, nullable
   int merge;           // out (float32) and lse hold a state: merge this call's into it
   int rank_major;      // workgroup order: query-tile rank first (see prefill_tile)
+  // Two key segments per sequence (new_lens non-null): the keys are segment A --
+  // positions [0, seq_lens[s]) of block_tables, seen by every query of s -- then
+  // segment B -- positions [0, new_lens[s]) of new_tables, seen causally: a query
+  // sees B's positions [0, positions[t] + 1) (B's positions are not read when
+  // new_lens[s] is 0).  The loop runs over one key space: A at [0, lenA), B from
+  // the next multiple of 32 (the gap between them is masked).
+  const int32_t* new_lens;
+  const int32_t* new_tables;
+  int new_max_blocks;
   const int32_t* status;
 };
 
@@ -146,10 +155,12 @@ struct PrefillLds {
 
 // One prefill workgroup's work: workgroup index L of the tile grid, its LDS in sh (a
 // kernel of its own launches it alone; the fused varlen kernel beside decode rows).
-// ALIBI: a.alibi is non-null; MERGE: a.merge is set (separate instantiations, so the
-// loop without them keeps its registers).
-template <typename T, int DK, int DV, bool ALIBI, bool MERGE>
+// ALIBI: a.alibi is non-null; MERGE: a.merge is set; SEG2: a.new_lens is non-null
+// (separate instantiations, so the loop without them keeps its registers and
+// instructions).
+template <typename T, int DK, int DV, bool ALIBI, bool MERGE, bool SEG2 = false>
 __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, PrefillLds<DK, DV>& sh) {
+  static_assert(!(SEG2 && ALIBI), "two key segments take no ALiBi");
   constexpr int KT = kPrefillKeys;
   constexpr int NTH = kPrefillThreads;
   constexpr int VROW = PrefillLds<DK, DV>::VROW;
@@ -206,6 +217,24 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
   int n = a.seq_lens[s];
   const int cap = a.max_blocks * a.block_size;
   n = n < 0 ? 0 : (n > cap ? cap : n);
+  // two segments: A = [0, n), B = [base_b, base_b + len_b) of the key space; the gap
+  // [n, base_b) is masked (gap_lo == gap_hi: none)
+  int len_b = 0, base_b = n;
+  if constexpr (SEG2) {
+    const int cap_b = a.new_max_blocks * a.block_size;
+    len_b = a.new_lens[s];
+    len_b = len_b < 0 ? 0 : (len_b > cap_b ? cap_b : len_b);
+    base_b = (n + kPrefillKeys - 1) & ~(kPrefillKeys - 1);
+  }
+  const int gap_lo = n, gap_hi = len_b > 0 ? base_b : n;
+  auto in_gap = [&](int j) {
+    if constexpr (SEG2) return j >= gap_lo && j < gap_hi;
+    return false;
+  };
+  auto tile_meets_gap = [&](int t0) {
+    if constexpr (SEG2) return t0 < gap_hi && t0 + kPrefillKeys > gap_lo;
+    return false;
+  };
 
   if (tid == 0) {
     range_lo = 0x7fffffff;
@@ -226,7 +255,13 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
     row_tok[rb] = q0 + (row_ok[rb] ? tl : 0);
     row_head[rb] = g * G + r % G;
     int end = n, start = 0;
-    if (a.causal) {
+    if constexpr (SEG2) {
+      if (len_b > 0) {
+        int pos = a.positions[row_tok[rb]];
+        pos = pos < 0 ? 0 : (pos >= len_b ? len_b - 1 : pos);
+        end = base_b + pos + 1;
+      }
+    } else if (a.causal) {
       int pos = a.positions[row_tok[rb]];
       pos = pos < 0 ? 0 : (pos >= n ? n - 1 : pos);
       end = n > 0 ? pos + 1 : 0;
@@ -364,6 +399,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
     }
     if (klo >= khi) return;
     const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks;
+    const int32_t* table_b = SEG2 ? a.new_tables + (int64_t)s * a.new_max_blocks : table;
     const char* kbase = static_cast<const char*>(a.k_pool) + (int64_t)g * DK * 2;
     const char* vbase = static_cast<const char*>(a.v_pool) + (int64_t)g * DV * 2;
     const int t_first = klo & ~(KT - 1);
@@ -381,11 +417,17 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
     struct Rows {
       uint32_t lo, hi;
     };
+    const int max_idx_b = SEG2 ? a.new_max_blocks - 1 : max_idx;
     auto tile_rows = [&](int i) -> Rows {
-      const int u0 = __builtin_amdgcn_readfirstlane(t_first + i * KT), u1 = u0 + 16;
-      const int i0 = min(u0 >> a.block_shift, max_idx), i1 = min(u1 >> a.block_shift, max_idx);
+      int u0 = __builtin_amdgcn_readfirstlane(t_first + i * KT);
+      // a tile lies in one segment (B starts at a multiple of the tile size)
+      const bool in_b = SEG2 && u0 >= base_b && len_b > 0;
+      const int32_t* tab = in_b ? table_b : table;
+      if (in_b) u0 -= base_b;
+      const int u1 = u0 + 16, mi = in_b ? max_idx_b : max_idx;
+      const int i0 = min(u0 >> a.block_shift, mi), i1 = min(u1 >> a.block_shift, mi);
       int b0, b1;
-      load_scalar_i32x2(table, (uint32_t)i0 * 4u, (uint32_t)i1 * 4u, b0, b1);
+      load_scalar_i32x2(tab, (uint32_t)i0 * 4u, (uint32_t)i1 * 4u, b0, b1);
       b0 = min(max(b0, 0), last_block);
       b1 = min(max(b1, 0), last_block);
       return Rows{((uint32_t)b0 << a.block_shift) | (uint32_t)(u0 & (b - 1)),
@@ -432,7 +474,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
     // range are replaced by -inf, whatever the bytes hold.)
     auto stash_v = [&](const Regs& R, int iv, int vb) {
       const int tv = t_first + iv * KT;
-      const bool edge = tv < klo || tv + KT > khi;
+      const bool edge = tv < klo || tv + KT > khi || tile_meets_gap(tv);
       const u32x4 zero = {0u, 0u, 0u, 0u};
       auto put = [&](bool masking) {
 #pragma unroll
@@ -442,7 +484,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
           if constexpr (T::code == PA_BF16 && !EXACT) x = bf16x8_to_f16x8(x);
           if (masking) {
             const int j = tv + v_key[u];
-            if (j < klo || j >= khi) x = zero;
+            if (j < klo || j >= khi || in_gap(j)) x = zero;
           }
           *dst = x;
         }
@@ -477,7 +519,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
     auto soft_max = [&](int i, f32x4 (&sc)[2][2]) {
       const int t0 = t_first + i * KT;
       // Tiles inside every row's visible range skip the masking.
-      const bool masked = !(w_lo_max <= t0 && w_hi_min >= t0 + KT);  // some row sees only part of it
+      // (the gap between two key segments is masked for every row)
+      const bool masked = !(w_lo_max <= t0 && w_hi_min >= t0 + KT) || tile_meets_gap(t0);
       if constexpr (ALIBI) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
@@ -498,7 +541,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
               const int j = t0 + kb * 16 + 4 * c + ii;
-              if (j < vis_lo[rb] || j >= vis_hi[rb]) sc[kb][rb][ii] = -INFINITY;
+              if (j < vis_lo[rb] || j >= vis_hi[rb] || in_gap(j)) sc[kb][rb][ii] = -INFINITY;
             }
         }
         // this lane's max; the row-wide max is only formed when the reference must move
@@ -744,21 +787,21 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
   }
 }
 
-template <typename T, int DK, int DV, bool ALIBI, bool MERGE>
+template <typename T, int DK, int DV, bool ALIBI, bool MERGE, bool SEG2 = false>
 __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const PrefillArgs a) {
   __shared__ PrefillLds<DK, DV> lds;
-  prefill_tile<T, DK, DV, ALIBI, MERGE>(a, blockIdx.x, lds);
+  prefill_tile<T, DK, DV, ALIBI, MERGE, SEG2>(a, blockIdx.x, lds);
 }
 
-template <typename T, bool ALIBI, bool MERGE>
+template <typename T, bool ALIBI, bool MERGE, bool SEG2 = false>
 hipError_t launch_prefill_dims(const PrefillArgs& a, int dk, int dv, dim3 grid, hipStream_t stream) {
   const dim3 block(kPrefillThreads);
   if (dk == 128 && dv == 128)
-    hipLaunchKernelGGL((prefill_kernel<T, 128, 128, ALIBI, MERGE>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<T, 128, 128, ALIBI, MERGE, SEG2>), grid, block, 0, stream, a);
   else if (dk == 192 && dv == 128)
-    hipLaunchKernelGGL((prefill_kernel<T, 192, 128, ALIBI, MERGE>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<T, 192, 128, ALIBI, MERGE, SEG2>), grid, block, 0, stream, a);
   else if (dk == 64 && dv == 64)
-    hipLaunchKernelGGL((prefill_kernel<T, 64, 64, ALIBI, MERGE>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<T, 64, 64, ALIBI, MERGE, SEG2>), grid, block, 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -766,6 +809,11 @@ hipError_t launch_prefill_dims(const PrefillArgs& a, int dk, int dv, dim3 grid, 
 
 template <typename T>
 hipError_t launch_prefill_typed(const PrefillArgs& a, int dk, int dv, dim3 grid, hipStream_t stream) {
+  if (a.new_lens != nullptr) {  // two key segments (no ALiBi)
+    if (a.alibi != nullptr) return hipErrorInvalidValue;
+    return a.merge ? launch_prefill_dims<T, false, true, true>(a, dk, dv, grid, stream)
+                   : launch_prefill_dims<T, false, false, true>(a, dk, dv, grid, stream);
+  }
   if (a.merge)
     return a.alibi != nullptr ? launch_prefill_dims<T, true, true>(a, dk, dv, grid, stream)
                               : launch_prefill_dims<T, false, true>(a, dk, dv, grid, stream);

@@ -19,8 +19,8 @@ def declared_functions():
 
 def test_header_declares_the_calls():
     names = declared_functions()
-    for n in ("pa_write_kv", "pa_decode", "pa_decode_noalloc", "pa_varlen", "pa_varlen_merge", "pa_merge_states",
-              "pa_gather_cache", "pa_strerror"):
+    for n in ("pa_write_kv", "pa_decode", "pa_decode_noalloc", "pa_varlen", "pa_varlen_merge", "pa_varlen_ctx_new",
+              "pa_merge_states", "pa_gather_cache", "pa_strerror"):
         assert n in names, names
 
 
@@ -259,3 +259,26 @@ def test_decode_noalloc_host_checks():
     assert call(big, 2, 4, 4, 24) == binding.PA_EINVAL               # not a multiple of the block size
     assert call(big, 2, 4, 4, -16) == binding.PA_EINVAL
     assert binding.strerror(binding.PA_ESCRATCH) != "unknown status"
+
+
+def test_varlen_ctx_new_host_checks():
+    lib = binding.load()
+    p = ctypes.byref(_pool(head_dim_k=128, head_dim_v=128))
+
+    def call(**kw):
+        a = dict(pool=p, q_dtype=binding.PA_F16, lse=FAKE, merge=0, ctx_lens=FAKE, new_positions=FAKE, ctx_mb=4,
+                 new_mb=4, S=2, T=10, H=4, scale=0.1)
+        a.update(kw)
+        return lib.pa_varlen_ctx_new(a["pool"], FAKE, a["q_dtype"], FAKE, a["lse"], a["merge"], FAKE, a["ctx_lens"],
+                                     FAKE, a["ctx_mb"], FAKE, a["new_positions"], FAKE, a["new_mb"], a["S"], a["T"], 8,
+                                     a["H"], a["scale"], None, None, None)
+
+    assert call(lse=None) == binding.PA_EINVAL            # the state's lse is required
+    assert call(new_positions=None) == binding.PA_EINVAL  # causal new tokens need their positions
+    assert call(ctx_lens=None) == binding.PA_EINVAL
+    assert call(ctx_mb=0) == binding.PA_EINVAL
+    assert call(H=5) == binding.PA_ESHAPE
+    assert call(q_dtype=binding.PA_BF16) == binding.PA_EUNSUPPORTED                      # q of the pool's type
+    assert call(pool=ctypes.byref(_pool(head_dim_k=32, head_dim_v=32))) == binding.PA_EUNSUPPORTED  # tiled shapes only
+    assert call(pool=ctypes.byref(_pool(head_dim_k=128, head_dim_v=128, block_size=8))) == binding.PA_EUNSUPPORTED
+    assert call(scale=0.0) == binding.PA_EINVAL

@@ -55,9 +55,11 @@ def test_no_register_reuse_under_inflight_loads(tmp_path, src, tname):
     out = tmp_path / (src + ".s")
     subprocess.run([HIPCC, *FLAGS, os.path.join(CSRC, src), "-o", str(out)], check=True, capture_output=True)
     asm = out.read_text()
+    # ALiBi; merged into a prior state; two key segments (without ALiBi)
+    flags = [(a, m, "0") for a in "01" for m in "01"] + [("0", m, "1") for m in "01"]
     for dims in ("128ELi128", "192ELi128", "64ELi64"):
-        for alibi, merge in (("0", "0"), ("1", "0"), ("0", "1"), ("1", "1")):  # ALiBi; merged into a prior state
-            kernel = f"_ZN2pa14prefill_kernelINS_{tname}ELi{dims}ELb{alibi}ELb{merge}EEEvNS_11PrefillArgsE"
+        for alibi, merge, seg2 in flags:
+            kernel = f"_ZN2pa14prefill_kernelINS_{tname}ELi{dims}ELb{alibi}ELb{merge}ELb{seg2}EEEvNS_11PrefillArgsE"
             loads, bad = untracked_load_hazards(asm, kernel)
             assert loads > 0, kernel
             assert not bad, f"{kernel}: {bad[:3]}"
