@@ -87,8 +87,8 @@ def parse():
 CSRC = os.path.join(ROOT, "paged_kv_attention_table_amd", "csrc")
 KERNEL_SOURCES = {"decode_mfma_kernel": ("pa_decode.h", "pa_common.h", "pa_misc.hip"),
                   "prefill_kernel": ("pa_prefill.h", "pa_common.h"),
-                  "pa_varlen_call": ("pa_prefill.h", "pa_decode.h", "pa_rows.h", "pa_common.h", "pa_misc.hip",
-                                     "pa_api.hip")}
+                  "pa_varlen_call": ("pa_prefill.h", "pa_decode.h", "pa_varlen_fused.h", "pa_rows.h", "pa_common.h",
+                                     "pa_misc.hip", "pa_api.hip")}
 TRAFFIC_TABLES = ("traffic.md", "traffic_prefill.md")
 
 
@@ -451,8 +451,8 @@ def prefill_entry(args, kind, cpu_budget_s):
         def write():
             pa_write_kv(kp, vp, k_new, v_new, slots)
 
-        kernel_label = ("pa_varlen call (prefill tile kernel + single-token row kernel"
-                        + (" split, + partition reduce)" if P else ")"))
+        kernel_label = ("pa_varlen call (" + ("prefill tile kernel + split single-token rows + partition reduce)"
+                                              if P else "fused kernel: prefill tiles and single-token decode rows)"))
         name, dtype = w.name, w.dtype
         cfg = {"workload": name, "prefill_seqs": 4, "decode_seqs": 12, "num_tokens": w.num_tokens,
                "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.dk,
@@ -476,12 +476,12 @@ def prefill_entry(args, kind, cpu_budget_s):
         def write():
             pa_write_kv(kp, vp, k_new, v_new, slots)
 
-        kernel_label = ("chunked prefill (pa_varlen on the first context chunk, pa_varlen_merge on the others "
-                        "and on the causal new tokens)")
+        kernel_label = ("chunked prefill (pa_varlen_ctx_new per context chunk, merging into the state after the "
+                        "first; each request's causal new tokens in its last chunk's call)")
         name, dtype = cp.name, cp.dtype
         cfg = {"workload": name, "requests": int(cp.ctx_lens.size), "num_tokens": cp.num_tokens,
                "num_heads": cp.num_heads, "head_dim_k": cp.dk, "head_dim_v": cp.dv, "chunk": cp.chunk,
-               "step": "pa_write_kv + chunked prefill (pa_varlen, then pa_varlen_merge)"}
+               "step": "pa_write_kv + chunked prefill (pa_varlen_ctx_new per context chunk)"}
     def step():
         write()
         attn()
