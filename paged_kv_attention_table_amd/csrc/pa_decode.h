@@ -179,7 +179,8 @@ struct DecodeLds {
 template <typename T, int DK, int NW, bool WP, int NB, bool F8, bool PR>
 __device__ __forceinline__ void decode_wg(const RowsArgs& a, int block_shift, uint32_t grid_rows, uint32_t wg,
                                           uint32_t num_wgs, DecodeLds<DK, NW, NB, F8>& L) {
-  static_assert(!WP || NW == 1, "split mode runs one wave per workgroup");
+  // WP: each wave answers one (row, kv head, partition) alone -- NW > 1: the
+  // workgroup's waves take NW consecutive kv heads of the same row and partition
   static_assert(NB >= 2 && NB <= 4, "2 to 4 tile buffers per wave");
   static_assert(!F8 || DK == 128, "fp8 tiles of 128-byte rows");
   static_assert(!PR || F8, "kv-head pairs on fp8 tiles only");
@@ -212,8 +213,9 @@ __device__ __forceinline__ void decode_wg(const RowsArgs& a, int block_shift, ui
   // workgroups in flight work on few rows at a time and their state stores fill
   // contiguous rows of the workspace (partition-major order measured about 10 %
   // slower on the long-context workload).
-  const uint32_t hkv_u = (uint32_t)(PR ? a.num_kv_heads / 2 : a.num_kv_heads);
-  const int g = (int)(wg % hkv_u);
+  const int wave_id = (int)(threadIdx.x / kWave);
+  const uint32_t hkv_u = (uint32_t)(PR ? a.num_kv_heads / 2 : a.num_kv_heads) / (WP ? NW : 1);
+  const int g = (int)(wg % hkv_u) * (WP ? NW : 1) + (WP ? wave_id : 0);
   int row, pz;
   if constexpr (WP) {
     const uint32_t parts_u = num_wgs / (hkv_u * grid_rows);
@@ -312,9 +314,12 @@ __device__ __forceinline__ void decode_wg(const RowsArgs& a, int block_shift, ui
   // fp8, 16 for fp8 kv-head pairs (the same 8 KB of K and V per tile).
   constexpr int TSH = F8 && !PR ? 5 : 4;
   constexpr int TP = 1 << TSH;
-  const int my_first = (lo >> TSH) + wave;  // this wave's tiles: my_first + NW * i, i < my_tiles
+  // this wave's tiles: my_first + TS * i, i < my_tiles -- dealt round-robin over the
+  // workgroup's waves, or (WP) all of the wave's own (kv head's) range
+  constexpr int TS = WP ? 1 : NW;
+  const int my_first = (lo >> TSH) + (WP ? 0 : wave);
   const int last = (hi - 1) >> TSH;
-  const int my_tiles = (lo < hi && last >= my_first) ? (last - my_first) / NW + 1 : 0;
+  const int my_tiles = (lo < hi && last >= my_first) ? (last - my_first) / TS + 1 : 0;
 
   // fp8 tiles: tile row r (0..31) holds its 16-byte chunk k in slot k ^ kswz(r) of
   // its 128-byte LDS row, which keeps both read kinds below free of bank conflicts.
@@ -350,7 +355,7 @@ __device__ __forceinline__ void decode_wg(const RowsArgs& a, int block_shift, ui
   auto load_ids = [&](int i0) {
     const int i = i0 + lane / IDS_PER_TILE;
     const int half = F8 && !PR ? (lane & 1) : 0;
-    int idx = (((my_first + NW * (i < my_tiles ? i : 0)) << TSH) + 16 * half) >> block_shift;
+    int idx = (((my_first + TS * (i < my_tiles ? i : 0)) << TSH) + 16 * half) >> block_shift;
     idx = idx < a.max_blocks ? idx : a.max_blocks - 1;
     const int id = table[idx];
     ids = id < 0 ? 0 : (id >= a.num_blocks ? (int)(a.num_blocks - 1) : id);
@@ -365,7 +370,7 @@ __device__ __forceinline__ void decode_wg(const RowsArgs& a, int block_shift, ui
   // (finite data, in the same block; their scores are masked), so every tile issues
   // exactly kTileLoads loads and a counted wait can tell tiles apart.
   auto fetch = [&](int i) {
-    const int t0 = (my_first + NW * i) << TSH;
+    const int t0 = (my_first + TS * i) << TSH;
     char* kl = sh.t.k[wave][i % NB];
     char* vl = sh.t.v[wave][i % NB];
     const int lim = n - 1 - t0;  // >= 0: every tile starts inside the sequence
@@ -467,7 +472,7 @@ __device__ __forceinline__ void decode_wg(const RowsArgs& a, int block_shift, ui
   // with tile i + NB, then S, softmax and PV from registers.  NB tiles per wave are
   // in flight while one is computed.
   auto step = [&](int i) {
-    const int t0 = (my_first + NW * i) << 4;
+    const int t0 = (my_first + TS * i) << 4;
     const char* kl = sh.t.k[wave][i % NB];
     const char* lb = sh.t.v[wave][i % NB];
     wait_tile(i);
@@ -553,7 +558,7 @@ __device__ __forceinline__ void decode_wg(const RowsArgs& a, int block_shift, ui
   // reduction index 8c + k is position pos(c, k) -- P^T's rows are already there:
   // lane (head, c) holds the two chains' positions 4c .. 4c + 3.
   auto step8 = [&](int i) {
-    const int t0 = (my_first + NW * i) << TSH;
+    const int t0 = (my_first + TS * i) << TSH;
     const uint32_t kl_a = lds_addr(sh.t.k[wave][i % NB]), lb_a = lds_addr(sh.t.v[wave][i % NB]);
     wait_tile(i);
     u32x4 k8[2][2];
@@ -773,6 +778,31 @@ constexpr int64_t kOneWaveItems = 8192;
 constexpr int kFp8Bufs = 2;
 constexpr int kFp8WholeWaves = 8;
 
+// Split calls with many (row, kv head, partition) items run one wave per item, the
+// waves of a workgroup on consecutive kv heads (or kv-head pairs) of the same row
+// and partition: 4 of them when the count divides, else 2 or 1.  The waves stream
+// the same blocks -- each slot's kv heads lie side by side -- at the same time on
+// one CU: on the long-context workload 5.59 TB/s with 4 heads per workgroup, 5.50
+// with 8, 5.27 with one (same box); a streaming probe of the access pattern alone
+// gives 7.0 TB/s with a block's heads in one workgroup, 6.6 with one head per
+// workgroup.
+inline int split_head_waves(int units) { return units % 4 == 0 ? 4 : units % 2 == 0 ? 2 : 1; }
+
+template <typename T, bool F8, bool PR>
+hipError_t launch_split_waves(const RowsArgs& a, int block_shift, uint32_t rows, uint64_t items, int units,
+                              hipStream_t stream) {
+  constexpr int bufs = F8 ? kFp8Bufs : kOneWaveBufs;
+  const int w = split_head_waves(units);
+  const dim3 grid((uint32_t)(items / (uint64_t)w)), block(64 * w);
+  if (w == 4)
+    hipLaunchKernelGGL((decode_mfma_kernel<T, 128, 4, true, bufs, F8, PR>), grid, block, 0, stream, a, block_shift, rows);
+  else if (w == 2)
+    hipLaunchKernelGGL((decode_mfma_kernel<T, 128, 2, true, bufs, F8, PR>), grid, block, 0, stream, a, block_shift, rows);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<T, 128, 1, true, bufs, F8, PR>), grid, block, 0, stream, a, block_shift, rows);
+  return hipGetLastError();
+}
+
 // `grid` is (rows, kv heads, partitions); the kernel takes it flattened.
 template <typename T, bool F8>
 hipError_t launch_decode_typed(const RowsArgs& a, int block_shift, int dk, int dv, dim3 grid, hipStream_t stream) {
@@ -780,19 +810,16 @@ hipError_t launch_decode_typed(const RowsArgs& a, int block_shift, int dk, int d
   const uint32_t rows = grid.x;
   const uint64_t n = (uint64_t)grid.x * grid.y * grid.z;
   if (n > 0xffffffffull) return hipErrorInvalidValue;
-  constexpr int one_bufs = F8 ? kFp8Bufs : kOneWaveBufs, part_bufs = F8 ? kFp8Bufs : kPartBufs,
-                whole_bufs = F8 ? kFp8Bufs : kWholeBufs;
+  constexpr int part_bufs = F8 ? kFp8Bufs : kPartBufs, whole_bufs = F8 ? kFp8Bufs : kWholeBufs;
   if constexpr (F8) {
     // split fp8 calls with an even number of kv heads and at most 8 q heads per kv
     // head: one workgroup per pair of kv heads (256-byte reads per slot)
     if (a.partition_size > 0 && a.num_kv_heads % 2 == 0 && 2 * a.group <= 16) {
       const uint64_t np = n / 2;
       if ((int64_t)np >= kOneWaveItems)
-        hipLaunchKernelGGL((decode_mfma_kernel<T, 128, 1, true, one_bufs, true, true>), dim3((uint32_t)np), dim3(64),
-                           0, stream, a, block_shift, rows);
-      else
-        hipLaunchKernelGGL((decode_mfma_kernel<T, 128, kPartWaves, false, part_bufs, true, true>),
-                           dim3((uint32_t)np), dim3(kPartWaves * 64), 0, stream, a, block_shift, rows);
+        return launch_split_waves<T, true, true>(a, block_shift, rows, np, a.num_kv_heads / 2, stream);
+      hipLaunchKernelGGL((decode_mfma_kernel<T, 128, kPartWaves, false, part_bufs, true, true>),
+                         dim3((uint32_t)np), dim3(kPartWaves * 64), 0, stream, a, block_shift, rows);
       return hipGetLastError();
     }
   }
@@ -801,9 +828,8 @@ hipError_t launch_decode_typed(const RowsArgs& a, int block_shift, int dk, int d
   // whether its batch holds prefill sequences.
   const bool varlen_rows = a.query_start_loc != nullptr && a.partition_size == 0 && !F8;
   if (a.partition_size > 0 && (int64_t)n >= kOneWaveItems)
-    hipLaunchKernelGGL((decode_mfma_kernel<T, 128, 1, true, one_bufs, F8>), dim3((uint32_t)n), dim3(64), 0, stream, a,
-                       block_shift, rows);
-  else if (a.partition_size > 0 || varlen_rows)
+    return launch_split_waves<T, F8, false>(a, block_shift, rows, n, a.num_kv_heads, stream);
+  if (a.partition_size > 0 || varlen_rows)
     hipLaunchKernelGGL((decode_mfma_kernel<T, 128, kPartWaves, false, part_bufs, F8>), dim3((uint32_t)n),
                        dim3(kPartWaves * 64), 0, stream, a, block_shift, rows);
   else
