@@ -227,6 +227,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
     base_b = (n + kPrefillKeys - 1) & ~(kPrefillKeys - 1);
   }
   const int gap_lo = n, gap_hi = len_b > 0 ? base_b : n;
+  // a sequence with no keys at all (an exhausted context chunk) loads no q: its rows
+  // only finish (zero output, or their state merged with an empty one)
+  const bool no_keys = n == 0 && len_b == 0;
   auto in_gap = [&](int j) {
     if constexpr (SEG2) return j >= gap_lo && j < gap_hi;
     return false;
@@ -293,7 +296,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (row_tok[rb] * a.num_heads + row_head[rb]) * DK;
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
-      if (row_ok[rb])
+      if (row_ok[rb] && !no_keys)
         qb[rb][kk] = *reinterpret_cast<const u32x4*>(qrow + 32 * kk + 8 * c);
       else
         qb[rb][kk] = u32x4{0u, 0u, 0u, 0u};
