@@ -761,10 +761,12 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
     if constexpr (MERGE) {
       // merge into the state held by out (float32) and lse: this call is the suffix.
       // The row's four lanes read its lse before one of them writes it (one wave).
+      // An empty suffix (no visible key) leaves out as it is (weights 1 and 0), so
+      // its rows touch only lse, which still turns +inf into -inf.
       float wp, ws, lse_m;
       bool keep;
       merge_state_weights(a.lse[li], lse_new, wp, ws, lse_m, keep);
-      if (!keep) {
+      if (!keep && lse_new != -INFINITY) {
 #pragma unroll
         for (int nd = 0; nd < ND; ++nd) {
           float* dst = static_cast<float*>(a.out) + obase + 16 * nd + 4 * c;
