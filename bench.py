@@ -193,20 +193,31 @@ def timed_loop(steps, pre, call, lead=False):
     """Runs pre(); call() per step.  Returns (ms per step, average and median event
     duration of call() in ms), with events recorded on the current stream.
 
-    By default ms per step is the host's wall clock.  With lead=True the loop is
-    queued behind eight 512 MiB device fills (4 GiB of writes, about 0.7 ms) so
-    that the host's launch overhead overlaps them: ms per step is then the device's
-    span from the first call's start event to the last call's end event, the rate
-    of back-to-back calls whose launches are not host-bound."""
+    By default ms per step is the host's wall clock and each call sits between its
+    own pair of events.  lead=True is for calls shorter than the host's launch path
+    (pre must do nothing): the calls are queued behind eight 512 MiB device fills
+    (4 GiB of writes, about 0.7 ms) so that the host's launch overhead overlaps
+    them, and one pair of events spans all of them back to back; every figure is
+    then that span divided by the number of calls, the rate of back-to-back calls
+    whose launches are not host-bound."""
     import torch
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    filler = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if lead else None
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     if lead:
+        filler = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
         for _ in range(8):
             filler.fill_(1)
+        s.record()
+        for _ in range(steps):
+            call()
+        e.record()
+        torch.cuda.synchronize()
+        per = s.elapsed_time(e) / steps
+        return per, per, per
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
     for s, e in evs:
         pre()
         s.record()
@@ -214,8 +225,6 @@ def timed_loop(steps, pre, call, lead=False):
         e.record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    if lead:
-        wall = evs[0][0].elapsed_time(evs[-1][1]) / steps
     durs = [s.elapsed_time(e) for s, e in evs]
     return wall, float(np.mean(durs)), float(np.median(durs))
 
