@@ -1,7 +1,7 @@
 """Benchmark of batched paged attention on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload all|decode|long|decode-fp8|long-fp8|varlen|mla|gather]
+                    [--workload all|decode|long|decode-fp8|long-fp8|varlen|mla|gather|tiles]
                     [--partition-size P] [--no-cpu-baseline] [--copy-calibration] [--sweep]
                     [--ceilings]
 
@@ -34,7 +34,8 @@ workload on the host cores (thread count and CPU model given).
 
 --workload X prints X's line alone (decode-fp8 / long-fp8 are the decode workloads
 over an fp8 (E4M3) cache with per-tensor k_scale / v_scale, one byte per K / V
-element; gather is the MLA latent-cache gather).  --copy-calibration appends, after
+element; gather is the MLA latent-cache gather; tiles is a diagnostic line, the prefill
+tile kernel on whole tiles).  --copy-calibration appends, after
 the timed region, three launches of a 1 GiB elementwise copy (torch.neg) that the
 counter runs use as the known-size reference.  --sweep adds, after the timed region,
 for the decode workloads each partition size in {0, 512, 1024}, the cost of device
@@ -73,7 +74,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="all",
-                    choices=["all", "decode", "long", "decode-fp8", "long-fp8", "varlen", "mla", "gather"])
+                    choices=["all", "decode", "long", "decode-fp8", "long-fp8", "varlen", "mla", "gather", "tiles"])
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
@@ -700,6 +701,52 @@ def as_line(entry, args, extra=None):
     return line
 
 
+def run_tiles(args):
+    """Diagnostic workload: the prefill tile kernel on whole tiles, no masking -- 8
+    sequences of 1024 queries over 5120 keys each, non-causal, H 128, Dqk 192 / Dv
+    128, bf16 (the MLA workload's head shape at its first chunk's size), through one
+    pa_varlen call.  Inputs are drawn on the GPU from a seeded generator; block ids
+    are a seeded permutation.  It measures the kernel's own rate, not a workload of
+    the metric, so it carries no CPU baseline."""
+    import torch
+
+    from paged_kv_attention_table_amd import pa_varlen
+
+    S, qlen, klen, H, dk, dv, b = 8, 1024, 5120, 128, 192, 128, 16
+    g = torch.Generator(device="cuda").manual_seed(2026)
+    nb = S * klen // b + 1
+    kp = torch.randn((nb, b, H, dk), device="cuda", generator=g).to(torch.bfloat16)
+    vp = torch.randn((nb, b, H, dv), device="cuda", generator=g).to(torch.bfloat16)
+    q = torch.randn((S * qlen, H, dk), device="cuda", generator=g).to(torch.bfloat16)
+    tables = torch.randperm(nb - 1, device="cuda", generator=g)[: S * klen // b].view(S, klen // b)
+    tables = tables.to(torch.int32).contiguous()
+    lens = torch.full((S,), klen, dtype=torch.int32, device="cuda")
+    qsl = torch.arange(0, S * qlen + 1, qlen, dtype=torch.int32, device="cuda")
+    pos = torch.zeros(S * qlen, dtype=torch.int32, device="cuda")
+    out = torch.empty((S * qlen, H, dv), device="cuda")
+    lse = torch.empty((H, S * qlen), device="cuda")
+    flops = S * H * qlen * klen * 2 * (dk + dv)
+
+    def call():
+        pa_varlen(kp, vp, q, out, qsl, lens, pos, tables, qlen, dk ** -0.5, causal=False, lse=lse)
+
+    for _ in range(args.warmup):
+        call()
+    ms, avg_ms, med_ms = timed_loop(args.steps, lambda: None, call)
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+    line = {"metric": "prefill tile kernel TFLOP/s on whole tiles (diagnostic)", "value": round(flops / (ms * 1e-3) / 1e12, 2),
+            "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "prefill-whole-tiles", "num_seqs": S, "queries": qlen, "keys": klen, "num_heads": H,
+                       "num_kv_heads": H, "head_dim_k": dk, "head_dim_v": dv, "causal": False,
+                       "flops_per_step": flops, "step": "pa_varlen"},
+            "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "kernel": "prefill_kernel<BF16, 192, 128, false, false>", "avg_ms": round(avg_ms, 5),
+                         "median_ms": round(med_ms, 5)}}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -711,6 +758,8 @@ def main():
     budget2 = 0.0 if args.no_cpu_baseline else args.secondary_cpu_budget_s
     if args.workload == "gather":
         return run_gather(args)
+    if args.workload == "tiles":
+        return run_tiles(args)
     if args.workload in ("varlen", "mla"):
         line = as_line(prefill_entry(args, args.workload, budget), args)
     elif args.workload != "all":
