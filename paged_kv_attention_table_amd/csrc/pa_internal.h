@@ -158,5 +158,8 @@ hipError_t launch_write(const WriteArgs& a, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 bool rows_supported(int dtype, int dk, int dv, int group);
+// Compute units of the current device (queried once per device), or 0 if the query
+// fails.
+int device_cu_count();
 
 }  // namespace pa

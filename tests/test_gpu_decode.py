@@ -192,3 +192,41 @@ def test_write_kv_status_rejects_bad_slot():
         torch.cuda.synchronize()
         assert int(st.item()) == 1
         assert bits_equal(host(d.k_pool), before_k) and bits_equal(host(d.v_pool), before_v)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "fp8_e4m3"])
+def test_decode_paired_units(orc, dtype):
+    """Unsplit calls of at least two rounds of the chip's CUs run two (row, kv head)
+    units per workgroup (the longest with the shortest).  515 sequences x 1 kv head
+    (an odd count: the middle workgroup answers one unit) against the oracle, and
+    every sampled sequence bit for bit against the same sequence in a call of 8
+    sequences, which runs one unit per workgroup."""
+    from paged_kv_attention_table_amd import workloads as W
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    S = max(515, 2 * cus + 3) | 1
+    rng = np.random.default_rng(4242)
+    lens = rng.integers(1, 300, size=S, endpoint=True)
+    w = W.make_decode("paired-units", 4242, seq_lens=lens, dtype="f16", num_heads=4, num_kv_heads=1, head_dim=128)
+    if dtype == "fp8_e4m3":
+        w = W.to_fp8(w)
+    d = OnDevice(w)
+    kp, vp = d.host_pools_after_write(orc)
+    out = torch.full((S, w.num_heads, w.dv), float("nan"), device="cuda")
+    status = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    pa_decode(d.k_pool, d.v_pool, d.q, out, d.tables, d.seq_lens, w.scale, k_scale=w.k_scale, v_scale=w.v_scale,
+              status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    full = host(out)
+    st, ref, _ = orc.decode(kp, vp, w.dtype, w.q, w.query_dtype, w.block_tables, w.seq_lens, w.scale,
+                            k_scale=w.k_scale, v_scale=w.v_scale, threads=threads())
+    assert st == 0
+    assert_close(full, ref, TOL["f16"], f"{dtype} paired out")
+    for s0 in (0, 8 * (S // 16), S - 8):
+        sl = slice(s0, s0 + 8)
+        o = torch.full((8, w.num_heads, w.dv), float("nan"), device="cuda")
+        pa_decode(d.k_pool, d.v_pool, d.q[sl].contiguous(), o, d.tables[sl].contiguous(), d.seq_lens[sl].contiguous(),
+                  w.scale, k_scale=w.k_scale, v_scale=w.v_scale)
+        torch.cuda.synchronize()
+        assert bits_equal(host(o), full[sl]), f"sequences {s0}..{s0 + 7}"
