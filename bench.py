@@ -1,7 +1,8 @@
 """Benchmark of batched paged attention on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload all|decode|long|decode-fp8|long-fp8|varlen|mla|gather|tiles]
+                    [--workload all|decode|long|decode-fp8|long-fp8|varlen|mla|varlen-fp8|mla-fp8|
+                                gather|tiles]
                     [--partition-size P] [--no-cpu-baseline] [--copy-calibration] [--sweep]
                     [--ceilings]
 
@@ -32,9 +33,9 @@ reported only while the kernels' source hash still matches the one recorded ther
 `cpu_baseline` times the CPU oracle, unchanged, on a bounded sample of the same
 workload on the host cores (thread count and CPU model given).
 
---workload X prints X's line alone (decode-fp8 / long-fp8 are the decode workloads
-over an fp8 (E4M3) cache with per-tensor k_scale / v_scale, one byte per K / V
-element; gather is the MLA latent-cache gather; tiles is a diagnostic line, the prefill
+--workload X prints X's line alone (decode-fp8 / long-fp8 / varlen-fp8 / mla-fp8
+are those workloads over an fp8 (E4M3) cache with per-tensor k_scale / v_scale, one
+byte per K / V element, the queries in the workload's 16-bit type; gather is the MLA latent-cache gather; tiles is a diagnostic line, the prefill
 tile kernel on whole tiles).  --copy-calibration appends, after
 the timed region, three launches of a 1 GiB elementwise copy (torch.neg) that the
 counter runs use as the known-size reference.  --sweep adds, after the timed region,
@@ -74,7 +75,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="all",
-                    choices=["all", "decode", "long", "decode-fp8", "long-fp8", "varlen", "mla", "gather", "tiles"])
+                    choices=["all", "decode", "long", "decode-fp8", "long-fp8", "varlen", "mla", "varlen-fp8",
+                             "mla-fp8", "gather", "tiles"])
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
@@ -86,7 +88,7 @@ def parse():
 
 
 CSRC = os.path.join(ROOT, "paged_kv_attention_table_amd", "csrc")
-KERNEL_SOURCES = {"decode_mfma_kernel": ("pa_decode.h", "pa_common.h", "pa_misc.hip"),
+KERNEL_SOURCES = {"decode_mfma_kernel": ("pa_decode.h", "pa_prefill.h", "pa_common.h", "pa_misc.hip"),
                   "prefill_kernel": ("pa_prefill.h", "pa_common.h"),
                   "pa_varlen_call": ("pa_prefill.h", "pa_decode.h", "pa_varlen_fused.h", "pa_rows.h", "pa_common.h",
                                      "pa_misc.hip", "pa_api.hip"),
@@ -371,8 +373,9 @@ def cpu_baseline_varlen(w, budget_s):
     def run(m):
         mask = np.zeros((T, H), dtype=np.uint8)
         mask[:m] = 1
-        st, _, _ = orc.varlen(kp, vp, w.dtype, w.q, w.dtype, w.query_start_loc, w.seq_lens, w.positions,
-                              w.block_tables, w.scale, True, w.sliding_window, row_mask=mask, threads=host_cores())
+        st, _, _ = orc.varlen(kp, vp, w.dtype, w.q, w.query_dtype, w.query_start_loc, w.seq_lens, w.positions,
+                              w.block_tables, w.scale, True, w.sliding_window, row_mask=mask, threads=host_cores(),
+                              k_scale=w.k_scale, v_scale=w.v_scale)
         assert st == 0
 
     return _timed_rows(run, per_row, T, budget_s, "oracle varlen call, causal, window")
@@ -406,11 +409,12 @@ def cpu_baseline_chunked(cp, budget_s):
                 tab = np.ascontiguousarray(cp.ctx_tables[:, c * per:(c + 1) * per])
                 if tab.shape[1] == 0:
                     continue
-                st, o, l = orc.varlen(kp, vp, cp.dtype, cp.q, cp.dtype, qsl, lens, None, tab, cp.scale, False, 0,
-                                      row_mask=mask, threads=host_cores())
+                st, o, l = orc.varlen(kp, vp, cp.dtype, cp.q, cp.query_dtype, qsl, lens, None, tab, cp.scale, False,
+                                      0, row_mask=mask, threads=host_cores(), k_scale=cp.k_scale, v_scale=cp.v_scale)
             else:
-                st, o, l = orc.varlen(kp, vp, cp.dtype, cp.q, cp.dtype, qsl, cp.new_lens.astype(np.int32), positions,
-                                      cp.new_tables, cp.scale, True, 0, row_mask=mask, threads=host_cores())
+                st, o, l = orc.varlen(kp, vp, cp.dtype, cp.q, cp.query_dtype, qsl, cp.new_lens.astype(np.int32),
+                                      positions, cp.new_tables, cp.scale, True, 0, row_mask=mask,
+                                      threads=host_cores(), k_scale=cp.k_scale, v_scale=cp.v_scale)
             assert st == 0
             o, l = o[:m].astype(np.float32), np.ascontiguousarray(l[:, :m]).astype(np.float32)
             state = (o, l) if state is None else orc.merge_states(state[0], state[1], o, l, "f32")[:2]
@@ -441,17 +445,21 @@ def cpu_baseline_gather(g, budget_s):
 
 def prefill_entry(args, kind, cpu_budget_s):
     """The mixed varlen call (4 prefill chunks + 12 decode tokens) or the MLA-style
-    chunked prefill: one entry in TFLOP/s of visible (query, key) pairs."""
+    chunked prefill, over a 16-bit cache or (kind ending in -fp8) an fp8 one: one entry
+    in TFLOP/s of visible (query, key) pairs."""
     import torch
 
     from paged_kv_attention_table_amd import pa_varlen, pa_write_kv
     from paged_kv_attention_table_amd import workloads as W
     from paged_kv_attention_table_amd.chunked import ChunkedPrefillPlan
 
-    if kind == "varlen":
+    fp8 = kind.endswith("-fp8")
+    if kind.removesuffix("-fp8") == "varlen":
         w = W.mixed_varlen()
+        if fp8:
+            w = W.to_fp8(w)
         kp, vp = dev(w.k_pool, w.dtype), dev(w.v_pool, w.dtype)
-        q = dev(w.q, w.dtype)
+        q = dev(w.q, w.query_dtype)
         qsl, lens, pos, tables = dev(w.query_start_loc), dev(w.seq_lens), dev(w.positions), dev(w.block_tables)
         k_new, v_new, slots = dev(w.k_new, w.dtype), dev(w.v_new, w.dtype), dev(w.slot_mapping)
         out = torch.empty((w.num_tokens, w.num_heads, w.dv), device="cuda")
@@ -469,22 +477,26 @@ def prefill_entry(args, kind, cpu_budget_s):
         def attn(status=None):
             pa_varlen(kp, vp, q, out, qsl, lens, pos, tables, max_q, w.scale, causal=True,
                       sliding_window=w.sliding_window, lse=lse, partition_size=P, max_logits=ws[0],
-                      exp_sums=ws[1], tmp_out=ws[2], status=status)
+                      exp_sums=ws[1], tmp_out=ws[2], status=status, k_scale=w.k_scale, v_scale=w.v_scale)
 
         def write():
             pa_write_kv(kp, vp, k_new, v_new, slots)
 
-        kernel_label = ("pa_varlen call (" + ("prefill tile kernel + split single-token rows + partition reduce)"
-                                              if P else "fused kernel: prefill tiles and single-token decode rows)"))
-        name, dtype = w.name, w.dtype
-        cfg = {"workload": name, "prefill_seqs": 4, "decode_seqs": 12, "num_tokens": w.num_tokens,
+        if P:
+            kernel_label = "pa_varlen call (prefill tile kernel + split single-token rows + partition reduce)"
+        else:
+            kernel_label = "pa_varlen call (fused kernel: prefill tiles and single-token decode rows)"
+        name, dtype = w.name, w.query_dtype
+        cfg = {"workload": name, "kv_dtype": w.dtype, "prefill_seqs": 4, "decode_seqs": 12, "num_tokens": w.num_tokens,
                "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.dk,
                "sliding_window": w.sliding_window, "single_token_partition_size": P,
                "step": "pa_write_kv + pa_varlen"}
     else:
         cp = W.mla_chunked()
+        if fp8:
+            cp = W.chunked_to_fp8(cp)
         kp, vp = dev(cp.k_pool, cp.dtype), dev(cp.v_pool, cp.dtype)
-        q = dev(cp.q, cp.dtype)
+        q = dev(cp.q, cp.query_dtype)
         k_new, v_new, slots = dev(cp.k_new, cp.dtype), dev(cp.v_new, cp.dtype), dev(cp.slot_mapping)
         plan = ChunkedPrefillPlan(ctx_lens=cp.ctx_lens, new_lens=cp.new_lens, ctx_tables=cp.ctx_tables,
                                   new_tables=cp.new_tables, chunk=cp.chunk, block_size=cp.block_size,
@@ -494,15 +506,15 @@ def prefill_entry(args, kind, cpu_budget_s):
         flops = chunked_flops(cp)
 
         def attn():
-            plan.run(kp, vp, q, out, lse)
+            plan.run(kp, vp, q, out, lse, k_scale=cp.k_scale, v_scale=cp.v_scale)
 
         def write():
             pa_write_kv(kp, vp, k_new, v_new, slots)
 
         kernel_label = ("chunked prefill (pa_varlen_ctx_new per context chunk, merging into the state after the "
                         "first; each request's causal new tokens in its last chunk's call)")
-        name, dtype = cp.name, cp.dtype
-        cfg = {"workload": name, "requests": int(cp.ctx_lens.size), "num_tokens": cp.num_tokens,
+        name, dtype = cp.name, cp.query_dtype
+        cfg = {"workload": name, "kv_dtype": cp.dtype, "requests": int(cp.ctx_lens.size), "num_tokens": cp.num_tokens,
                "num_heads": cp.num_heads, "head_dim_k": cp.dk, "head_dim_v": cp.dv, "chunk": cp.chunk,
                "step": "pa_write_kv + chunked prefill (pa_varlen_ctx_new per context chunk)"}
     def step():
@@ -524,21 +536,21 @@ def prefill_entry(args, kind, cpu_budget_s):
                           "median_ms": round(med_ms, 5), "achieved_flushed": round(cold, 2),
                           "frac_flushed": round(cold / MFMA_BF16_PEAK_TFLOPS, 4),
                           "median_ms_flushed": round(cold_ms, 5)}}
-    if args.sweep and kind == "varlen":
+    if args.sweep and kind.removesuffix("-fp8") == "varlen":
         # context, after the timed region: the cost of device validation
         status = torch.zeros(1, dtype=torch.int32, device="cuda")
         med_status = flushed_median_ms(lambda: attn(status))
         if int(status.item()) != 0:
             raise RuntimeError(f"device validation reported status {int(status.item())}")
         entry["sweep"] = {"validation_ms": round(med_status - cold_ms, 5)}
-    t = traffic_lookup("pa_varlen_call", name, P if kind == "varlen" else 0)
+    t = traffic_lookup("pa_varlen_call", name, P if kind.removesuffix("-fp8") == "varlen" else 0)
     if t is not None:
         entry["roofline"]["traffic"] = t[0] + t[1]
         entry["roofline"]["traffic_read"], entry["roofline"]["traffic_write"] = t
     if args.copy_calibration:
         copy_calibration()
     if cpu_budget_s > 0:
-        entry["cpu_baseline"] = (cpu_baseline_varlen(w, cpu_budget_s) if kind == "varlen"
+        entry["cpu_baseline"] = (cpu_baseline_varlen(w, cpu_budget_s) if kind.removesuffix("-fp8") == "varlen"
                                  else cpu_baseline_chunked(cp, cpu_budget_s))
     return entry
 
@@ -760,7 +772,7 @@ def main():
         return run_gather(args)
     if args.workload == "tiles":
         return run_tiles(args)
-    if args.workload in ("varlen", "mla"):
+    if args.workload in ("varlen", "mla", "varlen-fp8", "mla-fp8"):
         line = as_line(prefill_entry(args, args.workload, budget), args)
     elif args.workload != "all":
         line = as_line(decode_entry(args, args.workload, budget, args.partition_size), args)

@@ -194,16 +194,23 @@ int pa_decode_noalloc(const pa_kv_pool* pool, const void* q, int32_t q_dtype, vo
  * partition_size == 0: no split, workspaces may be NULL.  Ignored for shapes whose
  * single-token rows run on the tiled kernel (the row kernels do not take them).
  * Supported: (head_dim_k, head_dim_v) in {(32,32), (64,64), (128,128), (256,256),
- * (192,128)}; num_heads / num_kv_heads <= 16; any block_size.  PA_FP8_E4M3 pools: as
- * for pa_decode, and only calls whose sequences hold at most one query token each
- * (max_query_len <= 1).
+ * (192,128)}; num_heads / num_kv_heads <= 16; any block_size.  Beyond that, the
+ * tiled kernel's shapes (below) with num_heads / num_kv_heads up to 128.
+ * PA_FP8_E4M3 pools: q_dtype PA_F16 or PA_BF16, block_size a power of two >= 16,
+ * num_blocks * block_size < 2^32, and (head_dim_k, head_dim_v) = (128,128) with
+ * num_heads / num_kv_heads <= 16 (single-token sequences on the fp8 decode kernel,
+ * longer ones on the tiled kernel), or any call on the tiled kernel's fp8 shapes:
+ * (128,128) or (192,128), num_heads / num_kv_heads <= 128.
  * Which kernel runs: sequences of two or more query tokens run on the tiled MFMA
- * prefill kernel when the pool is F16 or BF16, (head_dim_k, head_dim_v) is (64,64),
- * (128,128) or (192,128), block_size is a power of two >= 16 and num_blocks *
- * block_size < 2^32; single-token sequences then run on the decode kernels.  Any
- * other supported shape (F32 pools, head dims 32 or 256, other block sizes) runs
- * every token on the per-row kernel, one workgroup per (token, kv head): the same
- * results, at a small fraction of the tiled kernel's rate for long prefills.
+ * prefill kernel when the pool is F16 or BF16 with (head_dim_k, head_dim_v) in
+ * {(64,64), (128,128), (192,128)}, or FP8_E4M3 with (128,128) or (192,128), and
+ * block_size is a power of two >= 16 and num_blocks * block_size < 2^32 (an fp8
+ * pool's K is widened exactly to q_dtype, V to f16, as the tiles are staged);
+ * single-token sequences then run on the decode kernels, or on the tiled kernel too
+ * where the decode kernels do not take the shape.  Any other supported shape (F32
+ * pools, head dims 32 or 256, other block sizes) runs every token on the per-row
+ * kernel, one workgroup per (token, kv head): the same results, at a small fraction
+ * of the tiled kernel's rate for long prefills.
  * ALiBi and merging: the bias is counted from each row's own end - 1, so a row's
  * lse carries an offset of slopes[h] * (end - 1) from the page's form.  States of
  * calls that see a row with different ends (for example context chunks read as
@@ -245,14 +252,16 @@ int pa_varlen_merge(const pa_kv_pool* pool, const void* q, int32_t q_dtype, floa
  * required) receive the result; with merge != 0 they hold a state and the result is
  * merged into it as the suffix, by pa_merge_states' rules.  Equal to merging the
  * context segment's state and then the new tokens' (up to rounding), without the
- * second pass over the state.  Pool element type = q_dtype; no window, ALiBi or
- * split-KV; sinks as for pa_varlen.  Device checks (with status): query_start_loc
+ * second pass over the state.  Pool element type = q_dtype, or PA_FP8_E4M3 with
+ * q_dtype PA_F16 or PA_BF16 (scales as everywhere); no window, ALiBi or split-KV;
+ * sinks as for pa_varlen.  Device checks (with status): query_start_loc
  * as for pa_varlen; ctx_lens and new_lens >= 0 with their first ceil(len /
  * block_size) ids in [0, num_blocks) and at most ctx_max_blocks / new_max_blocks of
  * them; every new_position in [0, new_lens[s]) where new_lens[s] > 0.  Supported:
- * the shapes pa_varlen runs on its tiled kernel (F16 / BF16, (head_dim_k,
- * head_dim_v) in {(64,64), (128,128), (192,128)}, power-of-two block_size >= 16,
- * num_blocks * block_size < 2^32); every sequence runs on the tiled kernel. */
+ * the shapes pa_varlen runs on its tiled kernel (F16 / BF16 with (head_dim_k,
+ * head_dim_v) in {(64,64), (128,128), (192,128)}, FP8_E4M3 with (128,128) or
+ * (192,128); power-of-two block_size >= 16, num_blocks * block_size < 2^32,
+ * num_heads / num_kv_heads <= 128); every sequence runs on the tiled kernel. */
 int pa_varlen_ctx_new(const pa_kv_pool* pool, const void* q, int32_t q_dtype, float* out, float* lse, int32_t merge,
                       const int32_t* query_start_loc, const int32_t* ctx_lens, const int32_t* ctx_tables,
                       int32_t ctx_max_blocks, const int32_t* new_lens, const int32_t* new_positions,

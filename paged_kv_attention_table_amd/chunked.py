@@ -63,14 +63,16 @@ class ChunkedPrefillPlan:
         ).to(device)
         self.state_lse = torch.empty((num_heads, self.T), dtype=torch.float32, device=device)
 
-    def run(self, k_pool, v_pool, q, out, out_lse=None, stream=None):
+    def run(self, k_pool, v_pool, q, out, out_lse=None, stream=None, k_scale=1.0, v_scale=1.0):
         """out [T, H, Dv] (float32) <- attention of q over context chunks + new tokens;
-        out_lse [H, T] (optional) <- its lse."""
+        out_lse [H, T] (optional) <- its lse.  k_scale / v_scale: the pools' per-tensor
+        scales (fp8 pools)."""
         lse = self.state_lse if out_lse is None else out_lse
         if not self.chunks:
             pa_varlen(k_pool, v_pool, q, out, self.qsl, self.new_lens, self.positions, self.new_tables, self.max_q,
-                      self.scale, causal=True, lse=lse, stream=stream)
+                      self.scale, causal=True, lse=lse, stream=stream, k_scale=k_scale, v_scale=v_scale)
             return
         for c, (lens, tab, joins) in enumerate(self.chunks):
             pa_varlen_ctx_new(k_pool, v_pool, q, out, lse, self.qsl, lens, tab, joins, self.positions,
-                              self.new_tables, self.max_q, self.scale, merge=c > 0, stream=stream)
+                              self.new_tables, self.max_q, self.scale, merge=c > 0, stream=stream, k_scale=k_scale,
+                              v_scale=v_scale)

@@ -20,19 +20,37 @@ hipError_t launch_rows(const RowsArgs& a, int dtype, int dk, int dv, dim3 grid, 
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int dk, int dv, dim3 grid, hipStream_t stream);
 hipError_t launch_prefill_f16(const PrefillArgs& a, int dk, int dv, dim3 grid, hipStream_t stream);
+hipError_t launch_prefill_fp8_bf16(const PrefillArgs& a, int dk, int dv, dim3 grid, hipStream_t stream);
+hipError_t launch_prefill_fp8_f16(const PrefillArgs& a, int dk, int dv, dim3 grid, hipStream_t stream);
 
-hipError_t launch_prefill(const PrefillArgs& a, int dtype, int dk, int dv, dim3 grid, hipStream_t stream) {
-  if (dtype == PA_BF16) return launch_prefill_bf16(a, dk, dv, grid, stream);
-  if (dtype == PA_F16) return launch_prefill_f16(a, dk, dv, grid, stream);
+// Tile kernel launch for a pool of kv_dtype and queries of q_dtype.
+hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, int q_dtype, int dk, int dv, dim3 grid,
+                          hipStream_t stream) {
+  if (kv_dtype == PA_FP8_E4M3) {
+    if (q_dtype == PA_BF16) return launch_prefill_fp8_bf16(a, dk, dv, grid, stream);
+    if (q_dtype == PA_F16) return launch_prefill_fp8_f16(a, dk, dv, grid, stream);
+    return hipErrorInvalidValue;
+  }
+  if (q_dtype != kv_dtype) return hipErrorInvalidValue;
+  if (kv_dtype == PA_BF16) return launch_prefill_bf16(a, dk, dv, grid, stream);
+  if (kv_dtype == PA_F16) return launch_prefill_f16(a, dk, dv, grid, stream);
   return hipErrorInvalidValue;
 }
 
-// The tiled prefill kernel: f16 / bf16, these head dims, a power-of-two block size
-// of at least 16 (a 32-key tile then spans at most two blocks, one per half), and
-// a pool of fewer than 2^32 rows (the kernel forms row indices in 32 bits).
-bool prefill_supported(int dtype, int dk, int dv, int group, int block_size, int64_t num_blocks) {
-  if (dtype != PA_BF16 && dtype != PA_F16) return false;
-  const bool dims = (dk == 128 && dv == 128) || (dk == 192 && dv == 128) || (dk == 64 && dv == 64);
+// The tiled prefill kernel: f16 / bf16 pools with queries of the same type, or fp8
+// pools with f16 / bf16 queries; these head dims (fp8: 128 / 128 and 192 / 128), a
+// power-of-two block size of at least 16 (a 32-key tile then spans at most two
+// blocks, one per half), and a pool of fewer than 2^32 rows (the kernel forms row
+// indices in 32 bits).
+bool prefill_supported(int kv_dtype, int q_dtype, int dk, int dv, int group, int block_size, int64_t num_blocks) {
+  bool dims;
+  if (kv_dtype == PA_FP8_E4M3) {
+    if (q_dtype != PA_BF16 && q_dtype != PA_F16) return false;
+    dims = (dk == 128 || dk == 192) && dv == 128;
+  } else {
+    if ((kv_dtype != PA_BF16 && kv_dtype != PA_F16) || q_dtype != kv_dtype) return false;
+    dims = (dk == 128 && dv == 128) || (dk == 192 && dv == 128) || (dk == 64 && dv == 64);
+  }
   const bool pow2 = block_size >= 16 && (block_size & (block_size - 1)) == 0;
   const bool rows32 = num_blocks * (int64_t)block_size <= 0xffffffffLL;
   return dims && pow2 && rows32 && group >= 1 && group <= kPrefillRows;
@@ -42,6 +60,22 @@ hipError_t launch_varlen_fused_f16(const PrefillArgs& p, const RowsArgs& r, int 
                                   hipStream_t stream);
 hipError_t launch_varlen_fused_bf16(const PrefillArgs& p, const RowsArgs& r, int block_shift, uint32_t prefill_wgs,
                                    hipStream_t stream);
+hipError_t launch_varlen_fused_fp8_f16(const PrefillArgs& p, const RowsArgs& r, int block_shift,
+                                      uint32_t prefill_wgs, hipStream_t stream);
+hipError_t launch_varlen_fused_fp8_bf16(const PrefillArgs& p, const RowsArgs& r, int block_shift,
+                                       uint32_t prefill_wgs, hipStream_t stream);
+
+// The fused varlen kernel (tiles and single-token rows in one launch) for a pool of
+// kv_dtype and queries of q_dtype.
+hipError_t launch_varlen_fused(const PrefillArgs& p, const RowsArgs& r, int kv_dtype, int q_dtype, int block_shift,
+                               uint32_t prefill_wgs, hipStream_t stream) {
+  const bool bf16 = q_dtype == PA_BF16;
+  if (kv_dtype == PA_FP8_E4M3)
+    return bf16 ? launch_varlen_fused_fp8_bf16(p, r, block_shift, prefill_wgs, stream)
+                : launch_varlen_fused_fp8_f16(p, r, block_shift, prefill_wgs, stream);
+  return bf16 ? launch_varlen_fused_bf16(p, r, block_shift, prefill_wgs, stream)
+              : launch_varlen_fused_f16(p, r, block_shift, prefill_wgs, stream);
+}
 
 hipError_t launch_decode_bf16(const RowsArgs& a, int block_shift, int dk, int dv, dim3 grid, hipStream_t stream);
 hipError_t launch_decode_f16(const RowsArgs& a, int block_shift, int dk, int dv, dim3 grid, hipStream_t stream);
@@ -312,16 +346,17 @@ static int varlen_impl(const pa_kv_pool* pool, const void* q, int32_t q_dtype, v
   if (!query_type_ok(pool, q_dtype)) return PA_EUNSUPPORTED;
   if (out_dtype != PA_F32 && out_dtype != q_dtype) return PA_EUNSUPPORTED;
   const int group = num_heads / pool->num_kv_heads;
-  if (pool->dtype == PA_FP8_E4M3) {
-    // fp8 pools: one query token per sequence, through the MFMA decode kernel
-    if (max_query_len > 1 ||
-        !decode_mfma_supported(q_dtype, pool->head_dim_k, pool->head_dim_v, group, pool->block_size))
-      return PA_EUNSUPPORTED;
-  } else if (!rows_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group) &&
-             !prefill_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group, pool->block_size,
-                                pool->num_blocks)) {
-    return PA_EUNSUPPORTED;
-  }
+  const bool fp8 = pool->dtype == PA_FP8_E4M3;
+  // The row kernels: every shape for 16-bit pools' single tokens and longer queries;
+  // for fp8 pools the MFMA decode kernel, single tokens only.  The tile kernel:
+  // queries of several tokens (and single tokens the row kernels cannot take).
+  const bool rows_ok = fp8 ? decode_mfma_supported(q_dtype, pool->head_dim_k, pool->head_dim_v, group,
+                                                   pool->block_size)
+                           : rows_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group);
+  const bool tiles_ok = prefill_supported(pool->dtype, q_dtype, pool->head_dim_k, pool->head_dim_v, group,
+                                          pool->block_size, pool->num_blocks);
+  if (!rows_ok && !tiles_ok) return PA_EUNSUPPORTED;
+  if (fp8 && max_query_len > 1 && !tiles_ok) return PA_EUNSUPPORTED;
   float scale_log2;
   if (!folded_scale(pool, scale, scale_log2)) return PA_EINVAL;
   if (num_tokens > 0x7fffffffLL || num_seqs > 65535) return PA_EUNSUPPORTED;
@@ -388,8 +423,7 @@ static int varlen_impl(const pa_kv_pool* pool, const void* q, int32_t q_dtype, v
   // Sequences of exactly one query token can run split-KV: partitions on the row
   // kernels (one row per sequence), then the log-sum-exp reduce, which writes their
   // outputs and lse.
-  const bool fp8 = pool->dtype == PA_FP8_E4M3;
-  const bool rows_take_singles = fp8 || rows_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group);
+  const bool rows_take_singles = rows_ok;
   const bool split = partition_size > 0 && rows_take_singles;
   auto split_singles = [&]() -> int {
     RowsArgs b = a;
@@ -425,7 +459,7 @@ static int varlen_impl(const pa_kv_pool* pool, const void* q, int32_t q_dtype, v
     return from_hip(launch_reduce(r, s));
   };
 
-  if (!prefill_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group, pool->block_size, pool->num_blocks) || max_query_len <= 1) {
+  if (!tiles_ok || (max_query_len <= 1 && rows_ok)) {
     // every token through the per-row kernel (single-token sequences split, if asked)
     if (split && max_query_len <= 1) return split_singles();
     a.single_token_seqs = 0;
@@ -470,17 +504,17 @@ static int varlen_impl(const pa_kv_pool* pool, const void* q, int32_t q_dtype, v
   const int64_t groups8 = ((int64_t)num_seqs * pool->num_kv_heads + 7) / 8 * 8;
   const int64_t wgs = groups8 * p.tiles_per_seq;
   if (wgs > 0x7fffffffLL) return PA_EUNSUPPORTED;
+  if (wgs == 0) return PA_OK;
   // Single-token sequences on the MFMA decode kernel's shapes share the tile launch
   // (the fused kernel); otherwise they follow it on a launch of their own.
   const bool fuse = rows_take_singles && !split &&
-                    decode_mfma_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group, pool->block_size);
+                    decode_mfma_supported(q_dtype, pool->head_dim_k, pool->head_dim_v, group, pool->block_size);
   if (fuse) {
     a.single_token_seqs = 1;
     const int shift = pow2_shift(pool->block_size);
-    return from_hip(pool->dtype == PA_BF16 ? launch_varlen_fused_bf16(p, a, shift, (uint32_t)wgs, s)
-                                           : launch_varlen_fused_f16(p, a, shift, (uint32_t)wgs, s));
+    return from_hip(launch_varlen_fused(p, a, pool->dtype, q_dtype, shift, (uint32_t)wgs, s));
   }
-  st = from_hip(launch_prefill(p, pool->dtype, pool->head_dim_k, pool->head_dim_v, dim3((unsigned)wgs), s));
+  st = from_hip(launch_prefill(p, pool->dtype, q_dtype, pool->head_dim_k, pool->head_dim_v, dim3((unsigned)wgs), s));
   if (st != PA_OK || !rows_take_singles) return st;
   if (split) return split_singles();
   a.single_token_seqs = 1;
@@ -526,9 +560,10 @@ int pa_varlen_ctx_new(const pa_kv_pool* pool, const void* q, int32_t q_dtype, fl
   if (num_tokens > 0 && (q == nullptr || out == nullptr || lse == nullptr || new_positions == nullptr || num_seqs == 0))
     return PA_EINVAL;
   if (num_heads % pool->num_kv_heads != 0) return PA_ESHAPE;
-  if (q_dtype != pool->dtype) return PA_EUNSUPPORTED;
+  if (!query_type_ok(pool, q_dtype)) return PA_EUNSUPPORTED;
   const int group = num_heads / pool->num_kv_heads;
-  if (!prefill_supported(pool->dtype, pool->head_dim_k, pool->head_dim_v, group, pool->block_size, pool->num_blocks))
+  if (!prefill_supported(pool->dtype, q_dtype, pool->head_dim_k, pool->head_dim_v, group, pool->block_size,
+                         pool->num_blocks))
     return PA_EUNSUPPORTED;
   float scale_log2;
   if (!folded_scale(pool, scale, scale_log2)) return PA_EINVAL;
@@ -600,7 +635,7 @@ int pa_varlen_ctx_new(const pa_kv_pool* pool, const void* q, int32_t q_dtype, fl
   const int64_t wgs = groups8 * p.tiles_per_seq;
   if (wgs > 0x7fffffffLL) return PA_EUNSUPPORTED;
   if (wgs == 0) return PA_OK;
-  return from_hip(launch_prefill(p, pool->dtype, pool->head_dim_k, pool->head_dim_v, dim3((unsigned)wgs), s));
+  return from_hip(launch_prefill(p, pool->dtype, q_dtype, pool->head_dim_k, pool->head_dim_v, dim3((unsigned)wgs), s));
 }
 
 int pa_merge_states(void* out, float* out_lse, const void* prefix_out, const float* prefix_lse,

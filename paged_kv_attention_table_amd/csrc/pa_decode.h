@@ -64,27 +64,6 @@ __device__ __forceinline__ f32x4 mfma_16x16x16<F16>(u32x2 a, u32x2 b, f32x4 c) {
                                                0);
 }
 
-// Two fp8 (E4M3) values -- bytes 0, 1 of w (HI: bytes 2, 3) -- widened exactly to the
-// queries' 16-bit type, packed low element first.
-template <typename T, bool HI>
-__device__ __forceinline__ uint32_t widen_fp8x2(uint32_t w);
-template <>
-__device__ __forceinline__ uint32_t widen_fp8x2<BF16, false>(uint32_t w) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
-}
-template <>
-__device__ __forceinline__ uint32_t widen_fp8x2<BF16, true>(uint32_t w) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
-}
-template <>
-__device__ __forceinline__ uint32_t widen_fp8x2<F16, false>(uint32_t w) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
-}
-template <>
-__device__ __forceinline__ uint32_t widen_fp8x2<F16, true>(uint32_t w) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
-}
-
 // Which sequence and which visible range a row workgroup covers (partition `part`
 // of it in split mode), and the row's last visible position `ref` (whole range, the
 // origin of ALiBi positions); false: nothing to do.

@@ -149,8 +149,9 @@ struct MergeArgs {
 // Returns hipErrorInvalidValue (without launching) for a combination not built.
 hipError_t launch_rows(const RowsArgs& a, int dtype, int dk, int dv, dim3 grid, hipStream_t stream);
 struct PrefillArgs;
-hipError_t launch_prefill(const PrefillArgs& a, int dtype, int dk, int dv, dim3 grid, hipStream_t stream);
-bool prefill_supported(int dtype, int dk, int dv, int group, int block_size, int64_t num_blocks);
+hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, int q_dtype, int dk, int dv, dim3 grid,
+                          hipStream_t stream);
+bool prefill_supported(int kv_dtype, int q_dtype, int dk, int dv, int group, int block_size, int64_t num_blocks);
 hipError_t launch_validate(const ValidateArgs& a, hipStream_t stream);
 // Stores PA_OK in *status (the first kernel of a validated call).
 hipError_t launch_status_clear(int32_t* status, hipStream_t stream);

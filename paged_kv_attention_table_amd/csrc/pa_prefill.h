@@ -121,6 +121,37 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 x) {
   return y;
 }
 
+// Two fp8 (E4M3) values -- bytes 0, 1 of w (HI: bytes 2, 3) -- widened exactly to the
+// queries' 16-bit type, packed low element first.
+template <typename T, bool HI>
+__device__ __forceinline__ uint32_t widen_fp8x2(uint32_t w);
+template <>
+__device__ __forceinline__ uint32_t widen_fp8x2<BF16, false>(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+}
+template <>
+__device__ __forceinline__ uint32_t widen_fp8x2<BF16, true>(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+}
+template <>
+__device__ __forceinline__ uint32_t widen_fp8x2<F16, false>(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+}
+template <>
+__device__ __forceinline__ uint32_t widen_fp8x2<F16, true>(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+}
+
+// Sixteen fp8 (E4M3) values (16 bytes, element e at byte e) widened exactly to T:
+// elements 0..7 in lo, 8..15 in hi.
+template <typename T>
+__device__ __forceinline__ void widen_fp8x16(u32x4 x, u32x4& lo, u32x4& hi) {
+  lo = u32x4{widen_fp8x2<T, false>(x[0]), widen_fp8x2<T, true>(x[0]), widen_fp8x2<T, false>(x[1]),
+             widen_fp8x2<T, true>(x[1])};
+  hi = u32x4{widen_fp8x2<T, false>(x[2]), widen_fp8x2<T, true>(x[2]), widen_fp8x2<T, false>(x[3]),
+             widen_fp8x2<T, true>(x[3])};
+}
+
 // max(a, b, c) in one instruction (no canonicalising copies of the operands).
 __device__ __forceinline__ float max3f(float a, float b, float c) {
   float r;
@@ -157,8 +188,10 @@ struct PrefillLds {
 // kernel of its own launches it alone; the fused varlen kernel beside decode rows).
 // ALIBI: a.alibi is non-null; MERGE: a.merge is set; SEG2: a.new_lens is non-null
 // (separate instantiations, so the loop without them keeps its registers and
-// instructions).
-template <typename T, int DK, int DV, bool ALIBI, bool MERGE, bool SEG2 = false>
+// instructions).  KV8: the pools hold fp8 (E4M3) and T is the queries' type; K is
+// widened to T and V to f16 as they are staged in LDS (both exact), so the products
+// run as for 16-bit caches, PV always in f16.
+template <typename T, int DK, int DV, bool ALIBI, bool MERGE, bool SEG2 = false, bool KV8 = false>
 __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, PrefillLds<DK, DV>& sh) {
   static_assert(!(SEG2 && ALIBI), "two key segments take no ALiBi");
   constexpr int KT = kPrefillKeys;
@@ -172,6 +205,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
   // Overlap S^T of the next key tile with the softmax of this one (head dims 128
   // and 192; at 64 the single-tile loop keeps three workgroups per CU).
   constexpr bool PIPE = DK >= 128;
+  static_assert(!KV8 || (PIPE && DV == 128), "fp8 caches: head dims 128 or 192 for K, 128 for V");
+  constexpr int EB = KV8 ? 1 : 2;  // bytes of a cached element
 
   // K rows sit unpadded, chunk ch of key row r in 16-byte slot ch ^ ksw(r): with
   // 256-byte rows the 16 rows one read touches get 16 distinct slots of the bank
@@ -347,7 +382,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
   static_assert(KHALF % kWave == 0 && VHALF % kWave == 0, "tile halves of whole waves");
   static_assert(KN * NTH == 2 * KHALF && VN * NTH == 2 * VHALF, "whole loads per thread");
   const int hkv = a.num_kv_heads, b = a.block_size;
-  const uint32_t krow_bytes = (uint32_t)hkv * DK * 2, vrow_bytes = (uint32_t)hkv * DV * 2;
+  const uint32_t krow_bytes = (uint32_t)hkv * DK * EB, vrow_bytes = (uint32_t)hkv * DV * EB;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   auto ksw = [](int r) { return DK == 128 ? (r & 15) : ((r >> 1) & 7); };
   uint32_t k_gofs[KN], v_gofs[VN], v_lofs[VN];
@@ -373,12 +408,41 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
 #pragma unroll
   for (int kk = 0; kk < KSTEPS; ++kk) k_rd[kk] = (uint32_t)(r16 * DK * 2 + (((4 * kk + c) ^ ksw(r16)) * 16));
 
+  // fp8 caches: K and V both come through registers, one 16-byte load (16 values)
+  // at a time, widened to two 16-bit chunks as they are stored to LDS.  K load u of
+  // a thread is fp8 chunk tid + NTH u of the tile (DK / 16 per key row; at DK = 192
+  // the second load is made by the first 128 threads only); its two halves go to
+  // the swizzled slots of 16-bit chunks 2 c8 and 2 c8 + 1 of the row.  The V load
+  // is fp8 chunk tid (eight per row): 16 values of key row tid / 8.  As above, the
+  // 16-key half of every load is wave-uniform.
+  constexpr int KCH8 = DK / 16, VCH8 = DV / 16;
+  constexpr int K8N = (KT * KCH8 + NTH - 1) / NTH;  // K loads per thread
+  constexpr int K8LAST = KT * KCH8 - NTH * (K8N - 1);  // threads that make the last one
+  static_assert(!KV8 || (KT * VCH8 == NTH && K8LAST % kWave == 0 && (16 * KCH8) % kWave == 0), "fp8 tile shares");
+  uint32_t k8_gofs[K8N], k8_l0[K8N], k8_l1[K8N], v8_gofs = 0, v8_lofs = 0;
+  bool k8_hi[K8N], v8_hi = false;  // wave-uniform
+  int v8_key = 0;
+  if constexpr (KV8) {
+#pragma unroll
+    for (int u = 0; u < K8N; ++u) {
+      k8_hi[u] = wave_u * kWave + NTH * u >= 16 * KCH8;
+      const int pos = tid + NTH * u, row = pos / KCH8, c8 = pos % KCH8;
+      k8_gofs[u] = (uint32_t)(row & 15) * krow_bytes + (uint32_t)(c8 * 16);
+      k8_l0[u] = (uint32_t)((row * DK + ((2 * c8) ^ ksw(row)) * 8) * 2);
+      k8_l1[u] = (uint32_t)((row * DK + ((2 * c8 + 1) ^ ksw(row)) * 8) * 2);
+    }
+    v8_hi = wave_u * kWave >= 16 * VCH8;
+    v8_key = tid / VCH8;
+    v8_gofs = (uint32_t)(v8_key & 15) * vrow_bytes + (uint32_t)(tid % VCH8 * 16);
+    v8_lofs = (uint32_t)((v8_key * VROW + 16 * (tid % VCH8)) * 2);
+  }
+
   // The whole key loop.  EXACT = false with a bf16 cache stages V as f16 and runs
   // PV on f16 MFMA with P in f16; EXACT = true keeps V in bf16 and splits P into
   // bf16 high and low parts (two MFMAs).  f16 caches always take the f16 path.
   auto run = [&](auto exact_tag) {
     constexpr bool EXACT = decltype(exact_tag)::value;
-    constexpr bool F16PV = T::code == PA_F16 || !EXACT;
+    constexpr bool F16PV = T::code == PA_F16 || !EXACT || KV8;
 #pragma unroll
     for (int nd = 0; nd < ND; ++nd)
 #pragma unroll
@@ -403,8 +467,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
     if (klo >= khi) return;
     const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks;
     const int32_t* table_b = SEG2 ? a.new_tables + (int64_t)s * a.new_max_blocks : table;
-    const char* kbase = static_cast<const char*>(a.k_pool) + (int64_t)g * DK * 2;
-    const char* vbase = static_cast<const char*>(a.v_pool) + (int64_t)g * DV * 2;
+    const char* kbase = static_cast<const char*>(a.k_pool) + (int64_t)g * DK * EB;
+    const char* vbase = static_cast<const char*>(a.v_pool) + (int64_t)g * DV * EB;
     const int t_first = klo & ~(KT - 1);
     const int num_tiles = (khi - t_first + KT - 1) / KT;
     char* const v_lds_b = reinterpret_cast<char*>(&v_lds[0][0][0]);
@@ -498,6 +562,62 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
       } else {
         put(false);
       }
+    };
+    // fp8 caches: global -> registers (untracked, as above), then widened into LDS.
+    struct Regs8 {
+      u32x4 k[K8N];
+      u32x4 v;
+    };
+    auto fetch_k8 = [&](Rows r, Regs8& R) {
+      const char* lo_p = kbase + (uint64_t)r.lo * krow_bytes;
+      const char* hi_p = kbase + (uint64_t)r.hi * krow_bytes;
+      pin_sgpr(lo_p);
+      pin_sgpr(hi_p);
+#pragma unroll
+      for (int u = 0; u < K8N; ++u) {
+        if (u + 1 < K8N || wave_u * kWave < K8LAST) {
+          const char* p =
+              NTH * u + NTH <= 16 * KCH8 ? lo_p : NTH * u >= 16 * KCH8 ? hi_p : k8_hi[u] ? hi_p : lo_p;
+          R.k[u] = load16_untracked(p, k8_gofs[u]);
+        }
+      }
+    };
+    auto fetch_v8 = [&](Rows r, Regs8& R) {
+      const char* lo_p = vbase + (uint64_t)r.lo * vrow_bytes;
+      const char* hi_p = vbase + (uint64_t)r.hi * vrow_bytes;
+      pin_sgpr(lo_p);
+      pin_sgpr(hi_p);
+      R.v = load16_untracked(v8_hi ? hi_p : lo_p, v8_gofs);
+    };
+    auto settle8 = [&](Regs8& R) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int u = 0; u < K8N; ++u) tie_reg(R.k[u]);
+      tie_reg(R.v);
+    };
+    // K of a tile into buffer kb (not cleared, as above)
+    auto stash_k8 = [&](const Regs8& R, int kb) {
+      char* dst = reinterpret_cast<char*>(&k_lds[kb][0][0]);
+#pragma unroll
+      for (int u = 0; u < K8N; ++u) {
+        if (u + 1 < K8N || wave_u * kWave < K8LAST) {
+          u32x4 lo, hi;
+          widen_fp8x16<T>(R.k[u], lo, hi);
+          *reinterpret_cast<u32x4*>(dst + k8_l0[u]) = lo;
+          *reinterpret_cast<u32x4*>(dst + k8_l1[u]) = hi;
+        }
+      }
+    };
+    // V of tile iv into buffer vb, as f16; zeros for keys outside [klo, khi)
+    auto stash_v8 = [&](const Regs8& R, int iv, int vb) {
+      const int tv = t_first + iv * KT;
+      u32x4 lo, hi;
+      widen_fp8x16<F16>(R.v, lo, hi);
+      const int j = tv + v8_key;
+      if (j < klo || j >= khi || in_gap(j)) lo = hi = u32x4{0u, 0u, 0u, 0u};
+      char* dst = v_lds_b + vb * sizeof(v_lds[0]) + v8_lofs;
+      *reinterpret_cast<u32x4*>(dst) = lo;
+      *reinterpret_cast<u32x4*>(dst + 16) = hi;
     };
     // S^T of a key tile (from K buffer `buf`) for two 16-key blocks and both row blocks
     auto qk = [&](int buf, f32x4 (&sc)[2][2]) {
@@ -641,34 +761,64 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
     // of one overlap the vector work of the other; K then runs KA = 3 tiles ahead
     // (buffer i % NBUF held K(i), last read in step i - 1), else KA = 2 (buffer
     // (i + 2) % NBUF held K(i - 1)).  Loads past the last tile are clamped to it.
+    // fp8 caches (always PIPE): step i loads V(i+1) and K(i+2) into registers and
+    // stores both, widened, behind its compute: buffer (i+2) % NBUF held K(i-1), last
+    // read in step i-2, and V(i-1), last read in step i-1.
     constexpr int KA = PIPE ? 3 : 2;
     const int last = num_tiles - 1;
     Regs RV;
+    Regs8 R8;
     Rows rq[NBUF];  // pool rows of tile j in rq[j % NBUF], from its K load on
-    rq[0] = tile_rows(0);
-    fetch_v(rq[0], RV);
-#pragma unroll
-    for (int j = 0; j < KA; ++j) {
-      if (j > 0) rq[j] = tile_rows(min(j, last));
-      dma_k(rq[j], j);
-    }
-    settle(RV);  // V0 and K0 .. K(KA-2) have landed
-    stash_v(RV, 0, 0);
-    lds_barrier();
     f32x4 sc[2][2];
-    if constexpr (PIPE) {
-      qk(0, sc);
-      lds_barrier();  // every wave is past K0 before step 0 reloads its buffer
+    if constexpr (KV8) {
+      Regs8 R1;
+      rq[0] = tile_rows(0);
+      fetch_k8(rq[0], R8);
+      fetch_v8(rq[0], R8);
+      rq[1] = tile_rows(min(1, last));
+      fetch_k8(rq[1], R1);
+      settle8(R8);
+#pragma unroll
+      for (int u = 0; u < K8N; ++u) tie_reg(R1.k[u]);
+      stash_k8(R8, 0);
+      stash_v8(R8, 0, 0);
+      stash_k8(R1, 1);
+      lds_barrier();
+      qk(0, sc);  // step 0 writes buffers 1 (V) and 2 (K) only: no second barrier
+    } else {
+      rq[0] = tile_rows(0);
+      fetch_v(rq[0], RV);
+#pragma unroll
+      for (int j = 0; j < KA; ++j) {
+        if (j > 0) rq[j] = tile_rows(min(j, last));
+        dma_k(rq[j], j);
+      }
+      settle(RV);  // V0 and K0 .. K(KA-2) have landed
+      stash_v(RV, 0, 0);
+      lds_barrier();
+      if constexpr (PIPE) {
+        qk(0, sc);
+        lds_barrier();  // every wave is past K0 before step 0 reloads its buffer
+      }
     }
     // one step on tile i in buffer B = i % NBUF; `more`: i + 1 < num_tiles; LIVE: the
     // wave has a real row
     auto step = [&](int i, auto slot_tag, auto more, auto live_tag) {
       constexpr bool LIVE = decltype(live_tag)::value;
       constexpr int B = decltype(slot_tag)::value, B1 = (B + 1) % NBUF, BK = (B + KA) % NBUF;
+      constexpr int B2 = (B + 2) % NBUF;
       // the next tiles' loads also issue at raised priority (pipelined), so that they
       // leave early and their latency hides under this step
       if constexpr (PIPE) __builtin_amdgcn_s_setprio(1);
-      if (more) {
+      if constexpr (KV8) {
+        if (more) {
+          fetch_v8(rq[B1], R8);
+          if (i + 2 < num_tiles) {
+            rq[B2] = tile_rows(i + 2);
+            fetch_k8(rq[B2], R8);
+          }
+        }
+      } else if (more) {
         fetch_v(rq[B1], RV);
         rq[BK] = tile_rows(min(i + KA, last));
         dma_k(rq[BK], BK);
@@ -695,7 +845,14 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
           soft_pv(B, sc);
         }
       }
-      if (more) {
+      if constexpr (KV8) {
+        if (more) {
+          settle8(R8);
+          stash_v8(R8, i + 1, B1);
+          if (i + 2 < num_tiles) stash_k8(R8, B2);
+          lds_barrier();
+        }
+      } else if (more) {
         settle(RV);
         stash_v(RV, i + 1, B1);
         lds_barrier();
@@ -722,7 +879,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
       steps(std::false_type{});
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // clamped loads past the last tile
   };
-  if constexpr (T::code == PA_BF16) {
+  if constexpr (T::code == PA_BF16 && !KV8) {
     run(std::false_type{});
     // A V value beyond f16's range became inf in the staged tile, which makes every
     // output it reaches inf or NaN (NaN where p = 0): any non-finite output of this
@@ -792,38 +949,43 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
   }
 }
 
-template <typename T, int DK, int DV, bool ALIBI, bool MERGE, bool SEG2 = false>
+template <typename T, int DK, int DV, bool ALIBI, bool MERGE, bool SEG2 = false, bool KV8 = false>
 __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(const PrefillArgs a) {
   __shared__ PrefillLds<DK, DV> lds;
-  prefill_tile<T, DK, DV, ALIBI, MERGE, SEG2>(a, blockIdx.x, lds);
+  prefill_tile<T, DK, DV, ALIBI, MERGE, SEG2, KV8>(a, blockIdx.x, lds);
 }
 
-template <typename T, bool ALIBI, bool MERGE, bool SEG2 = false>
+// KV8: fp8 pools (head dims 128 / 128 and 192 / 128 only); T is the queries' type.
+template <typename T, bool KV8, bool ALIBI, bool MERGE, bool SEG2 = false>
 hipError_t launch_prefill_dims(const PrefillArgs& a, int dk, int dv, dim3 grid, hipStream_t stream) {
   const dim3 block(kPrefillThreads);
   if (dk == 128 && dv == 128)
-    hipLaunchKernelGGL((prefill_kernel<T, 128, 128, ALIBI, MERGE, SEG2>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<T, 128, 128, ALIBI, MERGE, SEG2, KV8>), grid, block, 0, stream, a);
   else if (dk == 192 && dv == 128)
-    hipLaunchKernelGGL((prefill_kernel<T, 192, 128, ALIBI, MERGE, SEG2>), grid, block, 0, stream, a);
-  else if (dk == 64 && dv == 64)
-    hipLaunchKernelGGL((prefill_kernel<T, 64, 64, ALIBI, MERGE, SEG2>), grid, block, 0, stream, a);
-  else
+    hipLaunchKernelGGL((prefill_kernel<T, 192, 128, ALIBI, MERGE, SEG2, KV8>), grid, block, 0, stream, a);
+  else if constexpr (!KV8) {
+    if (dk == 64 && dv == 64)
+      hipLaunchKernelGGL((prefill_kernel<T, 64, 64, ALIBI, MERGE, SEG2>), grid, block, 0, stream, a);
+    else
+      return hipErrorInvalidValue;
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool KV8 = false>
 hipError_t launch_prefill_typed(const PrefillArgs& a, int dk, int dv, dim3 grid, hipStream_t stream) {
   if (a.new_lens != nullptr) {  // two key segments (no ALiBi)
     if (a.alibi != nullptr) return hipErrorInvalidValue;
-    return a.merge ? launch_prefill_dims<T, false, true, true>(a, dk, dv, grid, stream)
-                   : launch_prefill_dims<T, false, false, true>(a, dk, dv, grid, stream);
+    return a.merge ? launch_prefill_dims<T, KV8, false, true, true>(a, dk, dv, grid, stream)
+                   : launch_prefill_dims<T, KV8, false, false, true>(a, dk, dv, grid, stream);
   }
   if (a.merge)
-    return a.alibi != nullptr ? launch_prefill_dims<T, true, true>(a, dk, dv, grid, stream)
-                              : launch_prefill_dims<T, false, true>(a, dk, dv, grid, stream);
-  return a.alibi != nullptr ? launch_prefill_dims<T, true, false>(a, dk, dv, grid, stream)
-                            : launch_prefill_dims<T, false, false>(a, dk, dv, grid, stream);
+    return a.alibi != nullptr ? launch_prefill_dims<T, KV8, true, true>(a, dk, dv, grid, stream)
+                              : launch_prefill_dims<T, KV8, false, true>(a, dk, dv, grid, stream);
+  return a.alibi != nullptr ? launch_prefill_dims<T, KV8, true, false>(a, dk, dv, grid, stream)
+                            : launch_prefill_dims<T, KV8, false, false>(a, dk, dv, grid, stream);
 }
 
 }  // namespace pa

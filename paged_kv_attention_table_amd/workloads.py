@@ -19,6 +19,7 @@ hold NaN, so a stray read shows up in the output.
 """
 from __future__ import annotations
 
+import dataclasses
 import math
 import os
 from concurrent.futures import ThreadPoolExecutor
@@ -309,6 +310,13 @@ class ChunkedPrefill:
     slot_mapping: np.ndarray
     scale: float
     seed: int
+    q_dtype: str = ""     # the queries' storage type when it differs from the pools' (fp8 pools)
+    k_scale: float = 1.0  # the pools' per-tensor scales: element = stored value * scale
+    v_scale: float = 1.0
+
+    @property
+    def query_dtype(self):
+        return self.q_dtype or self.dtype
 
     @property
     def num_tokens(self):
@@ -484,6 +492,17 @@ def quantize_e4m3(values_f32: np.ndarray, scale: float) -> np.ndarray:
 
     t = torch.from_numpy(np.ascontiguousarray(values_f32, dtype=np.float32) / np.float32(scale))
     return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def chunked_to_fp8(cp: ChunkedPrefill, k_scale: float = 1.0 / 16, v_scale: float = 1.0 / 32) -> ChunkedPrefill:
+    """The chunked prefill over an fp8 (E4M3) cache, as to_fp8 does for a Paged
+    workload: pools and new tokens divided by their scales and rounded to E4M3, the
+    queries kept in the workload's 16-bit type."""
+    fp8 = lambda a, sc: quantize_e4m3(widen_storage(a, cp.dtype), sc)  # noqa: E731
+    return dataclasses.replace(cp, name=cp.name + "-fp8", dtype="fp8_e4m3", k_pool=fp8(cp.k_pool, k_scale),
+                               v_pool=fp8(cp.v_pool, v_scale), k_new=fp8(cp.k_new, k_scale),
+                               v_new=fp8(cp.v_new, v_scale), q_dtype=cp.dtype, k_scale=float(k_scale),
+                               v_scale=float(v_scale))
 
 
 def to_fp8(w: Paged, k_scale: float = 1.0 / 16, v_scale: float = 1.0 / 32, q_dtype: str | None = None) -> Paged:

@@ -74,6 +74,8 @@ def workload(name):
         "mla-chunked": lambda: W.mla_chunked(),
         "mla-chunked-small": lambda: W.mla_chunked(small=True),
         "mla-chunked-small-permuted": lambda: W.mla_chunked(small=True, permuted=True),
+        "mla-chunked-small-fp8": lambda: W.chunked_to_fp8(W.mla_chunked(small=True), 0.0703125, 0.04296875),
+        "mla-chunked-fp8": lambda: W.chunked_to_fp8(W.mla_chunked()),
     }
     return table[name]()
 

@@ -177,9 +177,18 @@ def test_fp8_decode_unsupported(change, q_dtype, out_dtype, H):
 
 
 def test_fp8_varlen_and_value_types():
-    # varlen over an fp8 pool: one query token per sequence only
-    assert _varlen(_pool(**FP8), max_query_len=2) == binding.PA_EUNSUPPORTED
+    # varlen over an fp8 pool: queries of several tokens on the tiled kernel's fp8 shapes
+    # (head dims 128 / 128 or 192 / 128, power-of-two blocks of >= 16) only
+    for change in (dict(head_dim_k=64, head_dim_v=64), dict(head_dim_k=256, head_dim_v=256), dict(block_size=8)):
+        assert _varlen(_pool(**{**FP8, **change}), max_query_len=2) == binding.PA_EUNSUPPORTED
     assert _varlen(_pool(**FP8), q_dtype=binding.PA_F32) == binding.PA_EUNSUPPORTED
+    # the context-and-new-tokens call likewise
+    lib = binding.load()
+    for change, qd in ((dict(head_dim_k=64, head_dim_v=64), binding.PA_BF16), ({}, binding.PA_F32),
+                       ({}, binding.PA_FP8_E4M3)):
+        assert lib.pa_varlen_ctx_new(ctypes.byref(_pool(**{**FP8, **change})), FAKE, qd, FAKE, FAKE, 0, FAKE, FAKE,
+                                     FAKE, 4, FAKE, FAKE, FAKE, 4, 2, 10, 8, 4, 0.1, None, None,
+                                     None) == binding.PA_EUNSUPPORTED
     # a non-fp8 pool still wants queries of its own type
     assert _decode(_pool(dtype=binding.PA_BF16), q_dtype=binding.PA_F16) == binding.PA_EUNSUPPORTED
     lib = binding.load()

@@ -8,6 +8,7 @@ import os
 import re
 import shutil
 import subprocess
+from concurrent.futures import ThreadPoolExecutor
 
 import pytest
 
@@ -16,6 +17,26 @@ CSRC = os.path.join(HERE, "..", "paged_kv_attention_table_amd", "csrc")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fno-fast-math", "-Xclang", "-target-feature", "-Xclang",
          "-packed-fp32-ops", "--cuda-device-only", "-S"]
+
+
+SOURCES = ("pa_prefill_bf16.hip", "pa_prefill_f16.hip", "pa_prefill_fp8_bf16.hip", "pa_prefill_fp8_f16.hip",
+           "pa_fused_bf16.hip", "pa_fused_f16.hip", "pa_fused_fp8_bf16.hip", "pa_fused_fp8_f16.hip")
+
+
+@pytest.fixture(scope="module")
+def device_asm(tmp_path_factory):
+    """The device assembly of every source above, compiled in parallel."""
+    if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
+        pytest.skip("hipcc not available")
+    d = tmp_path_factory.mktemp("asm")
+
+    def build(src):
+        out = d / (src + ".s")
+        subprocess.run([HIPCC, *FLAGS, os.path.join(CSRC, src), "-o", str(out)], check=True, capture_output=True)
+        return src, out.read_text()
+
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
+        return dict(ex.map(build, SOURCES))
 
 
 def vgprs(tok):
@@ -49,32 +70,34 @@ def untracked_load_hazards(asm, kernel):
     return loads, bad
 
 
-@pytest.mark.skipif(shutil.which(HIPCC) is None and not os.path.exists(HIPCC), reason="hipcc not available")
-@pytest.mark.parametrize("src,tname", [("pa_prefill_bf16.hip", "4BF16"), ("pa_prefill_f16.hip", "3F16")])
-def test_no_register_reuse_under_inflight_loads(tmp_path, src, tname):
-    out = tmp_path / (src + ".s")
-    subprocess.run([HIPCC, *FLAGS, os.path.join(CSRC, src), "-o", str(out)], check=True, capture_output=True)
-    asm = out.read_text()
+@pytest.mark.parametrize("src,tname,kv8", [("pa_prefill_bf16.hip", "4BF16", "0"), ("pa_prefill_f16.hip", "3F16", "0"),
+                                           ("pa_prefill_fp8_bf16.hip", "4BF16", "1"),
+                                           ("pa_prefill_fp8_f16.hip", "3F16", "1")])
+def test_no_register_reuse_under_inflight_loads(device_asm, src, tname, kv8):
+    """16-bit caches (K straight to LDS, V through registers) and fp8 caches (K and V
+    through registers)."""
+    asm = device_asm[src]
     # ALiBi; merged into a prior state; two key segments (without ALiBi)
     flags = [(a, m, "0") for a in "01" for m in "01"] + [("0", m, "1") for m in "01"]
-    for dims in ("128ELi128", "192ELi128", "64ELi64"):
+    for dims in ("128ELi128", "192ELi128") + (("64ELi64",) if kv8 == "0" else ()):
         for alibi, merge, seg2 in flags:
-            kernel = f"_ZN2pa14prefill_kernelINS_{tname}ELi{dims}ELb{alibi}ELb{merge}ELb{seg2}EEEvNS_11PrefillArgsE"
+            kernel = (f"_ZN2pa14prefill_kernelINS_{tname}ELi{dims}ELb{alibi}ELb{merge}ELb{seg2}ELb{kv8}"
+                      "EEEvNS_11PrefillArgsE")
             loads, bad = untracked_load_hazards(asm, kernel)
             assert loads > 0, kernel
             assert not bad, f"{kernel}: {bad[:3]}"
 
 
-@pytest.mark.skipif(shutil.which(HIPCC) is None and not os.path.exists(HIPCC), reason="hipcc not available")
-@pytest.mark.parametrize("src,tname", [("pa_fused_bf16.hip", "4BF16"), ("pa_fused_f16.hip", "3F16")])
-def test_fused_varlen_kernel_no_register_reuse(tmp_path, src, tname):
+@pytest.mark.parametrize("src,tname,f8", [("pa_fused_bf16.hip", "4BF16", "0"), ("pa_fused_f16.hip", "3F16", "0"),
+                                          ("pa_fused_fp8_bf16.hip", "4BF16", "1"),
+                                          ("pa_fused_fp8_f16.hip", "3F16", "1")])
+def test_fused_varlen_kernel_no_register_reuse(device_asm, src, tname, f8):
     """The fused varlen kernel carries the prefill tile loop (head dim 128) beside
     the decode rows: the same check on it."""
-    out = tmp_path / (src + ".s")
-    subprocess.run([HIPCC, *FLAGS, os.path.join(CSRC, src), "-o", str(out)], check=True, capture_output=True)
-    asm = out.read_text()
+    asm = device_asm[src]
     for alibi, merge in (("0", "0"), ("1", "0"), ("0", "1"), ("1", "1")):
-        kernel = f"_ZN2pa19varlen_fused_kernelINS_{tname}ELb{alibi}ELb{merge}EEEvNS_11PrefillArgsENS_8RowsArgsEij"
+        kernel = (f"_ZN2pa19varlen_fused_kernelINS_{tname}ELb{alibi}ELb{merge}ELb{f8}"
+                  "EEEvNS_11PrefillArgsENS_8RowsArgsEij")
         loads, bad = untracked_load_hazards(asm, kernel)
         assert loads > 0, kernel
         assert not bad, f"{kernel}: {bad[:3]}"

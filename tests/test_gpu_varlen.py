@@ -214,10 +214,10 @@ def chunked_on_device(cp):
     plan = ChunkedPrefillPlan(ctx_lens=cp.ctx_lens, new_lens=cp.new_lens, ctx_tables=cp.ctx_tables,
                               new_tables=cp.new_tables, chunk=cp.chunk, block_size=cp.block_size,
                               num_heads=cp.num_heads, head_dim_v=cp.dv, scale=cp.scale)
-    q = dev(cp.q, cp.dtype)
+    q = dev(cp.q, cp.query_dtype)
     out = torch.full((cp.num_tokens, cp.num_heads, cp.dv), float("nan"), device="cuda")
     lse = torch.full((cp.num_heads, cp.num_tokens), float("nan"), device="cuda")
-    plan.run(k_pool, v_pool, q, out, lse)
+    plan.run(k_pool, v_pool, q, out, lse, k_scale=cp.k_scale, v_scale=cp.v_scale)
     torch.cuda.synchronize()
     assert int(st.item()) == 0
     return host(out), host(lse)
@@ -233,7 +233,7 @@ def oracle_chunked(orc, cp, rows):
     kp, vp = cp.k_pool.copy(), cp.v_pool.copy()
     assert orc.write_kv(kp, vp, cp.dtype, cp.k_new, cp.v_new, cp.slot_mapping) == 0
     qsl = cp.query_start_loc
-    q64 = orc.decode_elems(cp.q, cp.dtype)
+    q64 = orc.decode_elems(cp.q, cp.query_dtype)
     want = {}
     for r in range(cp.ctx_lens.size):
         ctx, n = int(cp.ctx_lens[r]), int(cp.new_lens[r])
@@ -243,10 +243,11 @@ def oracle_chunked(orc, cp, rows):
                 by_head.setdefault(h, []).append(t)
         if not by_head:
             continue
-        K = np.concatenate([orc.gather(kp, cp.dtype, cp.block_size, cp.ctx_tables[r], ctx),
-                            orc.gather(kp, cp.dtype, cp.block_size, cp.new_tables[r], n)])
-        V = np.concatenate([orc.gather(vp, cp.dtype, cp.block_size, cp.ctx_tables[r], ctx),
-                            orc.gather(vp, cp.dtype, cp.block_size, cp.new_tables[r], n)])
+        # (an element is its stored value times the pool's scale)
+        K = cp.k_scale * np.concatenate([orc.gather(kp, cp.dtype, cp.block_size, cp.ctx_tables[r], ctx),
+                                         orc.gather(kp, cp.dtype, cp.block_size, cp.new_tables[r], n)])
+        V = cp.v_scale * np.concatenate([orc.gather(vp, cp.dtype, cp.block_size, cp.ctx_tables[r], ctx),
+                                         orc.gather(vp, cp.dtype, cp.block_size, cp.new_tables[r], n)])
 
         def head(h):
             ts = sorted(by_head[h])
@@ -262,7 +263,7 @@ def oracle_chunked(orc, cp, rows):
     return want
 
 
-@pytest.mark.parametrize("name", ["mla-chunked-small", "mla-chunked-small-permuted"])
+@pytest.mark.parametrize("name", ["mla-chunked-small", "mla-chunked-small-permuted", "mla-chunked-small-fp8"])
 def test_chunked_prefill_small(orc, name):
     cp = workload(name)
     out, lse = chunked_on_device(cp)
@@ -274,12 +275,14 @@ def test_chunked_prefill_small(orc, name):
     assert_close(lse, rlse, TOL[cp.dtype], "lse")
 
 
-def test_chunked_prefill_full_sampled(orc):
+@pytest.mark.parametrize("name", ["mla-chunked", "mla-chunked-fp8"])
+def test_chunked_prefill_full_sampled(orc, name):
     """Full-size MLA-style workload (8 requests, 128 heads, QK 192 / V 128, contexts to
-    16384 in chunks of 4096).  The oracle answers every (token, head) row of the two
-    requests with the least context + new tokens, and 4096 seeded distinct rows of
-    every other request, which always include each head's first and last token."""
-    cp = workload("mla-chunked")
+    16384 in chunks of 4096; bf16, and over an fp8 cache).  The oracle answers every
+    (token, head) row of the two requests with the least context + new tokens, and
+    4096 seeded distinct rows of every other request, which always include each head's
+    first and last token."""
+    cp = workload(name)
     out, lse = chunked_on_device(cp)
     rng = np.random.default_rng(5005)
     qsl = cp.query_start_loc

@@ -1,9 +1,9 @@
 """pa_varlen with split single-token rows (partition_size > 0) on the GPU against the
-CPU oracle's unsplit varlen: the tiled prefill kernel plus split single-token rows,
-the per-row kernel for every other token plus split single-token rows (a shape the
-tiled kernel does not take), single-token calls only (16-bit and fp8 caches),
-causal and not, windows, sinks and ALiBi, and the device check of the partition
-count.  Outputs and lse of every token are compared."""
+CPU oracle's unsplit varlen: the tiled prefill kernel plus split single-token rows
+(16-bit and fp8 caches), the per-row kernel for every other token plus split
+single-token rows (a shape the tiled kernel does not take), single-token calls only
+(16-bit and fp8 caches), causal and not, windows, sinks and ALiBi, and the device
+check of the partition count.  Outputs and lse of every token are compared."""
 import numpy as np
 import pytest
 import torch
@@ -51,6 +51,13 @@ def run(orc, w, P, causal=None, window=None, sinks=None, alibi=None, pmax=None, 
                                     ("mixed-varlen", 256)])
 def test_split_singles_beside_prefill_tiles(orc, name, P):
     run(orc, workload(name), P)
+
+
+@pytest.mark.parametrize("name,P", [("mixed-varlen-small", 64), ("mixed-varlen", 256)])
+def test_split_singles_beside_fp8_prefill_tiles(orc, name, P):
+    """fp8 cache: the tiled kernel's launch, then the split rows on the fp8 decode
+    kernel and the reduce."""
+    run(orc, W.to_fp8(workload(name), k_scale=0.0703125, v_scale=0.04296875), P)
 
 
 @pytest.mark.parametrize("causal,window", [(False, 0), (False, 100), (True, 0)])
