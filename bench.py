@@ -30,6 +30,9 @@ of the timed region (`achieved`, `frac`); beside it, `achieved_flushed` /
 bytes per call that rocprofv3's FETCH_SIZE and WRITE_SIZE counters gave, scaled by
 what the counters read for a copy of known size; it is read from profiles/ and
 reported only while the kernels' source hash still matches the one recorded there.
+`graph` gives the same step captured once in a HIP graph and replayed K times back
+to back (host wall clock per step): the step's rate without the Python binding's
+launch path between the calls, as a caller that captures its steps would see it.
 `cpu_baseline` times the CPU oracle, unchanged, on a bounded sample of the same
 workload on the host cores (thread count and CPU model given).
 
@@ -230,6 +233,46 @@ def timed_loop(steps, pre, call, lead=False):
     wall = (time.perf_counter() - t0) * 1e3 / steps
     durs = [s.elapsed_time(e) for s, e in evs]
     return wall, float(np.mean(durs)), float(np.median(durs))
+
+
+def graph_step_ms(steps, step):
+    """ms per step when step() (its library calls only) is captured once in a HIP graph
+    and the graph is replayed `steps` times back to back: host wall clock from the
+    first replay to the end of the last, and one pair of events around them, as
+    (wall, events)."""
+    import torch
+
+    side = torch.cuda.Stream()  # warm-up off the capturing stream, as torch asks
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    s.record()
+    for _ in range(steps):
+        g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    ev = s.elapsed_time(e) / steps
+    del g
+    return wall, ev
+
+
+def graph_entry(steps, step, work, unit_scale, unit):
+    """The `graph` field of an entry: the step replayed from a captured HIP graph."""
+    wall, ev = graph_step_ms(steps, step)
+    return {"ms_per_step": round(wall, 5), "value": round(work / (wall * 1e-3) / unit_scale, 2), "unit": unit,
+            "ms_per_step_events": round(ev, 5),
+            "what": "the step captured once in a HIP graph, replayed K times; wall clock per step"}
 
 
 def dev(a, dtype=None):
@@ -528,6 +571,7 @@ def prefill_entry(args, kind, cpu_budget_s):
     achieved = flops / (avg_ms * 1e-3) / 1e12
     cold_ms = flushed_median_ms(attn)
     cold = flops / (cold_ms * 1e-3) / 1e12
+    graph = graph_entry(args.steps, step, flops, 1e12, "TFLOP/s")
     entry = {"value": round(value, 2), "unit": "TFLOP/s", "steps": args.steps, "warmup": args.warmup,
              "ms_per_step": round(ms, 5), "dtype": dtype, "config": dict(cfg, flops_per_step=flops),
              "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
@@ -535,7 +579,8 @@ def prefill_entry(args, kind, cpu_budget_s):
                           "kernel": kernel_label, "flops_per_call": flops, "avg_ms": round(avg_ms, 5),
                           "median_ms": round(med_ms, 5), "achieved_flushed": round(cold, 2),
                           "frac_flushed": round(cold / MFMA_BF16_PEAK_TFLOPS, 4),
-                          "median_ms_flushed": round(cold_ms, 5)}}
+                          "median_ms_flushed": round(cold_ms, 5)},
+             "graph": graph}
     if args.sweep and kind.removesuffix("-fp8") == "varlen":
         # context, after the timed region: the cost of device validation
         status = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -653,6 +698,12 @@ def decode_entry(args, workload, cpu_budget_s, partition_size=None):
     cold_ms = flushed_median_ms(decode)
     cold = nbytes / (cold_ms * 1e-3) / 1e9
 
+    def step():
+        write()
+        decode()
+
+    graph = graph_entry(args.steps, step, nbytes, 1e9, "GB/s")
+
     kernel = "decode_mfma_kernel"
     roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
@@ -671,7 +722,7 @@ def decode_entry(args, workload, cpu_budget_s, partition_size=None):
                         "num_heads": H, "num_kv_heads": w.num_kv_heads, "head_dim": w.dk,
                         "block_size": w.block_size, "partition_size": P, "kv_bytes_per_step": nbytes,
                         "step": "pa_write_kv + pa_decode"},
-             "roofline": roof}
+             "roofline": roof, "graph": graph}
     if args.sweep:
         # context, after the timed region: each partition size, and the cost of device
         # validation (status word), sinks and ALiBi; median of 20 flushed calls
@@ -705,7 +756,7 @@ def as_line(entry, args, extra=None):
             "warmup": args.warmup, "ms_per_step": entry["ms_per_step"], "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": entry["dtype"], "data": "synthetic",
             "config": entry["config"], "roofline": entry["roofline"]}
-    for k in ("sweep", "cpu_baseline"):
+    for k in ("graph", "sweep", "cpu_baseline"):
         if k in entry:
             line[k] = entry[k]
     if extra:
