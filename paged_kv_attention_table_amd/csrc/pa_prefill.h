@@ -285,6 +285,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
   int64_t row_tok[2];
   int row_head[2];
   bool row_ok[2];
+  int pos_in[2] = {0, 0};  // the rows' positions, where the visible range needs them
+  const bool need_pos = SEG2 ? len_b > 0 : a.causal != 0;
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     const int r = wave * 32 + rb * 16 + r16;
@@ -292,16 +294,34 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
     row_ok[rb] = (r < TPT * G) && (tl < q_len);
     row_tok[rb] = q0 + (row_ok[rb] ? tl : 0);
     row_head[rb] = g * G + r % G;
+    if (need_pos) pos_in[rb] = a.positions[row_tok[rb]];
+  }
+
+  // --- q rows as the B operand of S^T = K Q^T ---------------------------------------
+  // (issued behind the positions loads, so both round trips overlap)
+  u32x4 qb[2][KSTEPS];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (row_tok[rb] * a.num_heads + row_head[rb]) * DK;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      if (row_ok[rb] && !no_keys)
+        qb[rb][kk] = *reinterpret_cast<const u32x4*>(qrow + 32 * kk + 8 * c);
+      else
+        qb[rb][kk] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
     int end = n, start = 0;
     if constexpr (SEG2) {
       if (len_b > 0) {
-        int pos = a.positions[row_tok[rb]];
-        pos = pos < 0 ? 0 : (pos >= len_b ? len_b - 1 : pos);
+        const int pos = pos_in[rb] < 0 ? 0 : (pos_in[rb] >= len_b ? len_b - 1 : pos_in[rb]);
         end = base_b + pos + 1;
       }
     } else if (a.causal) {
-      int pos = a.positions[row_tok[rb]];
-      pos = pos < 0 ? 0 : (pos >= n ? n - 1 : pos);
+      const int pos = pos_in[rb] < 0 ? 0 : (pos_in[rb] >= n ? n - 1 : pos_in[rb]);
       end = n > 0 ? pos + 1 : 0;
     }
     if (a.window > 0) start = end - a.window > 0 ? end - a.window : 0;
@@ -323,20 +343,6 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
       atomicMin(&range_lo, vis_lo[rb]);
       atomicMax(&range_hi, vis_hi[rb]);
     }
-
-  // --- q rows as the B operand of S^T = K Q^T ---------------------------------------
-  u32x4 qb[2][KSTEPS];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (row_tok[rb] * a.num_heads + row_head[rb]) * DK;
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      if (row_ok[rb] && !no_keys)
-        qb[rb][kk] = *reinterpret_cast<const u32x4*>(qrow + 32 * kk + 8 * c);
-      else
-        qb[rb][kk] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
   // take the q loads' wait here, before any untracked K/V load is issued
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
