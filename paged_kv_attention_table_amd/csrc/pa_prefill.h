@@ -265,14 +265,21 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
   // a sequence with no keys at all (an exhausted context chunk) loads no q: its rows
   // only finish (zero output, or their state merged with an empty one)
   const bool no_keys = n == 0 && len_b == 0;
-  auto in_gap = [&](int j) {
-    if constexpr (SEG2) return j >= gap_lo && j < gap_hi;
-    return false;
-  };
+  // The gap, when there is one, lies inside the one tile that starts at n rounded
+  // down to the tile size (B starts at the next multiple of it): on that tile a key
+  // j is in the gap when j >= n, and no other tile meets the gap.
+  const int gap_tile = gap_lo < gap_hi ? (gap_lo & ~(kPrefillKeys - 1)) : -1;
   auto tile_meets_gap = [&](int t0) {
-    if constexpr (SEG2) return t0 < gap_hi && t0 + kPrefillKeys > gap_lo;
+    if constexpr (SEG2) return t0 == gap_tile;
     return false;
   };
+  // key j of a tile for which tile_meets_gap gave gap_t: in the gap
+  auto in_gap = [&](bool gap_t, int j) {
+    if constexpr (SEG2) return gap_t && j >= gap_lo;
+    return false;
+  };
+  // start of segment B in the key space, or past every key when B is empty
+  const int seg_b = len_b > 0 ? base_b : 0x7fffffff;
 
   if (tid == 0) {
     range_lo = 0x7fffffff;
@@ -494,7 +501,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
     auto tile_rows = [&](int i) -> Rows {
       int u0 = __builtin_amdgcn_readfirstlane(t_first + i * KT);
       // a tile lies in one segment (B starts at a multiple of the tile size)
-      const bool in_b = SEG2 && u0 >= base_b && len_b > 0;
+      const bool in_b = SEG2 && u0 >= seg_b;
       const int32_t* tab = in_b ? table_b : table;
       if (in_b) u0 -= base_b;
       const int u1 = u0 + 16, mi = in_b ? max_idx_b : max_idx;
@@ -547,7 +554,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
     // range are replaced by -inf, whatever the bytes hold.)
     auto stash_v = [&](const Regs& R, int iv, int vb) {
       const int tv = t_first + iv * KT;
-      const bool edge = tv < klo || tv + KT > khi || tile_meets_gap(tv);
+      const bool gap_t = tile_meets_gap(tv);
+      const bool edge = tv < klo || tv + KT > khi || gap_t;
       const u32x4 zero = {0u, 0u, 0u, 0u};
       auto put = [&](bool masking) {
 #pragma unroll
@@ -557,7 +565,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
           if constexpr (T::code == PA_BF16 && !EXACT) x = bf16x8_to_f16x8(x);
           if (masking) {
             const int j = tv + v_key[u];
-            if (j < klo || j >= khi || in_gap(j)) x = zero;
+            if (j < klo || j >= khi || in_gap(gap_t, j)) x = zero;
           }
           *dst = x;
         }
@@ -620,7 +628,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
       u32x4 lo, hi;
       widen_fp8x16<F16>(R.v, lo, hi);
       const int j = tv + v8_key;
-      if (j < klo || j >= khi || in_gap(j)) lo = hi = u32x4{0u, 0u, 0u, 0u};
+      if (j < klo || j >= khi || in_gap(tile_meets_gap(tv), j)) lo = hi = u32x4{0u, 0u, 0u, 0u};
       char* dst = v_lds_b + vb * sizeof(v_lds[0]) + v8_lofs;
       *reinterpret_cast<u32x4*>(dst) = lo;
       *reinterpret_cast<u32x4*>(dst + 16) = hi;
@@ -649,7 +657,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
       const int t0 = t_first + i * KT;
       // Tiles inside every row's visible range skip the masking.
       // (the gap between two key segments is masked for every row)
-      const bool masked = !(w_lo_max <= t0 && w_hi_min >= t0 + KT) || tile_meets_gap(t0);
+      const bool gap_t = tile_meets_gap(t0);
+      const bool masked = !(w_lo_max <= t0 && w_hi_min >= t0 + KT) || gap_t;
       if constexpr (ALIBI) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
@@ -670,7 +679,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
               const int j = t0 + kb * 16 + 4 * c + ii;
-              if (j < vis_lo[rb] || j >= vis_hi[rb] || in_gap(j)) sc[kb][rb][ii] = -INFINITY;
+              if (j < vis_lo[rb] || j >= vis_hi[rb] || in_gap(gap_t, j)) sc[kb][rb][ii] = -INFINITY;
             }
         }
         // this lane's max; the row-wide max is only formed when the reference must move
