@@ -61,6 +61,8 @@ CASES = [
     ("f16", "f16", 16, 1, 192, 128, [(1709, 40), (0, 33)], False, 0, 16),
     # 32 q heads per kv head: beyond the decode kernel, everything on the tiled one
     ("bf16", "bf16", 32, 1, 128, 128, [(50, 1), (20, 9), (0, 1)], True, 0, 16),
+    # blocks of 128 positions (a 32-key tile inside one block)
+    ("f16", "bf16", 16, 2, 192, 128, [(900, 77), (0, 200), (130, 1)], True, 300, 128),
 ]
 
 
@@ -70,6 +72,30 @@ def test_fp8_varlen_prefill(orc, case):
     base = W.make_paged(f"fp8-prefill{case}", 3100 + case, dtype=dtype, block_size=b, num_heads=H, num_kv_heads=Hkv,
                         dk=dk, dv=dv, segments=segs, causal=causal, sliding_window=window)
     run_and_check(orc, W.to_fp8(base, k_scale=KS, v_scale=VS, q_dtype=qd), causal=causal)
+
+
+@pytest.mark.parametrize("qd", ["bf16", "f16"])
+def test_fp8_prefill_out_in_query_type(orc, qd):
+    """Outputs in the queries' 16-bit type: the oracle's result rounded to that type,
+    within one unit in its last place plus the bound."""
+    from tests.gpu_util import TORCH
+
+    w = W.to_fp8(workload("mixed-varlen-small"), k_scale=KS, v_scale=VS, q_dtype=qd)
+    d = OnDevice(w)
+    kp, vp = d.host_pools_after_write(orc)
+    out = torch.full((w.num_tokens, w.num_heads, w.dv), float("nan"), dtype=TORCH[qd], device="cuda")
+    max_q = int(np.diff(w.query_start_loc).max())
+    pa_varlen(d.k_pool, d.v_pool, d.q, out, d.qsl, d.seq_lens, d.positions, d.tables, max_q, w.scale, causal=True,
+              sliding_window=w.sliding_window, k_scale=w.k_scale, v_scale=w.v_scale)
+    torch.cuda.synchronize()
+    st, ref, _ = orc.varlen(kp, vp, w.dtype, w.q, w.query_dtype, w.query_start_loc, w.seq_lens, w.positions,
+                            w.block_tables, w.scale, True, w.sliding_window, threads=threads(), k_scale=w.k_scale,
+                            v_scale=w.v_scale)
+    assert st == 0
+    rt = torch.from_numpy(ref).to(TORCH[qd]).double().numpy()
+    err = np.abs(out.double().cpu().numpy() - rt)
+    ulp = np.abs(rt) * 2.0 ** (1 - (8 if qd == "bf16" else 11))
+    assert np.all(err <= ulp + TOL["fp8_e4m3"]), err.max()
 
 
 @pytest.mark.parametrize("name", ["mixed-varlen-small", "mixed-varlen-shuffled"])

@@ -81,9 +81,13 @@ def test_graph_write_and_decode(P):
     assert int(st_w.item()) == 0 and int(st_d.item()) == 0
 
 
-def test_graph_mixed_varlen():
-    """Prefill tiles and single-token rows of one pa_varlen call, with lse and status."""
+@pytest.mark.parametrize("fp8", [False, True])
+def test_graph_mixed_varlen(fp8):
+    """Prefill tiles and single-token rows of one pa_varlen call, with lse and status
+    (16-bit and fp8 caches)."""
     w = workload("mixed-varlen-small")
+    if fp8:
+        w = W.to_fp8(w, k_scale=0.0703125, v_scale=0.04296875)
     d = OnDevice(w)
     T, H = w.num_tokens, w.num_heads
     out = torch.empty((T, H, w.dv), dtype=d.q.dtype, device="cuda")
@@ -93,7 +97,7 @@ def test_graph_mixed_varlen():
 
     def run():
         pa_varlen(d.k_pool, d.v_pool, d.q, out, d.qsl, d.seq_lens, d.positions, d.tables, max_q, w.scale, causal=True,
-                  sliding_window=w.sliding_window, lse=lse, status=st)
+                  sliding_window=w.sliding_window, lse=lse, status=st, k_scale=w.k_scale, v_scale=w.v_scale)
 
     replays_match_eager(run, [out, lse, st])
     assert int(st.item()) == 0
@@ -123,22 +127,25 @@ def test_graph_varlen_merge_state_reset():
     replays_match_eager(run, [out, lse], reset=reset)
 
 
-def test_graph_chunked_prefill():
-    """The chunked-context driver (pa_varlen, then pa_varlen_merge per further chunk and
-    for the causal new tokens) captured whole."""
-    cp = workload("mla-chunked-small")
+@pytest.mark.parametrize("name", ["mla-chunked-small", "mla-chunked-small-fp8"])
+def test_graph_chunked_prefill(name):
+    """The chunked-context driver (one pa_varlen_ctx_new call per context chunk, the
+    first writing the state and the others merging into it) captured whole (16-bit
+    and fp8 caches)."""
+    cp = workload(name)
     k_pool, v_pool = dev(cp.k_pool, cp.dtype), dev(cp.v_pool, cp.dtype)
     st = torch.full((1,), -7, dtype=torch.int32, device="cuda")
     pa_write_kv(k_pool, v_pool, dev(cp.k_new, cp.dtype), dev(cp.v_new, cp.dtype), dev(cp.slot_mapping), status=st)
     plan = ChunkedPrefillPlan(ctx_lens=cp.ctx_lens, new_lens=cp.new_lens, ctx_tables=cp.ctx_tables,
                               new_tables=cp.new_tables, chunk=cp.chunk, block_size=cp.block_size,
                               num_heads=cp.num_heads, head_dim_v=cp.dv, scale=cp.scale)
-    q = dev(cp.q, cp.dtype)
+    q = dev(cp.q, cp.query_dtype)
     out = torch.empty((cp.num_tokens, cp.num_heads, cp.dv), device="cuda")
     lse = torch.empty((cp.num_heads, cp.num_tokens), device="cuda")
     torch.cuda.synchronize()
     assert int(st.item()) == 0
-    replays_match_eager(lambda: plan.run(k_pool, v_pool, q, out, lse), [out, lse])
+    replays_match_eager(lambda: plan.run(k_pool, v_pool, q, out, lse, k_scale=cp.k_scale, v_scale=cp.v_scale),
+                        [out, lse])
 
 
 def test_graph_merge_states_and_gather():
