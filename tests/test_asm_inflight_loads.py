@@ -2,8 +2,15 @@
 a global load issued as inline asm (not counted by the compiler) must not be read
 or written by any instruction before the next vector-memory wait.  A violation
 means the compiler moved or reused registers of a load still in flight (silent
-corruption, or an address overwritten by late data).  The scan follows
-fall-through order from each load up to the next `s_waitcnt vmcnt`."""
+corruption, or an address overwritten by late data).
+
+The scan follows fall-through order from each load up to the next `s_waitcnt
+vmcnt`, and the target of an unconditional branch.  A conditional branch is passed
+by falling through, except where it certainly goes the other way: the load's block
+is the fall-through of a branch on `vcc = exec & sX` with sX a uniform boolean
+(`s_cselect_b64 sX, -1, 0`), so sX is known on entry, and a later branch on a vcc
+formed from the same, unwritten sX is then taken for certain -- the scan follows
+its target instead of a fall-through path that cannot run."""
 import os
 import re
 import shutil
@@ -47,9 +54,111 @@ def vgprs(tok):
     return {int(m.group(1))} if m else set()
 
 
+def sgprs(tok):
+    m = re.match(r"s\[(\d+):(\d+)\]", tok)
+    if m:
+        return frozenset(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"s(\d+)$", tok)
+    return frozenset({int(m.group(1))}) if m else frozenset()
+
+
+# scalar instructions whose first operand is not a destination
+_NO_SDST = ("s_cmp", "s_bitcmp", "s_cbranch", "s_branch", "s_waitcnt", "s_barrier", "s_nop", "s_setprio", "s_sleep",
+            "s_sched", "s_endpgm", "s_store", "s_dcache", "s_wait", "s_setreg", "s_trap", "s_ttrace", "s_icache")
+
+
+def _label(t):
+    """The label a line defines (".LBB3_7:", possibly followed by a comment), or None."""
+    m = re.match(r"(\.L[\w.]+):", t)
+    return m.group(1) if m else None
+
+
+def _parse(t):
+    parts = t.split(None, 1)
+    ops = [o.strip().split()[0] for o in parts[1].split(",") if o.strip()] if len(parts) > 1 else []
+    return parts[0], ops
+
+
+def _sgpr_dst(op, ops):
+    """The SGPRs an instruction writes (its first operand, where that is one)."""
+    if not ops:
+        return frozenset()
+    if (op.startswith("s_") and not op.startswith(_NO_SDST)) or op.startswith(("v_readlane", "v_readfirstlane")) \
+            or (op.startswith("v_cmp") and op.endswith("_e64")):
+        return sgprs(ops[0])
+    return frozenset()
+
+
+def _writes_vcc(op, ops):
+    return (ops[:1] == ["vcc"] and not op.startswith("s_cbranch")) or (op.startswith("v_cmp") and op.endswith("_e32")) \
+        or op.startswith(("v_add_co", "v_sub_co", "v_subrev_co", "v_addc", "v_subb"))
+
+
+def _vcc_from(op, ops):
+    """(kind, sX) for vcc = exec & sX ("and") or exec & ~sX ("andn2"), else None."""
+    if op in ("s_and_b64", "s_andn2_b64") and len(ops) == 3 and ops[0] == "vcc" and ops[1] == "exec" and sgprs(ops[2]):
+        return ("and" if op == "s_and_b64" else "andn2", sgprs(ops[2]))
+    return None
+
+
+def _entry_knowledge(lines, n):
+    """What the path into the block holding line n fixes: {sX: True (all ones) | False
+    (zero)} when that block is entered only by falling through a vcc branch whose vcc
+    came from a uniform boolean sX that nothing writes before line n."""
+    j = n - 1
+    while j >= 0:
+        t = lines[j]
+        if _label(t):
+            return {}  # a label: other predecessors
+        if t and not t.startswith(";"):
+            op, ops = _parse(t)
+            if op.startswith("s_branch") or op == "s_endpgm":
+                return {}
+            if op.startswith("s_cbranch"):
+                break
+        j -= 1
+    else:
+        return {}
+    op, _ = _parse(lines[j])
+    if op not in ("s_cbranch_vccz", "s_cbranch_vccnz"):
+        return {}
+    between = [_parse(t) for t in lines[j + 1:n] if t and not t.startswith((";", "."))]
+    k = j - 1
+    while k >= 0 and (not lines[k] or lines[k].startswith(";")):
+        k -= 1
+    if k < 0:
+        return {}
+    src = _vcc_from(*_parse(lines[k]))
+    if src is None:
+        return {}
+    kind, sx = src
+    if any(_sgpr_dst(o, a) & sx for o, a in between):
+        return {}
+    d = k - 1  # sX must be a uniform boolean: its last definition an s_cselect_b64 sX, -1, 0
+    while d >= 0:
+        t = lines[d]
+        if _label(t):
+            return {}
+        if t and not t.startswith(";"):
+            o, a = _parse(t)
+            if _sgpr_dst(o, a) & sx:
+                if o == "s_cselect_b64" and a[1:3] == ["-1", "0"] and sgprs(a[0]) == sx:
+                    break
+                return {}
+        d -= 1
+    else:
+        return {}
+    # falling through vccz: vcc != 0; "and": sX != 0, so all ones; "andn2": ~sX != 0, so zero.
+    # Falling through vccnz (vcc == 0) fixes nothing (exec may be zero).
+    if op == "s_cbranch_vccz":
+        return {sx: kind == "and"}
+    return {}
+
+
 def untracked_load_hazards(asm, kernel):
     i = asm.index(kernel + ":")
     lines = [ln.strip() for ln in asm[i:asm.index(".Lfunc_end", i)].split("\n")]
+    labels = {_label(t): n for n, t in enumerate(lines) if _label(t)}
     loads, bad = 0, []
     for n, ln in enumerate(lines):
         # the asm loads use a scalar base (saddr form); the compiler's own use a VGPR pair
@@ -57,17 +166,108 @@ def untracked_load_hazards(asm, kernel):
             continue
         loads += 1
         dst = vgprs(ln.split()[1].rstrip(","))
-        for t in lines[n + 1:]:
+        known = _entry_knowledge(lines, n)
+        vsrc = None
+        hit = None
+        j, steps = n + 1, 0
+        while j < len(lines) and steps < 100000:
+            steps += 1
+            t = lines[j]
             if not t or t.startswith((";", ".")):
+                j += 1
                 continue
-            if (t.startswith("s_waitcnt") and "vmcnt" in t) or t.startswith("s_endpgm"):
+            op, ops = _parse(t)
+            if (op.startswith("s_waitcnt") and "vmcnt" in t) or op == "s_endpgm":
                 break
-            parts = t.split(None, 1)
-            ops = [o.strip().split()[0] for o in parts[1].split(",") if o.strip()] if len(parts) > 1 else []
             if any(vgprs(o) & dst for o in ops):
-                bad.append((ln, t))
+                hit = (ln, t)
                 break
+            w = _sgpr_dst(op, ops)
+            if w:
+                known = {k: v for k, v in known.items() if not (k & w)}
+                if vsrc is not None and vsrc[1] & w:
+                    vsrc = None
+            src = _vcc_from(op, ops)
+            if src is not None:
+                vsrc = src
+            elif _writes_vcc(op, ops):
+                vsrc = None
+            if op == "s_branch":
+                j = labels[ops[0]]
+                continue
+            if op == "s_cbranch_vccz" and vsrc is not None and vsrc[1] in known and \
+                    ((vsrc[0] == "and" and not known[vsrc[1]]) or (vsrc[0] == "andn2" and known[vsrc[1]])):
+                j = labels[ops[0]]  # vcc is certainly zero: the branch is taken
+                continue
+            j += 1
+        if hit is not None:
+            bad.append(hit)
     return loads, bad
+
+
+# Hand-written fragments that pin the scan itself: a read of a load's registers on a
+# feasible path is found, on a path the load's own guard rules out is not, and one
+# reached only through a branch target is found.
+_FRAGMENTS = {
+    "straight": ("""k:
+\ts_cselect_b64 s[10:11], -1, 0
+\ts_and_b64 vcc, exec, s[10:11]
+\ts_cbranch_vccz .LB1
+\tglobal_load_dwordx4 v[8:11], v2, s[0:1]
+.LB1:
+\tv_mov_b32_e32 v3, v9
+\ts_waitcnt vmcnt(0)
+\ts_endpgm
+.Lfunc_end0:
+""", 1),
+    "guarded": ("""k:
+\ts_cselect_b64 s[10:11], -1, 0
+\ts_and_b64 vcc, exec, s[10:11]
+\ts_cbranch_vccz .LB1
+\tglobal_load_dwordx4 v[8:11], v2, s[0:1]
+.LB1:
+\ts_andn2_b64 vcc, exec, s[10:11]
+\ts_cbranch_vccz .LB2
+\tds_read_b128 v[8:11], v4
+.LB2:
+\ts_waitcnt vmcnt(0)
+\ts_endpgm
+.Lfunc_end0:
+""", 0),
+    "guard rewritten": ("""k:
+\ts_cselect_b64 s[10:11], -1, 0
+\ts_and_b64 vcc, exec, s[10:11]
+\ts_cbranch_vccz .LB1
+\tglobal_load_dwordx4 v[8:11], v2, s[0:1]
+.LB1:
+\ts_cselect_b64 s[10:11], -1, 0
+\ts_andn2_b64 vcc, exec, s[10:11]
+\ts_cbranch_vccz .LB2
+\tds_read_b128 v[8:11], v4
+.LB2:
+\ts_waitcnt vmcnt(0)
+\ts_endpgm
+.Lfunc_end0:
+""", 1),
+    "through a branch": ("""k:
+\tglobal_load_dwordx4 v[8:11], v2, s[0:1]
+\ts_branch .LB3
+\tv_mov_b32_e32 v3, v1
+\ts_waitcnt vmcnt(0)
+.LB3:
+\tv_add_u32_e32 v10, v1, v1
+\ts_waitcnt vmcnt(0)
+\ts_endpgm
+.Lfunc_end0:
+""", 1),
+}
+
+
+@pytest.mark.parametrize("name", sorted(_FRAGMENTS))
+def test_scan_on_fragments(name):
+    asm, want = _FRAGMENTS[name]
+    loads, bad = untracked_load_hazards(asm, "k")
+    assert loads == 1 and len(bad) == want, bad
 
 
 @pytest.mark.parametrize("src,tname,kv8", [("pa_prefill_bf16.hip", "4BF16", "0"), ("pa_prefill_f16.hip", "3F16", "0"),
