@@ -12,8 +12,8 @@ and the values must agree to a few binary32 ulps (the kernels normalise by a
 reciprocal of the softmax sum, which may leave the last bit or two).  Covered: the
 MFMA decode kernel (unsplit, multi-wave split, one-wave split; 16-bit and fp8
 caches, the latter also on kv-head pairs), the tiled prefill kernel (several query
-tokens per sequence, causal, head dims 128, 192 / 128 and 64) and the single-token
-rows of a mixed varlen call.  K is random and unused blocks hold NaN, so a wrong
+tokens per sequence, causal, head dims 128, 192 / 128 and 64; 16-bit and fp8 caches)
+and the single-token rows of a mixed varlen call.  K is random and unused blocks hold NaN, so a wrong
 slot shows as a wrong index or a NaN."""
 import numpy as np
 import pytest
@@ -104,9 +104,12 @@ def test_decode_index_probe(dtype, P, pmax):
 
 
 @pytest.mark.parametrize("dtype,H,hkv,dk,dv", [("f16", 32, 8, 128, 128), ("bf16", 32, 8, 128, 128),
-                                               ("bf16", 16, 16, 192, 128), ("f16", 8, 2, 64, 64)])
+                                               ("bf16", 16, 16, 192, 128), ("f16", 8, 2, 64, 64),
+                                               ("fp8", 32, 8, 128, 128), ("fp8", 16, 16, 192, 128)])
 def test_varlen_index_probe(dtype, H, hkv, dk, dv):
-    """Prefill chunks (tiled kernel) and single tokens (decode kernel) in one call."""
+    """Prefill chunks (tiled kernel) and single tokens (decode kernel, or the tiled
+    kernel where the decode kernel does not take the shape) in one call; fp8 caches
+    with bf16 queries."""
     rng = np.random.default_rng(92)
     b = 16
     segments = [(0, 70), (333, 1), (45, 130), (1000, 1), (17, 33), (0, 1), (260, 64)]
