@@ -74,6 +74,31 @@ def test_fp8_varlen_prefill(orc, case):
     run_and_check(orc, W.to_fp8(base, k_scale=KS, v_scale=VS, q_dtype=qd), causal=causal)
 
 
+def test_fp8_prefill_empty_sequences_and_loose_bound(orc):
+    """A sequence with no query tokens between others, a context-free single token,
+    and max_query_len above the longest sequence (the grid then holds tiles past
+    every sequence's end, which exit)."""
+    base = W.make_paged("fp8-prefill-empty", 3500, dtype="bf16", block_size=16, num_heads=8, num_kv_heads=2, dk=128,
+                        dv=128, segments=[(40, 70), (129, 0), (0, 1), (300, 45), (7, 0)], causal=True,
+                        sliding_window=0)
+    w = W.to_fp8(base, k_scale=KS, v_scale=VS)
+    d = OnDevice(w)
+    kp, vp = d.host_pools_after_write(orc)
+    out = torch.full((w.num_tokens, w.num_heads, w.dv), float("nan"), device="cuda")
+    lse = torch.full((w.num_heads, w.num_tokens), float("nan"), device="cuda")
+    status = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    pa_varlen(d.k_pool, d.v_pool, d.q, out, d.qsl, d.seq_lens, d.positions, d.tables, 400, w.scale, causal=True,
+              lse=lse, status=status, k_scale=w.k_scale, v_scale=w.v_scale)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    st, ref, rlse = orc.varlen(kp, vp, w.dtype, w.q, w.query_dtype, w.query_start_loc, w.seq_lens, w.positions,
+                               w.block_tables, w.scale, True, 0, threads=threads(), k_scale=w.k_scale,
+                               v_scale=w.v_scale)
+    assert st == 0
+    assert_close(host(out), ref, TOL["fp8_e4m3"], "out")
+    assert_close(host(lse), rlse, TOL["fp8_e4m3"], "lse")
+
+
 @pytest.mark.parametrize("qd", ["bf16", "f16"])
 def test_fp8_prefill_out_in_query_type(orc, qd):
     """Outputs in the queries' 16-bit type: the oracle's result rounded to that type,
