@@ -11,6 +11,7 @@ import pytest
 import torch
 
 from paged_kv_attention_table_amd import PaError, binding, pa_decode, pa_decode_noalloc
+from paged_kv_attention_table_amd import workloads as W
 from tests.gpu_util import TOL, OnDevice, assert_close, bits_equal, host, threads, workload
 
 pytestmark = pytest.mark.gpu
@@ -24,7 +25,8 @@ def with_workspaces(d, P, sliding_window=0, sinks=None):
     out = torch.full((S, H, w.dv), float("nan"), device="cuda")
     st = torch.full((1,), -7, dtype=torch.int32, device="cuda")
     pa_decode(d.k_pool, d.v_pool, d.q, out, d.tables, d.seq_lens, w.scale, sliding_window=sliding_window,
-              partition_size=P, max_logits=ws[0], exp_sums=ws[1], tmp_out=ws[2], status=st, sinks=sinks)
+              partition_size=P, max_logits=ws[0], exp_sums=ws[1], tmp_out=ws[2], status=st, sinks=sinks,
+              k_scale=w.k_scale, v_scale=w.v_scale)
     torch.cuda.synchronize()
     assert int(st.item()) == 0
     return host(out)
@@ -35,7 +37,7 @@ def static(d, P, sliding_window=0, sinks=None):
     out = torch.full((w.num_seqs, w.num_heads, w.dv), float("nan"), device="cuda")
     st = torch.full((1,), -7, dtype=torch.int32, device="cuda")
     pa_decode_noalloc(d.k_pool, d.v_pool, d.q, out, d.tables, d.seq_lens, w.scale, sliding_window=sliding_window,
-                      partition_size=P, status=st, sinks=sinks)
+                      partition_size=P, status=st, sinks=sinks, k_scale=w.k_scale, v_scale=w.v_scale)
     torch.cuda.synchronize()
     assert int(st.item()) == 0
     return host(out)
@@ -57,6 +59,16 @@ def test_noalloc_matches_pa_decode_on_two_calls(orc):
                                 sliding_window=win, sinks=host(sinks).astype(np.float64), threads=threads())
         assert st == 0
         assert_close(got, ref, TOL[w.dtype], f"P {P} window {win} vs oracle")
+
+
+def test_noalloc_fp8_two_calls():
+    """fp8 caches: the long split decode (kv-head pairs) at full size, then a smaller
+    batch, both bit for bit as pa_decode with caller workspaces."""
+    big = OnDevice(W.to_fp8(workload("long-decode")))
+    assert bits_equal(static(big, 512), with_workspaces(big, 512)), "fp8 long split decode, P 512"
+    small = OnDevice(W.to_fp8(workload("batched-decode-small"), k_scale=0.0703125, v_scale=0.04296875))
+    assert bits_equal(static(small, 64, sliding_window=100), with_workspaces(small, 64, sliding_window=100)), \
+        "fp8 batch, P 64, window 100"
 
 
 def test_noalloc_refuses_what_does_not_fit():
