@@ -154,8 +154,8 @@ def test_fp8_prefill_merged_into_a_state(orc, dk):
 class Fp8CtxNewCase(CtxNewCase):
     """A CtxNewCase whose pools are rounded to E4M3 after division by the scales."""
 
-    def __init__(self, seed, ctx, new, H, Hkv, dk, dv, q_dtype):
-        super().__init__(seed, ctx, new, H, Hkv, dk, dv, q_dtype)
+    def __init__(self, seed, ctx, new, H, Hkv, dk, dv, q_dtype, b=16):
+        super().__init__(seed, ctx, new, H, Hkv, dk, dv, q_dtype, b=b)
         self.q_dtype = q_dtype
         self.k_pool = W.quantize_e4m3(W.widen_storage(self.k_pool, q_dtype), KS)
         self.v_pool = W.quantize_e4m3(W.widen_storage(self.v_pool, q_dtype), VS)
