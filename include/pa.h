@@ -133,7 +133,7 @@ int pa_write_kv(const pa_kv_pool* pool, const void* k_new, const void* v_new,
  * page's minus slopes[h] * (end - 1), which keeps them exact at long contexts.
  * Slopes must be finite.  A sink logit competes with these biased scores.
  * Supported: head_dim_k == head_dim_v in {32, 64, 128, 256}; num_heads /
- * num_kv_heads <= 16; any block_size.  PA_FP8_E4M3 pools: q_dtype PA_F16 or PA_BF16,
+ * num_kv_heads <= 16 (<= 8 at head dim 256); any block_size.  PA_FP8_E4M3 pools: q_dtype PA_F16 or PA_BF16,
  * head dims 128, block_size a power of two >= 16. */
 int pa_decode(const pa_kv_pool* pool, const void* q, int32_t q_dtype, void* out, int32_t out_dtype,
               const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
@@ -194,8 +194,9 @@ int pa_decode_noalloc(const pa_kv_pool* pool, const void* q, int32_t q_dtype, vo
  * partition_size == 0: no split, workspaces may be NULL.  Ignored for shapes whose
  * single-token rows run on the tiled kernel (the row kernels do not take them).
  * Supported: (head_dim_k, head_dim_v) in {(32,32), (64,64), (128,128), (256,256),
- * (192,128)}; num_heads / num_kv_heads <= 16; any block_size.  Beyond that, the
- * tiled kernel's shapes (below) with num_heads / num_kv_heads up to 128.
+ * (192,128)}; num_heads / num_kv_heads <= 16 (<= 8 at (256,256)); any block_size.
+ * Beyond that, the tiled kernel's shapes (below) with num_heads / num_kv_heads up
+ * to 128.
  * PA_FP8_E4M3 pools: q_dtype PA_F16 or PA_BF16, block_size a power of two >= 16,
  * num_blocks * block_size < 2^32, and (head_dim_k, head_dim_v) = (128,128) with
  * num_heads / num_kv_heads <= 16 (single-token sequences on the fp8 decode kernel,
