@@ -152,12 +152,38 @@ struct DecodeLds {
   float prev_lse[16];
 };
 
+// Unsplit decode of at most 64 rows: the r-th workgroup group takes the row with the
+// r-th longest visible range (ties by index), so the longest rows start first and
+// the last workgroups to be dispatched are the shortest.
+__device__ __forceinline__ bool rows_ranked(const RowsArgs& a, uint32_t grid_rows) {
+  return a.query_start_loc == nullptr && a.partition_size == 0 && grid_rows <= (uint32_t)kWave;
+}
+// The rows of ranks r0 and r1 (one read of the lengths, one count per lane).
+__device__ __forceinline__ void rows_by_rank(const RowsArgs& a, int S, int r0, int r1, int& row0, int& row1) {
+  const int lane = lane_id(), cap = a.max_blocks * a.block_size;
+  int len = -1;
+  if (lane < S) {
+    int nl = a.seq_lens[lane];
+    nl = nl < 0 ? 0 : (nl > cap ? cap : nl);
+    len = a.window > 0 && nl > a.window ? a.window : nl;
+  }
+  int rank = 0;
+  for (int r = 0; r < S; ++r) {
+    const int lr = __builtin_amdgcn_readlane(len, r);
+    rank += (lr > len) || (lr == len && r < lane);
+  }
+  const uint64_t h0 = __ballot(lane < S && rank == r0), h1 = __ballot(lane < S && rank == r1);
+  row0 = h0 ? __builtin_ctzll(h0) : r0;
+  row1 = h1 ? __builtin_ctzll(h1) : r1;
+}
+
 // One decode workgroup's work: workgroup index wg of a grid of num_wgs, with its
 // LDS in L (a kernel of its own launches it alone; the fused varlen kernel beside
-// the prefill tiles).
+// the prefill tiles).  ranked_row >= 0: the row of the ranked order (above) this
+// workgroup takes, found by the caller.
 template <typename T, int DK, int NW, bool WP, int NB, bool F8, bool PR>
 __device__ __forceinline__ void decode_wg(const RowsArgs& a, int block_shift, uint32_t grid_rows, uint32_t wg,
-                                          uint32_t num_wgs, DecodeLds<DK, NW, NB, F8>& L) {
+                                          uint32_t num_wgs, DecodeLds<DK, NW, NB, F8>& L, int ranked_row = -1) {
   // WP: each wave answers one (row, kv head, partition) alone -- NW > 1: the
   // workgroup's waves take NW consecutive kv heads of the same row and partition
   static_assert(NB >= 2 && NB <= 4, "2 to 4 tile buffers per wave");
@@ -205,24 +231,13 @@ __device__ __forceinline__ void decode_wg(const RowsArgs& a, int block_shift, ui
     pz = (int)(wg / (hkv_u * grid_rows));
   }
   const int lane = lane_id(), wave = threadIdx.x / kWave;
-  if (a.query_start_loc == nullptr && a.partition_size == 0 && grid_rows <= (uint32_t)kWave) {
-    // Unsplit decode of at most 64 rows: the r-th workgroup group takes the row with
-    // the r-th longest visible range (ties by index), so the longest rows start first
-    // and the last workgroups to be dispatched are the shortest.
-    const int S = (int)grid_rows, cap = a.max_blocks * a.block_size;
-    int len = -1;
-    if (lane < S) {
-      int nl = a.seq_lens[lane];
-      nl = nl < 0 ? 0 : (nl > cap ? cap : nl);
-      len = a.window > 0 && nl > a.window ? a.window : nl;
+  if (rows_ranked(a, grid_rows)) {
+    if (ranked_row >= 0) {
+      row = ranked_row;
+    } else {
+      int unused;
+      rows_by_rank(a, (int)grid_rows, row, row, row, unused);
     }
-    int rank = 0;
-    for (int r = 0; r < S; ++r) {
-      const int lr = __builtin_amdgcn_readlane(len, r);
-      rank += (lr > len) || (lr == len && r < lane);
-    }
-    const uint64_t hit = __ballot(lane < S && rank == row);
-    row = hit ? __builtin_ctzll(hit) : row;
   }
   int s, n, lo, hi, ref;
   int64_t q_row;
@@ -746,10 +761,17 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
   if constexpr (!WP) {
     if (paired_units > 0) {
       const uint32_t w = blockIdx.x, partner = paired_units - 1 - w;
-      decode_wg<T, DK, NW, WP, NB, F8, PR>(a, block_shift, grid_rows, w, paired_units, lds);
+      // both units' rows from one ranking, so the second unit starts at once
+      int row_w = -1, row_p = -1;
+      if (rows_ranked(a, grid_rows)) {
+        const uint32_t hkv_u = (uint32_t)(PR ? a.num_kv_heads / 2 : a.num_kv_heads);
+        rows_by_rank(a, (int)grid_rows, (int)((w / hkv_u) % grid_rows), (int)((partner / hkv_u) % grid_rows), row_w,
+                     row_p);
+      }
+      decode_wg<T, DK, NW, WP, NB, F8, PR>(a, block_shift, grid_rows, w, paired_units, lds, row_w);
       if (partner != w) {
         __syncthreads();  // the first unit's merge area becomes the second's tile ring
-        decode_wg<T, DK, NW, WP, NB, F8, PR>(a, block_shift, grid_rows, partner, paired_units, lds);
+        decode_wg<T, DK, NW, WP, NB, F8, PR>(a, block_shift, grid_rows, partner, paired_units, lds, row_p);
       }
       return;
     }

@@ -181,7 +181,8 @@ struct PrefillLds {
   static constexpr int VROW = DV + VPAD;
   __align__(16) uint16_t k[NBUF][kPrefillKeys][DK];
   __align__(16) uint16_t v[NBUF][kPrefillKeys][VROW];
-  int range_lo, range_hi, v_out_of_range;
+  int wave_lo[kPrefillThreads / kWave], wave_hi[kPrefillThreads / kWave];  // each wave's key range
+  int v_out_of_range;
 };
 
 // One prefill workgroup's work: workgroup index L of the tile grid, its LDS in sh (a
@@ -214,8 +215,6 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
   // 128-byte halves, and (r / 2) % 8 spreads eight of them over each half.
   auto& k_lds = sh.k;
   auto& v_lds = sh.v;
-  int& range_lo = sh.range_lo;
-  int& range_hi = sh.range_hi;
   int& v_out_of_range = sh.v_out_of_range;
 
   if (status_failed(a.status)) return;
@@ -281,11 +280,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
   // start of segment B in the key space, or past every key when B is empty
   const int seg_b = len_b > 0 ? base_b : 0x7fffffff;
 
-  if (tid == 0) {
-    range_lo = 0x7fffffff;
-    range_hi = 0;
-    v_out_of_range = 0;
-  }
+  if (tid == 0) v_out_of_range = 0;
 
   // --- this lane's two rows (one per 16-row block) --------------------------------
   int vis_lo[2], vis_hi[2];
@@ -343,20 +338,6 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
     for (int rb = 0; rb < 2; ++rb)
       slope_r[rb] = row_ok[rb] ? a.alibi[row_head[rb]] * (kLog2e / a.scale_log2) : 0.f;
   }
-  __syncthreads();
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-    if (vis_lo[rb] < vis_hi[rb]) {
-      atomicMin(&range_lo, vis_lo[rb]);
-      atomicMax(&range_hi, vis_hi[rb]);
-    }
-  // take the q loads' wait here, before any untracked K/V load is issued
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) asm volatile("" ::"v"(qb[rb][kk]));
-  __syncthreads();
-  const int klo = range_lo, khi = range_hi;
   // Wave-uniform bounds of the rows' visible ranges, for the per-tile tests:
   // [w_lo_min, w_hi_max) covers every non-empty range of this wave's rows, and a
   // tile inside [w_lo_max, w_hi_min) is seen whole by every row.
@@ -376,6 +357,26 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int L, Prefil
   w_hi_max = wave_max_i32(w_hi_max);
   w_lo_max = wave_max_i32(w_lo_max);
   w_hi_min = wave_min_i32(w_hi_min);
+  // The workgroup's key range [klo, khi): the union of its waves' ranges, one LDS
+  // word per wave.  (Not LDS atomics: with a divergent operand the compiler turns
+  // each into a 64-step loop on the scalar unit, which the CU's waves share; four of
+  // them per wave stalled every workgroup about 8 us.)
+  if (lane == 0) {
+    sh.wave_lo[wave] = w_lo_min;
+    sh.wave_hi[wave] = w_hi_max;
+  }
+  // take the q loads' wait here, before any untracked K/V load is issued
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) asm volatile("" ::"v"(qb[rb][kk]));
+  __syncthreads();
+  int klo = sh.wave_lo[0], khi = sh.wave_hi[0];
+#pragma unroll
+  for (int w = 1; w < NTH / kWave; ++w) {
+    klo = min(klo, sh.wave_lo[w]);
+    khi = max(khi, sh.wave_hi[w]);
+  }
   if (w_hi_min == 0x7fffffff) w_lo_max = 0x7fffffff;  // no row of the wave is real: mask every tile
   const bool wave_live = w_hi_min != 0x7fffffff;  // some row of the wave is real
 

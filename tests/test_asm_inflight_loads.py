@@ -10,7 +10,13 @@ by falling through, except where it certainly goes the other way: the load's blo
 is the fall-through of a branch on `vcc = exec & sX` with sX a uniform boolean
 (`s_cselect_b64 sX, -1, 0`), so sX is known on entry, and a later branch on a vcc
 formed from the same, unwritten sX is then taken for certain -- the scan follows
-its target instead of a fall-through path that cannot run."""
+its target instead of a fall-through path that cannot run.
+
+A second check: the tile kernels hold no LDS atomic and no loop over the lanes of a
+wave on the scalar unit (what the compiler makes of an atomic with a divergent
+operand: find the first active lane, read its value, fold it in, clear the lane,
+repeat).  The CU's waves share the scalar unit, so a few such loops per wave
+stall every workgroup for microseconds."""
 import os
 import re
 import shutil
@@ -301,3 +307,76 @@ def test_fused_varlen_kernel_no_register_reuse(device_asm, src, tname, f8):
         loads, bad = untracked_load_hazards(asm, kernel)
         assert loads > 0, kernel
         assert not bad, f"{kernel}: {bad[:3]}"
+
+
+_LDS_ATOMIC = re.compile(r"ds_(min|max|add|sub|rsub|inc|dec|and|or|xor|wrxchg|cmpst|cmpswap)_")
+
+
+def lane_serial_loops(asm, kernel):
+    """(LDS atomics, lane-serial loops) of a kernel.  A loop runs from a label the
+    compiler marks as a loop header to the first branch back to it; it is
+    lane-serial when it finds the first set bit of a lane mask (s_ff1_i32_b64)."""
+    i = asm.index(kernel + ":")
+    lines = [ln.strip() for ln in asm[i:asm.index(".Lfunc_end", i)].split("\n")]
+    atomics = [ln for ln in lines if _LDS_ATOMIC.match(ln)]
+    loops = []
+    for n, ln in enumerate(lines):
+        lab = _label(ln)
+        if lab is None or "Loop Header" not in ln:
+            continue
+        for m in range(n + 1, len(lines)):
+            op, ops = _parse(lines[m]) if lines[m] else ("", [])
+            if op.startswith(("s_cbranch", "s_branch")) and ops and ops[-1] == lab:
+                if any(t.startswith("s_ff1_i32_b64") for t in lines[n + 1:m]):
+                    loops.append(lab)
+                break
+    return atomics, loops
+
+
+_LOOP_FRAGMENTS = {
+    # an LDS min over divergent lanes, as the compiler expands it
+    "lane loop": ("""k:
+\ts_mov_b64 s[12:13], exec
+\ts_brev_b32 s20, -2
+.LBB3_40:                               ; =>This Inner Loop Header: Depth=1
+\ts_ff1_i32_b64 s21, s[12:13]
+\tv_readlane_b32 s24, v212, s21
+\ts_lshl_b64 s[22:23], 1, s21
+\ts_min_i32 s20, s20, s24
+\ts_andn2_b64 s[12:13], s[12:13], s[22:23]
+\ts_cmp_lg_u64 s[12:13], 0
+\ts_cbranch_scc1 .LBB3_40
+\tv_mov_b32_e32 v37, s20
+\tds_min_i32 v36, v37 offset:52224
+\ts_endpgm
+.Lfunc_end0:
+""", 1, 1),
+    # a find-first-lane outside any loop, and a loop without one
+    "single ff1, plain loop": ("""k:
+\ts_ff1_i32_b64 s4, vcc
+.LBB0_2:                                ; =>This Inner Loop Header: Depth=1
+\tv_add_u32_e32 v1, 1, v1
+\ts_add_i32 s5, s5, -1
+\ts_cmp_lg_u32 s5, 0
+\ts_cbranch_scc1 .LBB0_2
+\ts_endpgm
+.Lfunc_end0:
+""", 0, 0),
+}
+
+
+@pytest.mark.parametrize("name", sorted(_LOOP_FRAGMENTS))
+def test_lane_loop_scan_on_fragments(name):
+    asm, n_atomics, n_loops = _LOOP_FRAGMENTS[name]
+    atomics, loops = lane_serial_loops(asm, "k")
+    assert (len(atomics), len(loops)) == (n_atomics, n_loops), (atomics, loops)
+
+
+@pytest.mark.parametrize("src", SOURCES)
+def test_tile_kernels_no_lane_serial_loops(device_asm, src):
+    asm = device_asm[src]
+    kernels = re.findall(r"^(_ZN2pa(?:14prefill_kernel|19varlen_fused_kernel)\w+):", asm, re.M)
+    assert kernels, src
+    for kernel in kernels:
+        atomics, loops = lane_serial_loops(asm, kernel)
+        assert not atomics and not loops, f"{kernel}: {atomics[:2]} {loops[:2]}"
