@@ -787,10 +787,22 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const RowsArgs a, 
 constexpr int kWholeWaves = 8, kWholeBufs = 2;
 constexpr int kPartWaves = 4, kPartBufs = 2;
 constexpr int kOneWaveBufs = 2;
-// Split mode with at least this many (row, kv head, partition) items: one wave per
-// workgroup and partition.  Fewer items: kPartWaves waves share each partition, so
-// that every CU still gets enough waves.
-constexpr int64_t kOneWaveItems = 8192;
+// Split mode: one wave per (row, kv head, partition) item when there are at least
+// kOneWaveItems items, or when rows span at least kOneWaveParts partitions (so
+// nearly every item is a whole partition, long enough to amortise a wave's start)
+// and there are at least kOneWaveMinItems items (four waves per CU); otherwise
+// kPartWaves waves share each partition.  On the long-context workload (8 rows of
+// 32K-128K positions) one wave per item ran 0.72 / 0.73 / 0.78 of HBM at partitions
+// of 1024 / 2048 / 4096 against 0.63 / 0.67 / 0.66 shared (its fp8 version at 512:
+// 0.62 against 0.50); on the batched workload (64 rows of 512-4096, at most 8
+// partitions) sharing stayed ahead (0.63 against 0.61 at 512, 0.64 against 0.55 at
+// 1024).
+constexpr int64_t kOneWaveItems = 8192, kOneWaveMinItems = 1024;
+constexpr int kOneWaveParts = 16;
+inline bool one_wave_split(const RowsArgs& a, uint64_t items) {
+  return a.partition_size > 0 &&
+         ((int64_t)items >= kOneWaveItems || (a.max_partitions >= kOneWaveParts && (int64_t)items >= kOneWaveMinItems));
+}
 
 // fp8 tiles of 32 positions hold as many bytes as 16-bit tiles of 16: the same two
 // buffers per wave (unsplit: 8 waves x 2 x 8 KB = 128 KB of LDS).
@@ -838,7 +850,7 @@ hipError_t launch_decode_typed(const RowsArgs& a, int block_shift, int dk, int d
     // head: one workgroup per pair of kv heads (256-byte reads per slot)
     if (a.partition_size > 0 && a.num_kv_heads % 2 == 0 && 2 * a.group <= 16) {
       const uint64_t np = n / 2;
-      if ((int64_t)np >= kOneWaveItems)
+      if (one_wave_split(a, np))
         return launch_split_waves<T, true, true>(a, block_shift, rows, np, a.num_kv_heads / 2, stream);
       hipLaunchKernelGGL((decode_mfma_kernel<T, 128, kPartWaves, false, part_bufs, true, true>),
                          dim3((uint32_t)np), dim3(kPartWaves * 64), 0, stream, a, block_shift, rows, 0u);
@@ -849,7 +861,7 @@ hipError_t launch_decode_typed(const RowsArgs& a, int block_shift, int dk, int d
   // varlen kernel runs them beside prefill tiles: a row's bits then do not depend on
   // whether its batch holds prefill sequences.
   const bool varlen_rows = a.query_start_loc != nullptr && a.partition_size == 0 && !F8;
-  if (a.partition_size > 0 && (int64_t)n >= kOneWaveItems)
+  if (one_wave_split(a, n))
     return launch_split_waves<T, F8, false>(a, block_shift, rows, n, a.num_kv_heads, stream);
   if (a.partition_size > 0 || varlen_rows) {
     hipLaunchKernelGGL((decode_mfma_kernel<T, 128, kPartWaves, false, part_bufs, F8>), dim3((uint32_t)n),
